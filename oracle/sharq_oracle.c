@@ -1,0 +1,428 @@
+/*
+ * sharq_oracle.c -- TEST INFRASTRUCTURE ONLY.
+ *
+ * A plain, slow, obviously-correct CPU implementation of the SharQ sparse-dense
+ * FP4 linear layer, used to check the HIP path.  Only the test suite, the smoke
+ * check and the benchmark's CPU-baseline leg may load it.  It shares no code,
+ * header, table or helper with the HIP library, and the HIP library never calls it.
+ *
+ * What it follows (the pages: "SharQ: Bridging Activation Sparsity and FP4
+ * Quantization for LLM Inference", arXiv 2606.26587, as rendered on pith.science):
+ *   - abstract and "Core claim": per activation tensor, an input-adaptive N:M mask
+ *     picks an outlier-dominated sparse backbone; the backbone is quantized to FP4;
+ *     a dense residual is defined against the *quantized* backbone (not against the
+ *     unquantized sparse values) and is itself quantized to FP4 with its own scales;
+ *     a sparse FP4 GEMM over the backbone and a dense FP4 GEMM over the residual
+ *     share one FP4 weight payload and their outputs are summed.
+ *   - abstract: the method runs on the NVFP4, HiF4 and MXFP4 block formats.  The
+ *     pages cite, but do not reproduce, the OCP Microscaling specification and the
+ *     cuDNN block-scaling documentation; the format rules below are the plain
+ *     readings of those formats (listed with every other reading in the design notes).
+ *
+ * Readings taken where the pages are silent (all are also listed in the design notes):
+ *   R1 mask criterion: keep the n largest |x| in each group of m consecutive
+ *      elements along K; magnitude is compared on the bf16 bits with the sign
+ *      cleared; on equal magnitude the lower index wins.
+ *   R2 MX block scale: E = floor(log2(amax)) - 2 (2 = the E2M1 maximum exponent),
+ *      clamped to [-127, 127]; amax == 0 gives E = -127; stored as byte E + 127.
+ *   R3 E2M1 rounding: nearest value of {0,.5,1,1.5,2,3,4,6}; on an exact tie the
+ *      code whose lowest bit is 0 wins; magnitudes above 6 saturate to 6; the sign
+ *      bit is the sign of the scaled value (so a negative value that rounds to zero
+ *      gives code 0x8); positions the mask drops get code 0x0.
+ *   R4 residual: R = x - Bhat evaluated as one fp32 subtraction (exact for MXFP4).
+ *   R5 NVFP4: per-path tensor scale S = fp32(amax / 2688) (2688 = 6 * 448, S = 1
+ *      when amax == 0); 16-element block scale s = E4M3(fp32(amax_blk / fp32(6*S)))
+ *      rounded to nearest-even and saturated at 448; d = fp32(s * S);
+ *      code = E2M1(fp32(x / d)) (all 0x0 when d == 0); Bhat = fp32(value * d).
+ *   R6 packing: element 2c in the low nibble of byte c; scales row-major [rows,K/B];
+ *      mask bit k%8 of byte k/8.
+ *   R7 GEMM: Y = Bhat Ŵ^T + Rhat Ŵ^T, each a plain fp64 triple loop over dequantized
+ *      values, summed.
+ *
+ * Compile: gcc -O2 -ffp-contract=off -fno-fast-math -fopenmp -shared -fPIC.
+ * The row loops carry an OpenMP pragma; every output element has a fixed
+ * evaluation order, so results do not depend on the thread count.
+ */
+#include <math.h>
+#include <stdint.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+#include <stdlib.h>
+#include <string.h>
+
+#define ORACLE_MXFP4 0
+#define ORACLE_NVFP4 1
+
+/* ------------------------------------------------------------------ scalars */
+
+static float bf16_to_f32(uint16_t h) {
+  uint32_t u = (uint32_t)h << 16;
+  float f;
+  memcpy(&f, &u, 4);
+  return f;
+}
+
+/* The eight E2M1 magnitudes, indexed by the 3-bit magnitude code (1 sign bit,
+ * 2 exponent bits with bias 1, 1 mantissa bit; code 1 is the subnormal 0.5). */
+static const double kE2M1[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
+
+double oracle_e2m1_value(uint8_t code) {
+  double v = kE2M1[code & 7];
+  return (code & 8) ? -v : v;
+}
+
+/* R3: round |t| to the nearest E2M1 magnitude.  Walk the seven midpoints between
+ * neighbouring grid values; passing a midpoint moves to the upper neighbour, and
+ * sitting exactly on it moves up only when the upper neighbour's code is even.
+ * Anything above the last midpoint (5) ends at code 7 = 6.0, which is saturation. */
+uint8_t oracle_e2m1_encode(double t) {
+  double a = fabs(t);
+  uint8_t mag = 0;
+  for (int i = 0; i < 7; ++i) {
+    double mid = 0.5 * (kE2M1[i] + kE2M1[i + 1]);
+    int upper = i + 1;
+    if (a > mid || (a == mid && (upper & 1) == 0)) mag = (uint8_t)upper;
+  }
+  return (uint8_t)((signbit(t) ? 8 : 0) | mag);
+}
+
+/* R2: E8M0 exponent for a block whose largest magnitude is amax (exact value). */
+int oracle_mx_exponent(double amax) {
+  if (amax == 0.0) return -127;
+  int e2;
+  (void)frexp(amax, &e2); /* amax = f * 2^e2 with f in [0.5, 1): floor(log2) = e2 - 1 */
+  int e = (e2 - 1) - 2;
+  if (e < -127) e = -127;
+  if (e > 127) e = 127;
+  return e;
+}
+
+/* OCP E4M3 (bias 7, no infinities, max finite 448): value of an 8-bit code. */
+double oracle_e4m3_value(uint8_t code) {
+  int s = code >> 7, e = (code >> 3) & 15, m = code & 7;
+  double v;
+  if (e == 0) v = ldexp((double)m, -9); /* subnormal: m/8 * 2^-6 */
+  else v = ldexp(1.0 + m / 8.0, e - 7);
+  if (e == 15 && m == 7) v = NAN;
+  return s ? -v : v;
+}
+
+/* R5: non-negative q -> E4M3 code, round to nearest even, saturate at 448. */
+uint8_t oracle_e4m3_encode(float qf) {
+  double q = (double)qf;
+  if (!(q > 0.0)) return 0;
+  if (q >= 448.0) return 0x7E;
+  int e2;
+  (void)frexp(q, &e2);
+  int e = e2 - 1;                          /* floor(log2 q) */
+  double step = (e < -6) ? ldexp(1.0, -9)   /* subnormal spacing */
+                         : ldexp(1.0, e - 3);
+  double v = nearbyint(q / step) * step;    /* q/step is exact; nearbyint rounds half to even */
+  if (v >= 448.0) return 0x7E;              /* cannot pass 448 from below 448, kept for clarity */
+  if (v == 0.0) return 0;
+  (void)frexp(v, &e2);
+  e = e2 - 1;
+  if (e < -6) return (uint8_t)(v / ldexp(1.0, -9));
+  int mant = (int)((v / ldexp(1.0, e) - 1.0) * 8.0);
+  return (uint8_t)(((e + 7) << 3) | mant);
+}
+
+/* ------------------------------------------------------------------ the mask */
+
+/* R1: rank(j) = #{l in group : key(l) > key(j) or (key(l) == key(j) and l < j)};
+ * keep(j) <=> rank(j) < n. */
+static void mask_group(const uint16_t* xg, int n, int m, uint8_t* keep) {
+  for (int j = 0; j < m; ++j) {
+    uint16_t kj = xg[j] & 0x7FFF;
+    int rank = 0;
+    for (int l = 0; l < m; ++l) {
+      uint16_t kl = xg[l] & 0x7FFF;
+      if (kl > kj || (kl == kj && l < j)) ++rank;
+    }
+    keep[j] = rank < n;
+  }
+}
+
+/* ---------------------------------------------------------- block quantizers */
+
+/* MXFP4 block of 32 values v[] (exact, held as float).  Writes 32 codes, returns the
+ * scale byte.  When keep != NULL, positions with keep[i] == 0 are dropped: they get
+ * code 0x0 and take no part in the block maximum. */
+static uint8_t mx_block(const float* v, const uint8_t* keep, uint8_t* codes) {
+  double amax = 0.0;
+  for (int i = 0; i < 32; ++i)
+    if (!keep || keep[i]) {
+      double a = fabs((double)v[i]);
+      if (a > amax) amax = a;
+    }
+  int e = oracle_mx_exponent(amax);
+  for (int i = 0; i < 32; ++i) {
+    if (keep && !keep[i]) codes[i] = 0;
+    else codes[i] = oracle_e2m1_encode(ldexp((double)v[i], -e)); /* exact power-of-two scaling */
+  }
+  return (uint8_t)(e + 127);
+}
+
+static float mx_dequant(uint8_t code, uint8_t scale_byte) {
+  return (float)ldexp(oracle_e2m1_value(code), (int)scale_byte - 127);
+}
+
+/* NVFP4 tensor scale from a tensor maximum (R5). */
+float oracle_nv_tensor_scale(float amax) {
+  if (amax == 0.0f) return 1.0f;
+  return amax / 2688.0f;
+}
+
+/* NVFP4 block of 16 values with tensor scale S.  Fills codes, returns the E4M3 byte. */
+static uint8_t nv_block(const float* v, const uint8_t* keep, float S, uint8_t* codes) {
+  float amax = 0.0f;
+  for (int i = 0; i < 16; ++i)
+    if (!keep || keep[i]) {
+      float a = fabsf(v[i]);
+      if (a > amax) amax = a;
+    }
+  float six_s = 6.0f * S;
+  float q = amax / six_s;
+  uint8_t sb = oracle_e4m3_encode(q);
+  float d = (float)oracle_e4m3_value(sb) * S;
+  for (int i = 0; i < 16; ++i) {
+    if ((keep && !keep[i]) || d == 0.0f) codes[i] = 0;
+    else {
+      float t = v[i] / d;
+      codes[i] = oracle_e2m1_encode((double)t);
+    }
+  }
+  return sb;
+}
+
+static float nv_dequant(uint8_t code, uint8_t sb, float S) {
+  float d = (float)oracle_e4m3_value(sb) * S;
+  float val = (float)oracle_e2m1_value(code);
+  return val * d;
+}
+
+static void put_code(uint8_t* row_codes, int64_t k, uint8_t code) {
+  uint8_t* b = row_codes + (k >> 1);
+  if (k & 1) *b = (uint8_t)((*b & 0x0F) | (code << 4));
+  else *b = (uint8_t)((*b & 0xF0) | (code & 0x0F));
+}
+
+static uint8_t get_code(const uint8_t* row_codes, int64_t k) {
+  uint8_t b = row_codes[k >> 1];
+  return (k & 1) ? (uint8_t)(b >> 4) : (uint8_t)(b & 0x0F);
+}
+
+/* ------------------------------------------------------------ entry points */
+
+/* Validates the arguments shared by every entry point. */
+static int check_shape(int64_t rows, int64_t K, int64_t ld, int fmt) {
+  if (rows < 0 || K <= 0 || ld < K) return -1;
+  if (fmt == ORACLE_MXFP4 && K % 32) return -1;
+  if (fmt == ORACLE_NVFP4 && K % 16) return -1;
+  if (fmt != ORACLE_MXFP4 && fmt != ORACLE_NVFP4) return -1;
+  return 0;
+}
+
+/* Plain FP4 quantization of a bf16 matrix (no mask, no residual): what a weight
+ * payload holds.  codes [rows,K/2], scales [rows,K/B], tscale (NVFP4 only). */
+int oracle_quantize(const uint16_t* x, int64_t rows, int64_t K, int64_t ldx, int fmt,
+                    uint8_t* codes, uint8_t* scales, float* tscale) {
+  if (check_shape(rows, K, ldx, fmt)) return -1;
+  const int B = fmt == ORACLE_MXFP4 ? 32 : 16;
+  float S = 1.0f;
+  if (fmt == ORACLE_NVFP4) {
+    float amax = 0.0f;
+    for (int64_t i = 0; i < rows; ++i)
+      for (int64_t k = 0; k < K; ++k) {
+        float a = fabsf(bf16_to_f32(x[i * ldx + k]));
+        if (a > amax) amax = a;
+      }
+    S = oracle_nv_tensor_scale(amax);
+    if (tscale) *tscale = S;
+  }
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < rows; ++i) {
+    float v[32];
+    uint8_t c[32];
+    for (int64_t kb = 0; kb < K / B; ++kb) {
+      for (int j = 0; j < B; ++j) v[j] = bf16_to_f32(x[i * ldx + kb * B + j]);
+      uint8_t sb = fmt == ORACLE_MXFP4 ? mx_block(v, NULL, c) : nv_block(v, NULL, S, c);
+      scales[i * (K / B) + kb] = sb;
+      for (int j = 0; j < B; ++j) put_code(codes + i * (K / 2), kb * B + j, c[j]);
+    }
+  }
+  return 0;
+}
+
+/* The SharQ activation preparation (abstract; "Core claim"): mask, FP4 backbone,
+ * residual against the dequantized backbone, FP4 residual.
+ * Inputs:  x bf16 [M, ldx] (first K columns used), pattern n:m along K.
+ * Outputs: backbone codes/scales/tscale, residual codes/scales/tscale (layouts R6),
+ *          optional mask bits [M, K/8]; optional fp32 views of Bhat and R [M, K]
+ *          (bhat_out, resid_out; either may be NULL) for the invariant checks. */
+int oracle_prep(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, int n, int m, int fmt,
+                uint8_t* b_codes, uint8_t* b_scales, float* b_tscale,
+                uint8_t* r_codes, uint8_t* r_scales, float* r_tscale,
+                uint8_t* mask_bits, float* bhat_out, float* resid_out) {
+  if (check_shape(M, K, ldx, fmt)) return -1;
+  if (!((n == 2 && m == 4) || (n == 4 && m == 8))) return -2;
+  const int B = fmt == ORACLE_MXFP4 ? 32 : 16;
+  const int64_t nb = K / B;
+
+  /* Step 1 (both formats): the mask, as bytes. */
+  uint8_t* keep = (uint8_t*)malloc((size_t)(M > 0 ? M : 1) * (size_t)K);
+  float* resid = (float*)malloc(sizeof(float) * (size_t)(M > 0 ? M : 1) * (size_t)K);
+  if (!keep || !resid) { free(keep); free(resid); return -3; }
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < M; ++i)
+    for (int64_t g = 0; g < K / m; ++g) mask_group(x + i * ldx + g * m, n, m, keep + i * K + g * m);
+
+  /* NVFP4 backbone tensor scale: amax over the kept values (R5). */
+  float Sb = 1.0f, Sr = 1.0f;
+  if (fmt == ORACLE_NVFP4) {
+    float amax = 0.0f;
+    for (int64_t i = 0; i < M; ++i)
+      for (int64_t k = 0; k < K; ++k)
+        if (keep[i * K + k]) {
+          float a = fabsf(bf16_to_f32(x[i * ldx + k]));
+          if (a > amax) amax = a;
+        }
+    Sb = oracle_nv_tensor_scale(amax);
+  }
+
+  /* Step 2: backbone quantization and the residual R = x - Bhat (R4). */
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < M; ++i) {
+    float v[32], bh;
+    uint8_t c[32];
+    for (int64_t kb = 0; kb < nb; ++kb) {
+      const int64_t k0 = kb * B;
+      for (int j = 0; j < B; ++j) {
+        float xv = bf16_to_f32(x[i * ldx + k0 + j]);
+        v[j] = keep[i * K + k0 + j] ? xv : 0.0f; /* dropped positions hold +0 */
+      }
+      uint8_t sb = fmt == ORACLE_MXFP4 ? mx_block(v, keep + i * K + k0, c)
+                                       : nv_block(v, keep + i * K + k0, Sb, c);
+      b_scales[i * nb + kb] = sb;
+      for (int j = 0; j < B; ++j) {
+        put_code(b_codes + i * (K / 2), k0 + j, c[j]);
+        bh = fmt == ORACLE_MXFP4 ? mx_dequant(c[j], sb) : nv_dequant(c[j], sb, Sb);
+        float xv = bf16_to_f32(x[i * ldx + k0 + j]);
+        float r = xv - bh;
+        resid[i * K + k0 + j] = r;
+        if (bhat_out) bhat_out[i * K + k0 + j] = bh;
+        if (resid_out) resid_out[i * K + k0 + j] = r;
+      }
+    }
+  }
+
+  /* NVFP4 residual tensor scale: amax over all of R. */
+  if (fmt == ORACLE_NVFP4) {
+    float amax = 0.0f;
+    for (int64_t t = 0; t < M * K; ++t) {
+      float a = fabsf(resid[t]);
+      if (a > amax) amax = a;
+    }
+    Sr = oracle_nv_tensor_scale(amax);
+  }
+
+  /* Step 3: residual quantization with its own scales (all K positions). */
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < M; ++i) {
+    uint8_t c[32];
+    for (int64_t kb = 0; kb < nb; ++kb) {
+      const float* v = resid + i * K + kb * B;
+      uint8_t sb = fmt == ORACLE_MXFP4 ? mx_block(v, NULL, c) : nv_block(v, NULL, Sr, c);
+      r_scales[i * nb + kb] = sb;
+      for (int j = 0; j < B; ++j) put_code(r_codes + i * (K / 2), kb * B + j, c[j]);
+    }
+  }
+
+  if (fmt == ORACLE_NVFP4) {
+    if (b_tscale) *b_tscale = Sb;
+    if (r_tscale) *r_tscale = Sr;
+  }
+  if (mask_bits) {
+    for (int64_t i = 0; i < M; ++i)
+      for (int64_t k8 = 0; k8 < K / 8; ++k8) {
+        uint8_t byte = 0;
+        for (int b = 0; b < 8; ++b) byte |= (uint8_t)(keep[i * K + k8 * 8 + b] << b);
+        mask_bits[i * (K / 8) + k8] = byte;
+      }
+  }
+  free(keep);
+  free(resid);
+  return 0;
+}
+
+/* Dequantize one FP4 payload row-block into fp64 (exact: every product of an
+ * E2M1 value, an E8M0/E4M3 scale and an fp32 tensor scale fits in 53 bits). */
+int oracle_dequant(const uint8_t* codes, const uint8_t* scales, float tscale, int64_t rows,
+                   int64_t K, int fmt, double* out) {
+  if (check_shape(rows, K, K, fmt)) return -1;
+  const int B = fmt == ORACLE_MXFP4 ? 32 : 16;
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < rows; ++i)
+    for (int64_t k = 0; k < K; ++k) {
+      uint8_t c = get_code(codes + i * (K / 2), k);
+      uint8_t s = scales[i * (K / B) + k / B];
+      double v = oracle_e2m1_value(c);
+      out[i * K + k] = fmt == ORACLE_MXFP4 ? ldexp(v, (int)s - 127)
+                                           : v * oracle_e4m3_value(s) * (double)tscale;
+    }
+  return 0;
+}
+
+/* R7: Y[r, o] = sum_k Bhat[i,k] W[o,k] + sum_k Rhat[i,k] W[o,k], fp64, for the
+ * selected activation rows i = rows_sel[r] (all M rows when rows_sel == NULL,
+ * n_sel == M).  Y is [n_sel, N] row-major. */
+int oracle_linear(const uint8_t* b_codes, const uint8_t* b_scales, float b_tscale,
+                  const uint8_t* r_codes, const uint8_t* r_scales, float r_tscale,
+                  int64_t M, const uint8_t* w_codes, const uint8_t* w_scales, float w_tscale,
+                  int64_t N, int64_t K, int fmt, const int64_t* rows_sel, int64_t n_sel,
+                  double* y) {
+  if (check_shape(M, K, K, fmt) || N <= 0 || n_sel < 0) return -1;
+  const int B = fmt == ORACLE_MXFP4 ? 32 : 16;
+  double* wd = (double*)malloc(sizeof(double) * (size_t)N * (size_t)K);
+  if (!wd) return -3;
+  oracle_dequant(w_codes, w_scales, w_tscale, N, K, fmt, wd);
+  int bad = 0;
+#pragma omp parallel for schedule(dynamic)
+  for (int64_t r = 0; r < n_sel; ++r) {
+    int64_t i = rows_sel ? rows_sel[r] : r;
+    if (i < 0 || i >= M) { bad = 1; continue; }
+    double* bd = (double*)malloc(sizeof(double) * (size_t)K * 2);
+    if (!bd) { bad = 1; continue; }
+    double* rd = bd + K;
+    oracle_dequant(b_codes + i * (K / 2), b_scales + i * (K / B), b_tscale, 1, K, fmt, bd);
+    oracle_dequant(r_codes + i * (K / 2), r_scales + i * (K / B), r_tscale, 1, K, fmt, rd);
+    for (int64_t o = 0; o < N; ++o) {
+      const double* w = wd + o * K;
+      double yb = 0.0, yr = 0.0;
+      for (int64_t k = 0; k < K; ++k) yb += bd[k] * w[k]; /* backbone GEMM */
+      for (int64_t k = 0; k < K; ++k) yr += rd[k] * w[k]; /* residual GEMM */
+      y[r * N + o] = yb + yr;
+    }
+    free(bd);
+  }
+  free(wd);
+  return bad ? -1 : 0;
+}
+
+/* Element-wise helpers exported for the pins. */
+void oracle_e2m1_encode_array(const float* t, int64_t n, uint8_t* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = oracle_e2m1_encode((double)t[i]);
+}
+
+void oracle_e4m3_encode_array(const float* q, int64_t n, uint8_t* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = oracle_e4m3_encode(q[i]);
+}
+
+int oracle_omp_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}

@@ -1,0 +1,479 @@
+"""Pins for the CPU oracle: each check ties the oracle to something other than
+itself -- brute force over every code, closed-form properties, exact rational
+arithmetic, hand-worked examples, or identities the method fixes.
+
+Method: SharQ (arXiv 2606.26587), abstract and "Core claim": N:M top-|x| mask,
+FP4 backbone, dense residual against the dequantized backbone, FP4 residual, two
+FP4 GEMMs over one weight payload.  Format rules: the readings listed in the
+oracle's header (OCP MX E8M0/E2M1; NVFP4 with E4M3 block scales).
+"""
+import itertools
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+from activation_sparsity_fp4_sharq_amd.workloads import (WORKLOADS, adversarial_activation,
+                                                          bf16_bits_to_f32, f32_to_bf16_bits,
+                                                          make_activation, make_inputs)
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+E2M1_MAG = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+CODE_VALUES = np.array([(-1.0 if c & 8 else 1.0) * E2M1_MAG[c & 7] for c in range(16)])
+
+
+# ------------------------------------------------------------ independent decoders
+
+def unpack_codes(packed, K):
+    """[rows, K/2] bytes -> [rows, K] 4-bit codes, element 2c in the low nibble."""
+    packed = np.asarray(packed, np.uint8)
+    out = np.empty((packed.shape[0], K), np.uint8)
+    out[:, 0::2] = packed & 0x0F
+    out[:, 1::2] = packed >> 4
+    return out
+
+
+def e4m3_table():
+    """Values of the 127 finite non-negative E4M3 codes, from the format's fields."""
+    vals = []
+    for c in range(127):
+        e, m = c >> 3, c & 7
+        vals.append(m / 8.0 * 2.0 ** -6 if e == 0 else (1 + m / 8.0) * 2.0 ** (e - 7))
+    return np.array(vals)
+
+
+def decode_mx(codes_packed, scales, K):
+    c = unpack_codes(codes_packed, K)
+    v = CODE_VALUES[c]
+    e = np.repeat(scales.astype(np.int64) - 127, 32, axis=1)
+    return np.ldexp(v, e)
+
+
+def decode_nv(codes_packed, scales, tscale, K):
+    c = unpack_codes(codes_packed, K)
+    v = CODE_VALUES[c]
+    s = e4m3_table()[np.repeat(scales.astype(np.int64), 16, axis=1)]
+    return v * s * float(tscale)
+
+
+def x_values(bits):
+    return bf16_bits_to_f32(bits).astype(np.float64)
+
+
+# ------------------------------------------------------------ E2M1: brute force
+
+def _pick(cand):
+    even = cand & ((np.arange(cand.shape[1]) & 1) == 0)[None, :]
+    return np.where(even.any(1), even.argmax(1), cand.argmax(1)).astype(np.uint8)
+
+
+def brute_e2m1(t):
+    """Argmin over all 16 codes of |t - value|; the sign bit must match t's sign;
+    among equally near codes the one with a zero lowest bit (even mantissa).
+    Distances are exact: float64 for |t| < 2^10 (fp32 inputs there sit at least
+    2^-26 away from any midpoint, far above float64 rounding), Fractions above."""
+    t = np.asarray(t, np.float64)
+    sign_ok = (np.arange(16)[None, :] >= 8) == np.signbit(t)[:, None]
+    d = np.abs(t[:, None] - CODE_VALUES[None, :])
+    cand = (d == d.min(1, keepdims=True)) & sign_ok
+    big = np.nonzero(np.abs(t) >= 1024.0)[0]
+    vals = [Fraction(float(v)) for v in CODE_VALUES]
+    for i in big:
+        ft = Fraction(float(t[i]))
+        dist = [abs(ft - v) for v in vals]
+        dm = min(dist)
+        cand[i] = np.array([x == dm for x in dist]) & sign_ok[i]
+    return _pick(cand)
+
+
+def test_e2m1_every_bf16_pattern():
+    bits = np.arange(0, 1 << 16, dtype=np.uint32).astype(np.uint16)
+    t = bf16_bits_to_f32(bits)
+    t = t[np.isfinite(t)]
+    assert np.array_equal(oracle.e2m1_encode(t), brute_e2m1(t.astype(np.float64)))
+
+
+def test_e2m1_fp32_neighbourhoods_of_midpoints():
+    """fp32 values (up to 24 significant bits, as residuals have) around every grid
+    value and every midpoint, both signs, plus random fp32 in the active range."""
+    pts = sorted(set(E2M1_MAG) | {0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 7.0, 8.0})
+    vals = []
+    for p in pts:
+        for sgn in (1.0, -1.0):
+            x = np.float32(sgn * p)
+            up, dn = x, x
+            for _ in range(64):
+                up = np.nextafter(up, np.float32(np.inf))
+                dn = np.nextafter(dn, np.float32(-np.inf))
+                vals += [up, dn]
+            vals.append(x)
+    rng = np.random.default_rng(1)
+    r = (rng.random(200000) * 16 - 8).astype(np.float32)
+    t = np.concatenate([np.array(vals, np.float32), r, np.array([0.0, -0.0], np.float32)])
+    assert np.array_equal(oracle.e2m1_encode(t), brute_e2m1(t.astype(np.float64)))
+
+
+# ------------------------------------------------------------ E8M0 exponent
+
+def test_mx_exponent_brackets_block_max():
+    """Unclamped, the scaled block maximum lands in [4, 8): its exponent is the
+    largest E2M1 exponent (2).  Clamped at -127 below; zero gives -127."""
+    rng = np.random.default_rng(2)
+    samples = list(rng.random(2000) * 10.0 ** rng.integers(-40, 38, 2000))
+    samples += [2.0 ** k for k in range(-149, 128)] + [3 * 2.0 ** k for k in range(-140, 126)]
+    for a in samples:
+        a = float(np.float32(a))
+        if a == 0.0:
+            continue
+        e = oracle.mx_exponent(a)
+        if e > -127:
+            assert 4 * 2.0 ** e <= a < 8 * 2.0 ** e, (a, e)
+        else:
+            assert a < 8 * 2.0 ** -127, (a, e)
+    assert oracle.mx_exponent(0.0) == -127
+
+
+# ------------------------------------------------------------ E4M3: brute force
+
+def brute_e4m3(q):
+    """Nearest of the 127 finite non-negative codes, ties to the even code.  Inputs
+    are limited to [0, 2^20) so that float64 distances are exact."""
+    tab = e4m3_table()
+    q = np.asarray(q, np.float64)
+    assert np.all(q < 2.0 ** 20)
+    d = np.abs(q[:, None] - tab[None, :])
+    return _pick(d == d.min(1, keepdims=True))
+
+
+def test_e4m3_bruteforce_all_finite_codes():
+    tab = e4m3_table().astype(np.float32)
+    vals = [tab, (tab[:-1] + np.diff(tab) / 2).astype(np.float32)]  # exact midpoints (fp32-exact)
+    nb = []
+    for v in np.concatenate(vals):
+        up, dn = np.float32(v), np.float32(v)
+        for _ in range(3):
+            up = np.nextafter(up, np.float32(np.inf))
+            dn = np.nextafter(dn, np.float32(0))
+            nb += [up, dn]
+    rng = np.random.default_rng(3)
+    r = (rng.random(100000) * 2.0 ** rng.integers(-14, 10, 100000)).astype(np.float32)
+    big = np.array([448, 449, 463.9, 464, 480, 1e5, 9e5], np.float32)
+    q = np.concatenate(vals + [np.array(nb, np.float32), r, big, np.zeros(1, np.float32)])
+    assert np.array_equal(oracle.e4m3_encode(q), brute_e4m3(q))
+
+
+# ------------------------------------------------------------ hand-worked examples
+
+def _golden():
+    with open(os.path.join(GOLDEN, "hand_examples.json")) as f:
+        return json.load(f)["examples"]
+
+
+def _num(v):
+    return -0.0 if v == "-0" else float(v)
+
+
+@pytest.mark.parametrize("ex", _golden(), ids=lambda e: e["name"])
+def test_hand_examples(ex):
+    x = np.array([_num(v) for v in ex["x"]], np.float32)[None, :]
+    xb = f32_to_bf16_bits(x)
+    assert np.array_equal(bf16_bits_to_f32(xb), x), "example values must be bf16-exact"
+    fmt = oracle.MXFP4 if ex["fmt"] == "mxfp4" else oracle.NVFP4
+    K = x.shape[1]
+    bb, rr, mask, bhat, resid = oracle.prep(xb, ex["n"], ex["m"], fmt, want_values=True)
+    assert mask[0].tolist() == ex["mask_bytes"]
+    assert unpack_codes(bb.codes, K)[0].tolist() == ex["backbone_codes"]
+    assert bb.scales[0].tolist() == ex["backbone_scales"]
+    assert unpack_codes(rr.codes, K)[0].tolist() == ex["residual_codes"]
+    assert rr.scales[0].tolist() == ex["residual_scales"]
+    want_r = np.array([_num(v) for v in ex["residual"]], np.float32)
+    assert np.array_equal(resid[0].view(np.uint32), want_r.view(np.uint32)), "signed zeros too"
+    if fmt == oracle.NVFP4:
+        assert bb.tscale == ex["backbone_tensor_scale"]
+        assert rr.tscale == ex["residual_tensor_scale"]
+
+
+# ------------------------------------------------------------ the mask: brute force
+
+def brute_mask_group(keys, n):
+    """Subset of size n maximising the key sum; among equal sums the
+    lexicographically smallest index tuple."""
+    best = None
+    for sub in itertools.combinations(range(len(keys)), n):
+        s = sum(keys[j] for j in sub)
+        if best is None or s > best[0]:
+            best = (s, sub)
+    return set(best[1])
+
+
+@pytest.mark.parametrize("n,m,levels", [(2, 4, [0.0, 1.0, 2.0, 3.0]), (4, 8, [0.0, 1.0, 2.0])])
+def test_mask_exhaustive_small_integers(n, m, levels):
+    combos = list(itertools.product(range(len(levels)), repeat=m))
+    rng = np.random.default_rng(4)
+    per_row = 32 // m
+    rows = (len(combos) + per_row - 1) // per_row
+    x = np.zeros((rows, 32), np.float32)
+    flat = x.reshape(-1, m)
+    for gi, c in enumerate(combos):
+        sign = np.where(rng.random(m) < 0.5, -1.0, 1.0)
+        flat[gi] = np.array([levels[j] for j in c]) * sign
+    xb = f32_to_bf16_bits(x)
+    _, _, mask = oracle.prep(xb, n, m, oracle.MXFP4)
+    bits = np.unpackbits(mask, axis=1, bitorder="little").reshape(-1, m)
+    keys = (xb & 0x7FFF).reshape(-1, m).astype(np.int64)
+    for gi in range(len(combos)):
+        want = brute_mask_group(list(keys[gi]), n)
+        got = set(np.nonzero(bits[gi])[0].tolist())
+        assert got == want, (gi, keys[gi], got, want)
+
+
+# ------------------------------------------------------------ invariants (MXFP4)
+
+def _random_x(M, K, seed):
+    rng = np.random.default_rng(seed)
+    return make_activation(rng, M, K, "student_t3", n_out=max(1, K // 64), out_scale=30.0,
+                           token_sigma=0.5)
+
+
+@pytest.mark.parametrize("n,m", [(2, 4), (4, 8)])
+@pytest.mark.parametrize("kind", ["random", "adversarial"])
+def test_mx_invariants(n, m, kind):
+    M, K = 48, 256
+    xb = _random_x(M, K, 5) if kind == "random" else adversarial_activation(M, K, seed=6)
+    x = x_values(xb)
+    bb, rr, mask, bhat, resid = oracle.prep(xb, n, m, oracle.MXFP4, want_values=True)
+    keep = np.unpackbits(mask, axis=1, bitorder="little").astype(bool)
+    # exactly n kept per group
+    assert np.all(keep.reshape(M, K // m, m).sum(-1) == n)
+    # dropped positions carry the +0 code
+    bcodes = unpack_codes(bb.codes, K)
+    assert np.all(bcodes[~keep] == 0)
+    # the backbone scale equals the plain MXFP4 scale of X (each group's max is kept)
+    plain = oracle.quantize(xb, oracle.MXFP4)
+    assert np.array_equal(bb.scales, plain.scales)
+    # Bhat is what the codes and scales decode to
+    bdec = decode_mx(bb.codes, bb.scales, K)
+    assert np.array_equal(bdec, bhat.astype(np.float64))
+    # residual against the *quantized* backbone: Bhat + R == X exactly
+    assert np.array_equal(bhat.astype(np.float64) + resid.astype(np.float64), x)
+    # residual quantization error bound |R - Rhat| <= 2^(E_R + 1)
+    rdec = decode_mx(rr.codes, rr.scales, K)
+    er = np.repeat(rr.scales.astype(np.int64) - 127, 32, axis=1)
+    assert np.all(np.abs(resid.astype(np.float64) - rdec) <= np.ldexp(1.0, er + 1))
+    # the residual scale is R's own plain MXFP4 scale: scaled max lands in [4, 8)
+    ramax = np.abs(resid.astype(np.float64)).reshape(M, K // 32, 32).max(-1)
+    e = rr.scales.astype(np.int64) - 127
+    nz = (ramax > 0) & (e > -127)
+    assert np.all(ramax[nz] >= np.ldexp(4.0, e[nz])) and np.all(ramax[nz] < np.ldexp(8.0, e[nz]))
+    assert np.all(rr.scales[ramax == 0] == 0)
+
+
+@pytest.mark.parametrize("k", [-3, 1, 5])
+def test_mx_power_of_two_scaling(k):
+    M, K = 16, 128
+    rng = np.random.default_rng(7)
+    x = rng.standard_normal((M, K)).astype(np.float32)
+    xb = f32_to_bf16_bits(x)
+    xs = f32_to_bf16_bits(bf16_bits_to_f32(xb) * np.float32(2.0 ** k))
+    a = oracle.prep(xb, 2, 4)
+    b = oracle.prep(xs, 2, 4)
+    assert np.array_equal(a[2], b[2])
+    for pa, pb in ((a[0], b[0]), (a[1], b[1])):
+        assert np.array_equal(pa.codes, pb.codes)
+        nz = pa.scales > 0
+        assert np.array_equal(pb.scales[nz].astype(int), pa.scales[nz].astype(int) + k)
+
+
+def test_mx_negation_flips_sign_bits():
+    M, K = 16, 128
+    xb = _random_x(M, K, 8)
+    nb = xb ^ np.uint16(0x8000)
+    a_b, a_r, a_m, _, a_res = oracle.prep(xb, 2, 4, want_values=True)
+    b_b, b_r, b_m, _, _ = oracle.prep(nb, 2, 4, want_values=True)
+    assert np.array_equal(a_m, b_m)
+    keep = np.unpackbits(a_m, axis=1, bitorder="little").astype(bool)
+    ca, cb = unpack_codes(a_b.codes, K), unpack_codes(b_b.codes, K)
+    assert np.array_equal(ca[keep] ^ 8, cb[keep])
+    assert np.array_equal(a_b.scales, b_b.scales) and np.array_equal(a_r.scales, b_r.scales)
+    ra, rb = unpack_codes(a_r.codes, K), unpack_codes(b_r.codes, K)
+    nonzero = a_res != 0
+    assert np.array_equal(ra[nonzero] ^ 8, rb[nonzero])
+
+
+@pytest.mark.parametrize("n,m", [(2, 4), (4, 8)])
+def test_mx_zero_residual_on_representable_sparse_input(n, m):
+    """X already n:m sparse and exactly an E2M1 value times 2^e per block, with each
+    block's maximum code 4 or 6: the backbone reproduces X, so R == 0, the residual
+    codes are all 0x0 with scale byte 0x00, and the backbone codes are the generating ones."""
+    M, K = 32, 256
+    rng = np.random.default_rng(9)
+    codes = np.zeros((M, K), np.uint8)
+    for i in range(M):
+        for g in range(K // m):
+            pos = rng.choice(m, n, replace=False)
+            codes[i, g * m + pos] = rng.integers(1, 8, n) | (rng.integers(0, 2, n) << 3)
+        for b in range(K // 32):
+            blk = codes[i, b * 32:(b + 1) * 32]
+            j = np.nonzero(blk)[0][0]
+            if max(blk & 7) < 6:  # make the block maximum 4.0 or 6.0 (magnitude code 6 or 7)
+                blk[j] = (blk[j] & 8) | rng.choice([6, 7])
+    e = rng.integers(-30, 30, (M, K // 32))
+    x = (CODE_VALUES[codes] * np.ldexp(1.0, np.repeat(e, 32, axis=1))).astype(np.float32)
+    xb = f32_to_bf16_bits(x)
+    assert np.array_equal(bf16_bits_to_f32(xb).astype(np.float64), x.astype(np.float64))
+    bb, rr, mask, _, resid = oracle.prep(xb, n, m, want_values=True)
+    assert np.all(resid == 0)
+    assert np.all(rr.codes == 0) and np.all(rr.scales == 0)
+    got = unpack_codes(bb.codes, K)
+    assert np.array_equal(got, codes)
+    assert np.array_equal(bb.scales.astype(np.int64) - 127, e)
+
+
+def test_mx_all_zero_input():
+    xb = np.zeros((4, 64), np.uint16)
+    bb, rr, mask = oracle.prep(xb, 2, 4)
+    assert np.all(bb.codes == 0) and np.all(bb.scales == 0)
+    assert np.all(rr.codes == 0) and np.all(rr.scales == 0)
+    bits = np.unpackbits(mask, axis=1, bitorder="little").reshape(4, 16, 4)
+    assert np.all(bits[..., :2] == 1) and np.all(bits[..., 2:] == 0)  # lower indices on ties
+
+
+def test_prep_rejects_bad_arguments():
+    with pytest.raises(ValueError):
+        oracle.prep(np.zeros((2, 48), np.uint16), 2, 4)       # K not a multiple of 32
+    with pytest.raises(ValueError):
+        oracle.prep(np.zeros((2, 64), np.uint16), 3, 4)       # unsupported pattern
+    # empty input is fine
+    bb, rr, mask = oracle.prep(np.zeros((0, 64), np.uint16), 2, 4)
+    assert bb.codes.shape == (0, 32)
+
+
+# ------------------------------------------------------------ GEMM: exact arithmetic
+
+def _frac_decode_mx(p, K):
+    c = unpack_codes(p.codes, K)
+    rows = []
+    for i in range(c.shape[0]):
+        row = []
+        for k in range(K):
+            v = Fraction(CODE_VALUES[c[i, k]]).limit_denominator(2)
+            row.append(v * Fraction(2) ** (int(p.scales[i, k // 32]) - 127))
+        rows.append(row)
+    return rows
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 1, 32), (3, 4, 64), (4, 2, 128), (2, 3, 96)])
+def test_linear_matches_exact_rationals(M, N, K):
+    rng = np.random.default_rng(10 + K)
+    xb = make_activation(rng, M, K, "normal", n_out=1, out_scale=20.0)
+    wb = f32_to_bf16_bits(rng.normal(0, 0.02, (N, K)).astype(np.float32))
+    bb, rr, _ = oracle.prep(xb, 2, 4)
+    w = oracle.quantize(wb)
+    y = oracle.linear(bb, rr, w)
+    B, R, W = _frac_decode_mx(bb, K), _frac_decode_mx(rr, K), _frac_decode_mx(w, K)
+    for i in range(M):
+        for o in range(N):
+            exact = sum(B[i][k] * W[o][k] for k in range(K)) + sum(R[i][k] * W[o][k] for k in range(K))
+            mag = sum(abs(B[i][k] * W[o][k]) + abs(R[i][k] * W[o][k]) for k in range(K))
+            assert abs(Fraction(y[i, o]) - exact) <= Fraction(2 * K + 2) * Fraction(2) ** -53 * mag
+
+
+def test_linear_identity_weight_returns_dequantized_sum():
+    K = 64
+    rng = np.random.default_rng(11)
+    xb = make_activation(rng, 5, K, "laplace", n_out=2, out_scale=20.0)
+    bb, rr, _ = oracle.prep(xb, 2, 4)
+    codes = np.zeros((K, K), np.uint8)
+    codes[np.arange(K), np.arange(K)] = 0x2  # E2M1 1.0
+    packed = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+    w = oracle.Payload(packed, np.full((K, K // 32), 127, np.uint8))
+    y = oracle.linear(bb, rr, w)
+    want = decode_mx(bb.codes, bb.scales, K) + decode_mx(rr.codes, rr.scales, K)
+    assert np.array_equal(y, want)
+
+
+def test_linear_zero_input_and_row_selection():
+    K, N = 64, 8
+    rng = np.random.default_rng(12)
+    wb = f32_to_bf16_bits(rng.normal(0, 0.02, (N, K)).astype(np.float32))
+    w = oracle.quantize(wb)
+    bb, rr, _ = oracle.prep(np.zeros((3, K), np.uint16), 2, 4)
+    assert np.all(oracle.linear(bb, rr, w) == 0)
+    xb = make_activation(rng, 6, K, "normal")
+    bb, rr, _ = oracle.prep(xb, 2, 4)
+    full = oracle.linear(bb, rr, w)
+    sel = oracle.linear(bb, rr, w, rows=[5, 0, 3])
+    assert np.array_equal(sel, full[[5, 0, 3]])
+
+
+# ------------------------------------------------------------ NVFP4 invariants
+
+def test_nv_invariants_random():
+    M, K = 24, 256
+    xb = _random_x(M, K, 13)
+    x = x_values(xb)
+    bb, rr, mask, bhat, resid = oracle.prep(xb, 2, 4, oracle.NVFP4, want_values=True)
+    keep = np.unpackbits(mask, axis=1, bitorder="little").astype(bool)
+    assert np.all(keep.reshape(M, K // 4, 4).sum(-1) == 2)
+    assert np.all(unpack_codes(bb.codes, K)[~keep] == 0)
+    # tensor scales: amax / (6 * 448), from fp32 maxima
+    assert bb.tscale == np.float32(np.float32(np.abs(x).max()) / np.float32(2688.0))
+    assert rr.tscale == np.float32(np.float32(np.abs(resid).max()) / np.float32(2688.0))
+    # R is the fp32 rounding of x - Bhat
+    exact = x - bhat.astype(np.float64)
+    assert np.array_equal(exact.astype(np.float32), resid)
+    # Bhat decodes from codes and scales within one fp32 rounding of each product
+    bdec = decode_nv(bb.codes, bb.scales, bb.tscale, K)
+    assert np.allclose(bdec, bhat, rtol=2.0 ** -22, atol=0)
+    # scaled block maxima stay inside the E2M1 range up to E4M3 rounding (+1/16)
+    rdec = decode_nv(rr.codes, rr.scales, rr.tscale, K)
+    assert np.all(np.abs(rdec) <= np.abs(resid).max() * (1 + 2.0 ** -4) * (1 + 1e-6))
+
+
+def test_nv_zero_residual_on_representable_input():
+    """Blocks holding E2M1 values times 448 * 2^-j with a +-6 in every block, and a
+    global maximum of 2688: S_b = 1, every block scale is exact, R == 0."""
+    M, K = 8, 128
+    rng = np.random.default_rng(14)
+    codes = np.zeros((M, K), np.uint8)
+    for i in range(M):
+        for g in range(K // 4):
+            pos = rng.choice(4, 2, replace=False)
+            codes[i, g * 4 + pos] = rng.integers(1, 8, 2) | (rng.integers(0, 2, 2) << 3)
+        for b in range(K // 16):
+            blk = codes[i, b * 16:(b + 1) * 16]
+            j = np.nonzero(blk)[0][0]
+            blk[j] = (blk[j] & 8) | 7
+    j = rng.integers(0, 10, (M, K // 16))
+    j[0, 0] = 0
+    x = (CODE_VALUES[codes] * 448.0 * np.ldexp(1.0, -np.repeat(j, 16, axis=1))).astype(np.float32)
+    xb = f32_to_bf16_bits(x)
+    assert np.array_equal(bf16_bits_to_f32(xb), x)
+    bb, rr, mask, _, resid = oracle.prep(xb, 2, 4, oracle.NVFP4, want_values=True)
+    assert bb.tscale == 1.0
+    assert np.all(resid == 0)
+    assert np.all(rr.codes == 0) and np.all(rr.scales == 0) and rr.tscale == 1.0
+    assert np.array_equal(unpack_codes(bb.codes, K), codes)
+
+
+# ------------------------------------------------------------ method sanity
+
+@pytest.mark.parametrize("name", ["tiny", "decode", "dit"])
+def test_decomposition_beats_plain_mxfp4(name):
+    """Not a pin: on each workload's activations, Bhat + Rhat reconstructs X better
+    than plain MXFP4 of X, and better than the residual-less N:M backbone."""
+    w = WORKLOADS[name]
+    xb, _ = make_inputs(w, with_weight=False, rows=min(w.M, 64))
+    x = x_values(xb)
+    K = w.K
+    bb, rr, _ = oracle.prep(xb, w.n, w.m)
+    rec = decode_mx(bb.codes, bb.scales, K) + decode_mx(rr.codes, rr.scales, K)
+    plain = oracle.quantize(xb)
+    err_sharq = np.linalg.norm(x - rec)
+    err_plain = np.linalg.norm(x - decode_mx(plain.codes, plain.scales, K))
+    err_backbone = np.linalg.norm(x - decode_mx(bb.codes, bb.scales, K))
+    assert err_sharq < err_plain < err_backbone
