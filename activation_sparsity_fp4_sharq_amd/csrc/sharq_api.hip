@@ -1,0 +1,186 @@
+// sharq_api.hip -- the C ABI of libsharq (declared in include/sharq.h): argument
+// validation, workspace sizing and dispatch to the gfx950 kernels.  Every check
+// runs before anything is enqueued; no exception crosses the ABI.
+#include <string.h>
+
+#include "sharq_internal.h"
+
+using namespace sharq;
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int block_of(int fmt) { return fmt == SHARQ_MXFP4 ? 32 : 16; }
+
+sharq_status check_format(int fmt) {
+  return (fmt == SHARQ_MXFP4 || fmt == SHARQ_NVFP4) ? SHARQ_OK : SHARQ_E_FORMAT;
+}
+
+sharq_status check_pattern(int n, int m) {
+  return ((n == 2 && m == 4) || (n == 4 && m == 8)) ? SHARQ_OK : SHARQ_E_PATTERN;
+}
+
+sharq_status check_payload(const sharq_fp4* p, int fmt, bool need_tensor_scale) {
+  if (!p || !p->codes || !p->scales) return SHARQ_E_NULL;
+  if (fmt == SHARQ_NVFP4 && need_tensor_scale && !p->tensor_scale) return SHARQ_E_NULL;
+  if (!aligned16(p->codes) || !aligned16(p->scales)) return SHARQ_E_ALIGN;
+  if (fmt == SHARQ_NVFP4 && (reinterpret_cast<uintptr_t>(p->tensor_scale) & 3u)) return SHARQ_E_ALIGN;
+  return SHARQ_OK;
+}
+
+// The activation / bf16-input checks shared by sharq_prep and sharq_quantize.
+sharq_status check_input(const void* x, int64_t rows, int64_t K, int64_t ldx, int fmt) {
+  sharq_status s = check_format(fmt);
+  if (s != SHARQ_OK) return s;
+  if (rows < 0 || K <= 0 || K % block_of(fmt) || ldx < K) return SHARQ_E_SHAPE;
+  if (rows > (int64_t)1 << 31 || K > (int64_t)1 << 30) return SHARQ_E_SHAPE;
+  if (rows > 0 && !x) return SHARQ_E_NULL;
+  if (x && (!aligned16(x) || ldx % 8)) return SHARQ_E_ALIGN;
+  return SHARQ_OK;
+}
+
+sharq_status check_device() {
+  static thread_local int cached_dev = -1;
+  static thread_local bool cached_ok = false;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return SHARQ_E_DEVICE;
+  if (dev != cached_dev) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return SHARQ_E_DEVICE;
+    cached_ok = strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+    cached_dev = dev;
+  }
+  return cached_ok ? SHARQ_OK : SHARQ_E_DEVICE;
+}
+
+sharq_status launched(hipError_t e) { return e == hipSuccess ? SHARQ_OK : SHARQ_E_LAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+int sharq_abi_version(void) { return SHARQ_ABI_VERSION; }
+
+const char* sharq_status_str(int status) {
+  switch (status) {
+    case SHARQ_OK: return "ok";
+    case SHARQ_E_NULL: return "required pointer is NULL";
+    case SHARQ_E_SHAPE: return "invalid shape (size, block multiple or leading dimension)";
+    case SHARQ_E_PATTERN: return "unsupported N:M pattern (2:4 and 4:8 are supported)";
+    case SHARQ_E_FORMAT: return "unknown block format or output dtype";
+    case SHARQ_E_ALIGN: return "pointer or leading dimension misaligned";
+    case SHARQ_E_WORKSPACE: return "workspace missing or too small";
+    case SHARQ_E_LAUNCH: return "kernel launch failed";
+    case SHARQ_E_DEVICE: return "current device is not a gfx950";
+    default: return "unknown status";
+  }
+}
+
+size_t sharq_prep_workspace_bytes(int64_t, int64_t, int fmt) {
+  return fmt == SHARQ_NVFP4 ? kNvPrepWorkspace : 0;
+}
+
+size_t sharq_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, int fmt) {
+  if (M <= 0 || N <= 0 || K <= 0) return 0;
+  return fmt == SHARQ_NVFP4 ? linear_nv_workspace(M, N, K) : linear_mx_workspace(M, N, K);
+}
+
+sharq_status sharq_quantize(const void* x, int64_t rows, int64_t K, int64_t ldx, int fmt,
+                            const sharq_fp4* out, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+  sharq_status s = check_input(x, rows, K, ldx, fmt);
+  if (s != SHARQ_OK) return s;
+  if ((s = check_payload(out, fmt, true)) != SHARQ_OK) return s;
+  const size_t need = sharq_prep_workspace_bytes(rows, K, fmt);
+  if (need && (!workspace || workspace_bytes < need)) return SHARQ_E_WORKSPACE;
+  if (need && !aligned16(workspace)) return SHARQ_E_ALIGN;
+  if ((s = check_device()) != SHARQ_OK) return s;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const uint16_t* xb = reinterpret_cast<const uint16_t*>(x);
+  if (fmt == SHARQ_MXFP4) return launched(launch_quant_mx(xb, rows, K, ldx, out->codes, out->scales, st));
+  return launched(launch_quant_nv(xb, rows, K, ldx, out->codes, out->scales, out->tensor_scale,
+                                  reinterpret_cast<uint32_t*>(workspace), st));
+}
+
+sharq_status sharq_prep(const void* x, int64_t M, int64_t K, int64_t ldx, int sp_n, int sp_m, int fmt,
+                        const sharq_fp4* backbone, const sharq_fp4* residual, uint8_t* mask_bits,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+  sharq_status s = check_input(x, M, K, ldx, fmt);
+  if (s != SHARQ_OK) return s;
+  if ((s = check_pattern(sp_n, sp_m)) != SHARQ_OK) return s;
+  if ((s = check_payload(backbone, fmt, true)) != SHARQ_OK) return s;
+  if ((s = check_payload(residual, fmt, true)) != SHARQ_OK) return s;
+  if (mask_bits && (reinterpret_cast<uintptr_t>(mask_bits) & 3u)) return SHARQ_E_ALIGN;
+  const size_t need = sharq_prep_workspace_bytes(M, K, fmt);
+  if (need && (!workspace || workspace_bytes < need)) return SHARQ_E_WORKSPACE;
+  if (need && !aligned16(workspace)) return SHARQ_E_ALIGN;
+  if ((s = check_device()) != SHARQ_OK) return s;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const uint16_t* xb = reinterpret_cast<const uint16_t*>(x);
+  if (fmt == SHARQ_MXFP4)
+    return launched(launch_prep_mx(xb, M, K, ldx, sp_n, sp_m, backbone->codes, backbone->scales,
+                                   residual->codes, residual->scales, mask_bits, st));
+  return launched(launch_prep_nv(xb, M, K, ldx, sp_n, sp_m, backbone->codes, backbone->scales,
+                                 backbone->tensor_scale, residual->codes, residual->scales,
+                                 residual->tensor_scale, mask_bits,
+                                 reinterpret_cast<uint32_t*>(workspace), st));
+}
+
+sharq_status sharq_linear(const sharq_fp4* backbone, const sharq_fp4* residual, int64_t M,
+                          const sharq_fp4* weight, int64_t N, int64_t K, int fmt, void* y, int64_t ldy,
+                          int out_dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  sharq_status s = check_format(fmt);
+  if (s != SHARQ_OK) return s;
+  if (out_dtype != SHARQ_OUT_BF16 && out_dtype != SHARQ_OUT_FP32) return SHARQ_E_FORMAT;
+  if (M < 0 || N <= 0 || K <= 0 || K % block_of(fmt) || ldy < N) return SHARQ_E_SHAPE;
+  if (M > (int64_t)1 << 31 || N > (int64_t)1 << 30 || K > (int64_t)1 << 30) return SHARQ_E_SHAPE;
+  if ((s = check_payload(weight, fmt, true)) != SHARQ_OK) return s;
+  if (M > 0) {
+    if ((s = check_payload(backbone, fmt, true)) != SHARQ_OK) return s;
+    if ((s = check_payload(residual, fmt, true)) != SHARQ_OK) return s;
+    if (!y) return SHARQ_E_NULL;
+    if (reinterpret_cast<uintptr_t>(y) & (out_dtype == SHARQ_OUT_FP32 ? 3u : 1u)) return SHARQ_E_ALIGN;
+  }
+  const size_t need = sharq_linear_workspace_bytes(M, N, K, fmt);
+  if (need && (!workspace || workspace_bytes < need)) return SHARQ_E_WORKSPACE;
+  if (need && !aligned16(workspace)) return SHARQ_E_ALIGN;
+  if ((s = check_device()) != SHARQ_OK) return s;
+  if (M == 0) return SHARQ_OK;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const int f32 = out_dtype == SHARQ_OUT_FP32;
+  if (fmt == SHARQ_MXFP4)
+    return launched(launch_linear_mx(*backbone, *residual, M, *weight, N, K, y, ldy, f32, workspace,
+                                     workspace_bytes, st));
+  return launched(launch_linear_nv(*backbone, *residual, M, *weight, N, K, y, ldy, f32, workspace,
+                                   workspace_bytes, st));
+}
+
+sharq_status sharq_forward(const void* x, int64_t M, int64_t K, int64_t ldx, int sp_n, int sp_m, int fmt,
+                           const sharq_fp4* backbone, const sharq_fp4* residual, const sharq_fp4* weight,
+                           int64_t N, void* y, int64_t ldy, int out_dtype, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  // validate the linear half first so that nothing is enqueued when it would fail
+  sharq_status s = check_input(x, M, K, ldx, fmt);
+  if (s != SHARQ_OK) return s;
+  if ((s = check_pattern(sp_n, sp_m)) != SHARQ_OK) return s;
+  if (out_dtype != SHARQ_OUT_BF16 && out_dtype != SHARQ_OUT_FP32) return SHARQ_E_FORMAT;
+  if (N <= 0 || ldy < N || N > (int64_t)1 << 30) return SHARQ_E_SHAPE;
+  if ((s = check_payload(backbone, fmt, true)) != SHARQ_OK) return s;
+  if ((s = check_payload(residual, fmt, true)) != SHARQ_OK) return s;
+  if ((s = check_payload(weight, fmt, true)) != SHARQ_OK) return s;
+  if (M > 0 && !y) return SHARQ_E_NULL;
+  if (reinterpret_cast<uintptr_t>(y) & (out_dtype == SHARQ_OUT_FP32 ? 3u : 1u)) return SHARQ_E_ALIGN;
+  size_t need = sharq_prep_workspace_bytes(M, K, fmt);
+  const size_t need_lin = sharq_linear_workspace_bytes(M, N, K, fmt);
+  if (need_lin > need) need = need_lin;
+  if (need && (!workspace || workspace_bytes < need)) return SHARQ_E_WORKSPACE;
+  if (need && !aligned16(workspace)) return SHARQ_E_ALIGN;
+  s = sharq_prep(x, M, K, ldx, sp_n, sp_m, fmt, backbone, residual, nullptr, workspace, workspace_bytes,
+                 stream);
+  if (s != SHARQ_OK) return s;
+  return sharq_linear(backbone, residual, M, weight, N, K, fmt, y, ldy, out_dtype, workspace,
+                      workspace_bytes, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,39 @@
+// sharq_internal.h -- declarations shared by the HIP sources of libsharq (not installed).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/sharq.h"
+
+namespace sharq {
+
+// Launchers: each validates nothing (the C ABI layer does), enqueues its kernels on
+// `stream` and returns hipGetLastError().
+hipError_t launch_prep_mx(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, int sp_n,
+                          int sp_m, uint8_t* bcodes, uint8_t* bscales, uint8_t* rcodes,
+                          uint8_t* rscales, uint8_t* mask, hipStream_t stream);
+hipError_t launch_quant_mx(const uint16_t* x, int64_t rows, int64_t K, int64_t ldx,
+                           uint8_t* codes, uint8_t* scales, hipStream_t stream);
+
+hipError_t launch_prep_nv(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, int sp_n,
+                          int sp_m, uint8_t* bcodes, uint8_t* bscales, float* btscale,
+                          uint8_t* rcodes, uint8_t* rscales, float* rtscale, uint8_t* mask,
+                          uint32_t* work, hipStream_t stream);
+hipError_t launch_quant_nv(const uint16_t* x, int64_t rows, int64_t K, int64_t ldx,
+                           uint8_t* codes, uint8_t* scales, float* tscale, uint32_t* work,
+                           hipStream_t stream);
+
+hipError_t launch_linear_mx(const sharq_fp4& b, const sharq_fp4& r, int64_t M, const sharq_fp4& w,
+                            int64_t N, int64_t K, void* y, int64_t ldy, int out_fp32,
+                            void* work, size_t work_bytes, hipStream_t stream);
+size_t linear_mx_workspace(int64_t M, int64_t N, int64_t K);
+
+hipError_t launch_linear_nv(const sharq_fp4& b, const sharq_fp4& r, int64_t M, const sharq_fp4& w,
+                            int64_t N, int64_t K, void* y, int64_t ldy, int out_fp32,
+                            void* work, size_t work_bytes, hipStream_t stream);
+size_t linear_nv_workspace(int64_t M, int64_t N, int64_t K);
+
+constexpr size_t kNvPrepWorkspace = 256;
+constexpr int kMaxDevices = 64;
+
+}  // namespace sharq

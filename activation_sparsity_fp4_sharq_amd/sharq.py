@@ -1,0 +1,188 @@
+"""ctypes binding of libsharq (include/sharq.h).
+
+Argument marshalling only: every step of the SharQ path runs in the HIP library.
+PyTorch provides device memory and the current stream.  A missing library or a
+non-zero status raises; there is no CPU fallback.
+"""
+import ctypes
+import os
+
+import torch
+
+MXFP4 = 0
+NVFP4 = 1
+OUT_BF16 = 0
+OUT_FP32 = 1
+BLOCK = {MXFP4: 32, NVFP4: 16}
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libsharq.so")
+
+SYMBOLS = ["sharq_abi_version", "sharq_status_str", "sharq_prep_workspace_bytes",
+           "sharq_linear_workspace_bytes", "sharq_quantize", "sharq_prep", "sharq_linear",
+           "sharq_forward"]
+
+
+class SharqFp4(ctypes.Structure):
+    _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p),
+                ("tensor_scale", ctypes.c_void_p)]
+
+
+class SharqError(RuntimeError):
+    def __init__(self, fn, status, msg):
+        super().__init__(f"{fn} failed: status {status} ({msg})")
+        self.status = status
+
+
+_lib = None
+
+
+def lib():
+    """Load libsharq.so (built in-tree by build.py); raise if it is absent."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m activation_sparsity_fp4_sharq_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        i64, vp, sz = ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t
+        P = ctypes.POINTER(SharqFp4)
+        L.sharq_abi_version.restype = ctypes.c_int
+        L.sharq_abi_version.argtypes = []
+        L.sharq_status_str.restype = ctypes.c_char_p
+        L.sharq_status_str.argtypes = [ctypes.c_int]
+        L.sharq_prep_workspace_bytes.restype = sz
+        L.sharq_prep_workspace_bytes.argtypes = [i64, i64, ctypes.c_int]
+        L.sharq_linear_workspace_bytes.restype = sz
+        L.sharq_linear_workspace_bytes.argtypes = [i64, i64, i64, ctypes.c_int]
+        L.sharq_quantize.restype = ctypes.c_int
+        L.sharq_quantize.argtypes = [vp, i64, i64, i64, ctypes.c_int, P, vp, sz, vp]
+        L.sharq_prep.restype = ctypes.c_int
+        L.sharq_prep.argtypes = [vp, i64, i64, i64, ctypes.c_int, ctypes.c_int, ctypes.c_int, P, P, vp,
+                                 vp, sz, vp]
+        L.sharq_linear.restype = ctypes.c_int
+        L.sharq_linear.argtypes = [P, P, i64, P, i64, i64, ctypes.c_int, vp, i64, ctypes.c_int, vp, sz,
+                                   vp]
+        L.sharq_forward.restype = ctypes.c_int
+        L.sharq_forward.argtypes = [vp, i64, i64, i64, ctypes.c_int, ctypes.c_int, ctypes.c_int, P, P, P,
+                                    i64, vp, i64, ctypes.c_int, vp, sz, vp]
+        _lib = L
+    return _lib
+
+
+def _check(fn, status):
+    if status != 0:
+        raise SharqError(fn, status, lib().sharq_status_str(status).decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+class Payload:
+    """Device FP4 tensor: codes uint8 [rows, K/2], scales uint8 [rows, K/B],
+    tensor_scale float32 [1] (NVFP4)."""
+
+    def __init__(self, codes, scales, tensor_scale, fmt):
+        self.codes, self.scales, self.tensor_scale, self.fmt = codes, scales, tensor_scale, fmt
+
+    @classmethod
+    def empty(cls, rows, K, fmt, device):
+        codes = torch.empty((rows, K // 2), dtype=torch.uint8, device=device)
+        scales = torch.empty((rows, K // BLOCK[fmt]), dtype=torch.uint8, device=device)
+        ts = torch.empty(4, dtype=torch.float32, device=device)  # 16 bytes, first element used
+        return cls(codes, scales, ts, fmt)
+
+    @property
+    def K(self):
+        return self.codes.shape[1] * 2
+
+    def struct(self):
+        return SharqFp4(self.codes.data_ptr(), self.scales.data_ptr(), self.tensor_scale.data_ptr())
+
+    def to_host(self):
+        ts = float(self.tensor_scale[0].item()) if self.fmt == NVFP4 else 1.0
+        return self.codes.cpu().numpy(), self.scales.cpu().numpy(), ts
+
+
+def workspace(nbytes, device):
+    if nbytes == 0:
+        return None
+    return torch.empty((nbytes + 15) // 16 * 16, dtype=torch.uint8, device=device)
+
+
+def _as_bf16_2d(x):
+    if x.dtype != torch.bfloat16 or x.dim() != 2 or not x.is_cuda:
+        raise ValueError("expected a 2-D bfloat16 CUDA tensor")
+    if x.stride(1) != 1:
+        raise ValueError("the last dimension must be contiguous")
+    return x
+
+
+def quantize(x, fmt=MXFP4, stream=None):
+    """Plain FP4 quantization of a bf16 matrix (a weight payload)."""
+    x = _as_bf16_2d(x)
+    rows, K = x.shape
+    out = Payload.empty(rows, K, fmt, x.device)
+    ws = workspace(lib().sharq_prep_workspace_bytes(rows, K, fmt), x.device)
+    st = out.struct()
+    _check("sharq_quantize", lib().sharq_quantize(_ptr(x), rows, K, x.stride(0), fmt, ctypes.byref(st),
+                                                  _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream)))
+    return out
+
+
+def prep(x, n=2, m=4, fmt=MXFP4, want_mask=False, out=None, ws=None, stream=None):
+    """SharQ activation preparation: returns (backbone, residual, mask_bits or None)."""
+    x = _as_bf16_2d(x)
+    M, K = x.shape
+    bb, rr = out if out is not None else (Payload.empty(M, K, fmt, x.device), Payload.empty(M, K, fmt, x.device))
+    mask = torch.empty((M, K // 8), dtype=torch.uint8, device=x.device) if want_mask else None
+    if ws is None:
+        ws = workspace(lib().sharq_prep_workspace_bytes(M, K, fmt), x.device)
+    sb, sr = bb.struct(), rr.struct()
+    _check("sharq_prep", lib().sharq_prep(_ptr(x), M, K, x.stride(0), n, m, fmt, ctypes.byref(sb),
+                                          ctypes.byref(sr), _ptr(mask), _ptr(ws),
+                                          0 if ws is None else ws.numel(), _stream(stream)))
+    return bb, rr, mask
+
+
+def linear(backbone, residual, weight, out_dtype=OUT_BF16, y=None, ws=None, stream=None):
+    """Y = Bhat W^T + Rhat W^T on the device; returns Y [M, N] (bf16 or fp32)."""
+    fmt = weight.fmt
+    M, K, N = backbone.codes.shape[0], backbone.K, weight.codes.shape[0]
+    dev = weight.codes.device
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.float32 if out_dtype == OUT_FP32 else torch.bfloat16, device=dev)
+    if ws is None:
+        ws = workspace(lib().sharq_linear_workspace_bytes(M, N, K, fmt), dev)
+    sb, sr, sw = backbone.struct(), residual.struct(), weight.struct()
+    _check("sharq_linear", lib().sharq_linear(ctypes.byref(sb), ctypes.byref(sr), M, ctypes.byref(sw), N, K,
+                                              fmt, _ptr(y), y.stride(0), out_dtype, _ptr(ws),
+                                              0 if ws is None else ws.numel(), _stream(stream)))
+    return y
+
+
+def forward(x, weight, n=2, m=4, out_dtype=OUT_BF16, bufs=None, y=None, ws=None, stream=None):
+    """One SharQ linear layer: prep then both GEMMs, on one stream."""
+    x = _as_bf16_2d(x)
+    fmt = weight.fmt
+    M, K = x.shape
+    N = weight.codes.shape[0]
+    bb, rr = bufs if bufs is not None else (Payload.empty(M, K, fmt, x.device), Payload.empty(M, K, fmt, x.device))
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.float32 if out_dtype == OUT_FP32 else torch.bfloat16,
+                        device=x.device)
+    if ws is None:
+        need = max(lib().sharq_prep_workspace_bytes(M, K, fmt), lib().sharq_linear_workspace_bytes(M, N, K, fmt))
+        ws = workspace(need, x.device)
+    sb, sr, sw = bb.struct(), rr.struct(), weight.struct()
+    _check("sharq_forward", lib().sharq_forward(_ptr(x), M, K, x.stride(0), n, m, fmt, ctypes.byref(sb),
+                                                ctypes.byref(sr), ctypes.byref(sw), N, _ptr(y), y.stride(0),
+                                                out_dtype, _ptr(ws), 0 if ws is None else ws.numel(),
+                                                _stream(stream)))
+    return y, (bb, rr)

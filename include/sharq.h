@@ -1,0 +1,156 @@
+/*
+ * sharq.h -- C ABI of libsharq, the SharQ sparse-dense FP4 linear layer on AMD
+ * MI355X (gfx950).
+ *
+ * The method (SharQ: Bridging Activation Sparsity and FP4 Quantization for LLM
+ * Inference, arXiv 2606.26587; abstract and "Core claim"): for each activation
+ * tensor X[M,K], an input-adaptive N:M mask along K keeps the n largest |x| of
+ * every m consecutive elements (the outlier-dominated sparse backbone); the
+ * backbone is quantized to FP4; a dense residual R = X - dequant(backbone) is
+ * formed against the *quantized* backbone and quantized to FP4 with its own
+ * block scales; a sparse-backbone FP4 GEMM and a dense-residual FP4 GEMM share
+ * one FP4 weight payload and their products are summed:
+ *     Y[M,N] = Bhat * What^T + Rhat * What^T.
+ * Figure 2 of the pages shows the preparation fused into one kernel ahead of the
+ * two GEMMs; here the preparation is sharq_prep and both GEMMs are one kernel,
+ * sharq_linear, accumulating into one fp32 tile.
+ *
+ * Conventions for every entry point
+ *  - Pointers marked "device" are HIP device pointers on the current device;
+ *    pointers marked "host" are host memory.  The caller owns every buffer.
+ *  - All work is enqueued on `stream` (a hipStream_t; NULL = the null stream)
+ *    and is asynchronous.  Nothing is allocated, freed or synchronized.
+ *  - Arguments are validated before anything is launched; on error the status
+ *    is returned and nothing has been enqueued or written.
+ *  - Non-finite inputs are outside the contract: they produce unspecified codes
+ *    but never an out-of-bounds access.
+ *  - Thread-safe: no global mutable state.
+ *
+ * FP4 payload layout (struct sharq_fp4), for a [rows, K] tensor:
+ *  - codes: [rows, K/2] bytes, row-major, dense (row pitch K/2).  Element 2c of a
+ *    row sits in the low nibble of byte c, element 2c+1 in the high nibble.  A
+ *    code is E2M1: bit 3 sign, bits 2..1 exponent (bias 1), bit 0 mantissa; the
+ *    magnitudes are 0, 0.5, 1, 1.5, 2, 3, 4, 6.
+ *  - scales: MXFP4: [rows, K/32] E8M0 bytes (value 2^(byte-127)), one per 32
+ *    consecutive elements along K.  NVFP4: [rows, K/16] E4M3 bytes (OCP E4M3,
+ *    bias 7, max 448), one per 16 consecutive elements.
+ *  - tensor_scale: NVFP4 only, one fp32 in device memory; element value =
+ *    E2M1 * block scale * tensor_scale.  Ignored (may be NULL) for MXFP4.
+ *  - codes and scales must be 16-byte aligned.
+ */
+#ifndef SHARQ_H_
+#define SHARQ_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SHARQ_ABI_VERSION 1
+
+typedef enum sharq_status {
+  SHARQ_OK = 0,
+  SHARQ_E_NULL = 1,      /* a required pointer is NULL                                   */
+  SHARQ_E_SHAPE = 2,     /* negative/zero size, K not a multiple of the block, ld < K     */
+  SHARQ_E_PATTERN = 3,   /* n:m is not 2:4 or 4:8                                         */
+  SHARQ_E_FORMAT = 4,    /* unknown block format or output dtype                          */
+  SHARQ_E_ALIGN = 5,     /* pointer or leading dimension not aligned as required          */
+  SHARQ_E_WORKSPACE = 6, /* workspace NULL or smaller than the *_workspace_bytes value    */
+  SHARQ_E_LAUNCH = 7,    /* a kernel launch failed (hipGetLastError after the launch)     */
+  SHARQ_E_DEVICE = 8     /* the current device is not a gfx950                            */
+} sharq_status;
+
+typedef enum sharq_format { SHARQ_MXFP4 = 0, SHARQ_NVFP4 = 1 } sharq_format;
+typedef enum sharq_out_dtype { SHARQ_OUT_BF16 = 0, SHARQ_OUT_FP32 = 1 } sharq_out_dtype;
+
+typedef struct sharq_fp4 {
+  uint8_t* codes;      /* device, [rows, K/2]                                    */
+  uint8_t* scales;     /* device, [rows, K/32] (MXFP4) or [rows, K/16] (NVFP4)   */
+  float* tensor_scale; /* device, 1 float (NVFP4); unused for MXFP4              */
+} sharq_fp4;
+
+/* Version of this ABI (SHARQ_ABI_VERSION). */
+int sharq_abi_version(void);
+
+/* Static text for a status code; never NULL. */
+const char* sharq_status_str(int status);
+
+/* Bytes of device workspace sharq_prep / sharq_quantize need for these sizes
+ * (0 for MXFP4; a few hundred bytes for NVFP4, which keeps its two running
+ * tensor maxima there).  Host-only, launches nothing. */
+size_t sharq_prep_workspace_bytes(int64_t rows, int64_t K, int fmt);
+
+/* Bytes of device workspace sharq_linear needs for these sizes (the split-K
+ * partial sums of small-M shapes; 0 when the shape runs without split-K). */
+size_t sharq_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, int fmt);
+
+/* Plain FP4 quantization (no mask, no residual) of a bf16 matrix -- how a weight
+ * payload W is produced (the pages pre-quantize the weights once; "share a single
+ * FP4 weight payload", abstract).  Each block is quantized as the residual blocks
+ * of sharq_prep are: MXFP4 E8M0 exponent floor(log2 amax) - 2 and E2M1
+ * round-to-nearest-even with saturation; NVFP4 with a tensor scale amax/2688.
+ *   x       device bf16 [rows, ldx], first K columns used; 16-byte aligned, ldx % 8 == 0
+ *   rows    >= 0 (0 enqueues nothing for MXFP4; NVFP4 still writes tensor_scale = 1)
+ *   K       > 0, multiple of 32 (MXFP4) or 16 (NVFP4)
+ *   out     payload to write (codes, scales, and tensor_scale for NVFP4)
+ *   workspace / workspace_bytes: >= sharq_prep_workspace_bytes(rows, K, fmt), device
+ */
+sharq_status sharq_quantize(const void* x, int64_t rows, int64_t K, int64_t ldx, int fmt,
+                            const sharq_fp4* out, void* workspace, size_t workspace_bytes,
+                            void* stream);
+
+/* The SharQ activation preparation (abstract; "Core claim"; Figure 2's fused
+ * preparation kernel, without the layer normalization):
+ *   1. mask: in every group of m consecutive elements along K keep the n with the
+ *      largest |x| (compared on the bf16 bits with the sign cleared; on equal
+ *      magnitude the lower index wins), so exactly n are kept per group;
+ *   2. backbone: FP4-quantize X with the dropped positions set to +0 (code 0x0);
+ *      the block scale is taken over the kept values;
+ *   3. residual: R = X - dequant(backbone), one fp32 subtraction per element;
+ *   4. FP4-quantize R over all positions with its own scales (and, for NVFP4, its
+ *      own tensor scale amax(R)/2688).
+ *   x          device bf16 [M, ldx], first K columns used; 16-byte aligned, ldx % 8 == 0
+ *   M          >= 0;  K > 0, multiple of 32 (MXFP4) or 16 (NVFP4)
+ *   sp_n:sp_m  2:4 or 4:8
+ *   backbone   output payload [M, K] (zero-filled dense: dropped positions hold code 0x0)
+ *   residual   output payload [M, K]
+ *   mask_bits  device [M, K/8] or NULL: bit (k % 8) of byte k/8 set when element k is kept
+ *   workspace  device, >= sharq_prep_workspace_bytes(M, K, fmt) bytes (NULL allowed when 0)
+ * Masks, codes and scale bytes are deterministic and identical for every launch shape. */
+sharq_status sharq_prep(const void* x, int64_t M, int64_t K, int64_t ldx, int sp_n, int sp_m,
+                        int fmt, const sharq_fp4* backbone, const sharq_fp4* residual,
+                        uint8_t* mask_bits, void* workspace, size_t workspace_bytes,
+                        void* stream);
+
+/* The two SharQ GEMMs over one weight payload (abstract: a sparse FP4 GEMM for the
+ * backbone, a dense FP4 GEMM for the residual, one FP4 weight payload), summed in
+ * one fp32 accumulator per output:  Y = Bhat W^T + Rhat W^T.
+ *   backbone, residual  payloads [M, K] from sharq_prep (same format)
+ *   weight              payload [N, K] (e.g. from sharq_quantize)
+ *   y                   device [M, ldy] bf16 (round to nearest even) or fp32; ldy >= N;
+ *                       aligned to its element size
+ *   workspace           device, >= sharq_linear_workspace_bytes(M, N, K, fmt) bytes
+ * MXFP4 runs on the gfx950 block-scaled FP4 matrix cores, so every product of two
+ * FP4 values and their scales is exact and only the fp32 summation order differs
+ * from an exact result.  NVFP4 (E4M3 block scales, which the FP4 matrix cores
+ * cannot apply) runs exactly on the fp16 matrix cores. */
+sharq_status sharq_linear(const sharq_fp4* backbone, const sharq_fp4* residual, int64_t M,
+                          const sharq_fp4* weight, int64_t N, int64_t K, int fmt, void* y,
+                          int64_t ldy, int out_dtype, void* workspace, size_t workspace_bytes,
+                          void* stream);
+
+/* One SharQ linear layer end to end: sharq_prep into the caller's backbone and
+ * residual payloads, then sharq_linear, on one stream.  Arguments as above; the
+ * workspace must cover both calls (max of the two *_workspace_bytes values). */
+sharq_status sharq_forward(const void* x, int64_t M, int64_t K, int64_t ldx, int sp_n, int sp_m,
+                           int fmt, const sharq_fp4* backbone, const sharq_fp4* residual,
+                           const sharq_fp4* weight, int64_t N, void* y, int64_t ldy,
+                           int out_dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SHARQ_H_ */

@@ -1,0 +1,227 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Bar: masks, FP4 codes, scale bytes and tensor scales bit-exact; GEMM output within
+max-norm relative error 2e-3 of the oracle's fp64 result (fp32 output), and for the
+bf16 output every element within one bf16 ulp of the oracle rounded to bf16 plus a
+Frobenius relative error <= 2e-3.  Inputs come from the seeded generators only.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from activation_sparsity_fp4_sharq_amd import sharq
+from activation_sparsity_fp4_sharq_amd.workloads import (WORKLOADS, adversarial_activation,
+                                                          f32_to_bf16_bits, make_inputs, make_shape)
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-3
+DEV = torch.device("cuda:0")
+
+
+def to_dev(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(DEV)
+
+
+def assert_payload_equal(got, want, what):
+    gc, gs, gt = got.to_host()
+    assert gc.shape == want.codes.shape and gs.shape == want.scales.shape, what
+    bad = np.nonzero(gc != want.codes)
+    assert bad[0].size == 0, f"{what}: {bad[0].size} code bytes differ, first at {bad[0][0]},{bad[1][0]}"
+    bad = np.nonzero(gs != want.scales)
+    assert bad[0].size == 0, f"{what}: {bad[0].size} scale bytes differ, first at {bad[0][0]},{bad[1][0]}"
+    if got.fmt == sharq.NVFP4:
+        assert np.float32(gt) == np.float32(want.tscale), f"{what}: tensor scale {gt} != {want.tscale}"
+
+
+def check_prep(xb, n, m, fmt, ldx_pad=0):
+    M, K = xb.shape
+    if ldx_pad:
+        wide = np.zeros((M, K + ldx_pad), np.uint16)
+        wide[:, :K] = xb
+        x = to_dev(wide)[:, :K]
+    else:
+        x = to_dev(xb)
+    bb, rr, mask = sharq.prep(x, n, m, fmt, want_mask=True)
+    torch.cuda.synchronize()
+    ob, orr, omask = oracle.prep(xb, n, m, fmt)
+    assert np.array_equal(mask.cpu().numpy(), omask), "mask bits differ"
+    assert_payload_equal(bb, ob, "backbone")
+    assert_payload_equal(rr, orr, "residual")
+    return ob, orr
+
+
+def rel_maxnorm(y, yref):
+    den = np.abs(yref).max()
+    return np.abs(y - yref).max() / (den if den > 0 else 1.0)
+
+
+def bf16_ulp_check(ybf, yref):
+    """Every bf16 output within one ulp of the oracle value rounded to bf16."""
+    want = f32_to_bf16_bits(yref.astype(np.float32)).astype(np.int32)
+    got = ybf.view(torch.int16).cpu().numpy().astype(np.uint16).astype(np.int32)
+    # bf16 bits are sign-magnitude; compare as ordered integers
+    def ordered(b):
+        return np.where(b & 0x8000, -(b & 0x7FFF), b & 0x7FFF)
+    return np.abs(ordered(got) - ordered(want)).max()
+
+
+# ------------------------------------------------------------------ prep parity
+
+@pytest.mark.parametrize("name", list(WORKLOADS))
+def test_prep_workloads_full_size(name):
+    w = WORKLOADS[name]
+    print(f"[prep] {name} M={w.M} K={w.K} {w.n}:{w.m} fmt={w.fmt}", flush=True)
+    xb, _ = make_inputs(w, with_weight=False)
+    check_prep(xb, w.n, w.m, w.fmt)
+
+
+@pytest.mark.parametrize("fmt", [sharq.MXFP4, sharq.NVFP4])
+@pytest.mark.parametrize("n,m", [(2, 4), (4, 8)])
+@pytest.mark.parametrize("M,K", [(1, 32), (3, 64), (17, 96), (100, 160), (300, 512), (65, 1056)])
+def test_prep_shapes(fmt, n, m, M, K):
+    print(f"[prep] shape M={M} K={K} {n}:{m} fmt={fmt}", flush=True)
+    xb, _ = make_shape(M, 8, K, seed=M * 131 + K, dist="student_t3", token_sigma=0.5)
+    check_prep(xb, n, m, fmt)
+
+
+@pytest.mark.parametrize("fmt", [sharq.MXFP4, sharq.NVFP4])
+@pytest.mark.parametrize("n,m", [(2, 4), (4, 8)])
+def test_prep_adversarial(fmt, n, m):
+    print(f"[prep] adversarial {n}:{m} fmt={fmt}", flush=True)
+    xb = adversarial_activation(96, 256, seed=3)
+    check_prep(xb, n, m, fmt)
+
+
+@pytest.mark.parametrize("fmt", [sharq.MXFP4, sharq.NVFP4])
+def test_prep_strided_rows(fmt):
+    print(f"[prep] strided ldx fmt={fmt}", flush=True)
+    xb, _ = make_shape(37, 8, 256, seed=5)
+    check_prep(xb, 2, 4, fmt, ldx_pad=24)
+
+
+@pytest.mark.parametrize("fmt", [sharq.MXFP4, sharq.NVFP4])
+def test_prep_empty_and_zero(fmt):
+    print(f"[prep] empty/zero fmt={fmt}", flush=True)
+    x = torch.zeros((0, 64), dtype=torch.bfloat16, device=DEV)
+    bb, rr, _ = sharq.prep(x, 2, 4, fmt)
+    torch.cuda.synchronize()
+    assert bb.codes.shape == (0, 32)
+    if fmt == sharq.NVFP4:
+        assert bb.tensor_scale[0].item() == 1.0 and rr.tensor_scale[0].item() == 1.0
+    check_prep(np.zeros((5, 64), np.uint16), 2, 4, fmt)
+
+
+@pytest.mark.parametrize("fmt", [sharq.MXFP4, sharq.NVFP4])
+@pytest.mark.parametrize("rows,K", [(512, 512), (77, 96), (14336, 4096)])
+def test_quantize_weight(fmt, rows, K):
+    print(f"[quant] rows={rows} K={K} fmt={fmt}", flush=True)
+    rng = np.random.default_rng(rows + K)
+    wb = f32_to_bf16_bits(rng.normal(0, 0.02, (rows, K)).astype(np.float32))
+    got = sharq.quantize(to_dev(wb), fmt)
+    torch.cuda.synchronize()
+    assert_payload_equal(got, oracle.quantize(wb, fmt), "weight")
+
+
+def test_prep_deterministic_and_no_overrun():
+    """Two runs are bitwise identical; bytes past the outputs stay untouched."""
+    print("[prep] determinism/guard", flush=True)
+    xb, _ = make_shape(123, 8, 352, seed=9)
+    x = to_dev(xb)
+    M, K = xb.shape
+    outs = []
+    for _ in range(2):
+        big_c = torch.full((M * K // 2 + 4096,), 0xAA, dtype=torch.uint8, device=DEV)
+        big_s = torch.full((M * K // 32 + 4096,), 0xAA, dtype=torch.uint8, device=DEV)
+        big_rc = torch.full_like(big_c, 0xAA)
+        big_rs = torch.full_like(big_s, 0xAA)
+        ts = torch.zeros(4, dtype=torch.float32, device=DEV)
+        bb = sharq.Payload(big_c[:M * K // 2].view(M, K // 2), big_s[:M * K // 32].view(M, K // 32), ts, sharq.MXFP4)
+        rr = sharq.Payload(big_rc[:M * K // 2].view(M, K // 2), big_rs[:M * K // 32].view(M, K // 32), ts, sharq.MXFP4)
+        sharq.prep(x, 2, 4, sharq.MXFP4, out=(bb, rr))
+        torch.cuda.synchronize()
+        for big, n in ((big_c, M * K // 2), (big_s, M * K // 32), (big_rc, M * K // 2), (big_rs, M * K // 32)):
+            assert torch.all(big[n:] == 0xAA), "write past the end of an output"
+        outs.append([t.cpu().numpy().copy() for t in (big_c, big_s, big_rc, big_rs)])
+    for a, b in zip(*outs):
+        assert np.array_equal(a, b)
+
+
+# ------------------------------------------------------------------ GEMM parity
+
+def run_linear(xb, wb, n, m, fmt):
+    x, wt = to_dev(xb), to_dev(wb)
+    weight = sharq.quantize(wt, fmt)
+    bb, rr, _ = sharq.prep(x, n, m, fmt)
+    y32 = sharq.linear(bb, rr, weight, sharq.OUT_FP32)
+    y16 = sharq.linear(bb, rr, weight, sharq.OUT_BF16)
+    torch.cuda.synchronize()
+    return weight, bb, rr, y32, y16
+
+
+@pytest.mark.parametrize("fmt", [sharq.MXFP4, sharq.NVFP4])
+@pytest.mark.parametrize("M,N,K", [(1, 1, 32), (16, 512, 512), (37, 70, 96), (300, 260, 160),
+                                   (257, 513, 1056), (64, 256, 2048)])
+def test_linear_small_full_compare(fmt, M, N, K):
+    if fmt == sharq.NVFP4 and K % 16:
+        pytest.skip("K must be a multiple of 16")
+    print(f"[linear] M={M} N={N} K={K} fmt={fmt}", flush=True)
+    xb, wb = make_shape(M, N, K, seed=M + N + K, dist="laplace", token_sigma=0.3)
+    weight, bb, rr, y32, y16 = run_linear(xb, wb, 2, 4, fmt)
+    ob, orr, _ = oracle.prep(xb, 2, 4, fmt)
+    ow = oracle.quantize(wb, fmt)
+    assert_payload_equal(weight, ow, "weight")
+    yref = oracle.linear(ob, orr, ow, fmt)
+    err = rel_maxnorm(y32.cpu().numpy().astype(np.float64), yref)
+    assert err <= TOL, f"fp32 output max-norm rel err {err}"
+    assert bf16_ulp_check(y16, yref) <= 1
+    fro = np.linalg.norm(y16.float().cpu().numpy() - yref) / max(np.linalg.norm(yref), 1e-300)
+    assert fro <= TOL
+
+
+@pytest.mark.parametrize("name", list(WORKLOADS))
+def test_linear_workloads_sampled_rows(name):
+    """Full-size shapes in the benchmark's launch configuration; the oracle computes
+    a sample of rows (first, last, and a spread in between) over all N columns."""
+    w = WORKLOADS[name]
+    print(f"[linear] {name} M={w.M} N={w.N} K={w.K} fmt={w.fmt}", flush=True)
+    xb, wb = make_inputs(w)
+    x, wt = to_dev(xb), to_dev(wb)
+    weight = sharq.quantize(wt, w.fmt)
+    y32, (bb, rr) = sharq.forward(x, weight, w.n, w.m, out_dtype=sharq.OUT_FP32)
+    y16, _ = sharq.forward(x, weight, w.n, w.m, out_dtype=sharq.OUT_BF16, bufs=(bb, rr))
+    torch.cuda.synchronize()
+    ob, orr, _ = oracle.prep(xb, w.n, w.m, w.fmt)
+    ow = oracle.quantize(wb, w.fmt)
+    assert_payload_equal(weight, ow, "weight")
+    assert_payload_equal(bb, ob, "backbone")
+    assert_payload_equal(rr, orr, "residual")
+    rows = np.unique(np.concatenate([np.arange(min(8, w.M)), np.arange(max(0, w.M - 8), w.M),
+                                     np.linspace(0, w.M - 1, 16).astype(np.int64)]))
+    yref = oracle.linear(ob, orr, ow, w.fmt, rows=rows)
+    y = y32.cpu().numpy()[rows].astype(np.float64)
+    err = rel_maxnorm(y, yref)
+    assert err <= TOL, f"{name}: fp32 output max-norm rel err {err}"
+    assert bf16_ulp_check(y16[torch.from_numpy(rows).to(DEV)], yref) <= 1
+
+
+def test_linear_deterministic_and_guarded():
+    print("[linear] determinism/guard", flush=True)
+    M, N, K = 300, 260, 256
+    xb, wb = make_shape(M, N, K, seed=77)
+    x, wt = to_dev(xb), to_dev(wb)
+    weight = sharq.quantize(wt, sharq.MXFP4)
+    bb, rr, _ = sharq.prep(x, 2, 4)
+    res = []
+    for _ in range(2):
+        ld = N + 8
+        big = torch.full(((M + 2) * ld,), float("nan"), dtype=torch.float32, device=DEV)
+        y = big[:M * ld].view(M, ld)
+        sharq.linear(bb, rr, weight, sharq.OUT_FP32, y=y)
+        torch.cuda.synchronize()
+        out = big.cpu().numpy()
+        assert np.all(np.isnan(out[M * ld:])), "write past the output"
+        assert np.all(np.isnan(out[:M * ld].reshape(M, ld)[:, N:])), "write into the ld padding"
+        res.append(out[:M * ld].reshape(M, ld)[:, :N].copy())
+    assert np.array_equal(res[0], res[1])
