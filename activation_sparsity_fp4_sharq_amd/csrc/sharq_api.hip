@@ -21,9 +21,12 @@ sharq_status check_pattern(int n, int m) {
   return ((n == 2 && m == 4) || (n == 4 && m == 8)) ? SHARQ_OK : SHARQ_E_PATTERN;
 }
 
-sharq_status check_payload(const sharq_fp4* p, int fmt, bool need_tensor_scale) {
-  if (!p || !p->codes || !p->scales) return SHARQ_E_NULL;
-  if (fmt == SHARQ_NVFP4 && need_tensor_scale && !p->tensor_scale) return SHARQ_E_NULL;
+// A payload of `rows` rows; an empty one (rows == 0) may have NULL codes and scales,
+// but an NVFP4 tensor scale is always written or read, so it must exist.
+sharq_status check_payload(const sharq_fp4* p, int fmt, int64_t rows) {
+  if (!p) return SHARQ_E_NULL;
+  if (rows > 0 && (!p->codes || !p->scales)) return SHARQ_E_NULL;
+  if (fmt == SHARQ_NVFP4 && !p->tensor_scale) return SHARQ_E_NULL;
   if (!aligned16(p->codes) || !aligned16(p->scales)) return SHARQ_E_ALIGN;
   if (fmt == SHARQ_NVFP4 && (reinterpret_cast<uintptr_t>(p->tensor_scale) & 3u)) return SHARQ_E_ALIGN;
   return SHARQ_OK;
@@ -91,7 +94,7 @@ sharq_status sharq_quantize(const void* x, int64_t rows, int64_t K, int64_t ldx,
                             void* stream) {
   sharq_status s = check_input(x, rows, K, ldx, fmt);
   if (s != SHARQ_OK) return s;
-  if ((s = check_payload(out, fmt, true)) != SHARQ_OK) return s;
+  if ((s = check_payload(out, fmt, rows)) != SHARQ_OK) return s;
   const size_t need = sharq_prep_workspace_bytes(rows, K, fmt);
   if (need && (!workspace || workspace_bytes < need)) return SHARQ_E_WORKSPACE;
   if (need && !aligned16(workspace)) return SHARQ_E_ALIGN;
@@ -109,8 +112,8 @@ sharq_status sharq_prep(const void* x, int64_t M, int64_t K, int64_t ldx, int sp
   sharq_status s = check_input(x, M, K, ldx, fmt);
   if (s != SHARQ_OK) return s;
   if ((s = check_pattern(sp_n, sp_m)) != SHARQ_OK) return s;
-  if ((s = check_payload(backbone, fmt, true)) != SHARQ_OK) return s;
-  if ((s = check_payload(residual, fmt, true)) != SHARQ_OK) return s;
+  if ((s = check_payload(backbone, fmt, M)) != SHARQ_OK) return s;
+  if ((s = check_payload(residual, fmt, M)) != SHARQ_OK) return s;
   if (mask_bits && (reinterpret_cast<uintptr_t>(mask_bits) & 3u)) return SHARQ_E_ALIGN;
   const size_t need = sharq_prep_workspace_bytes(M, K, fmt);
   if (need && (!workspace || workspace_bytes < need)) return SHARQ_E_WORKSPACE;
@@ -135,10 +138,10 @@ sharq_status sharq_linear(const sharq_fp4* backbone, const sharq_fp4* residual, 
   if (out_dtype != SHARQ_OUT_BF16 && out_dtype != SHARQ_OUT_FP32) return SHARQ_E_FORMAT;
   if (M < 0 || N <= 0 || K <= 0 || K % block_of(fmt) || ldy < N) return SHARQ_E_SHAPE;
   if (M > (int64_t)1 << 31 || N > (int64_t)1 << 30 || K > (int64_t)1 << 30) return SHARQ_E_SHAPE;
-  if ((s = check_payload(weight, fmt, true)) != SHARQ_OK) return s;
+  if ((s = check_payload(weight, fmt, N)) != SHARQ_OK) return s;
+  if ((s = check_payload(backbone, fmt, M)) != SHARQ_OK) return s;
+  if ((s = check_payload(residual, fmt, M)) != SHARQ_OK) return s;
   if (M > 0) {
-    if ((s = check_payload(backbone, fmt, true)) != SHARQ_OK) return s;
-    if ((s = check_payload(residual, fmt, true)) != SHARQ_OK) return s;
     if (!y) return SHARQ_E_NULL;
     if (reinterpret_cast<uintptr_t>(y) & (out_dtype == SHARQ_OUT_FP32 ? 3u : 1u)) return SHARQ_E_ALIGN;
   }
@@ -166,9 +169,9 @@ sharq_status sharq_forward(const void* x, int64_t M, int64_t K, int64_t ldx, int
   if ((s = check_pattern(sp_n, sp_m)) != SHARQ_OK) return s;
   if (out_dtype != SHARQ_OUT_BF16 && out_dtype != SHARQ_OUT_FP32) return SHARQ_E_FORMAT;
   if (N <= 0 || ldy < N || N > (int64_t)1 << 30) return SHARQ_E_SHAPE;
-  if ((s = check_payload(backbone, fmt, true)) != SHARQ_OK) return s;
-  if ((s = check_payload(residual, fmt, true)) != SHARQ_OK) return s;
-  if ((s = check_payload(weight, fmt, true)) != SHARQ_OK) return s;
+  if ((s = check_payload(backbone, fmt, M)) != SHARQ_OK) return s;
+  if ((s = check_payload(residual, fmt, M)) != SHARQ_OK) return s;
+  if ((s = check_payload(weight, fmt, N)) != SHARQ_OK) return s;
   if (M > 0 && !y) return SHARQ_E_NULL;
   if (reinterpret_cast<uintptr_t>(y) & (out_dtype == SHARQ_OUT_FP32 ? 3u : 1u)) return SHARQ_E_ALIGN;
   size_t need = sharq_prep_workspace_bytes(M, K, fmt);

@@ -36,7 +36,8 @@
  *    bias 7, max 448), one per 16 consecutive elements.
  *  - tensor_scale: NVFP4 only, one fp32 in device memory; element value =
  *    E2M1 * block scale * tensor_scale.  Ignored (may be NULL) for MXFP4.
- *  - codes and scales must be 16-byte aligned.
+ *  - codes and scales must be 16-byte aligned; an empty payload (0 rows) may
+ *    pass NULL codes and scales, but an NVFP4 tensor_scale must always exist.
  */
 #ifndef SHARQ_H_
 #define SHARQ_H_

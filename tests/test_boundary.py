@@ -1,0 +1,142 @@
+"""The C ABI boundary on the CPU: the library loads, exports every function that
+include/sharq.h declares, and rejects every invalid argument with its status before
+touching the GPU (validation runs first, so these calls never reach HIP)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from activation_sparsity_fp4_sharq_amd import sharq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sharq.h")
+
+OK, E_NULL, E_SHAPE, E_PATTERN, E_FORMAT, E_ALIGN, E_WORKSPACE, E_LAUNCH, E_DEVICE = range(9)
+A = 0x10000  # a 16-byte aligned fake device address: never dereferenced by these calls
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sharq_[a-z_]+)\s*\(", text)))
+
+
+def test_header_symbols_exported():
+    names = declared_functions()
+    assert {"sharq_prep", "sharq_linear", "sharq_quantize", "sharq_forward"} <= set(names)
+    L = sharq.lib()
+    for n in names:
+        assert hasattr(L, n), f"{n} declared in sharq.h but not exported"
+    assert set(names) == set(sharq.SYMBOLS)
+
+
+def test_version_and_status_strings():
+    L = sharq.lib()
+    assert L.sharq_abi_version() == 1
+    for s in range(9):
+        assert L.sharq_status_str(s)
+    assert L.sharq_status_str(99) == b"unknown status"
+
+
+def test_workspace_sizes():
+    L = sharq.lib()
+    assert L.sharq_prep_workspace_bytes(4096, 4096, sharq.MXFP4) == 0
+    assert L.sharq_prep_workspace_bytes(4096, 4096, sharq.NVFP4) >= 8
+    assert L.sharq_linear_workspace_bytes(0, 10, 32, sharq.MXFP4) == 0
+
+
+def fp4(codes=A, scales=A, ts=A):
+    return sharq.SharqFp4(codes, scales, ts)
+
+
+def prep(x=A, M=4, K=64, ldx=64, n=2, m=4, fmt=0, bb=None, rr=None, mask=None, ws=None, wsb=0):
+    bb = bb if bb is not None else fp4()
+    rr = rr if rr is not None else fp4()
+    return sharq.lib().sharq_prep(x, M, K, ldx, n, m, fmt, ctypes.byref(bb), ctypes.byref(rr), mask, ws, wsb,
+                                  None)
+
+
+@pytest.mark.parametrize("kwargs,status", [
+    (dict(x=None), E_NULL),
+    (dict(K=48), E_SHAPE),                 # not a multiple of 32 (MXFP4)
+    (dict(K=0), E_SHAPE),
+    (dict(M=-1), E_SHAPE),
+    (dict(ldx=32), E_SHAPE),               # ldx < K
+    (dict(n=3, m=4), E_PATTERN),
+    (dict(n=2, m=8), E_PATTERN),
+    (dict(fmt=7), E_FORMAT),
+    (dict(x=A + 2), E_ALIGN),
+    (dict(ldx=68), E_ALIGN),               # row starts not 16-byte aligned
+    (dict(bb=fp4(codes=None)), E_NULL),
+    (dict(rr=fp4(scales=A + 4)), E_ALIGN),
+    (dict(mask=A + 1), E_ALIGN),
+    (dict(fmt=1, bb=fp4(ts=None)), E_NULL),  # NVFP4 needs tensor scales
+    (dict(fmt=1), E_WORKSPACE),              # NVFP4 needs workspace
+])
+def test_prep_rejects(kwargs, status):
+    assert prep(**kwargs) == status
+
+
+def test_prep_nvfp4_accepts_k16_shape_check():
+    # K = 48 is valid for NVFP4 (multiple of 16); fails later only on the workspace
+    assert prep(K=48, ldx=48, fmt=1) == E_WORKSPACE
+
+
+def linear(M=4, N=8, K=64, fmt=0, y=A, ldy=8, out=0, bb=None, rr=None, w=None, ws=None, wsb=0):
+    bb = bb if bb is not None else fp4()
+    rr = rr if rr is not None else fp4()
+    w = w if w is not None else fp4()
+    return sharq.lib().sharq_linear(ctypes.byref(bb), ctypes.byref(rr), M, ctypes.byref(w), N, K, fmt, y, ldy,
+                                    out, ws, wsb, None)
+
+
+@pytest.mark.parametrize("kwargs,status", [
+    (dict(y=None), E_NULL),
+    (dict(N=0), E_SHAPE),
+    (dict(K=40), E_SHAPE),
+    (dict(ldy=4), E_SHAPE),
+    (dict(M=-2), E_SHAPE),
+    (dict(fmt=3), E_FORMAT),
+    (dict(out=5), E_FORMAT),
+    (dict(y=A + 1), E_ALIGN),
+    (dict(y=A + 2, out=1), E_ALIGN),
+    (dict(w=fp4(codes=A + 8)), E_ALIGN),
+    (dict(bb=fp4(scales=None)), E_NULL),
+    (dict(fmt=1, w=fp4(ts=None)), E_NULL),
+])
+def test_linear_rejects(kwargs, status):
+    assert linear(**kwargs) == status
+
+
+def test_quantize_rejects():
+    L = sharq.lib()
+    out = fp4()
+    assert L.sharq_quantize(None, 4, 64, 64, 0, ctypes.byref(out), None, 0, None) == E_NULL
+    assert L.sharq_quantize(A, 4, 60, 64, 0, ctypes.byref(out), None, 0, None) == E_SHAPE
+    assert L.sharq_quantize(A, 4, 64, 64, 1, ctypes.byref(out), None, 0, None) == E_WORKSPACE
+    assert L.sharq_quantize(A, 4, 64, 64, 1, ctypes.byref(out), A + 8, 256, None) == E_ALIGN
+
+
+def test_forward_rejects_before_launch():
+    L = sharq.lib()
+    bb, rr, w = fp4(), fp4(), fp4()
+    args = dict(x=A, M=4, K=64, ldx=64, n=2, m=4, fmt=0, N=8, y=A, ldy=8, out=0)
+
+    def call(**kw):
+        a = {**args, **kw}
+        return L.sharq_forward(a["x"], a["M"], a["K"], a["ldx"], a["n"], a["m"], a["fmt"], ctypes.byref(bb),
+                               ctypes.byref(rr), ctypes.byref(w), a["N"], a["y"], a["ldy"], a["out"], None, 0,
+                               None)
+    assert call(ldy=4) == E_SHAPE        # the linear half is checked before the prep runs
+    assert call(out=9) == E_FORMAT
+    assert call(n=1) == E_PATTERN
+    assert call(y=None) == E_NULL
+
+
+def test_valid_call_without_gfx950_reports_device():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present; covered by the GPU tests")
+    assert prep() == E_DEVICE
+    assert linear() == E_DEVICE
