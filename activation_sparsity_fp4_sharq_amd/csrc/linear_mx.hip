@@ -79,6 +79,30 @@ __device__ __forceinline__ void tile_of(int id, int tiles_m, int tiles_n, int& t
   tn = in_group / gm;
 }
 
+// Epilogue shared by both kernels: lane holds column r32 of each 32x32 tile and rows
+// 8*(j/4) + 4*h + j%4 of it (the 32x32 accumulator layout); bf16 is rounded to nearest-even.
+template <bool OUT_F32>
+__device__ __forceinline__ void store_tile(const Args& a, const v16f (&acc)[2][4], int64_t m0, int64_t n0,
+                                           int wm, int wn, int r32, int h) {
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      const int64_t col = n0 + wn * 128 + nt * 32 + r32;
+      if (col >= a.N) continue;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int64_t row = m0 + wm * 64 + mt * 32 + 8 * (j >> 2) + 4 * h + (j & 3);
+        if (row < a.M) {
+          if constexpr (OUT_F32)
+            reinterpret_cast<float*>(a.y)[row * a.ldy + col] = acc[mt][nt][j];
+          else
+            reinterpret_cast<uint16_t*>(a.y)[row * a.ldy + col] = f32_to_bf16_rne(acc[mt][nt][j]);
+        }
+      }
+    }
+}
+
 template <bool K_ALIGNED>
 __device__ __forceinline__ uint32_t load_scale_dword(const uint8_t* s, int64_t row, int64_t nbk, int kstep) {
   if constexpr (K_ALIGNED) {
@@ -209,24 +233,7 @@ __global__ __launch_bounds__(kThreads, 1) void linear_mx_kernel(Args a) {
     __syncthreads();
   }
 
-  // ---- epilogue: lane holds column r32 of each 32x32 tile, rows 8*(j/4) + 4*h + j%4
-#pragma unroll
-  for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      const int64_t col = n0 + wn * 128 + nt * 32 + r32;
-      if (col >= a.N) continue;
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int64_t row = m0 + wm * 64 + mt * 32 + 8 * (j >> 2) + 4 * h + (j & 3);
-        if (row < a.M) {
-          if constexpr (OUT_F32)
-            reinterpret_cast<float*>(a.y)[row * a.ldy + col] = acc[mt][nt][j];
-          else
-            reinterpret_cast<uint16_t*>(a.y)[row * a.ldy + col] = f32_to_bf16_rne(acc[mt][nt][j]);
-        }
-      }
-    }
+  store_tile<OUT_F32>(a, acc, m0, n0, wm, wn, r32, h);
 }
 
 template <bool OUT_F32, bool K_ALIGNED>
