@@ -124,6 +124,68 @@ __device__ __forceinline__ void store_scales(uint8_t* dst, int64_t b, int64_t nb
   }
 }
 
+// The per-block codec of one lane: 8 consecutive bf16 of a 32-element block (the
+// quad's other three lanes hold the rest).  MODE 0: mask, backbone codes and scale,
+// residual against the dequantized backbone, residual codes and scale.  MODE 1:
+// plain MXFP4 of the 8 values into (rbyte, rpacked).  Every lane of the quad must
+// call it together (the block maxima are quad exchanges).
+template <int MODE, int SPM>
+__device__ __forceinline__ void codec_block(const uint32_t w[4], uint32_t& keep, uint32_t& bbyte,
+                                            uint32_t& bpacked, uint32_t& rbyte, uint32_t& rpacked) {
+  // x as fp32 (exact)
+  float xf[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    xf[2 * i] = __uint_as_float(w[i] << 16);
+    xf[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+  }
+
+  float r[8];
+  keep = 0xFFu; bbyte = 0; bpacked = 0;
+  if constexpr (MODE == 0) {
+    keep = keep_bits<SPM>(w);
+    // Backbone block maximum: every group's largest element is kept and the
+    // groups tile the block, so the kept maximum is the block maximum of |x|.
+    uint32_t kmax = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) kmax = umax(kmax, umax(w[i] & 0x7FFFu, (w[i] >> 16) & 0x7FFFu));
+    kmax = quad_max(kmax);
+    bbyte = e8m0_from_expfield(kmax >> 7);
+    const float bscale = scale_operand(bbyte);
+    // dropped positions become +0 (bf16 bits 0), which encodes as code 0x0
+    uint32_t wm[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      wm[i] = w[i] & (((keep >> (2 * i)) & 1 ? 0x0000FFFFu : 0u) |
+                      ((keep >> (2 * i + 1)) & 1 ? 0xFFFF0000u : 0u));
+    bpacked = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(bpacked, as_bf16x2(wm[0]), bscale, 0);
+    bpacked = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(bpacked, as_bf16x2(wm[1]), bscale, 1);
+    bpacked = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(bpacked, as_bf16x2(wm[2]), bscale, 2);
+    bpacked = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(bpacked, as_bf16x2(wm[3]), bscale, 3);
+    // residual against the dequantized backbone: one fp32 subtraction each
+    float bh[8];
+    dequant8(bpacked, bscale, bh);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) r[j] = xf[j] - bh[j];
+  } else {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) r[j] = xf[j];
+  }
+
+  // residual (or plain) quantization with its own block scale
+  uint32_t rmax = 0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) rmax = umax(rmax, __float_as_uint(r[j]) & 0x7FFFFFFFu);
+  rmax = quad_max(rmax);
+  rbyte = e8m0_from_expfield(rmax >> 23);
+  const float rscale = scale_operand(rbyte);
+  rpacked = 0;
+  rpacked = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(rpacked, r[0], r[1], rscale, 0);
+  rpacked = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(rpacked, r[2], r[3], rscale, 1);
+  rpacked = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(rpacked, r[4], r[5], rscale, 2);
+  rpacked = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(rpacked, r[6], r[7], rscale, 3);
+}
+
 // MODE 0: SharQ preparation (mask, backbone, residual).  MODE 1: plain MXFP4
 // quantization of X into (rcodes, rscales) -- used for weight payloads.
 template <int MODE, int SPM, bool DENSE_ROWS, bool WRITE_MASK>
@@ -159,58 +221,8 @@ __global__ __launch_bounds__(kThreads) void prep_mx_kernel(
     const bool valid = b < nblocks;
     const uint32_t w[4] = {v[u][0], v[u][1], v[u][2], v[u][3]};
 
-    // x as fp32 (exact)
-    float xf[8];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      xf[2 * i] = __uint_as_float(w[i] << 16);
-      xf[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
-    }
-
-    float r[8];
-    uint32_t keep = 0xFFu, bbyte = 0, bpacked = 0;
-    if constexpr (MODE == 0) {
-      keep = keep_bits<SPM>(w);
-      // Backbone block maximum: every group's largest element is kept and the
-      // groups tile the block, so the kept maximum is the block maximum of |x|.
-      uint32_t kmax = 0;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) kmax = umax(kmax, umax(w[i] & 0x7FFFu, (w[i] >> 16) & 0x7FFFu));
-      kmax = quad_max(kmax);
-      bbyte = e8m0_from_expfield(kmax >> 7);
-      const float bscale = scale_operand(bbyte);
-      // dropped positions become +0 (bf16 bits 0), which encodes as code 0x0
-      uint32_t wm[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        wm[i] = w[i] & (((keep >> (2 * i)) & 1 ? 0x0000FFFFu : 0u) |
-                        ((keep >> (2 * i + 1)) & 1 ? 0xFFFF0000u : 0u));
-      bpacked = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(bpacked, as_bf16x2(wm[0]), bscale, 0);
-      bpacked = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(bpacked, as_bf16x2(wm[1]), bscale, 1);
-      bpacked = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(bpacked, as_bf16x2(wm[2]), bscale, 2);
-      bpacked = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(bpacked, as_bf16x2(wm[3]), bscale, 3);
-      // residual against the dequantized backbone: one fp32 subtraction each
-      float bh[8];
-      dequant8(bpacked, bscale, bh);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) r[j] = xf[j] - bh[j];
-    } else {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) r[j] = xf[j];
-    }
-
-    // residual (or plain) quantization with its own block scale
-    uint32_t rmax = 0;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) rmax = umax(rmax, __float_as_uint(r[j]) & 0x7FFFFFFFu);
-    rmax = quad_max(rmax);
-    const uint32_t rbyte = e8m0_from_expfield(rmax >> 23);
-    const float rscale = scale_operand(rbyte);
-    uint32_t rpacked = 0;
-    rpacked = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(rpacked, r[0], r[1], rscale, 0);
-    rpacked = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(rpacked, r[2], r[3], rscale, 1);
-    rpacked = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(rpacked, r[4], r[5], rscale, 2);
-    rpacked = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(rpacked, r[6], r[7], rscale, 3);
+    uint32_t keep, bbyte, bpacked, rbyte, rpacked;
+    codec_block<MODE, SPM>(w, keep, bbyte, bpacked, rbyte, rpacked);
 
     // scale bytes: gathered by every lane (wave-wide shuffles), stored by 4 lanes
     const int64_t b0 = base + u * kBlocksPerWave + 4 * (lane >> 4);
@@ -228,6 +240,73 @@ __global__ __launch_bounds__(kThreads) void prep_mx_kernel(
     store_scales(rscales, b0, nblocks, lane, rpk);
     if constexpr (MODE == 0) store_scales(bscales, b0, nblocks, lane, bpk);
   }
+}
+
+// Tiled-layout output (the layout the fused GEMM loads; see sharq.h).  A wave owns
+// 16 consecutive rows x one 128-element K-step: quad k is row 16*rg + k and walks the
+// step's 4 blocks (u = 0..3).  Each store instruction then writes the 16-byte slots of
+// 16 consecutive rows of one fragment (256 contiguous bytes), and each quad leader
+// ends with its row's 4 scale bytes = one scale word, so a wave's scale words are 64
+// contiguous bytes.  Rows >= M and blocks >= K/32 are processed as zeros, which
+// writes the layout's zero padding.
+template <int MODE, int SPM, bool WRITE_MASK>
+__global__ __launch_bounds__(kThreads) void prep_mx_tiled_kernel(
+    const uint16_t* __restrict__ x, int64_t M, int64_t K, int64_t ldx, int64_t Mp, int64_t Kp,
+    uint8_t* __restrict__ bcodes, uint8_t* __restrict__ bscales, uint8_t* __restrict__ rcodes,
+    uint8_t* __restrict__ rscales, uint8_t* __restrict__ mask) {
+  const int lane = threadIdx.x & 63;
+  const int q = lane & 3, k = lane >> 2;
+  const int64_t nks = Kp / 128;
+  const int64_t task = (int64_t)blockIdx.x * (kThreads / 64) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (task >= (Mp / 16) * nks) return;  // whole waves only
+  const int64_t rg = task / nks, ks = task - rg * nks;
+  const int64_t r = rg * 16 + k;
+  const int64_t nbk = K / 32;
+
+  u32x4 v[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int64_t b = ks * 4 + u;
+    v[u] = u32x4{0u, 0u, 0u, 0u};
+    if (r < M && b < nbk)
+      v[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(x + r * ldx + b * 32 + q * 8));
+  }
+  const int64_t frag_row = (r >> 5) * (Kp / 64);
+  const int slot_row = (int)(r & 31);
+  uint32_t bword = 0, rword = 0;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int64_t b = ks * 4 + u;
+    const uint32_t w[4] = {v[u][0], v[u][1], v[u][2], v[u][3]};
+    uint32_t keep, bbyte, bpacked, rbyte, rpacked;
+    codec_block<MODE, SPM>(w, keep, bbyte, bpacked, rbyte, rpacked);
+    const int64_t off = (frag_row + (b >> 1)) * 1024 + (slot_row + 32 * (int)(b & 1)) * 16 + q * 4;
+    __builtin_nontemporal_store(rpacked, reinterpret_cast<uint32_t*>(rcodes + off));
+    rword |= rbyte << (8 * u);
+    if constexpr (MODE == 0) {
+      __builtin_nontemporal_store(bpacked, reinterpret_cast<uint32_t*>(bcodes + off));
+      bword |= bbyte << (8 * u);
+      if constexpr (WRITE_MASK)
+        if (r < M && b < nbk) mask[r * (K / 8) + b * 4 + q] = (uint8_t)keep;
+    }
+  }
+  if (q == 0) {
+    reinterpret_cast<uint32_t*>(rscales)[ks * Mp + r] = rword;
+    if constexpr (MODE == 0) reinterpret_cast<uint32_t*>(bscales)[ks * Mp + r] = bword;
+  }
+}
+
+template <int MODE, int SPM, bool WRITE_MASK>
+hipError_t launch_tiled(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, uint8_t* bcodes,
+                        uint8_t* bscales, uint8_t* rcodes, uint8_t* rscales, uint8_t* mask,
+                        hipStream_t stream) {
+  const int64_t Mp = (M + 31) / 32 * 32, Kp = (K + 127) / 128 * 128;
+  const int64_t tasks = (Mp / 16) * (Kp / 128);
+  if (tasks == 0) return hipSuccess;
+  const int64_t grid = (tasks + kThreads / 64 - 1) / (kThreads / 64);
+  prep_mx_tiled_kernel<MODE, SPM, WRITE_MASK><<<dim3((unsigned)grid), dim3(kThreads), 0, stream>>>(
+      x, M, K, ldx, Mp, Kp, bcodes, bscales, rcodes, rscales, mask);
+  return hipGetLastError();
 }
 
 template <int MODE, int SPM, bool WRITE_MASK>
@@ -252,8 +331,15 @@ hipError_t launch_dense_or_strided(const uint16_t* x, int64_t M, int64_t K, int6
 
 hipError_t launch_prep_mx(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, int sp_n, int sp_m,
                           uint8_t* bcodes, uint8_t* bscales, uint8_t* rcodes, uint8_t* rscales,
-                          uint8_t* mask, hipStream_t stream) {
+                          uint8_t* mask, int tiled, hipStream_t stream) {
   (void)sp_n;  // n = m/2 for both supported patterns
+  if (tiled) {
+    if (sp_m == 4)
+      return mask ? launch_tiled<0, 4, true>(x, M, K, ldx, bcodes, bscales, rcodes, rscales, mask, stream)
+                  : launch_tiled<0, 4, false>(x, M, K, ldx, bcodes, bscales, rcodes, rscales, mask, stream);
+    return mask ? launch_tiled<0, 8, true>(x, M, K, ldx, bcodes, bscales, rcodes, rscales, mask, stream)
+                : launch_tiled<0, 8, false>(x, M, K, ldx, bcodes, bscales, rcodes, rscales, mask, stream);
+  }
   if (sp_m == 4) {
     if (mask)
       return launch_dense_or_strided<0, 4, true>(x, M, K, ldx, bcodes, bscales, rcodes, rscales, mask, stream);
@@ -265,7 +351,9 @@ hipError_t launch_prep_mx(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, 
 }
 
 hipError_t launch_quant_mx(const uint16_t* x, int64_t rows, int64_t K, int64_t ldx, uint8_t* codes,
-                           uint8_t* scales, hipStream_t stream) {
+                           uint8_t* scales, int tiled, hipStream_t stream) {
+  if (tiled)
+    return launch_tiled<1, 4, false>(x, rows, K, ldx, nullptr, nullptr, codes, scales, nullptr, stream);
   return launch_dense_or_strided<1, 4, false>(x, rows, K, ldx, nullptr, nullptr, codes, scales, nullptr,
                                               stream);
 }

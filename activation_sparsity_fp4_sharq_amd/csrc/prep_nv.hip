@@ -11,8 +11,9 @@
 //                                         largest element is kept)
 //   pass 1  mask, backbone, R; amax|R|
 //   pass 2  mask, backbone, R again; write backbone and residual codes and scales
-// The two maxima live in the caller's workspace (two dwords, reset by a fill kernel
-// first); a final one-thread kernel writes both tensor scales.
+// The maximum passes leave one partial per work-group in the caller's workspace and a
+// one-work-group kernel reduces them (no contended atomics); a final one-thread
+// kernel writes both tensor scales.
 //
 // Arithmetic per 16-element block, each step one correctly rounded fp32 operation:
 //   q = amax_blk / (6*S);  s = E4M3(q) (nearest-even, saturating at 448);
@@ -34,6 +35,10 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kThreads = 256;
 constexpr int kUnroll = 2;
 constexpr float kUnitScale = 1.0f;
+// workspace (uint32): [0] max|X|, [1] max|R|, partial maxima from kPartialBase on
+constexpr int kPartialBase = 16;
+constexpr int kMaxPartials = 2048;
+static_assert((kPartialBase + 2 * kMaxPartials) * 4 <= (int)kNvPrepWorkspace, "workspace too small");
 
 __device__ __forceinline__ uint32_t umax(uint32_t a, uint32_t b) { return a > b ? a : b; }
 __device__ __forceinline__ uint32_t umin(uint32_t a, uint32_t b) { return a < b ? a : b; }
@@ -163,12 +168,16 @@ __global__ __launch_bounds__(kThreads) void prep_nv_kernel(
     uint8_t* __restrict__ rscales, uint8_t* __restrict__ mask, uint32_t* __restrict__ work) {
   const int lane = threadIdx.x & 63;
   const int64_t wave = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
-  const int64_t base = wave * 64 * kUnroll;
+  // the maximum passes walk the chunks grid-stride with a bounded grid; the emitting
+  // pass covers everything with one iteration per wave
+  const int64_t stride = PASS <= 1 ? (int64_t)gridDim.x * (kThreads / 64) * 64 * kUnroll : nchunks;
 
   float Sb = 1.0f, Sr = 1.0f;
   if constexpr (PASS >= 1) Sb = tensor_scale_of(work[0]);
   if constexpr (PASS == 2 && MODE == 0) Sr = tensor_scale_of(work[1]);
 
+  uint32_t run_max = 0;
+  for (int64_t base = wave * 64 * kUnroll; base < nchunks; base += stride) {
   u32x4 v[kUnroll];
 #pragma unroll
   for (int u = 0; u < kUnroll; ++u) {
@@ -186,7 +195,6 @@ __global__ __launch_bounds__(kThreads) void prep_nv_kernel(
     }
   }
 
-  uint32_t run_max = 0;
 #pragma unroll
   for (int u = 0; u < kUnroll; ++u) {
     const int64_t c = base + u * 64 + lane;
@@ -261,10 +269,33 @@ __global__ __launch_bounds__(kThreads) void prep_nv_kernel(
       }
     }
   }
-  if constexpr (PASS <= 1) {
-    run_max = wave_max(run_max);
-    if (lane == 0 && run_max) atomicMax(work + PASS, run_max);
   }
+  if constexpr (PASS <= 1) {
+    // work-group maximum -> one partial per work-group (no contended atomics)
+    __shared__ uint32_t red[kThreads / 64];
+    run_max = wave_max(run_max);
+    if (lane == 0) red[threadIdx.x >> 6] = run_max;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      uint32_t m = 0;
+      for (int i = 0; i < kThreads / 64; ++i) m = umax(m, red[i]);
+      work[kPartialBase + PASS * kMaxPartials + blockIdx.x] = m;
+    }
+  }
+}
+
+// work[slot] = max of the `n` partials of a maximum pass (one work-group).
+__global__ void nv_reduce_kernel(uint32_t* work, int slot, int n) {
+  __shared__ uint32_t red[256];
+  uint32_t m = 0;
+  for (int i = threadIdx.x; i < n; i += 256) m = umax(m, work[kPartialBase + slot * kMaxPartials + i]);
+  red[threadIdx.x] = m;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if ((int)threadIdx.x < w) red[threadIdx.x] = umax(red[threadIdx.x], red[threadIdx.x + w]);
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) work[slot] = red[0];
 }
 
 __global__ void nv_reset_kernel(uint32_t* work) {
@@ -284,11 +315,15 @@ hipError_t run_passes(const uint16_t* x, int64_t ldx, int64_t cpr, int64_t nchun
                       hipStream_t st) {
   const int64_t per_wg = (kThreads / 64) * 64 * kUnroll;
   const unsigned grid = (unsigned)((nchunks + per_wg - 1) / per_wg);
-  prep_nv_kernel<0, MODE, SPM, DENSE, WRITE_MASK><<<grid, kThreads, 0, st>>>(
+  const unsigned rgrid = grid < (unsigned)kMaxPartials ? grid : (unsigned)kMaxPartials;
+  prep_nv_kernel<0, MODE, SPM, DENSE, WRITE_MASK><<<rgrid, kThreads, 0, st>>>(
       x, ldx, cpr, nchunks, bcodes, bscales, rcodes, rscales, mask, work);
-  if constexpr (MODE == 0)
-    prep_nv_kernel<1, MODE, SPM, DENSE, WRITE_MASK><<<grid, kThreads, 0, st>>>(
+  nv_reduce_kernel<<<1, 256, 0, st>>>(work, 0, (int)rgrid);
+  if constexpr (MODE == 0) {
+    prep_nv_kernel<1, MODE, SPM, DENSE, WRITE_MASK><<<rgrid, kThreads, 0, st>>>(
         x, ldx, cpr, nchunks, bcodes, bscales, rcodes, rscales, mask, work);
+    nv_reduce_kernel<<<1, 256, 0, st>>>(work, 1, (int)rgrid);
+  }
   prep_nv_kernel<2, MODE, SPM, DENSE, WRITE_MASK><<<grid, kThreads, 0, st>>>(
       x, ldx, cpr, nchunks, bcodes, bscales, rcodes, rscales, mask, work);
   return hipGetLastError();

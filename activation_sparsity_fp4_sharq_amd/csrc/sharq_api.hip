@@ -25,6 +25,9 @@ sharq_status check_pattern(int n, int m) {
 // but an NVFP4 tensor scale is always written or read, so it must exist.
 sharq_status check_payload(const sharq_fp4* p, int fmt, int64_t rows) {
   if (!p) return SHARQ_E_NULL;
+  if (p->reserved != 0) return SHARQ_E_FORMAT;
+  if (p->layout != SHARQ_LAYOUT_ROWMAJOR && p->layout != SHARQ_LAYOUT_TILED) return SHARQ_E_FORMAT;
+  if (p->layout == SHARQ_LAYOUT_TILED && fmt != SHARQ_MXFP4) return SHARQ_E_FORMAT;
   if (rows > 0 && (!p->codes || !p->scales)) return SHARQ_E_NULL;
   if (fmt == SHARQ_NVFP4 && !p->tensor_scale) return SHARQ_E_NULL;
   if (!aligned16(p->codes) || !aligned16(p->scales)) return SHARQ_E_ALIGN;
@@ -80,6 +83,37 @@ const char* sharq_status_str(int status) {
   }
 }
 
+size_t sharq_payload_bytes(int64_t rows, int64_t K, int fmt, int layout, size_t* codes_bytes,
+                           size_t* scales_bytes) {
+  if (check_format(fmt) != SHARQ_OK || rows < 0 || K <= 0 || K % block_of(fmt)) return 0;
+  if (layout != SHARQ_LAYOUT_ROWMAJOR && layout != SHARQ_LAYOUT_TILED) return 0;
+  if (layout == SHARQ_LAYOUT_TILED && fmt != SHARQ_MXFP4) return 0;
+  size_t c, sc;
+  if (layout == SHARQ_LAYOUT_TILED) {
+    const int64_t Rp = round_up(rows, 32), Kp = round_up(K, 128);
+    c = (size_t)(Rp * Kp / 2);
+    sc = (size_t)(Rp * Kp / 32);
+  } else {
+    c = (size_t)(rows * K / 2);
+    sc = (size_t)(rows * K / block_of(fmt));
+  }
+  if (codes_bytes) *codes_bytes = c;
+  if (scales_bytes) *scales_bytes = sc;
+  return c + sc;
+}
+
+sharq_status sharq_convert_layout(const sharq_fp4* src, const sharq_fp4* dst, int64_t rows, int64_t K, int fmt,
+                                  void* stream) {
+  sharq_status s = check_format(fmt);
+  if (s != SHARQ_OK) return s;
+  if (fmt != SHARQ_MXFP4) return SHARQ_E_FORMAT;
+  if (rows < 0 || K <= 0 || K % 32 || rows > (int64_t)1 << 31 || K > (int64_t)1 << 30) return SHARQ_E_SHAPE;
+  if ((s = check_payload(src, fmt, rows)) != SHARQ_OK) return s;
+  if ((s = check_payload(dst, fmt, rows)) != SHARQ_OK) return s;
+  if ((s = check_device()) != SHARQ_OK) return s;
+  return launched(launch_convert_mx(*src, *dst, rows, K, reinterpret_cast<hipStream_t>(stream)));
+}
+
 size_t sharq_prep_workspace_bytes(int64_t, int64_t, int fmt) {
   return fmt == SHARQ_NVFP4 ? kNvPrepWorkspace : 0;
 }
@@ -101,7 +135,9 @@ sharq_status sharq_quantize(const void* x, int64_t rows, int64_t K, int64_t ldx,
   if ((s = check_device()) != SHARQ_OK) return s;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   const uint16_t* xb = reinterpret_cast<const uint16_t*>(x);
-  if (fmt == SHARQ_MXFP4) return launched(launch_quant_mx(xb, rows, K, ldx, out->codes, out->scales, st));
+  if (fmt == SHARQ_MXFP4)
+    return launched(launch_quant_mx(xb, rows, K, ldx, out->codes, out->scales,
+                                    out->layout == SHARQ_LAYOUT_TILED, st));
   return launched(launch_quant_nv(xb, rows, K, ldx, out->codes, out->scales, out->tensor_scale,
                                   reinterpret_cast<uint32_t*>(workspace), st));
 }
@@ -114,6 +150,7 @@ sharq_status sharq_prep(const void* x, int64_t M, int64_t K, int64_t ldx, int sp
   if ((s = check_pattern(sp_n, sp_m)) != SHARQ_OK) return s;
   if ((s = check_payload(backbone, fmt, M)) != SHARQ_OK) return s;
   if ((s = check_payload(residual, fmt, M)) != SHARQ_OK) return s;
+  if (backbone->layout != residual->layout) return SHARQ_E_FORMAT;
   if (mask_bits && (reinterpret_cast<uintptr_t>(mask_bits) & 3u)) return SHARQ_E_ALIGN;
   const size_t need = sharq_prep_workspace_bytes(M, K, fmt);
   if (need && (!workspace || workspace_bytes < need)) return SHARQ_E_WORKSPACE;
@@ -123,7 +160,8 @@ sharq_status sharq_prep(const void* x, int64_t M, int64_t K, int64_t ldx, int sp
   const uint16_t* xb = reinterpret_cast<const uint16_t*>(x);
   if (fmt == SHARQ_MXFP4)
     return launched(launch_prep_mx(xb, M, K, ldx, sp_n, sp_m, backbone->codes, backbone->scales,
-                                   residual->codes, residual->scales, mask_bits, st));
+                                   residual->codes, residual->scales, mask_bits,
+                                   backbone->layout == SHARQ_LAYOUT_TILED, st));
   return launched(launch_prep_nv(xb, M, K, ldx, sp_n, sp_m, backbone->codes, backbone->scales,
                                  backbone->tensor_scale, residual->codes, residual->scales,
                                  residual->tensor_scale, mask_bits,
@@ -141,6 +179,7 @@ sharq_status sharq_linear(const sharq_fp4* backbone, const sharq_fp4* residual, 
   if ((s = check_payload(weight, fmt, N)) != SHARQ_OK) return s;
   if ((s = check_payload(backbone, fmt, M)) != SHARQ_OK) return s;
   if ((s = check_payload(residual, fmt, M)) != SHARQ_OK) return s;
+  if (backbone->layout != residual->layout || backbone->layout != weight->layout) return SHARQ_E_FORMAT;
   if (M > 0) {
     if (!y) return SHARQ_E_NULL;
     if (reinterpret_cast<uintptr_t>(y) & (out_dtype == SHARQ_OUT_FP32 ? 3u : 1u)) return SHARQ_E_ALIGN;
@@ -172,6 +211,7 @@ sharq_status sharq_forward(const void* x, int64_t M, int64_t K, int64_t ldx, int
   if ((s = check_payload(backbone, fmt, M)) != SHARQ_OK) return s;
   if ((s = check_payload(residual, fmt, M)) != SHARQ_OK) return s;
   if ((s = check_payload(weight, fmt, N)) != SHARQ_OK) return s;
+  if (backbone->layout != residual->layout || backbone->layout != weight->layout) return SHARQ_E_FORMAT;
   if (M > 0 && !y) return SHARQ_E_NULL;
   if (reinterpret_cast<uintptr_t>(y) & (out_dtype == SHARQ_OUT_FP32 ? 3u : 1u)) return SHARQ_E_ALIGN;
   size_t need = sharq_prep_workspace_bytes(M, K, fmt);

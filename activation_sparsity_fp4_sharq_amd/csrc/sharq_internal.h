@@ -3,17 +3,22 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include "../../include/sharq.h"
+#include "sharq.h"
 
 namespace sharq {
 
 // Launchers: each validates nothing (the C ABI layer does), enqueues its kernels on
 // `stream` and returns hipGetLastError().
+// `tiled` selects the output layout (SHARQ_LAYOUT_TILED when non-zero).
 hipError_t launch_prep_mx(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, int sp_n,
                           int sp_m, uint8_t* bcodes, uint8_t* bscales, uint8_t* rcodes,
-                          uint8_t* rscales, uint8_t* mask, hipStream_t stream);
+                          uint8_t* rscales, uint8_t* mask, int tiled, hipStream_t stream);
 hipError_t launch_quant_mx(const uint16_t* x, int64_t rows, int64_t K, int64_t ldx,
-                           uint8_t* codes, uint8_t* scales, hipStream_t stream);
+                           uint8_t* codes, uint8_t* scales, int tiled, hipStream_t stream);
+hipError_t launch_convert_mx(const sharq_fp4& src, const sharq_fp4& dst, int64_t rows, int64_t K,
+                             hipStream_t stream);
+
+inline int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
 
 hipError_t launch_prep_nv(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, int sp_n,
                           int sp_m, uint8_t* bcodes, uint8_t* bscales, float* btscale,
@@ -33,7 +38,7 @@ hipError_t launch_linear_nv(const sharq_fp4& b, const sharq_fp4& r, int64_t M, c
                             void* work, size_t work_bytes, hipStream_t stream);
 size_t linear_nv_workspace(int64_t M, int64_t N, int64_t K);
 
-constexpr size_t kNvPrepWorkspace = 256;
+constexpr size_t kNvPrepWorkspace = 16448;  // 16 + 2 * 2048 dwords
 constexpr int kMaxDevices = 64;
 
 }  // namespace sharq

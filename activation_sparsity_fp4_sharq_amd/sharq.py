@@ -13,19 +13,21 @@ MXFP4 = 0
 NVFP4 = 1
 OUT_BF16 = 0
 OUT_FP32 = 1
+ROWMAJOR = 0
+TILED = 1
 BLOCK = {MXFP4: 32, NVFP4: 16}
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libsharq.so")
 
-SYMBOLS = ["sharq_abi_version", "sharq_status_str", "sharq_prep_workspace_bytes",
-           "sharq_linear_workspace_bytes", "sharq_quantize", "sharq_prep", "sharq_linear",
-           "sharq_forward"]
+SYMBOLS = ["sharq_abi_version", "sharq_status_str", "sharq_payload_bytes", "sharq_convert_layout",
+           "sharq_prep_workspace_bytes", "sharq_linear_workspace_bytes", "sharq_quantize", "sharq_prep",
+           "sharq_linear", "sharq_forward"]
 
 
 class SharqFp4(ctypes.Structure):
     _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p),
-                ("tensor_scale", ctypes.c_void_p)]
+                ("tensor_scale", ctypes.c_void_p), ("layout", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
 class SharqError(RuntimeError):
@@ -51,6 +53,11 @@ def lib():
         L.sharq_abi_version.argtypes = []
         L.sharq_status_str.restype = ctypes.c_char_p
         L.sharq_status_str.argtypes = [ctypes.c_int]
+        L.sharq_payload_bytes.restype = sz
+        L.sharq_payload_bytes.argtypes = [i64, i64, ctypes.c_int, ctypes.c_int, ctypes.POINTER(sz),
+                                          ctypes.POINTER(sz)]
+        L.sharq_convert_layout.restype = ctypes.c_int
+        L.sharq_convert_layout.argtypes = [P, P, i64, i64, ctypes.c_int, vp]
         L.sharq_prep_workspace_bytes.restype = sz
         L.sharq_prep_workspace_bytes.argtypes = [i64, i64, ctypes.c_int]
         L.sharq_linear_workspace_bytes.restype = sz
@@ -84,30 +91,61 @@ def _stream(stream=None):
     return ctypes.c_void_p(s.cuda_stream)
 
 
-class Payload:
-    """Device FP4 tensor: codes uint8 [rows, K/2], scales uint8 [rows, K/B],
-    tensor_scale float32 [1] (NVFP4)."""
+def payload_sizes(rows, K, fmt, layout):
+    """(codes bytes, scales bytes) of a payload, from the library."""
+    c, sc = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    if lib().sharq_payload_bytes(rows, K, fmt, layout, ctypes.byref(c), ctypes.byref(sc)) == 0 and rows * K:
+        raise ValueError(f"invalid payload: rows={rows} K={K} fmt={fmt} layout={layout}")
+    return c.value, sc.value
 
-    def __init__(self, codes, scales, tensor_scale, fmt):
-        self.codes, self.scales, self.tensor_scale, self.fmt = codes, scales, tensor_scale, fmt
+
+def default_layout(fmt):
+    return TILED if fmt == MXFP4 else ROWMAJOR
+
+
+class Payload:
+    """Device FP4 tensor [rows, K]: flat uint8 codes and scales in `layout`, plus a
+    float32 tensor scale (NVFP4)."""
+
+    def __init__(self, codes, scales, tensor_scale, fmt, layout=ROWMAJOR, rows=None, K=None):
+        self.codes, self.scales, self.tensor_scale, self.fmt, self.layout = codes, scales, tensor_scale, fmt, layout
+        self.rows = codes.shape[0] if rows is None else rows
+        self.K = codes.shape[1] * 2 if K is None else K
 
     @classmethod
-    def empty(cls, rows, K, fmt, device):
-        codes = torch.empty((rows, K // 2), dtype=torch.uint8, device=device)
-        scales = torch.empty((rows, K // BLOCK[fmt]), dtype=torch.uint8, device=device)
+    def empty(cls, rows, K, fmt, device, layout=None):
+        layout = default_layout(fmt) if layout is None else layout
+        cb, sb = payload_sizes(rows, K, fmt, layout)
+        codes = torch.empty(cb, dtype=torch.uint8, device=device)
+        scales = torch.empty(sb, dtype=torch.uint8, device=device)
         ts = torch.empty(4, dtype=torch.float32, device=device)  # 16 bytes, first element used
-        return cls(codes, scales, ts, fmt)
-
-    @property
-    def K(self):
-        return self.codes.shape[1] * 2
+        return cls(codes, scales, ts, fmt, layout, rows, K)
 
     def struct(self):
-        return SharqFp4(self.codes.data_ptr(), self.scales.data_ptr(), self.tensor_scale.data_ptr())
+        return SharqFp4(self.codes.data_ptr(), self.scales.data_ptr(), self.tensor_scale.data_ptr(),
+                        self.layout, 0)
+
+    def convert(self, layout, stream=None):
+        """This payload in another layout (a new payload; on-device re-layout)."""
+        out = Payload.empty(self.rows, self.K, self.fmt, self.codes.device, layout)
+        src, dst = self.struct(), out.struct()
+        _check("sharq_convert_layout", lib().sharq_convert_layout(ctypes.byref(src), ctypes.byref(dst), self.rows,
+                                                                  self.K, self.fmt, _stream(stream)))
+        if self.fmt == NVFP4:
+            out.tensor_scale.copy_(self.tensor_scale)
+        return out
 
     def to_host(self):
-        ts = float(self.tensor_scale[0].item()) if self.fmt == NVFP4 else 1.0
-        return self.codes.cpu().numpy(), self.scales.cpu().numpy(), ts
+        """(codes [rows, K/2], scales [rows, K/B], tensor scale) as numpy, row-major."""
+        p = self if self.layout == ROWMAJOR else self.convert(ROWMAJOR)
+        ts = float(p.tensor_scale[0].item()) if p.fmt == NVFP4 else 1.0
+        codes = p.codes.cpu().numpy().reshape(p.rows, p.K // 2)
+        scales = p.scales.cpu().numpy().reshape(p.rows, p.K // BLOCK[p.fmt])
+        return codes, scales, ts
+
+    def raw_host(self):
+        """The raw device bytes (codes, scales) as numpy, in this payload's layout."""
+        return self.codes.cpu().numpy(), self.scales.cpu().numpy()
 
 
 def workspace(nbytes, device):
@@ -124,11 +162,11 @@ def _as_bf16_2d(x):
     return x
 
 
-def quantize(x, fmt=MXFP4, stream=None):
+def quantize(x, fmt=MXFP4, layout=None, stream=None):
     """Plain FP4 quantization of a bf16 matrix (a weight payload)."""
     x = _as_bf16_2d(x)
     rows, K = x.shape
-    out = Payload.empty(rows, K, fmt, x.device)
+    out = Payload.empty(rows, K, fmt, x.device, layout)
     ws = workspace(lib().sharq_prep_workspace_bytes(rows, K, fmt), x.device)
     st = out.struct()
     _check("sharq_quantize", lib().sharq_quantize(_ptr(x), rows, K, x.stride(0), fmt, ctypes.byref(st),
@@ -136,11 +174,12 @@ def quantize(x, fmt=MXFP4, stream=None):
     return out
 
 
-def prep(x, n=2, m=4, fmt=MXFP4, want_mask=False, out=None, ws=None, stream=None):
+def prep(x, n=2, m=4, fmt=MXFP4, want_mask=False, out=None, ws=None, layout=None, stream=None):
     """SharQ activation preparation: returns (backbone, residual, mask_bits or None)."""
     x = _as_bf16_2d(x)
     M, K = x.shape
-    bb, rr = out if out is not None else (Payload.empty(M, K, fmt, x.device), Payload.empty(M, K, fmt, x.device))
+    bb, rr = out if out is not None else (Payload.empty(M, K, fmt, x.device, layout),
+                                          Payload.empty(M, K, fmt, x.device, layout))
     mask = torch.empty((M, K // 8), dtype=torch.uint8, device=x.device) if want_mask else None
     if ws is None:
         ws = workspace(lib().sharq_prep_workspace_bytes(M, K, fmt), x.device)
@@ -154,7 +193,7 @@ def prep(x, n=2, m=4, fmt=MXFP4, want_mask=False, out=None, ws=None, stream=None
 def linear(backbone, residual, weight, out_dtype=OUT_BF16, y=None, ws=None, stream=None):
     """Y = Bhat W^T + Rhat W^T on the device; returns Y [M, N] (bf16 or fp32)."""
     fmt = weight.fmt
-    M, K, N = backbone.codes.shape[0], backbone.K, weight.codes.shape[0]
+    M, K, N = backbone.rows, backbone.K, weight.rows
     dev = weight.codes.device
     if y is None:
         y = torch.empty((M, N), dtype=torch.float32 if out_dtype == OUT_FP32 else torch.bfloat16, device=dev)
@@ -172,8 +211,9 @@ def forward(x, weight, n=2, m=4, out_dtype=OUT_BF16, bufs=None, y=None, ws=None,
     x = _as_bf16_2d(x)
     fmt = weight.fmt
     M, K = x.shape
-    N = weight.codes.shape[0]
-    bb, rr = bufs if bufs is not None else (Payload.empty(M, K, fmt, x.device), Payload.empty(M, K, fmt, x.device))
+    N = weight.rows
+    bb, rr = bufs if bufs is not None else (Payload.empty(M, K, fmt, x.device, weight.layout),
+                                            Payload.empty(M, K, fmt, x.device, weight.layout))
     if y is None:
         y = torch.empty((M, N), dtype=torch.float32 if out_dtype == OUT_FP32 else torch.bfloat16,
                         device=x.device)

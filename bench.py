@@ -116,7 +116,7 @@ def main():
 
     # independent input sets (activation, weight payload, outputs) to defeat the cache
     act_bytes = M * K * 2
-    pay_bytes = 2 * (M * K // 2 + M * K // sharq.BLOCK[w.fmt])
+    pay_bytes = 2 * (M * K // 2 + M * K // sharq.BLOCK[w.fmt])   # algorithmic: real elements only
     w_bytes = N * K // 2 + N * K // sharq.BLOCK[w.fmt]
     y_bytes = M * N * 2
     per_set = act_bytes + pay_bytes + w_bytes + y_bytes
@@ -126,7 +126,8 @@ def main():
         # every set holds the same values; distinct buffers are what matters for caching
         x = x0 if i == 0 else x0.clone()
         weight = weight0 if i == 0 else sharq.Payload(weight0.codes.clone(), weight0.scales.clone(),
-                                                      weight0.tensor_scale.clone(), w.fmt)
+                                                      weight0.tensor_scale.clone(), w.fmt, weight0.layout,
+                                                      weight0.rows, weight0.K)
         bb = sharq.Payload.empty(M, K, w.fmt, dev)
         rr = sharq.Payload.empty(M, K, w.fmt, dev)
         y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
@@ -191,6 +192,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "M": M, "N": N, "K": K, "pattern": f"{w.n}:{w.m}",
                    "format": "mxfp4" if w.fmt == sharq.MXFP4 else "nvfp4", "input_sets": nsets,
+                   "payload_layout": "tiled" if weight0.layout == sharq.TILED else "row-major",
                    "description": w.note},
         "pct_mxfp4_peak": round(100.0 * eff / t_step / 1e12 / PEAK_MXFP4_TFLOPS, 3),
         "roofline": {"bound": "mfma", "kernel": kernel_key.split(":")[0], "achieved": round(ach, 2),

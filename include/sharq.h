@@ -26,16 +26,27 @@
  *    but never an out-of-bounds access.
  *  - Thread-safe: no global mutable state.
  *
- * FP4 payload layout (struct sharq_fp4), for a [rows, K] tensor:
- *  - codes: [rows, K/2] bytes, row-major, dense (row pitch K/2).  Element 2c of a
- *    row sits in the low nibble of byte c, element 2c+1 in the high nibble.  A
- *    code is E2M1: bit 3 sign, bits 2..1 exponent (bias 1), bit 0 mantissa; the
- *    magnitudes are 0, 0.5, 1, 1.5, 2, 3, 4, 6.
- *  - scales: MXFP4: [rows, K/32] E8M0 bytes (value 2^(byte-127)), one per 32
- *    consecutive elements along K.  NVFP4: [rows, K/16] E4M3 bytes (OCP E4M3,
- *    bias 7, max 448), one per 16 consecutive elements.
- *  - tensor_scale: NVFP4 only, one fp32 in device memory; element value =
- *    E2M1 * block scale * tensor_scale.  Ignored (may be NULL) for MXFP4.
+ * FP4 payload (struct sharq_fp4) of a [rows, K] tensor.  A code is E2M1: bit 3
+ * sign, bits 2..1 exponent (bias 1), bit 0 mantissa; magnitudes 0, 0.5, 1, 1.5,
+ * 2, 3, 4, 6.  Within 16 bytes holding 32 consecutive elements, element 2c sits in
+ * the low nibble of byte c.  Block scales: MXFP4 one E8M0 byte (2^(byte-127)) per
+ * 32 consecutive elements along K; NVFP4 one OCP E4M3 byte (bias 7, max 448) per
+ * 16, times one fp32 tensor_scale (device; ignored for MXFP4).
+ *
+ * Two layouts (field `layout`):
+ *  - SHARQ_LAYOUT_ROWMAJOR (both formats): codes [rows, K/2], scales [rows, K/B]
+ *    (B = 32 or 16), both row-major and dense.  This is the plain MX/NV layout.
+ *  - SHARQ_LAYOUT_TILED (MXFP4 only), the layout the gfx950 FP4 matrix
+ *    instruction consumes directly.  Let Rp = rows rounded up to 32 and Kp = K
+ *    rounded up to 128; padding holds code 0 and scale byte 0.
+ *      codes: 1 KiB fragments, fragment (rt, kc) = rows 32rt..32rt+31, elements
+ *        64kc..64kc+63, at byte ((rt * Kp/64) + kc) * 1024; inside it, the 16
+ *        bytes of row r's block b (= 2kc + c, c in {0,1}) sit at slot
+ *        (r % 32) + 32c, i.e. bytes 16*slot .. 16*slot+15.  Total Rp*Kp/2 bytes.
+ *      scales: one 32-bit word per (row, 128-element K-step ks): byte (b % 4) of
+ *        word (ks * Rp + r) is the scale of block b = 4ks + (b % 4).  Total
+ *        Rp*Kp/32 bytes.
+ *    sharq_payload_bytes gives the sizes; sharq_convert_layout converts.
  *  - codes and scales must be 16-byte aligned; an empty payload (0 rows) may
  *    pass NULL codes and scales, but an NVFP4 tensor_scale must always exist.
  */
@@ -49,7 +60,7 @@
 extern "C" {
 #endif
 
-#define SHARQ_ABI_VERSION 1
+#define SHARQ_ABI_VERSION 2
 
 typedef enum sharq_status {
   SHARQ_OK = 0,
@@ -66,10 +77,14 @@ typedef enum sharq_status {
 typedef enum sharq_format { SHARQ_MXFP4 = 0, SHARQ_NVFP4 = 1 } sharq_format;
 typedef enum sharq_out_dtype { SHARQ_OUT_BF16 = 0, SHARQ_OUT_FP32 = 1 } sharq_out_dtype;
 
+typedef enum sharq_layout { SHARQ_LAYOUT_ROWMAJOR = 0, SHARQ_LAYOUT_TILED = 1 } sharq_layout;
+
 typedef struct sharq_fp4 {
-  uint8_t* codes;      /* device, [rows, K/2]                                    */
-  uint8_t* scales;     /* device, [rows, K/32] (MXFP4) or [rows, K/16] (NVFP4)   */
+  uint8_t* codes;      /* device, see the layouts above                          */
+  uint8_t* scales;     /* device, see the layouts above                          */
   float* tensor_scale; /* device, 1 float (NVFP4); unused for MXFP4              */
+  int32_t layout;      /* sharq_layout                                           */
+  int32_t reserved;    /* must be 0                                              */
 } sharq_fp4;
 
 /* Version of this ABI (SHARQ_ABI_VERSION). */
@@ -77,6 +92,20 @@ int sharq_abi_version(void);
 
 /* Static text for a status code; never NULL. */
 const char* sharq_status_str(int status);
+
+/* Sizes in bytes of the codes and scales arrays of a [rows, K] payload in the given
+ * format and layout (writes *codes_bytes and *scales_bytes; either may be NULL).
+ * Returns the total, or 0 when the combination is invalid (tiled NVFP4, K not a
+ * multiple of the block, negative sizes).  Host-only. */
+size_t sharq_payload_bytes(int64_t rows, int64_t K, int fmt, int layout, size_t* codes_bytes,
+                           size_t* scales_bytes);
+
+/* Re-lays out an MXFP4 payload [rows, K] from src->layout into dst->layout (row-major
+ * <-> tiled; the same layout is a plain copy).  Values are unchanged; the tiled
+ * padding is written as zeros.  Asynchronous on `stream`; src and dst must not
+ * overlap.  Errors as for the other entry points; tiled NVFP4 is SHARQ_E_FORMAT. */
+sharq_status sharq_convert_layout(const sharq_fp4* src, const sharq_fp4* dst, int64_t rows, int64_t K,
+                                  int fmt, void* stream);
 
 /* Bytes of device workspace sharq_prep / sharq_quantize need for these sizes
  * (0 for MXFP4; a few hundred bytes for NVFP4, which keeps its two running
@@ -95,7 +124,7 @@ size_t sharq_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, int fmt);
  *   x       device bf16 [rows, ldx], first K columns used; 16-byte aligned, ldx % 8 == 0
  *   rows    >= 0 (0 enqueues nothing for MXFP4; NVFP4 still writes tensor_scale = 1)
  *   K       > 0, multiple of 32 (MXFP4) or 16 (NVFP4)
- *   out     payload to write (codes, scales, and tensor_scale for NVFP4)
+ *   out     payload to write (codes, scales, and tensor_scale for NVFP4), in out->layout
  *   workspace / workspace_bytes: >= sharq_prep_workspace_bytes(rows, K, fmt), device
  */
 sharq_status sharq_quantize(const void* x, int64_t rows, int64_t K, int64_t ldx, int fmt,
@@ -115,8 +144,9 @@ sharq_status sharq_quantize(const void* x, int64_t rows, int64_t K, int64_t ldx,
  *   x          device bf16 [M, ldx], first K columns used; 16-byte aligned, ldx % 8 == 0
  *   M          >= 0;  K > 0, multiple of 32 (MXFP4) or 16 (NVFP4)
  *   sp_n:sp_m  2:4 or 4:8
- *   backbone   output payload [M, K] (zero-filled dense: dropped positions hold code 0x0)
- *   residual   output payload [M, K]
+ *   backbone   output payload [M, K] (zero-filled dense: dropped positions hold code 0x0),
+ *              in the layout its `layout` field names (tiled is MXFP4 only)
+ *   residual   output payload [M, K], likewise
  *   mask_bits  device [M, K/8] or NULL: bit (k % 8) of byte k/8 set when element k is kept
  *   workspace  device, >= sharq_prep_workspace_bytes(M, K, fmt) bytes (NULL allowed when 0)
  * Masks, codes and scale bytes are deterministic and identical for every launch shape. */
@@ -130,6 +160,8 @@ sharq_status sharq_prep(const void* x, int64_t M, int64_t K, int64_t ldx, int sp
  * one fp32 accumulator per output:  Y = Bhat W^T + Rhat W^T.
  *   backbone, residual  payloads [M, K] from sharq_prep (same format)
  *   weight              payload [N, K] (e.g. from sharq_quantize)
+ *                       MXFP4 runs its fast pipelined kernel when all three payloads
+ *                       are tiled; any row-major payload takes a slower generic kernel.
  *   y                   device [M, ldy] bf16 (round to nearest even) or fp32; ldy >= N;
  *                       aligned to its element size
  *   workspace           device, >= sharq_linear_workspace_bytes(M, N, K, fmt) bytes

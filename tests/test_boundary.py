@@ -33,7 +33,7 @@ def test_header_symbols_exported():
 
 def test_version_and_status_strings():
     L = sharq.lib()
-    assert L.sharq_abi_version() == 1
+    assert L.sharq_abi_version() == 2
     for s in range(9):
         assert L.sharq_status_str(s)
     assert L.sharq_status_str(99) == b"unknown status"
@@ -46,8 +46,8 @@ def test_workspace_sizes():
     assert L.sharq_linear_workspace_bytes(0, 10, 32, sharq.MXFP4) == 0
 
 
-def fp4(codes=A, scales=A, ts=A):
-    return sharq.SharqFp4(codes, scales, ts)
+def fp4(codes=A, scales=A, ts=A, layout=0, reserved=0):
+    return sharq.SharqFp4(codes, scales, ts, layout, reserved)
 
 
 def prep(x=A, M=4, K=64, ldx=64, n=2, m=4, fmt=0, bb=None, rr=None, mask=None, ws=None, wsb=0):
@@ -73,6 +73,10 @@ def prep(x=A, M=4, K=64, ldx=64, n=2, m=4, fmt=0, bb=None, rr=None, mask=None, w
     (dict(mask=A + 1), E_ALIGN),
     (dict(fmt=1, bb=fp4(ts=None)), E_NULL),  # NVFP4 needs tensor scales
     (dict(fmt=1), E_WORKSPACE),              # NVFP4 needs workspace
+    (dict(bb=fp4(layout=2)), E_FORMAT),       # unknown layout
+    (dict(bb=fp4(reserved=1)), E_FORMAT),     # reserved field must be 0
+    (dict(fmt=1, bb=fp4(layout=1), rr=fp4(layout=1)), E_FORMAT),  # tiled is MXFP4 only
+    (dict(bb=fp4(layout=1)), E_FORMAT),       # backbone and residual layouts differ
 ])
 def test_prep_rejects(kwargs, status):
     assert prep(**kwargs) == status
@@ -104,6 +108,7 @@ def linear(M=4, N=8, K=64, fmt=0, y=A, ldy=8, out=0, bb=None, rr=None, w=None, w
     (dict(w=fp4(codes=A + 8)), E_ALIGN),
     (dict(bb=fp4(scales=None)), E_NULL),
     (dict(fmt=1, w=fp4(ts=None)), E_NULL),
+    (dict(w=fp4(layout=1)), E_FORMAT),        # mixed layouts
 ])
 def test_linear_rejects(kwargs, status):
     assert linear(**kwargs) == status
@@ -115,7 +120,7 @@ def test_quantize_rejects():
     assert L.sharq_quantize(None, 4, 64, 64, 0, ctypes.byref(out), None, 0, None) == E_NULL
     assert L.sharq_quantize(A, 4, 60, 64, 0, ctypes.byref(out), None, 0, None) == E_SHAPE
     assert L.sharq_quantize(A, 4, 64, 64, 1, ctypes.byref(out), None, 0, None) == E_WORKSPACE
-    assert L.sharq_quantize(A, 4, 64, 64, 1, ctypes.byref(out), A + 8, 256, None) == E_ALIGN
+    assert L.sharq_quantize(A, 4, 64, 64, 1, ctypes.byref(out), A + 8, 1 << 20, None) == E_ALIGN
 
 
 def test_forward_rejects_before_launch():
@@ -140,3 +145,24 @@ def test_valid_call_without_gfx950_reports_device():
         pytest.skip("a GPU is present; covered by the GPU tests")
     assert prep() == E_DEVICE
     assert linear() == E_DEVICE
+
+
+def test_payload_bytes():
+    L = sharq.lib()
+    c, sc = ctypes.c_size_t(), ctypes.c_size_t()
+    assert L.sharq_payload_bytes(100, 96, 0, 0, ctypes.byref(c), ctypes.byref(sc)) == 100 * 48 + 100 * 3
+    assert (c.value, sc.value) == (4800, 300)
+    # tiled pads rows to 32 and K to 128
+    assert L.sharq_payload_bytes(100, 96, 0, 1, ctypes.byref(c), ctypes.byref(sc)) == 128 * 64 + 128 * 4
+    assert (c.value, sc.value) == (128 * 64, 128 * 4)
+    assert L.sharq_payload_bytes(10, 64, 1, 1, None, None) == 0      # tiled NVFP4 does not exist
+    assert L.sharq_payload_bytes(10, 48, 0, 0, None, None) == 0      # K not a multiple of 32
+    assert L.sharq_payload_bytes(10, 48, 1, 0, None, None) == 10 * 24 + 10 * 3
+
+
+def test_convert_rejects():
+    L = sharq.lib()
+    a, b = fp4(), fp4(layout=1)
+    assert L.sharq_convert_layout(ctypes.byref(a), ctypes.byref(b), 4, 64, 1, None) == E_FORMAT
+    assert L.sharq_convert_layout(ctypes.byref(a), ctypes.byref(b), 4, 48, 0, None) == E_SHAPE
+    assert L.sharq_convert_layout(ctypes.byref(a), ctypes.byref(fp4(codes=None)), 4, 64, 0, None) == E_NULL

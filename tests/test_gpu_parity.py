@@ -9,6 +9,7 @@ import numpy as np
 import pytest
 import torch
 
+import layout_ref
 import oracle
 from activation_sparsity_fp4_sharq_amd import sharq
 from activation_sparsity_fp4_sharq_amd.workloads import (WORKLOADS, adversarial_activation,
@@ -24,8 +25,19 @@ def to_dev(bits):
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(DEV)
 
 
+def host_rowmajor(p):
+    """A device payload as row-major numpy arrays; tiled payloads are un-tiled on the host
+    by the test's own reference of the layout (not by the library)."""
+    if p.layout == sharq.TILED:
+        ct, st = p.raw_host()
+        assert layout_ref.padding_is_zero(ct, st, p.rows, p.K), "tiled padding not zero"
+        c, s = layout_ref.untile(ct, st, p.rows, p.K)
+        return c, s, 1.0
+    return p.to_host()
+
+
 def assert_payload_equal(got, want, what):
-    gc, gs, gt = got.to_host()
+    gc, gs, gt = host_rowmajor(got)
     assert gc.shape == want.codes.shape and gs.shape == want.scales.shape, what
     bad = np.nonzero(gc != want.codes)
     assert bad[0].size == 0, f"{what}: {bad[0].size} code bytes differ, first at {bad[0][0]},{bad[1][0]}"
@@ -35,7 +47,7 @@ def assert_payload_equal(got, want, what):
         assert np.float32(gt) == np.float32(want.tscale), f"{what}: tensor scale {gt} != {want.tscale}"
 
 
-def check_prep(xb, n, m, fmt, ldx_pad=0):
+def check_prep(xb, n, m, fmt, ldx_pad=0, layout=None):
     M, K = xb.shape
     if ldx_pad:
         wide = np.zeros((M, K + ldx_pad), np.uint16)
@@ -43,7 +55,7 @@ def check_prep(xb, n, m, fmt, ldx_pad=0):
         x = to_dev(wide)[:, :K]
     else:
         x = to_dev(xb)
-    bb, rr, mask = sharq.prep(x, n, m, fmt, want_mask=True)
+    bb, rr, mask = sharq.prep(x, n, m, fmt, want_mask=True, layout=layout)
     torch.cuda.synchronize()
     ob, orr, omask = oracle.prep(xb, n, m, fmt)
     assert np.array_equal(mask.cpu().numpy(), omask), "mask bits differ"
@@ -77,28 +89,32 @@ def test_prep_workloads_full_size(name):
     check_prep(xb, w.n, w.m, w.fmt)
 
 
-@pytest.mark.parametrize("fmt", [sharq.MXFP4, sharq.NVFP4])
+FMT_LAYOUTS = [(sharq.MXFP4, sharq.TILED), (sharq.MXFP4, sharq.ROWMAJOR), (sharq.NVFP4, sharq.ROWMAJOR)]
+FL_IDS = ["mx-tiled", "mx-rowmajor", "nv-rowmajor"]
+
+
+@pytest.mark.parametrize("fmt,layout", FMT_LAYOUTS, ids=FL_IDS)
 @pytest.mark.parametrize("n,m", [(2, 4), (4, 8)])
 @pytest.mark.parametrize("M,K", [(1, 32), (3, 64), (17, 96), (100, 160), (300, 512), (65, 1056)])
-def test_prep_shapes(fmt, n, m, M, K):
-    print(f"[prep] shape M={M} K={K} {n}:{m} fmt={fmt}", flush=True)
+def test_prep_shapes(fmt, layout, n, m, M, K):
+    print(f"[prep] shape M={M} K={K} {n}:{m} fmt={fmt} layout={layout}", flush=True)
     xb, _ = make_shape(M, 8, K, seed=M * 131 + K, dist="student_t3", token_sigma=0.5)
-    check_prep(xb, n, m, fmt)
+    check_prep(xb, n, m, fmt, layout=layout)
 
 
-@pytest.mark.parametrize("fmt", [sharq.MXFP4, sharq.NVFP4])
+@pytest.mark.parametrize("fmt,layout", FMT_LAYOUTS, ids=FL_IDS)
 @pytest.mark.parametrize("n,m", [(2, 4), (4, 8)])
-def test_prep_adversarial(fmt, n, m):
-    print(f"[prep] adversarial {n}:{m} fmt={fmt}", flush=True)
+def test_prep_adversarial(fmt, layout, n, m):
+    print(f"[prep] adversarial {n}:{m} fmt={fmt} layout={layout}", flush=True)
     xb = adversarial_activation(96, 256, seed=3)
-    check_prep(xb, n, m, fmt)
+    check_prep(xb, n, m, fmt, layout=layout)
 
 
-@pytest.mark.parametrize("fmt", [sharq.MXFP4, sharq.NVFP4])
-def test_prep_strided_rows(fmt):
-    print(f"[prep] strided ldx fmt={fmt}", flush=True)
+@pytest.mark.parametrize("fmt,layout", FMT_LAYOUTS, ids=FL_IDS)
+def test_prep_strided_rows(fmt, layout):
+    print(f"[prep] strided ldx fmt={fmt} layout={layout}", flush=True)
     xb, _ = make_shape(37, 8, 256, seed=5)
-    check_prep(xb, 2, 4, fmt, ldx_pad=24)
+    check_prep(xb, 2, 4, fmt, ldx_pad=24, layout=layout)
 
 
 @pytest.mark.parametrize("fmt", [sharq.MXFP4, sharq.NVFP4])
@@ -107,19 +123,19 @@ def test_prep_empty_and_zero(fmt):
     x = torch.zeros((0, 64), dtype=torch.bfloat16, device=DEV)
     bb, rr, _ = sharq.prep(x, 2, 4, fmt)
     torch.cuda.synchronize()
-    assert bb.codes.shape == (0, 32)
+    assert bb.codes.numel() == 0 and bb.rows == 0
     if fmt == sharq.NVFP4:
         assert bb.tensor_scale[0].item() == 1.0 and rr.tensor_scale[0].item() == 1.0
     check_prep(np.zeros((5, 64), np.uint16), 2, 4, fmt)
 
 
-@pytest.mark.parametrize("fmt", [sharq.MXFP4, sharq.NVFP4])
+@pytest.mark.parametrize("fmt,layout", FMT_LAYOUTS, ids=FL_IDS)
 @pytest.mark.parametrize("rows,K", [(512, 512), (77, 96), (14336, 4096)])
-def test_quantize_weight(fmt, rows, K):
-    print(f"[quant] rows={rows} K={K} fmt={fmt}", flush=True)
+def test_quantize_weight(fmt, layout, rows, K):
+    print(f"[quant] rows={rows} K={K} fmt={fmt} layout={layout}", flush=True)
     rng = np.random.default_rng(rows + K)
     wb = f32_to_bf16_bits(rng.normal(0, 0.02, (rows, K)).astype(np.float32))
-    got = sharq.quantize(to_dev(wb), fmt)
+    got = sharq.quantize(to_dev(wb), fmt, layout=layout)
     torch.cuda.synchronize()
     assert_payload_equal(got, oracle.quantize(wb, fmt), "weight")
 
@@ -137,8 +153,8 @@ def test_prep_deterministic_and_no_overrun():
         big_rc = torch.full_like(big_c, 0xAA)
         big_rs = torch.full_like(big_s, 0xAA)
         ts = torch.zeros(4, dtype=torch.float32, device=DEV)
-        bb = sharq.Payload(big_c[:M * K // 2].view(M, K // 2), big_s[:M * K // 32].view(M, K // 32), ts, sharq.MXFP4)
-        rr = sharq.Payload(big_rc[:M * K // 2].view(M, K // 2), big_rs[:M * K // 32].view(M, K // 32), ts, sharq.MXFP4)
+        bb = sharq.Payload(big_c[:M * K // 2], big_s[:M * K // 32], ts, sharq.MXFP4, sharq.ROWMAJOR, M, K)
+        rr = sharq.Payload(big_rc[:M * K // 2], big_rs[:M * K // 32], ts, sharq.MXFP4, sharq.ROWMAJOR, M, K)
         sharq.prep(x, 2, 4, sharq.MXFP4, out=(bb, rr))
         torch.cuda.synchronize()
         for big, n in ((big_c, M * K // 2), (big_s, M * K // 32), (big_rc, M * K // 2), (big_rs, M * K // 32)):
@@ -150,25 +166,23 @@ def test_prep_deterministic_and_no_overrun():
 
 # ------------------------------------------------------------------ GEMM parity
 
-def run_linear(xb, wb, n, m, fmt):
+def run_linear(xb, wb, n, m, fmt, layout=None):
     x, wt = to_dev(xb), to_dev(wb)
-    weight = sharq.quantize(wt, fmt)
-    bb, rr, _ = sharq.prep(x, n, m, fmt)
+    weight = sharq.quantize(wt, fmt, layout=layout)
+    bb, rr, _ = sharq.prep(x, n, m, fmt, layout=layout)
     y32 = sharq.linear(bb, rr, weight, sharq.OUT_FP32)
     y16 = sharq.linear(bb, rr, weight, sharq.OUT_BF16)
     torch.cuda.synchronize()
     return weight, bb, rr, y32, y16
 
 
-@pytest.mark.parametrize("fmt", [sharq.MXFP4, sharq.NVFP4])
+@pytest.mark.parametrize("fmt,layout", FMT_LAYOUTS, ids=FL_IDS)
 @pytest.mark.parametrize("M,N,K", [(1, 1, 32), (16, 512, 512), (37, 70, 96), (300, 260, 160),
-                                   (257, 513, 1056), (64, 256, 2048)])
-def test_linear_small_full_compare(fmt, M, N, K):
-    if fmt == sharq.NVFP4 and K % 16:
-        pytest.skip("K must be a multiple of 16")
-    print(f"[linear] M={M} N={N} K={K} fmt={fmt}", flush=True)
+                                   (257, 513, 1056), (64, 256, 2048), (520, 300, 384)])
+def test_linear_small_full_compare(fmt, layout, M, N, K):
+    print(f"[linear] M={M} N={N} K={K} fmt={fmt} layout={layout}", flush=True)
     xb, wb = make_shape(M, N, K, seed=M + N + K, dist="laplace", token_sigma=0.3)
-    weight, bb, rr, y32, y16 = run_linear(xb, wb, 2, 4, fmt)
+    weight, bb, rr, y32, y16 = run_linear(xb, wb, 2, 4, fmt, layout)
     ob, orr, _ = oracle.prep(xb, 2, 4, fmt)
     ow = oracle.quantize(wb, fmt)
     assert_payload_equal(weight, ow, "weight")
@@ -228,3 +242,34 @@ def test_linear_deterministic_and_guarded():
         assert np.all(np.isnan(out[:M * ld].reshape(M, ld)[:, N:])), "write into the ld padding"
         res.append(out[:M * ld].reshape(M, ld)[:, :N].copy())
     assert np.array_equal(res[0], res[1])
+
+
+# ------------------------------------------------------------------ layouts
+
+@pytest.mark.parametrize("rows,K", [(1, 32), (37, 96), (300, 1056), (64, 4096)])
+def test_convert_layout_matches_reference(rows, K):
+    """sharq_convert_layout against the test's host reference of the tiled layout, both ways."""
+    print(f"[layout] rows={rows} K={K}", flush=True)
+    rng = np.random.default_rng(rows * 7 + K)
+    codes = rng.integers(0, 256, (rows, K // 2), dtype=np.uint8)
+    scales = rng.integers(0, 256, (rows, K // 32), dtype=np.uint8)
+    rm = sharq.Payload(torch.from_numpy(codes.reshape(-1)).to(DEV), torch.from_numpy(scales.reshape(-1)).to(DEV),
+                       torch.ones(4, device=DEV), sharq.MXFP4, sharq.ROWMAJOR, rows, K)
+    t = rm.convert(sharq.TILED)
+    back = t.convert(sharq.ROWMAJOR)
+    torch.cuda.synchronize()
+    ct, st = layout_ref.tile(codes, scales)
+    gct, gst = t.raw_host()
+    assert np.array_equal(gct, ct) and np.array_equal(gst, st)
+    bc, bs, _ = back.to_host()
+    assert np.array_equal(bc, codes) and np.array_equal(bs, scales)
+
+
+def test_linear_rejects_mixed_layouts():
+    xb, wb = make_shape(64, 64, 128, seed=1)
+    x, wt = to_dev(xb), to_dev(wb)
+    w_rm = sharq.quantize(wt, sharq.MXFP4, layout=sharq.ROWMAJOR)
+    bb, rr, _ = sharq.prep(x, 2, 4, sharq.MXFP4, layout=sharq.TILED)
+    with pytest.raises(sharq.SharqError) as e:
+        sharq.linear(bb, rr, w_rm)
+    assert e.value.status == 4
