@@ -53,6 +53,7 @@ struct Args {
   int64_t M, N, K, ldy;
   int tiles_m, tiles_n;
   int64_t Mp, Np, Kp;  // padded extents of the tiled layout
+  bool y_aligned;      // y 16-byte aligned and ldy a multiple of 8 elements
 };
 
 __device__ __forceinline__ v8i widen(v4i a) {
@@ -260,6 +261,65 @@ constexpr int kDmaStages = 3;
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
+// Epilogue of the tiled kernels.  The weights are the instruction's A operand, so in
+// accumulator acc[mt][nt] lane (r32, h) holds output row (row0 + 32mt + r32) and
+// columns col0 + 32nt + 8g + 4h + {0,1,2,3} in elements 4g..4g+3 -- four consecutive
+// outputs.  A wave whose tile lies inside Y (and a 16-byte aligned Y) stages its bf16
+// tile through its private LDS region (rows padded to 16 bytes past the tile width)
+// and writes whole 16-byte runs, 16 lanes per row; other waves, and fp32 output,
+// store the 4-value runs directly with bounds checks.
+constexpr int kEpiPad = 16;
+
+template <bool OUT_F32, int MT, int NT>
+__device__ __forceinline__ void store_swapped(const Args& a, const v16f (&acc)[MT][NT], int64_t row0,
+                                              int64_t col0, int lane, uint8_t* lds, bool y_aligned) {
+  const int r32 = lane & 31, h = lane >> 5;
+  const bool inside = row0 + 32 * MT <= a.M && col0 + 32 * NT <= a.N;
+  if constexpr (!OUT_F32) {
+    if (inside && y_aligned) {
+      constexpr int pitch = 32 * NT * 2 + kEpiPad;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const uint32_t lo = f32_to_bf16_rne(acc[mt][nt][4 * g]) | ((uint32_t)f32_to_bf16_rne(acc[mt][nt][4 * g + 1]) << 16);
+            const uint32_t hi = f32_to_bf16_rne(acc[mt][nt][4 * g + 2]) | ((uint32_t)f32_to_bf16_rne(acc[mt][nt][4 * g + 3]) << 16);
+            *reinterpret_cast<uint2*>(lds + (mt * 32 + r32) * pitch + (nt * 32 + 8 * g + 4 * h) * 2) = make_uint2(lo, hi);
+          }
+      constexpr int lanes_per_row = 32 * NT * 2 / 16;
+      constexpr int rows_per_iter = 64 / lanes_per_row;
+      const int lr = lane / lanes_per_row, lc = lane % lanes_per_row;
+#pragma unroll
+      for (int it = 0; it < 32 * MT / rows_per_iter; ++it) {
+        const int row = it * rows_per_iter + lr;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(lds + row * pitch + lc * 16);
+        *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(a.y) + (row0 + row) * a.ldy + col0 + lc * 8) = v;
+      }
+      return;
+    }
+  }
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int64_t row = row0 + mt * 32 + r32;
+        const int64_t col = col0 + nt * 32 + 8 * g + 4 * h;
+        if (row >= a.M) continue;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (col + i < a.N) {
+            if constexpr (OUT_F32)
+              reinterpret_cast<float*>(a.y)[row * a.ldy + col + i] = acc[mt][nt][4 * g + i];
+            else
+              reinterpret_cast<uint16_t*>(a.y)[row * a.ldy + col + i] = f32_to_bf16_rne(acc[mt][nt][4 * g + i]);
+          }
+      }
+}
+
 // s_waitcnt with only the vector-memory counter constrained (expcnt/lgkmcnt left free).
 #define SHARQ_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (7 << 4) | (15 << 8) | (((n) >> 4) << 14))
 
@@ -293,29 +353,33 @@ __global__ __launch_bounds__(kThreads, 1) void linear_mx_dma_kernel(Args a) {
     fsrc[j] = base + (t * (a.Kp / 64) + sub) * kFragBytes + lane * 16;
     fdst[j] = op * kOpTileBytes + fi * kFragBytes;
   }
-  // Scale words: one operand's 256 words per K-step are 1 KiB contiguous -> waves 0..2
-  // load one operand each.
-  const bool scale_wave = wave < 3;
+  // Scale words: one operand's 256 words per K-step are 1 KiB contiguous; waves 0..2
+  // load one operand each and waves 3..7 repeat wave 2's load (identical bytes to the
+  // same place), so every wave issues the same 7 loads per stage and no branch sits
+  // between them -- the compiler's vmcnt bookkeeping then never degrades to a full wait.
   const uint8_t* ssrc;
   int64_t sstep;
+  int sdst;
   {
-    const int op = scale_wave ? wave : 0;
+    const int op = wave < 3 ? wave : 2;
     const uint8_t* base = op == 0 ? a.bs : op == 1 ? a.rs : a.ws;
     const int64_t rp = op == 2 ? a.Np : a.Mp;
     int64_t row = (op == 2 ? n0 : m0) + 4 * lane;
     row = row < rp - 4 ? row : rp - 4;
     ssrc = base + row * 4;
     sstep = rp * 4;
+    sdst = 3 * kOpTileBytes + op * 1024;
   }
-  const int sdst = 3 * kOpTileBytes + (scale_wave ? wave : 0) * 1024;
-
-  auto issue = [&](int ks, int stage) {
-    uint8_t* st = smem + stage * kDmaStageBytes;
-#pragma unroll
-    for (int j = 0; j < 6; ++j)
-      __builtin_amdgcn_global_load_lds(fsrc[j] + (int64_t)ks * 2 * kFragBytes, (lds_void_t*)(st + fdst[j]), 16, 0, 0);
-    if (scale_wave)
-      __builtin_amdgcn_global_load_lds(ssrc + (int64_t)ks * sstep, (lds_void_t*)(st + sdst), 16, 0, 0);
+  constexpr int kLoads = 7;  // per wave and stage
+  // load j of stage ks (indices past the last K-step re-load the last one into a slot
+  // nobody reads again, keeping the count per iteration constant)
+  auto issue_one = [&](int j, int ks) {
+    uint8_t* st = smem + (ks % kDmaStages) * kDmaStageBytes;
+    const int64_t kc = ks < nk ? ks : nk - 1;
+    if (j < 6)
+      __builtin_amdgcn_global_load_lds(fsrc[j] + kc * 2 * kFragBytes, (lds_void_t*)(st + fdst[j]), 16, 0, 0);
+    else
+      __builtin_amdgcn_global_load_lds(ssrc + kc * sstep, (lds_void_t*)(st + sdst), 16, 0, 0);
   };
 
   v16f acc[2][4];
@@ -324,19 +388,16 @@ __global__ __launch_bounds__(kThreads, 1) void linear_mx_dma_kernel(Args a) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = v16f{};
 
-  issue(0, 0);
-  if (nk > 1) issue(1, 1);
+#pragma unroll
+  for (int j = 0; j < kLoads; ++j) issue_one(j, 0);
+#pragma unroll
+  for (int j = 0; j < kLoads; ++j) issue_one(j, 1);
 
   for (int ks = 0; ks < nk; ++ks) {
-    // this wave's loads for stage ks are done once at most one stage's loads remain
-    if (ks + 1 < nk) {
-      if (scale_wave) SHARQ_WAIT_VMCNT(7); else SHARQ_WAIT_VMCNT(6);
-    } else {
-      SHARQ_WAIT_VMCNT(0);
-    }
-    __builtin_amdgcn_s_barrier();  // every wave's stage-ks data is in LDS; stage ks-1 is free
+    // this wave's loads of stage ks are done when at most one stage's loads remain
+    SHARQ_WAIT_VMCNT(kLoads);
+    __builtin_amdgcn_s_barrier();  // every wave's stage ks landed; slot (ks+2)%3 is free
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-    if (ks + 2 < nk) issue(ks + 2, (ks + 2) % kDmaStages);
 
     const uint8_t* st = smem + (ks % kDmaStages) * kDmaStageBytes;
     const uint32_t* sc = reinterpret_cast<const uint32_t*>(st + 3 * kOpTileBytes);
@@ -366,17 +427,25 @@ __global__ __launch_bounds__(kThreads, 1) void linear_mx_dma_kernel(Args a) {
         for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
           for (int nt = 0; nt < 4; ++nt) {
+            // weights as the instruction's A operand: each lane's accumulators are then
+            // 4 consecutive output columns of one output row (see store_swapped)
             if (sub == 0)
               acc[mt][nt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                  widen(af[p][mt]), widen(wf[nt]), acc[mt][nt], 4, 4, 0, (int)as[p][mt], 0, (int)ws[nt]);
+                  widen(wf[nt]), widen(af[p][mt]), acc[mt][nt], 4, 4, 0, (int)ws[nt], 0, (int)as[p][mt]);
             else
               acc[mt][nt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                  widen(af[p][mt]), widen(wf[nt]), acc[mt][nt], 4, 4, 2, (int)as[p][mt], 2, (int)ws[nt]);
+                  widen(wf[nt]), widen(af[p][mt]), acc[mt][nt], 4, 4, 2, (int)ws[nt], 2, (int)as[p][mt]);
+            // the next-but-one stage's loads, spread through the instructions
+            const int i = sub * 16 + (p * 2 + mt) * 4 + nt;
+            if (i % 4 == 3 && i / 4 < kLoads) issue_one(i / 4, ks + 2);
           }
     }
   }
+  SHARQ_WAIT_VMCNT(0);  // trailing loads land before the stage ring is reused
 
-  store_tile<OUT_F32>(a, acc, m0, n0, wm, wn, r32, h);
+  __syncthreads();  // every wave is done with the stage ring; reuse it for the epilogue
+  store_swapped<OUT_F32, 2, 4>(a, acc, m0 + wm * 64, n0 + wn * 128, lane,
+                               smem + wave * (64 * (256 + kEpiPad)), a.y_aligned);
 }
 
 template <bool OUT_F32>
@@ -450,30 +519,8 @@ __device__ __forceinline__ void mma_substep(v16f (&acc)[4][4], const Frags& f, c
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt)
         acc[mt][nt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-            widen(f.a[p][mt]), widen(f.w[nt]), acc[mt][nt], 4, 4, 2 * SUB, (int)sc.a[p][mt], 2 * SUB,
-            (int)sc.w[nt]);
-}
-
-template <bool OUT_F32>
-__device__ __forceinline__ void store_tile_4x4(const Args& a, const v16f (&acc)[4][4], int64_t m0, int64_t n0,
-                                               int wm, int wn, int r32, int h) {
-#pragma unroll
-  for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      const int64_t col = n0 + wn * 128 + nt * 32 + r32;
-      if (col >= a.N) continue;
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int64_t row = m0 + wm * 128 + mt * 32 + 8 * (j >> 2) + 4 * h + (j & 3);
-        if (row < a.M) {
-          if constexpr (OUT_F32)
-            reinterpret_cast<float*>(a.y)[row * a.ldy + col] = acc[mt][nt][j];
-          else
-            reinterpret_cast<uint16_t*>(a.y)[row * a.ldy + col] = f32_to_bf16_rne(acc[mt][nt][j]);
-        }
-      }
-    }
+            widen(f.w[nt]), widen(f.a[p][mt]), acc[mt][nt], 4, 4, 2 * SUB, (int)sc.w[nt], 2 * SUB,
+            (int)sc.a[p][mt]);
 }
 
 template <bool OUT_F32>
@@ -571,7 +618,9 @@ void linear_mx_pipe_kernel(Args a) {
     sc = scn;
   }
 
-  store_tile_4x4<OUT_F32>(a, acc, m0, n0, wm, wn, r32, h);
+  __syncthreads();  // every wave is done with the stage ring; reuse it for the epilogue
+  store_swapped<OUT_F32, 4, 4>(a, acc, m0 + wm * 128, n0 + wn * 128, lane,
+                               smem + wave * (128 * (256 + kEpiPad)), a.y_aligned);
 }
 
 template <bool OUT_F32>
@@ -588,6 +637,183 @@ hipError_t launch_pipe(const Args& a, hipStream_t stream) {
   }
   const int grid = a.tiles_m * a.tiles_n;
   linear_mx_pipe_kernel<OUT_F32><<<dim3(grid), dim3(kPipeThreads), kDmaStages * kDmaStageBytes, stream>>>(a);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------------
+// Streaming kernel (the default for tiled payloads).  4 waves, one per SIMD; wave w
+// owns output rows m0+64w .. +63 and all 256 columns of the work-group tile (2 x 8
+// instructions per path and sub-step, 256 fp32 accumulators per lane), so a weight
+// fragment read from LDS feeds 4 instructions and an activation fragment 8.
+// Everything reaches LDS by DMA: per K-step and wave, its own 8 activation
+// fragments (backbone and residual; tiled fragments are exactly instruction
+// operands) and their scale words into a wave-private region, plus a quarter of the
+// 16 shared weight fragments and of their scale words -- 15 loads, the same for
+// every wave and every iteration (indices past the last K-step are clamped), with
+// no branch between them, so a single constant vmcnt threshold means "the stage I
+// need next has landed" and the compiler never has to add a conservative wait.
+// Three LDS slots; stage i+2 is issued right after the barrier that frees its slot.
+constexpr int kAregThreads = 256;
+constexpr int kSWFrag = 0;                              // 16 weight fragments
+constexpr int kSWScale = 16 * kFragBytes;               // 256 weight scale words
+constexpr int kSAWave = kSWScale + 1024;                // per wave: 8 A fragments + 128 scale words
+constexpr int kSAWaveBytes = 8 * kFragBytes + 512;
+constexpr int kSStageBytes = kSAWave + 4 * kSAWaveBytes;  // 52224
+constexpr int kSSlots = 3;
+constexpr int kAregEpiPitch = 8 * 32 * 2 + kEpiPad;       // bf16 row of a 64x256 wave tile
+constexpr int kAregLds = (4 * 64 * kAregEpiPitch > kSSlots * kSStageBytes) ? 4 * 64 * kAregEpiPitch
+                                                                            : kSSlots * kSStageBytes;
+constexpr int kSLoadsPerStage = 15;
+
+template <bool OUT_F32>
+__global__ __launch_bounds__(kAregThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void linear_mx_areg_kernel(Args a) {
+  extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r32 = lane & 31, h = lane >> 5;
+
+  int tm, tn;
+  tile_of(blockIdx.x, a.tiles_m, a.tiles_n, tm, tn);
+  const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
+  const int nk = (int)(a.Kp / 128);
+  const int64_t kc_per_rt = a.Kp / 64;
+
+  // ---- load descriptors (per lane source, per wave LDS offset within a stage)
+  const uint8_t* src[10];  // 8 A fragments, 4 W fragments below, scale words separately
+  int dst[10];
+#pragma unroll
+  for (int p = 0; p < 2; ++p)
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      int64_t t = (m0 + 64 * wave) / 32 + mt;
+      t = t < a.Mp / 32 ? t : a.Mp / 32 - 1;
+      const uint8_t* base = p == 0 ? a.bc : a.rc;
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub) {
+        const int j = (p * 2 + mt) * 2 + sub;
+        src[j] = base + (t * kc_per_rt + sub) * kFragBytes + lane * 16;
+        dst[j] = kSAWave + wave * kSAWaveBytes + j * kFragBytes;
+      }
+    }
+  const uint8_t* wsrc[4];
+  int wdst[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int fi = wave * 4 + j, nt = fi >> 1, sub = fi & 1;
+    int64_t t = n0 / 32 + nt;
+    t = t < a.Np / 32 ? t : a.Np / 32 - 1;
+    wsrc[j] = a.wc + (t * kc_per_rt + sub) * kFragBytes + lane * 16;
+    wdst[j] = kSWFrag + fi * kFragBytes;
+  }
+  const uint8_t* asrc[2];
+  {
+    int64_t row = m0 + 64 * wave + lane;
+    row = row < a.Mp ? row : a.Mp - 1;
+    asrc[0] = a.bs + row * 4;
+    asrc[1] = a.rs + row * 4;
+  }
+  const uint8_t* wssrc;
+  {
+    int64_t row = n0 + 64 * wave + lane;
+    row = row < a.Np ? row : a.Np - 1;
+    wssrc = a.ws + row * 4;
+  }
+  // Load j (0..14) of stage ks.  The 15 loads of a stage are spread through the
+  // matrix instructions of the current K-step (one after every fourth instruction):
+  // the texture unit takes ~16 cycles per 1 KiB request, and a burst of 60 requests
+  // per work-group would stall every wave for ~1000 cycles at the start of a step.
+  auto issue_one = [&](int j, int ks) {
+    uint8_t* st = smem + (ks % kSSlots) * kSStageBytes;
+    const int64_t kc = ks < nk ? ks : nk - 1;
+    if (j < 8)
+      __builtin_amdgcn_global_load_lds(src[j] + kc * 2 * kFragBytes, (lds_void_t*)(st + dst[j]), 16, 0, 0);
+    else if (j < 12)
+      __builtin_amdgcn_global_load_lds(wsrc[j - 8] + kc * 2 * kFragBytes, (lds_void_t*)(st + wdst[j - 8]), 16, 0, 0);
+    else if (j < 14)
+      __builtin_amdgcn_global_load_lds(asrc[j - 12] + kc * a.Mp * 4,
+                                       (lds_void_t*)(st + kSAWave + wave * kSAWaveBytes + 8 * kFragBytes + (j - 12) * 256),
+                                       4, 0, 0);
+    else
+      __builtin_amdgcn_global_load_lds(wssrc + kc * a.Np * 4, (lds_void_t*)(st + kSWScale + 256 * wave), 4, 0, 0);
+  };
+  auto issue = [&](int ks) {
+#pragma unroll
+    for (int j = 0; j < kSLoadsPerStage; ++j) issue_one(j, ks);
+  };
+
+  v16f acc[2][8];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[i][j] = v16f{};
+
+  issue(0);
+  issue(1);
+  for (int ks = 0; ks < nk; ++ks) {
+    // this wave's loads of stage ks are done when at most one stage's remain
+    SHARQ_WAIT_VMCNT(kSLoadsPerStage);
+    __builtin_amdgcn_s_barrier();  // every wave's stage ks landed; slot (ks+2)%3 is free
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+
+    const uint8_t* st = smem + (ks % kSSlots) * kSStageBytes;
+    const uint8_t* ab = st + kSAWave + wave * kSAWaveBytes;
+    const uint32_t* wsw = reinterpret_cast<const uint32_t*>(st + kSWScale);
+    const uint32_t* asw = reinterpret_cast<const uint32_t*>(ab + 8 * kFragBytes);
+    uint32_t ws[8], as[2][2];
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt) ws[nt] = wsw[nt * 32 + r32] >> (8 * h);
+#pragma unroll
+    for (int p = 0; p < 2; ++p)
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) as[p][mt] = asw[p * 64 + mt * 32 + r32] >> (8 * h);
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) {
+      v4i af[2][2], wf[8];
+#pragma unroll
+      for (int p = 0; p < 2; ++p)
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+          af[p][mt] = *reinterpret_cast<const v4i*>(ab + ((p * 2 + mt) * 2 + sub) * kFragBytes + lane * 16);
+#pragma unroll
+      for (int nt = 0; nt < 8; ++nt)
+        wf[nt] = *reinterpret_cast<const v4i*>(st + kSWFrag + (nt * 2 + sub) * kFragBytes + lane * 16);
+#pragma unroll
+      for (int p = 0; p < 2; ++p)
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+          for (int nt = 0; nt < 8; ++nt) {
+            if (sub == 0)
+              acc[mt][nt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                  widen(wf[nt]), widen(af[p][mt]), acc[mt][nt], 4, 4, 0, (int)ws[nt], 0, (int)as[p][mt]);
+            else
+              acc[mt][nt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                  widen(wf[nt]), widen(af[p][mt]), acc[mt][nt], 4, 4, 2, (int)ws[nt], 2, (int)as[p][mt]);
+            const int i = sub * 32 + (p * 2 + mt) * 8 + nt;  // instruction index in the K-step
+            if (i % 4 == 3 && i / 4 < kSLoadsPerStage) issue_one(i / 4, ks + 2);
+          }
+    }
+  }
+  SHARQ_WAIT_VMCNT(0);  // the clamped trailing loads land before LDS is reused
+  __syncthreads();
+  store_swapped<OUT_F32, 2, 8>(a, acc, m0 + 64 * wave, n0, lane, smem + wave * (64 * kAregEpiPitch), a.y_aligned);
+}
+
+template <bool OUT_F32>
+hipError_t launch_areg(const Args& a, hipStream_t stream) {
+  static std::atomic<bool> configured[kMaxDevices];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices || !configured[dev].load(std::memory_order_acquire)) {
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&linear_mx_areg_kernel<OUT_F32>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, kAregLds);
+    if (e != hipSuccess) return e;
+    if (dev >= 0 && dev < kMaxDevices) configured[dev].store(true, std::memory_order_release);
+  }
+  linear_mx_areg_kernel<OUT_F32><<<dim3(a.tiles_m * a.tiles_n), dim3(kAregThreads), kAregLds, stream>>>(a);
   return hipGetLastError();
 }
 
@@ -618,7 +844,8 @@ hipError_t launch_linear_mx(const sharq_fp4& b, const sharq_fp4& r, int64_t M, c
                             hipStream_t stream) {
   if (M == 0 || N == 0) return hipSuccess;
   Args a{b.codes, b.scales, r.codes, r.scales, w.codes, w.scales, y, M, N, K, ldy,
-         (int)((M + BM - 1) / BM), (int)((N + BN - 1) / BN), round_up(M, 32), round_up(N, 32), round_up(K, 128)};
+         (int)((M + BM - 1) / BM), (int)((N + BN - 1) / BN), round_up(M, 32), round_up(N, 32), round_up(K, 128),
+         (reinterpret_cast<uintptr_t>(y) & 15u) == 0 && ldy % 8 == 0};
   if (b.layout == SHARQ_LAYOUT_TILED)  // all three are tiled (checked by the caller)
     return out_fp32 ? launch_dma<true>(a, stream) : launch_dma<false>(a, stream);
   const bool k_aligned = K % 128 == 0;
