@@ -817,6 +817,117 @@ hipError_t launch_areg(const Args& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------------
+// Small-M kernel (M <= 32, the decode shape).  The product is a stream of the weight
+// payload, so the design goal is bytes in flight, not matrix throughput.  A work-group
+// owns NT 32-row weight tiles (32*NT output columns) and its 8 waves split K; each
+// wave issues every load of a chunk of CH K-steps straight into registers before its
+// first instruction uses one (a tiled fragment is an instruction operand: 1 KiB of
+// contiguous codes), so a wave keeps CH*NT*2 KiB of weights in flight.  The activation
+// fragments of a K-step are shared by the NT tiles.  Trailing steps of a chunk load
+// clamped (valid) addresses and multiply zeroed weights, so the load sequence has no
+// branches.  The 8 partial tiles are summed through LDS.
+constexpr int kSmallWaves = 8;
+constexpr int kSmallThreads = 64 * kSmallWaves;
+
+template <bool OUT_F32, int NT, int CH>
+__global__ __launch_bounds__(kSmallThreads, 1) void linear_mx_small_kernel(Args a) {
+  __shared__ float part[kSmallWaves][NT][16][64];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r32 = lane & 31, h = lane >> 5;
+  const int64_t tn0 = (int64_t)blockIdx.x * NT;
+  const int nk = (int)(a.Kp / 128);
+  const int64_t kc_per_rt = a.Kp / 64;
+  const int k0 = (int)((int64_t)nk * wave / kSmallWaves);
+  const int k1 = (int)((int64_t)nk * (wave + 1) / kSmallWaves);
+
+  const uint8_t* wsrc[NT];
+  const uint32_t* wssrc[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    // a tile past the last one (odd tile count) re-reads the last tile; its result is
+    // not stored
+    const int64_t tn = tn0 + t < a.Np / 32 ? tn0 + t : a.Np / 32 - 1;
+    wsrc[t] = a.wc + tn * kc_per_rt * kFragBytes + lane * 16;
+    wssrc[t] = reinterpret_cast<const uint32_t*>(a.ws) + tn * 32 + r32;
+  }
+  const uint8_t* bsrc = a.bc + lane * 16;  // activation row tile 0
+  const uint8_t* rsrc = a.rc + lane * 16;
+  const uint32_t* bssrc = reinterpret_cast<const uint32_t*>(a.bs) + r32;
+  const uint32_t* rssrc = reinterpret_cast<const uint32_t*>(a.rs) + r32;
+
+  v16f acc[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) acc[t] = v16f{};
+  for (int c = k0; c < k1; c += CH) {
+    v4i wf[CH][NT][2], bf[CH][2], rf[CH][2];
+    uint32_t wsw[CH][NT], bsw[CH], rsw[CH];
+#pragma unroll
+    for (int j = 0; j < CH; ++j) {
+      const int64_t ks = c + j < k1 ? c + j : k1 - 1;
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+          wf[j][t][sub] = *reinterpret_cast<const v4i*>(wsrc[t] + (2 * ks + sub) * kFragBytes);
+        bf[j][sub] = *reinterpret_cast<const v4i*>(bsrc + (2 * ks + sub) * kFragBytes);
+        rf[j][sub] = *reinterpret_cast<const v4i*>(rsrc + (2 * ks + sub) * kFragBytes);
+      }
+#pragma unroll
+      for (int t = 0; t < NT; ++t) wsw[j][t] = wssrc[t][ks * a.Np];
+      bsw[j] = bssrc[ks * a.Mp];
+      rsw[j] = rssrc[ks * a.Mp];
+    }
+    __builtin_amdgcn_sched_barrier(0);  // keep every load of the chunk ahead of the math
+#pragma unroll
+    for (int j = 0; j < CH; ++j) {
+      const bool live = c + j < k1;
+      const int bs = (int)(bsw[j] >> (8 * h)), rs = (int)(rsw[j] >> (8 * h));
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const int ws = (int)(wsw[j][t] >> (8 * h));
+        const v4i w0 = live ? wf[j][t][0] : v4i{0, 0, 0, 0};
+        const v4i w1 = live ? wf[j][t][1] : v4i{0, 0, 0, 0};
+        acc[t] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(widen(w0), widen(bf[j][0]), acc[t], 4, 4, 0, ws, 0, bs);
+        acc[t] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(widen(w0), widen(rf[j][0]), acc[t], 4, 4, 0, ws, 0, rs);
+        acc[t] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(widen(w1), widen(bf[j][1]), acc[t], 4, 4, 2, ws, 2, bs);
+        acc[t] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(widen(w1), widen(rf[j][1]), acc[t], 4, 4, 2, ws, 2, rs);
+      }
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) part[wave][t][j][lane] = acc[t][j];
+  __syncthreads();
+  // reduction over the 8 waves, one output per thread per pass, columns fastest
+  for (int q = tid; q < NT * 32 * 32; q += kSmallThreads) {
+    const int row = q / (32 * NT), colw = q - row * (32 * NT);
+    const int t = colw >> 5, cc = colw & 31;
+    const int j = 4 * (cc >> 3) + (cc & 3), src_lane = row + 32 * ((cc >> 2) & 1);
+    const int64_t col = (tn0 + t) * 32 + cc;
+    if (row >= a.M || col >= a.N) continue;
+    float v = 0.f;
+#pragma unroll
+    for (int w = 0; w < kSmallWaves; ++w) v += part[w][t][j][src_lane];
+    if constexpr (OUT_F32)
+      reinterpret_cast<float*>(a.y)[row * a.ldy + col] = v;
+    else
+      reinterpret_cast<uint16_t*>(a.y)[row * a.ldy + col] = f32_to_bf16_rne(v);
+  }
+}
+
+template <bool OUT_F32>
+hipError_t launch_small(const Args& a, hipStream_t stream) {
+  constexpr int NT = 2, CH = 4;
+  const int64_t tiles = a.Np / 32;
+  linear_mx_small_kernel<OUT_F32, NT, CH>
+      <<<dim3((unsigned)((tiles + NT - 1) / NT)), dim3(kSmallThreads), 0, stream>>>(a);
+  return hipGetLastError();
+}
+
 template <bool OUT_F32, bool K_ALIGNED>
 hipError_t launch(const Args& a, hipStream_t stream) {
   // The dynamic-LDS limit is a per-device function attribute; setting it twice is harmless.
@@ -846,8 +957,10 @@ hipError_t launch_linear_mx(const sharq_fp4& b, const sharq_fp4& r, int64_t M, c
   Args a{b.codes, b.scales, r.codes, r.scales, w.codes, w.scales, y, M, N, K, ldy,
          (int)((M + BM - 1) / BM), (int)((N + BN - 1) / BN), round_up(M, 32), round_up(N, 32), round_up(K, 128),
          (reinterpret_cast<uintptr_t>(y) & 15u) == 0 && ldy % 8 == 0};
-  if (b.layout == SHARQ_LAYOUT_TILED)  // all three are tiled (checked by the caller)
+  if (b.layout == SHARQ_LAYOUT_TILED) {  // all three are tiled (checked by the caller)
+    if (M <= 32) return out_fp32 ? launch_small<true>(a, stream) : launch_small<false>(a, stream);
     return out_fp32 ? launch_dma<true>(a, stream) : launch_dma<false>(a, stream);
+  }
   const bool k_aligned = K % 128 == 0;
   if (out_fp32) return k_aligned ? launch<true, true>(a, stream) : launch<true, false>(a, stream);
   return k_aligned ? launch<false, true>(a, stream) : launch<false, false>(a, stream);

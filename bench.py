@@ -90,6 +90,35 @@ def cpu_baseline(w, xb, wb, target_s):
     }
 
 
+def back_to_back_seconds(launch, reps, stream):
+    """Average device time of one launch, from HIP events on the launch stream around
+    `reps` consecutive launches.  A spin kernel holds the stream while the host queues
+    them, so the events bracket back-to-back execution rather than host submission
+    gaps (which would otherwise dominate for microsecond kernels)."""
+    import torch
+
+    cycles = 1 << 23
+    while True:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(stream):
+            s0.record(stream)
+            torch.cuda._sleep(cycles)
+            s1.record(stream)
+        t0 = time.perf_counter()
+        e0.record(stream)
+        for i in range(reps):
+            launch(i)
+        e1.record(stream)
+        host_s = time.perf_counter() - t0
+        torch.cuda.synchronize()
+        if s0.elapsed_time(s1) * 1e-3 > 1.5 * host_s:
+            return e0.elapsed_time(e1) * 1e-3 / reps
+        cycles *= 4
+        if cycles > 1 << 34:
+            raise RuntimeError("could not hold the stream long enough to queue the launches")
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -136,16 +165,10 @@ def main():
                              sharq.lib().sharq_linear_workspace_bytes(M, N, K, w.fmt)), dev)
     stream = torch.cuda.current_stream()
 
-    def step(i, ev=None):
+    def step(i):
         x, weight, bb, rr, y = sets[i % nsets]
-        if ev is not None:
-            ev[0].record(stream)
         sharq.prep(x, w.n, w.m, w.fmt, out=(bb, rr), ws=ws, stream=stream)
-        if ev is not None:
-            ev[1].record(stream)
         sharq.linear(bb, rr, weight, sharq.OUT_BF16, y=y, ws=ws, stream=stream)
-        if ev is not None:
-            ev[2].record(stream)
 
     for i in range(args.warmup):
         step(i)
@@ -159,12 +182,16 @@ def main():
     t_step = (time.perf_counter() - t0) / args.steps
 
     # per-kernel durations with HIP events on the launch stream (separate pass)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    for i in range(args.steps):
-        step(i, evs[i])
-    torch.cuda.synchronize()
-    t_prep = float(np.mean([e[0].elapsed_time(e[1]) for e in evs])) * 1e-3
-    t_lin = float(np.mean([e[1].elapsed_time(e[2]) for e in evs])) * 1e-3
+    def prep_only(i):
+        x, weight, bb, rr, y = sets[i % nsets]
+        sharq.prep(x, w.n, w.m, w.fmt, out=(bb, rr), ws=ws, stream=stream)
+
+    def linear_only(i):
+        x, weight, bb, rr, y = sets[i % nsets]
+        sharq.linear(bb, rr, weight, sharq.OUT_BF16, y=y, ws=ws, stream=stream)
+
+    t_prep = back_to_back_seconds(prep_only, args.steps, stream)
+    t_lin = back_to_back_seconds(linear_only, args.steps, stream)
 
     eff = 2.0 * M * N * K
     alg = eff * (1.0 + w.n / w.m)
