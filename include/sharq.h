@@ -24,7 +24,8 @@
  *    is returned and nothing has been enqueued or written.
  *  - Non-finite inputs are outside the contract: they produce unspecified codes
  *    but never an out-of-bounds access.
- *  - Thread-safe: no global mutable state.
+ *  - Thread-safe: the only global state is a per-device flag array for the one-time
+ *    kernel attribute set-up (atomic) and a per-thread cache of the device check.
  *
  * FP4 payload (struct sharq_fp4) of a [rows, K] tensor.  A code is E2M1: bit 3
  * sign, bits 2..1 exponent (bias 1), bit 0 mantissa; magnitudes 0, 0.5, 1, 1.5,
