@@ -36,62 +36,81 @@ __device__ __forceinline__ uint32_t quad_max(uint32_t v) {
   return v;
 }
 
-// Sort (a >= b).
-__device__ __forceinline__ void cswap(uint32_t& a, uint32_t& b) {
-  uint32_t hi = umax(a, b), lo = umin(a, b);
-  a = hi;
-  b = lo;
+__device__ __forceinline__ uint32_t umax3(uint32_t a, uint32_t b, uint32_t c) { return umax(umax(a, b), c); }
+__device__ __forceinline__ uint32_t umin3(uint32_t a, uint32_t b, uint32_t c) { return umin(umin(a, b), c); }
+
+// Median of three unsigned integers (one v_med3_u32; the compiler does not form it
+// from min/max expressions).
+__device__ __forceinline__ uint32_t umed3(uint32_t a, uint32_t b, uint32_t c) {
+  uint32_t r;
+  asm("v_med3_u32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
 }
 
-// Keep bits (bit j = element j of the lane's 8) for the top-n-of-m mask.  Every
-// element gets a compound key (|x| bits, then a reversed index) so that keys are
-// distinct and "larger key" means "ranks earlier": bigger magnitude first, lower
-// index first among equal magnitudes.  The kept elements are those at or above
-// the n-th largest compound key of their group.
+// Second largest of four: with m = the median of (a, b, c), the second largest of
+// all four is m unless d lies above m, in which case it is min(max(a, b, c), d).
+__device__ __forceinline__ uint32_t second_of_4(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  return umax(umed3(a, b, c), umin(umax3(a, b, c), d));
+}
+
+// Descending sort of four (s0 >= s1 >= s2 >= s3) from the max, min and median of
+// the first three and the fourth value.
+__device__ __forceinline__ void sort4(uint32_t a, uint32_t b, uint32_t c, uint32_t d, uint32_t s[4]) {
+  const uint32_t hi = umax3(a, b, c), lo = umin3(a, b, c), md = umed3(a, b, c);
+  s[0] = umax(hi, d);
+  s[1] = umax(md, umin(hi, d));
+  s[2] = umin(md, umax(lo, d));
+  s[3] = umin(lo, d);
+}
+
+// Fourth largest of eight: the top four of two descending runs a and b are
+// max(a_i, b_{3-i}), so the fourth largest is the smallest of those four.
+__device__ __forceinline__ uint32_t fourth_of_8(const uint32_t c[8]) {
+  uint32_t a[4], b[4];
+  sort4(c[0], c[1], c[2], c[3], a);
+  sort4(c[4], c[5], c[6], c[7], b);
+  return umin(umin3(umax(a[0], b[3]), umax(a[1], b[2]), umax(a[2], b[1])), umax(a[3], b[0]));
+}
+
+// Top-n-of-m selection on the lane's 8 elements.  Each element gets a compound key:
+// its magnitude (the fp32 image of a bf16 value has 16 zero low bits) with a
+// reversed in-group index in the low bits, so keys are distinct and "larger key"
+// means "ranks earlier": bigger magnitude first, lower index first among equal
+// magnitudes (+0 and -0 are equal).  An element is kept when its key is at or
+// above the n-th largest key of its group.
 template <int SPM>
-__device__ __forceinline__ uint32_t keep_bits(const uint32_t w[4]) {
+__device__ __forceinline__ void keep_mask(const float xf[8], bool kept[8]) {
   uint32_t ck[8];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    uint32_t key = (j & 1) ? (w[j >> 1] >> 16) & 0x7FFFu : w[j >> 1] & 0x7FFFu;
-    ck[j] = SPM == 4 ? (key << 2) | (3u - (j & 3)) : (key << 3) | (7u - j);
-  }
-  uint32_t bits = 0;
+  for (int j = 0; j < 8; ++j)
+    ck[j] = (__float_as_uint(xf[j]) & 0x7FFF0000u) | (uint32_t)(SPM == 4 ? 3 - (j & 3) : 7 - j);
   if constexpr (SPM == 4) {
+    const uint32_t t0 = second_of_4(ck[0], ck[1], ck[2], ck[3]);
+    const uint32_t t1 = second_of_4(ck[4], ck[5], ck[6], ck[7]);
 #pragma unroll
-    for (int g = 0; g < 2; ++g) {
-      const uint32_t* c = ck + 4 * g;
-      uint32_t hi1 = umax(c[0], c[1]), lo1 = umin(c[0], c[1]);
-      uint32_t hi2 = umax(c[2], c[3]), lo2 = umin(c[2], c[3]);
-      uint32_t second = umax(umin(hi1, hi2), umax(lo1, lo2));  // 2nd largest of 4
-#pragma unroll
-      for (int j = 0; j < 4; ++j) bits |= (c[j] >= second ? 1u : 0u) << (4 * g + j);
-    }
+    for (int j = 0; j < 8; ++j) kept[j] = ck[j] >= (j < 4 ? t0 : t1);
   } else {
-    uint32_t a0 = ck[0], a1 = ck[1], a2 = ck[2], a3 = ck[3];
-    uint32_t b0 = ck[4], b1 = ck[5], b2 = ck[6], b3 = ck[7];
-    cswap(a0, a1); cswap(a2, a3); cswap(a0, a2); cswap(a1, a3); cswap(a1, a2);
-    cswap(b0, b1); cswap(b2, b3); cswap(b0, b2); cswap(b1, b3); cswap(b1, b2);
-    // top half of two descending runs: max(a_i, b_{3-i}); its minimum is the 4th largest
-    uint32_t fourth = umin(umin(umax(a0, b3), umax(a1, b2)), umin(umax(a2, b1), umax(a3, b0)));
+    const uint32_t t = fourth_of_8(ck);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) bits |= (ck[j] >= fourth ? 1u : 0u) << j;
+    for (int j = 0; j < 8; ++j) kept[j] = ck[j] >= t;
   }
-  return bits;
 }
 
-// E8M0 byte for a block whose largest magnitude has IEEE exponent field `e`
-// (bf16 or fp32 alike): E = floor(log2 amax) - 2, clamped at -127; byte = E + 127.
-__device__ __forceinline__ uint32_t e8m0_from_expfield(uint32_t e) { return e > 2 ? e - 2 : 0; }
+// Scale-operand bits for a block whose largest magnitude has fp32 bits `amax_bits`:
+// E = floor(log2 amax) - 2 clamped at -127, i.e. exponent field minus 2 saturating
+// at 0; the E8M0 byte is that field.  The conversion instructions read the scale's
+// exponent field, so field 0 (bit pattern +0.0) means 2^-127.
+__device__ __forceinline__ uint32_t scale_bits_of(uint32_t amax_bits) {
+  return __builtin_elementwise_sub_sat(amax_bits & 0x7F800000u, 0x01000000u);
+}
 
-// fp32 whose exponent bits are the E8M0 byte: the conversion instructions read
-// the scale's exponent field, so byte 0 (bit pattern +0.0) means 2^-127.
-__device__ __forceinline__ float scale_operand(uint32_t byte) { return __uint_as_float(byte << 23); }
-
-__device__ __forceinline__ bf16x2_t as_bf16x2(uint32_t v) {
-  bf16x2_t r;
-  __builtin_memcpy(&r, &v, 4);
-  return r;
+// Largest |v| of the lane's 8 values, as fp32 bits (non-negative floats order like
+// their bit patterns, so the quad exchange can use integer maxima).
+__device__ __forceinline__ uint32_t abs_max8(const float v[8]) {
+  const float m0 = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fabsf(v[2]));
+  const float m1 = fmaxf(fmaxf(fabsf(v[3]), fabsf(v[4])), fabsf(v[5]));
+  const float m2 = fmaxf(fmaxf(fabsf(v[6]), fabsf(v[7])), m0);
+  return __float_as_uint(fmaxf(m1, m2));
 }
 
 // Eight E2M1 codes (one dword, element 2i in the low nibble of byte i) times 2^E.
@@ -102,6 +121,17 @@ __device__ __forceinline__ void dequant8(uint32_t packed, float scale, float out
   auto p3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(packed, scale, 3);
   out[0] = p0[0]; out[1] = p0[1]; out[2] = p1[0]; out[3] = p1[1];
   out[4] = p2[0]; out[5] = p2[1]; out[6] = p3[0]; out[7] = p3[1];
+}
+
+// Eight fp32 values to E2M1 codes with scale 2^E (round to nearest even, saturating).
+__device__ __forceinline__ uint32_t quant8(const float v[8], float scale) {
+  // the four conversions write all four bytes, so the initial contents do not matter
+  uint32_t p = __float_as_uint(v[0]);
+  p = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p, v[0], v[1], scale, 0);
+  p = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p, v[2], v[3], scale, 1);
+  p = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p, v[4], v[5], scale, 2);
+  p = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p, v[6], v[7], scale, 3);
+  return p;
 }
 
 // Gather the scale bytes of the 16 blocks of a wave into 4 dwords held by lanes
@@ -128,7 +158,8 @@ __device__ __forceinline__ void store_scales(uint8_t* dst, int64_t b, int64_t nb
 // quad's other three lanes hold the rest).  MODE 0: mask, backbone codes and scale,
 // residual against the dequantized backbone, residual codes and scale.  MODE 1:
 // plain MXFP4 of the 8 values into (rbyte, rpacked).  Every lane of the quad must
-// call it together (the block maxima are quad exchanges).
+// call it together (the block maxima are quad exchanges).  `keep` (bit j = element
+// j kept) is only computed when a caller uses it.
 template <int MODE, int SPM>
 __device__ __forceinline__ void codec_block(const uint32_t w[4], uint32_t& keep, uint32_t& bbyte,
                                             uint32_t& bpacked, uint32_t& rbyte, uint32_t& rpacked) {
@@ -143,25 +174,21 @@ __device__ __forceinline__ void codec_block(const uint32_t w[4], uint32_t& keep,
   float r[8];
   keep = 0xFFu; bbyte = 0; bpacked = 0;
   if constexpr (MODE == 0) {
-    keep = keep_bits<SPM>(w);
-    // Backbone block maximum: every group's largest element is kept and the
-    // groups tile the block, so the kept maximum is the block maximum of |x|.
-    uint32_t kmax = 0;
+    bool kept[8];
+    keep_mask<SPM>(xf, kept);
+    keep = 0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) kmax = umax(kmax, umax(w[i] & 0x7FFFu, (w[i] >> 16) & 0x7FFFu));
-    kmax = quad_max(kmax);
-    bbyte = e8m0_from_expfield(kmax >> 7);
-    const float bscale = scale_operand(bbyte);
-    // dropped positions become +0 (bf16 bits 0), which encodes as code 0x0
-    uint32_t wm[4];
+    for (int j = 0; j < 8; ++j) keep |= (kept[j] ? 1u : 0u) << j;
+    // Backbone block maximum: every group's largest element is kept and the groups
+    // tile the block, so the kept maximum is the block maximum of |x|.
+    const uint32_t bsb = scale_bits_of(quad_max(abs_max8(xf)));
+    bbyte = bsb >> 23;
+    const float bscale = __uint_as_float(bsb);
+    // dropped positions become +0, which encodes as code 0x0
+    float xm[8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      wm[i] = w[i] & (((keep >> (2 * i)) & 1 ? 0x0000FFFFu : 0u) |
-                      ((keep >> (2 * i + 1)) & 1 ? 0xFFFF0000u : 0u));
-    bpacked = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(bpacked, as_bf16x2(wm[0]), bscale, 0);
-    bpacked = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(bpacked, as_bf16x2(wm[1]), bscale, 1);
-    bpacked = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(bpacked, as_bf16x2(wm[2]), bscale, 2);
-    bpacked = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(bpacked, as_bf16x2(wm[3]), bscale, 3);
+    for (int j = 0; j < 8; ++j) xm[j] = kept[j] ? xf[j] : 0.0f;
+    bpacked = quant8(xm, bscale);
     // residual against the dequantized backbone: one fp32 subtraction each
     float bh[8];
     dequant8(bpacked, bscale, bh);
@@ -173,17 +200,9 @@ __device__ __forceinline__ void codec_block(const uint32_t w[4], uint32_t& keep,
   }
 
   // residual (or plain) quantization with its own block scale
-  uint32_t rmax = 0;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) rmax = umax(rmax, __float_as_uint(r[j]) & 0x7FFFFFFFu);
-  rmax = quad_max(rmax);
-  rbyte = e8m0_from_expfield(rmax >> 23);
-  const float rscale = scale_operand(rbyte);
-  rpacked = 0;
-  rpacked = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(rpacked, r[0], r[1], rscale, 0);
-  rpacked = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(rpacked, r[2], r[3], rscale, 1);
-  rpacked = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(rpacked, r[4], r[5], rscale, 2);
-  rpacked = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(rpacked, r[6], r[7], rscale, 3);
+  const uint32_t rsb = scale_bits_of(quad_max(abs_max8(r)));
+  rbyte = rsb >> 23;
+  rpacked = quant8(r, __uint_as_float(rsb));
 }
 
 // MODE 0: SharQ preparation (mask, backbone, residual).  MODE 1: plain MXFP4
@@ -248,48 +267,70 @@ __global__ __launch_bounds__(kThreads) void prep_mx_kernel(
 // 16 consecutive rows of one fragment (256 contiguous bytes), and each quad leader
 // ends with its row's 4 scale bytes = one scale word, so a wave's scale words are 64
 // contiguous bytes.  Rows >= M and blocks >= K/32 are processed as zeros, which
-// writes the layout's zero padding.
+// writes the layout's zero padding.  The grid is (K-step groups of 4, row groups):
+// a work-group's 4 waves take 4 consecutive K-steps of the same 16 rows.
 template <int MODE, int SPM, bool WRITE_MASK>
 __global__ __launch_bounds__(kThreads) void prep_mx_tiled_kernel(
     const uint16_t* __restrict__ x, int64_t M, int64_t K, int64_t ldx, int64_t Mp, int64_t Kp,
-    uint8_t* __restrict__ bcodes, uint8_t* __restrict__ bscales, uint8_t* __restrict__ rcodes,
-    uint8_t* __restrict__ rscales, uint8_t* __restrict__ mask) {
+    int64_t rg0, uint8_t* __restrict__ bcodes, uint8_t* __restrict__ bscales,
+    uint8_t* __restrict__ rcodes, uint8_t* __restrict__ rscales, uint8_t* __restrict__ mask) {
   const int lane = threadIdx.x & 63;
   const int q = lane & 3, k = lane >> 2;
   const int64_t nks = Kp / 128;
-  const int64_t task = (int64_t)blockIdx.x * (kThreads / 64) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  if (task >= (Mp / 16) * nks) return;  // whole waves only
-  const int64_t rg = task / nks, ks = task - rg * nks;
-  const int64_t r = rg * 16 + k;
+  const int64_t ks = (int64_t)blockIdx.x * (kThreads / 64) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (ks >= nks) return;  // whole waves only
+  const int64_t rg = rg0 + blockIdx.y;
+  const int64_t r0 = rg * 16;  // first row of the wave (uniform)
+  const int64_t r = r0 + k;
   const int64_t nbk = K / 32;
 
+  // loads: the 16 rows x 4 blocks; a wave wholly inside X loads unguarded
   u32x4 v[4];
+  const uint16_t* xrow = x + r0 * ldx + ks * 128;  // uniform base
+  const int64_t lane_off = (int64_t)k * ldx + q * 8;
+  if (r0 + 16 <= M && ks * 4 + 4 <= nbk) {
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int64_t b = ks * 4 + u;
-    v[u] = u32x4{0u, 0u, 0u, 0u};
-    if (r < M && b < nbk)
-      v[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(x + r * ldx + b * 32 + q * 8));
+    for (int u = 0; u < 4; ++u)
+      v[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(xrow + lane_off + u * 32));
+  } else {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      v[u] = u32x4{0u, 0u, 0u, 0u};
+      if (r < M && ks * 4 + u < nbk)
+        v[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(xrow + lane_off + u * 32));
+    }
   }
-  const int64_t frag_row = (r >> 5) * (Kp / 64);
-  const int slot_row = (int)(r & 31);
+
+  // Codes go through a wave-private LDS tile so that every global store writes 16 B
+  // per lane: lane L then holds slot (row L%16, block u = L/16), and the four 256-byte
+  // row runs of the wave are fragment (r/32, 2ks + u/2), slots (r%32) + 32(u%2).
+  __shared__ uint32_t tile[kThreads / 64][2][4 * 16 * 4];
+  uint32_t* my = tile[threadIdx.x >> 6][0];
+  uint32_t* myb = tile[threadIdx.x >> 6][1];
   uint32_t bword = 0, rword = 0;
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
-    const int64_t b = ks * 4 + u;
     const uint32_t w[4] = {v[u][0], v[u][1], v[u][2], v[u][3]};
     uint32_t keep, bbyte, bpacked, rbyte, rpacked;
     codec_block<MODE, SPM>(w, keep, bbyte, bpacked, rbyte, rpacked);
-    const int64_t off = (frag_row + (b >> 1)) * 1024 + (slot_row + 32 * (int)(b & 1)) * 16 + q * 4;
-    __builtin_nontemporal_store(rpacked, reinterpret_cast<uint32_t*>(rcodes + off));
+    my[u * 64 + lane] = rpacked;  // = slot (u, k), dword q
     rword |= rbyte << (8 * u);
     if constexpr (MODE == 0) {
-      __builtin_nontemporal_store(bpacked, reinterpret_cast<uint32_t*>(bcodes + off));
+      myb[u * 64 + lane] = bpacked;
       bword |= bbyte << (8 * u);
       if constexpr (WRITE_MASK)
-        if (r < M && b < nbk) mask[r * (K / 8) + b * 4 + q] = (uint8_t)keep;
+        if (r < M && ks * 4 + u < nbk) mask[r * (K / 8) + (ks * 4 + u) * 4 + q] = (uint8_t)keep;
     }
   }
+  // the tile is wave-private: a wave-level wait on the LDS writes is enough
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+  __builtin_amdgcn_wave_barrier();
+  const int64_t frag0 = ((r0 >> 5) * (Kp / 64) + 2 * ks) * 1024;
+  const int su = lane >> 4;
+  const int off = (su >> 1) * 1024 + (su & 1) * 512 + (int)(((r0 & 31) + (lane & 15)) * 16);
+  __builtin_nontemporal_store(reinterpret_cast<const u32x4*>(my)[lane], reinterpret_cast<u32x4*>(rcodes + frag0 + off));
+  if constexpr (MODE == 0)
+    __builtin_nontemporal_store(reinterpret_cast<const u32x4*>(myb)[lane], reinterpret_cast<u32x4*>(bcodes + frag0 + off));
   if (q == 0) {
     reinterpret_cast<uint32_t*>(rscales)[ks * Mp + r] = rword;
     if constexpr (MODE == 0) reinterpret_cast<uint32_t*>(bscales)[ks * Mp + r] = bword;
@@ -301,12 +342,18 @@ hipError_t launch_tiled(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, ui
                         uint8_t* bscales, uint8_t* rcodes, uint8_t* rscales, uint8_t* mask,
                         hipStream_t stream) {
   const int64_t Mp = (M + 31) / 32 * 32, Kp = (K + 127) / 128 * 128;
-  const int64_t tasks = (Mp / 16) * (Kp / 128);
-  if (tasks == 0) return hipSuccess;
-  const int64_t grid = (tasks + kThreads / 64 - 1) / (kThreads / 64);
-  prep_mx_tiled_kernel<MODE, SPM, WRITE_MASK><<<dim3((unsigned)grid), dim3(kThreads), 0, stream>>>(
-      x, M, K, ldx, Mp, Kp, bcodes, bscales, rcodes, rscales, mask);
-  return hipGetLastError();
+  const int64_t nks = Kp / 128, nrg = Mp / 16;
+  if (nks == 0 || nrg == 0) return hipSuccess;
+  const int64_t gx = (nks + kThreads / 64 - 1) / (kThreads / 64);
+  constexpr int64_t kMaxGridY = 65535;
+  for (int64_t rg0 = 0; rg0 < nrg; rg0 += kMaxGridY) {
+    const int64_t gy = nrg - rg0 < kMaxGridY ? nrg - rg0 : kMaxGridY;
+    prep_mx_tiled_kernel<MODE, SPM, WRITE_MASK><<<dim3((unsigned)gx, (unsigned)gy), dim3(kThreads), 0, stream>>>(
+        x, M, K, ldx, Mp, Kp, rg0, bcodes, bscales, rcodes, rscales, mask);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 template <int MODE, int SPM, bool WRITE_MASK>
