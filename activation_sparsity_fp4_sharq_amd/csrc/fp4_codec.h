@@ -1,0 +1,77 @@
+// fp4_codec.h -- device helpers shared by the two activation preparations: the
+// top-n-of-m selection on a lane's 8 consecutive elements (SharQ's input-adaptive N:M
+// mask: keep the n largest magnitudes of every group of m consecutive elements along
+// K, lower index first on equal magnitude).
+#pragma once
+#include <stdint.h>
+
+#include <hip/hip_runtime.h>
+
+namespace sharq {
+namespace codec {
+
+__device__ __forceinline__ uint32_t umax(uint32_t a, uint32_t b) { return a > b ? a : b; }
+__device__ __forceinline__ uint32_t umin(uint32_t a, uint32_t b) { return a < b ? a : b; }
+
+__device__ __forceinline__ uint32_t umax3(uint32_t a, uint32_t b, uint32_t c) { return umax(umax(a, b), c); }
+__device__ __forceinline__ uint32_t umin3(uint32_t a, uint32_t b, uint32_t c) { return umin(umin(a, b), c); }
+
+// Median of three unsigned integers (one v_med3_u32; the compiler does not form it
+// from min/max expressions).
+__device__ __forceinline__ uint32_t umed3(uint32_t a, uint32_t b, uint32_t c) {
+  uint32_t r;
+  asm("v_med3_u32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
+// Second largest of four: with m = the median of (a, b, c), the second largest of
+// all four is m unless d lies above m, in which case it is min(max(a, b, c), d).
+__device__ __forceinline__ uint32_t second_of_4(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  return umax(umed3(a, b, c), umin(umax3(a, b, c), d));
+}
+
+// Descending sort of four (s0 >= s1 >= s2 >= s3) from the max, min and median of
+// the first three and the fourth value.
+__device__ __forceinline__ void sort4(uint32_t a, uint32_t b, uint32_t c, uint32_t d, uint32_t s[4]) {
+  const uint32_t hi = umax3(a, b, c), lo = umin3(a, b, c), md = umed3(a, b, c);
+  s[0] = umax(hi, d);
+  s[1] = umax(md, umin(hi, d));
+  s[2] = umin(md, umax(lo, d));
+  s[3] = umin(lo, d);
+}
+
+// Fourth largest of eight: the top four of two descending runs a and b are
+// max(a_i, b_{3-i}), so the fourth largest is the smallest of those four.
+__device__ __forceinline__ uint32_t fourth_of_8(const uint32_t c[8]) {
+  uint32_t a[4], b[4];
+  sort4(c[0], c[1], c[2], c[3], a);
+  sort4(c[4], c[5], c[6], c[7], b);
+  return umin(umin3(umax(a[0], b[3]), umax(a[1], b[2]), umax(a[2], b[1])), umax(a[3], b[0]));
+}
+
+// Top-n-of-m selection on the lane's 8 elements.  Each element gets a compound key:
+// its magnitude (the fp32 image of a bf16 value has 16 zero low bits) with a
+// reversed in-group index in the low bits, so keys are distinct and "larger key"
+// means "ranks earlier": bigger magnitude first, lower index first among equal
+// magnitudes (+0 and -0 are equal).  An element is kept when its key is at or
+// above the n-th largest key of its group.
+template <int SPM>
+__device__ __forceinline__ void keep_mask(const float xf[8], bool kept[8]) {
+  uint32_t ck[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    ck[j] = (__float_as_uint(xf[j]) & 0x7FFF0000u) | (uint32_t)(SPM == 4 ? 3 - (j & 3) : 7 - j);
+  if constexpr (SPM == 4) {
+    const uint32_t t0 = second_of_4(ck[0], ck[1], ck[2], ck[3]);
+    const uint32_t t1 = second_of_4(ck[4], ck[5], ck[6], ck[7]);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) kept[j] = ck[j] >= (j < 4 ? t0 : t1);
+  } else {
+    const uint32_t t = fourth_of_8(ck);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) kept[j] = ck[j] >= t;
+  }
+}
+
+}  // namespace codec
+}  // namespace sharq

@@ -56,8 +56,10 @@ struct Args {
   bool y_aligned;      // y 16-byte aligned and ldy a multiple of 8 elements
 };
 
+// An FP4 operand is the low 4 dwords of the instruction's 8-dword operand; the upper
+// half is ignored, so it is left undefined (no register copies).
 __device__ __forceinline__ v8i widen(v4i a) {
-  return __builtin_shufflevector(a, a, 0, 1, 2, 3, 0, 1, 2, 3);
+  return __builtin_shufflevector(a, a, 0, 1, 2, 3, -1, -1, -1, -1);
 }
 
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {

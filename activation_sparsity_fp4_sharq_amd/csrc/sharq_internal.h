@@ -38,7 +38,7 @@ hipError_t launch_linear_nv(const sharq_fp4& b, const sharq_fp4& r, int64_t M, c
                             void* work, size_t work_bytes, hipStream_t stream);
 size_t linear_nv_workspace(int64_t M, int64_t N, int64_t K);
 
-constexpr size_t kNvPrepWorkspace = 16448;  // 16 + 2 * 2048 dwords
+constexpr size_t kNvPrepWorkspace = 16448;  // 16 + 2 * 2048 dwords: maxima and partials
 constexpr int kMaxDevices = 64;
 
 }  // namespace sharq
