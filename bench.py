@@ -38,7 +38,24 @@ def parse():
     p.add_argument("--workload", default="prefill")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time for the CPU baseline")
+    p.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                   help="only run a plain device copy of MIB MiB (5 times): the reference dispatch that "
+                        "scales hardware byte counters to bytes")
     return p.parse_args()
+
+
+def calibrate_copy(mib):
+    """A plain device-to-device copy of a known byte count, for counter calibration."""
+    import torch
+
+    n = mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "device copy", "bytes_read": n, "bytes_written": n, "dispatches": 5}))
 
 
 def kernel_source_digest(paths):
@@ -121,6 +138,9 @@ def back_to_back_seconds(launch, reps, stream):
 
 def main():
     args = parse()
+    if args.calibrate_copy:
+        calibrate_copy(args.calibrate_copy)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(json.dumps({"error": "this benchmark runs on exactly one GPU; the SharQ layer is timed on "
@@ -202,6 +222,11 @@ def main():
                else "activation_sparsity_fp4_sharq_amd/csrc/linear_nv.hip"]
     kernel_key = f"{'linear_mx' if w.fmt == sharq.MXFP4 else 'linear_nv'}:{w.name}"
     traffic = load_traffic(kernel_key, kernel_source_digest(lin_src))
+    prep_src = (["activation_sparsity_fp4_sharq_amd/csrc/prep_mx.hip"] if w.fmt == sharq.MXFP4
+                else ["activation_sparsity_fp4_sharq_amd/csrc/prep_nv.hip"]) + \
+        ["activation_sparsity_fp4_sharq_amd/csrc/fp4_codec.h"]
+    prep_key = f"{'prep_mx' if w.fmt == sharq.MXFP4 else 'prep_nv'}:{w.name}"
+    prep_traffic = load_traffic(prep_key, kernel_source_digest(prep_src))
     ach = alg / t_lin / 1e12
 
     out = {
@@ -228,7 +253,7 @@ def main():
                      "flop_convention": "algorithmic 2MNK(1+n/m): sparse backbone + dense residual"},
         "prep": {"ms": round(t_prep * 1e3, 4), "GB_s": round(prep_bytes / t_prep / 1e9, 1),
                  "pct_hbm": round(100.0 * prep_bytes / t_prep / 1e9 / PEAK_HBM_GBS, 2),
-                 "bytes_per_launch": prep_bytes},
+                 "bytes_per_launch": prep_bytes, "traffic": prep_traffic},
         "linear": {"ms": round(t_lin * 1e3, 4), "TFLOPS_effective": round(eff / t_lin / 1e12, 2),
                    "TFLOPS_algorithmic": round(alg / t_lin / 1e12, 2),
                    "TFLOPS_issued": round(issued / t_lin / 1e12, 2),
