@@ -66,6 +66,8 @@ def lib():
         L.oracle_linear.argtypes = [_u8p, _u8p, ctypes.c_float, _u8p, _u8p, ctypes.c_float, _i64,
                                     _u8p, _u8p, ctypes.c_float, _i64, _i64, ctypes.c_int, _vp, _i64,
                                     _f64p]
+        L.oracle_rmsnorm.restype = ctypes.c_int
+        L.oracle_rmsnorm.argtypes = [_u16p, _i64, _i64, _i64, _u16p, ctypes.c_float, _u16p, _vp]
         L.oracle_omp_threads.restype = ctypes.c_int
         L.oracle_omp_threads.argtypes = []
         _lib = L
@@ -102,6 +104,22 @@ def quantize(x_bits, fmt=MXFP4):
     if rc:
         raise ValueError(f"oracle_quantize rejected shape {x_bits.shape} fmt {fmt}")
     return Payload(codes, scales, ts[0])
+
+
+def rmsnorm(x_bits, gamma_bits, eps):
+    """RMS normalization with a bf16 gain (reading R8): returns (y bf16 bits [M, K],
+    the per-row factors r as float32 [M])."""
+    x_bits = np.ascontiguousarray(x_bits, dtype=np.uint16)
+    gamma_bits = np.ascontiguousarray(gamma_bits, dtype=np.uint16)
+    M, K = x_bits.shape
+    if gamma_bits.shape != (K,):
+        raise ValueError("gamma must have K entries")
+    y = np.zeros((M, K), np.uint16)
+    r = np.zeros(max(M, 1), np.float32)
+    rc = lib().oracle_rmsnorm(x_bits, M, K, K, gamma_bits, float(eps), y, _ptr(r))
+    if rc:
+        raise ValueError("oracle_rmsnorm rejected its arguments")
+    return y, r[:M]
 
 
 def prep(x_bits, n, m, fmt=MXFP4, want_values=False):

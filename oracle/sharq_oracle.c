@@ -38,6 +38,13 @@
  *      mask bit k%8 of byte k/8.
  *   R7 GEMM: Y = Bhat Ŵ^T + Rhat Ŵ^T, each a plain fp64 triple loop over dequantized
  *      values, summed.
+ *   R8 normalization absorbed by the preparation ("Core claim" and abstract: the
+ *      fused preparation also takes over the layer normalization): RMS normalization
+ *      with a per-channel bf16 gain g and no bias, producing the bf16 tensor the
+ *      preparation then decomposes:
+ *        r_i = fp32( 1 / sqrt( (sum_k x_ik^2) / K + eps ) )   (sum, mean, sqrt and
+ *              division in fp64; the sum of squares of bf16 values is exact to ~1e-16)
+ *        y_ik = bf16_rne( fp32( fp32(x_ik * r_i) * g_k ) ).
  *
  * Compile: gcc -O2 -ffp-contract=off -fno-fast-math -fopenmp -shared -fPIC.
  * The row loops carry an OpenMP pragma; every output element has a fixed
@@ -250,6 +257,36 @@ int oracle_quantize(const uint16_t* x, int64_t rows, int64_t K, int64_t ldx, int
       uint8_t sb = fmt == ORACLE_MXFP4 ? mx_block(v, NULL, c) : nv_block(v, NULL, S, c);
       scales[i * (K / B) + kb] = sb;
       for (int j = 0; j < B; ++j) put_code(codes + i * (K / 2), kb * B + j, c[j]);
+    }
+  }
+  return 0;
+}
+
+static uint16_t f32_to_bf16(float f) {
+  uint32_t u;
+  memcpy(&u, &f, 4);
+  u += 0x7FFFu + ((u >> 16) & 1u); /* round to nearest, ties to even (finite inputs) */
+  return (uint16_t)(u >> 16);
+}
+
+/* R8: RMS normalization of x bf16 [M, ldx] (first K columns) with gain g bf16 [K]
+ * into y bf16 [M, K]; r_out (optional) receives the per-row factors r_i. */
+int oracle_rmsnorm(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, const uint16_t* g, float eps,
+                   uint16_t* y, float* r_out) {
+  if (M < 0 || K <= 0 || ldx < K || !(eps >= 0.0f)) return -1;
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < M; ++i) {
+    double ss = 0.0;
+    for (int64_t k = 0; k < K; ++k) {
+      const double v = (double)bf16_to_f32(x[i * ldx + k]);
+      ss += v * v;
+    }
+    const float r = (float)(1.0 / sqrt(ss / (double)K + (double)eps));
+    if (r_out) r_out[i] = r;
+    for (int64_t k = 0; k < K; ++k) {
+      const float t = bf16_to_f32(x[i * ldx + k]) * r;
+      const float u = t * bf16_to_f32(g[k]);
+      y[i * K + k] = f32_to_bf16(u);
     }
   }
   return 0;

@@ -477,3 +477,58 @@ def test_decomposition_beats_plain_mxfp4(name):
     err_plain = np.linalg.norm(x - decode_mx(plain.codes, plain.scales, K))
     err_backbone = np.linalg.norm(x - decode_mx(bb.codes, bb.scales, K))
     assert err_sharq < err_plain < err_backbone
+
+
+# ------------------------------------------------------------ RMS normalization (reading R8)
+
+def _norm_inputs(M=6, K=96, seed=5):
+    rng = np.random.default_rng(seed)
+    x = f32_to_bf16_bits((rng.standard_t(3, (M, K)) * rng.lognormal(0, 1, (M, 1))).astype(np.float32))
+    g = f32_to_bf16_bits(rng.normal(1.0, 0.2, K).astype(np.float32))
+    return x, g
+
+
+@pytest.mark.parametrize("k", [-6, -1, 3, 9])
+def test_rmsnorm_invariant_under_power_of_two_input_scaling(k):
+    """With eps = 0, scaling a row by 2^k scales the sum of squares by 4^k and r by
+    2^-k, all exactly, so the normalized tensor is unchanged bit for bit."""
+    x, g = _norm_inputs()
+    y0, r0 = oracle.rmsnorm(x, g, 0.0)
+    xs = f32_to_bf16_bits((bf16_bits_to_f32(x) * np.float32(2.0 ** k)).astype(np.float32))
+    y1, r1 = oracle.rmsnorm(xs, g, 0.0)
+    assert np.array_equal(y0, y1)
+    assert np.array_equal(r1, (r0 * np.float32(2.0 ** -k)).astype(np.float32))
+
+
+@pytest.mark.parametrize("j", [-3, 2])
+def test_rmsnorm_gain_power_of_two_is_exact(j):
+    x, g = _norm_inputs(seed=9)
+    y0, _ = oracle.rmsnorm(x, g, 1e-6)
+    gs = f32_to_bf16_bits((bf16_bits_to_f32(g) * np.float32(2.0 ** j)).astype(np.float32))
+    y1, _ = oracle.rmsnorm(x, gs, 1e-6)
+    assert np.array_equal(bf16_bits_to_f32(y1), bf16_bits_to_f32(y0) * np.float32(2.0 ** j))
+
+
+def test_rmsnorm_unit_mean_square_with_unit_gain():
+    x, _ = _norm_inputs(M=16, K=512, seed=3)
+    g = f32_to_bf16_bits(np.ones(512, np.float32))
+    y, _ = oracle.rmsnorm(x, g, 0.0)
+    ms = (bf16_bits_to_f32(y).astype(np.float64) ** 2).mean(axis=1)
+    # bf16 rounding moves each element by at most 2^-8 relatively (8 significant
+    # bits), so each square by at most 2^-7, plus fp32 rounding in r
+    assert np.all(np.abs(ms - 1.0) <= 2.0 ** -7 + 1e-6)
+    assert np.abs(ms - 1.0).mean() < 2.0 ** -9  # rounding errors mostly cancel
+
+
+def test_rmsnorm_closed_forms():
+    K = 64
+    # a constant row of c = -2^e normalizes to -g exactly (r = 2^-e exactly)
+    g = f32_to_bf16_bits(np.linspace(0.5, 2.0, K).astype(np.float32))
+    x = f32_to_bf16_bits(np.full((1, K), -8.0, np.float32))
+    y, r = oracle.rmsnorm(x, g, 0.0)
+    assert r[0] == np.float32(0.125)
+    assert np.array_equal(bf16_bits_to_f32(y[0]), -bf16_bits_to_f32(g))
+    # a zero row with eps > 0: r = fp32(1/sqrt(eps)), y = 0
+    z = np.zeros((1, K), np.uint16)
+    y, r = oracle.rmsnorm(z, g, 0.25)
+    assert r[0] == np.float32(2.0) and np.all(bf16_bits_to_f32(y) == 0.0)
