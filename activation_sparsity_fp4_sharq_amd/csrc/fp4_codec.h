@@ -75,3 +75,24 @@ __device__ __forceinline__ void keep_mask(const float xf[8], bool kept[8]) {
 
 }  // namespace codec
 }  // namespace sharq
+
+namespace sharq {
+namespace codec {
+
+// RMS normalization folded into the preparation (SharQ's fused preparation takes over
+// the layer normalization): each bf16 element x of row i becomes
+// bf16_rne(fp32(fp32(x * r_i) * g_k)), r_i the row's factor, g_k the channel's bf16
+// gain.  Applied to a dword of two bf16 values and the matching dword of gains.
+__device__ __forceinline__ uint32_t bf16_rne_bits(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;  // finite values (the contract)
+}
+
+__device__ __forceinline__ uint32_t rms_scale_pair(uint32_t w, uint32_t gw, float r) {
+  const float y0 = __fmul_rn(__fmul_rn(__uint_as_float(w << 16), r), __uint_as_float(gw << 16));
+  const float y1 = __fmul_rn(__fmul_rn(__uint_as_float(w & 0xFFFF0000u), r), __uint_as_float(gw & 0xFFFF0000u));
+  return bf16_rne_bits(y0) | (bf16_rne_bits(y1) << 16);
+}
+
+}  // namespace codec
+}  // namespace sharq

@@ -145,13 +145,27 @@ __device__ __forceinline__ void codec_block(const uint32_t w[4], uint32_t& keep,
   rpacked = quant8(r, __uint_as_float(rsb));
 }
 
+// Optional RMS normalization applied to the loaded bf16 values (NORM): per-row
+// factors r[M] and per-channel bf16 gains g[K] (see rms_scale_pair).
+struct Norm {
+  const float* r;
+  const uint16_t* g;
+};
+
+__device__ __forceinline__ u32x4 rms_scale8(const u32x4& v, const Norm& nm, int64_t row, int64_t col) {
+  const float r = nm.r[row];
+  const u32x4 g = *reinterpret_cast<const u32x4*>(nm.g + col);
+  return u32x4{rms_scale_pair(v[0], g[0], r), rms_scale_pair(v[1], g[1], r), rms_scale_pair(v[2], g[2], r),
+               rms_scale_pair(v[3], g[3], r)};
+}
+
 // MODE 0: SharQ preparation (mask, backbone, residual).  MODE 1: plain MXFP4
 // quantization of X into (rcodes, rscales) -- used for weight payloads.
-template <int MODE, int SPM, bool DENSE_ROWS, bool WRITE_MASK>
+template <int MODE, int SPM, bool DENSE_ROWS, bool WRITE_MASK, bool NORM>
 __global__ __launch_bounds__(kThreads) void prep_mx_kernel(
     const uint16_t* __restrict__ x, int64_t ldx, int64_t nbk, int64_t nblocks,
     uint8_t* __restrict__ bcodes, uint8_t* __restrict__ bscales, uint8_t* __restrict__ rcodes,
-    uint8_t* __restrict__ rscales, uint8_t* __restrict__ mask) {
+    uint8_t* __restrict__ rscales, uint8_t* __restrict__ mask, Norm nm) {
   const int lane = threadIdx.x & 63;
   const int q = lane & 3;
   const int64_t wave = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
@@ -171,6 +185,10 @@ __global__ __launch_bounds__(kThreads) void prep_mx_kernel(
         off = row * ldx + (b - row * nbk) * 32 + q * 8;
       }
       v[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(x + off));
+      if constexpr (NORM) {
+        const int64_t row = b / nbk;
+        v[u] = rms_scale8(v[u], nm, row, (b - row * nbk) * 32 + q * 8);
+      }
     }
   }
 
@@ -209,11 +227,11 @@ __global__ __launch_bounds__(kThreads) void prep_mx_kernel(
 // contiguous bytes.  Rows >= M and blocks >= K/32 are processed as zeros, which
 // writes the layout's zero padding.  The grid is (K-step groups of 4, row groups):
 // a work-group's 4 waves take 4 consecutive K-steps of the same 16 rows.
-template <int MODE, int SPM, bool WRITE_MASK>
+template <int MODE, int SPM, bool WRITE_MASK, bool NORM>
 __global__ __launch_bounds__(kThreads) void prep_mx_tiled_kernel(
     const uint16_t* __restrict__ x, int64_t M, int64_t K, int64_t ldx, int64_t Mp, int64_t Kp,
     int64_t rg0, uint8_t* __restrict__ bcodes, uint8_t* __restrict__ bscales,
-    uint8_t* __restrict__ rcodes, uint8_t* __restrict__ rscales, uint8_t* __restrict__ mask) {
+    uint8_t* __restrict__ rcodes, uint8_t* __restrict__ rscales, uint8_t* __restrict__ mask, Norm nm) {
   const int lane = threadIdx.x & 63;
   const int q = lane & 3, k = lane >> 2;
   const int64_t nks = Kp / 128;
@@ -230,14 +248,18 @@ __global__ __launch_bounds__(kThreads) void prep_mx_tiled_kernel(
   const int64_t lane_off = (int64_t)k * ldx + q * 8;
   if (r0 + 16 <= M && ks * 4 + 4 <= nbk) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
+    for (int u = 0; u < 4; ++u) {
       v[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(xrow + lane_off + u * 32));
+      if constexpr (NORM) v[u] = rms_scale8(v[u], nm, r, ks * 128 + u * 32 + q * 8);
+    }
   } else {
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       v[u] = u32x4{0u, 0u, 0u, 0u};
-      if (r < M && ks * 4 + u < nbk)
+      if (r < M && ks * 4 + u < nbk) {
         v[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(xrow + lane_off + u * 32));
+        if constexpr (NORM) v[u] = rms_scale8(v[u], nm, r, ks * 128 + u * 32 + q * 8);
+      }
     }
   }
 
@@ -277,9 +299,9 @@ __global__ __launch_bounds__(kThreads) void prep_mx_tiled_kernel(
   }
 }
 
-template <int MODE, int SPM, bool WRITE_MASK>
+template <int MODE, int SPM, bool WRITE_MASK, bool NORM>
 hipError_t launch_tiled(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, uint8_t* bcodes,
-                        uint8_t* bscales, uint8_t* rcodes, uint8_t* rscales, uint8_t* mask,
+                        uint8_t* bscales, uint8_t* rcodes, uint8_t* rscales, uint8_t* mask, Norm nm,
                         hipStream_t stream) {
   const int64_t Mp = (M + 31) / 32 * 32, Kp = (K + 127) / 128 * 128;
   const int64_t nks = Kp / 128, nrg = Mp / 16;
@@ -288,61 +310,73 @@ hipError_t launch_tiled(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, ui
   constexpr int64_t kMaxGridY = 65535;
   for (int64_t rg0 = 0; rg0 < nrg; rg0 += kMaxGridY) {
     const int64_t gy = nrg - rg0 < kMaxGridY ? nrg - rg0 : kMaxGridY;
-    prep_mx_tiled_kernel<MODE, SPM, WRITE_MASK><<<dim3((unsigned)gx, (unsigned)gy), dim3(kThreads), 0, stream>>>(
-        x, M, K, ldx, Mp, Kp, rg0, bcodes, bscales, rcodes, rscales, mask);
+    prep_mx_tiled_kernel<MODE, SPM, WRITE_MASK, NORM><<<dim3((unsigned)gx, (unsigned)gy), dim3(kThreads), 0, stream>>>(
+        x, M, K, ldx, Mp, Kp, rg0, bcodes, bscales, rcodes, rscales, mask, nm);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
 }
 
-template <int MODE, int SPM, bool WRITE_MASK>
+template <int MODE, int SPM, bool WRITE_MASK, bool NORM>
 hipError_t launch_dense_or_strided(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
                                    uint8_t* bcodes, uint8_t* bscales, uint8_t* rcodes,
-                                   uint8_t* rscales, uint8_t* mask, hipStream_t stream) {
+                                   uint8_t* rscales, uint8_t* mask, Norm nm, hipStream_t stream) {
   const int64_t nbk = K / 32;
   const int64_t nblocks = M * nbk;
   if (nblocks == 0) return hipSuccess;
   const int64_t per_wg = (kThreads / 64) * kBlocksPerWave * kUnroll;
   const int64_t grid = (nblocks + per_wg - 1) / per_wg;
   if (ldx == K)
-    prep_mx_kernel<MODE, SPM, true, WRITE_MASK><<<dim3((unsigned)grid), dim3(kThreads), 0, stream>>>(
-        x, ldx, nbk, nblocks, bcodes, bscales, rcodes, rscales, mask);
+    prep_mx_kernel<MODE, SPM, true, WRITE_MASK, NORM><<<dim3((unsigned)grid), dim3(kThreads), 0, stream>>>(
+        x, ldx, nbk, nblocks, bcodes, bscales, rcodes, rscales, mask, nm);
   else
-    prep_mx_kernel<MODE, SPM, false, WRITE_MASK><<<dim3((unsigned)grid), dim3(kThreads), 0, stream>>>(
-        x, ldx, nbk, nblocks, bcodes, bscales, rcodes, rscales, mask);
+    prep_mx_kernel<MODE, SPM, false, WRITE_MASK, NORM><<<dim3((unsigned)grid), dim3(kThreads), 0, stream>>>(
+        x, ldx, nbk, nblocks, bcodes, bscales, rcodes, rscales, mask, nm);
   return hipGetLastError();
+}
+
+
+// Dispatch over the compile-time variants: pattern, mask output, normalization, layout.
+template <int SPM, bool WRITE_MASK, bool NORM>
+hipError_t prep_variant(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, uint8_t* bcodes, uint8_t* bscales,
+                        uint8_t* rcodes, uint8_t* rscales, uint8_t* mask, Norm nm, int tiled, hipStream_t stream) {
+  if (tiled)
+    return launch_tiled<0, SPM, WRITE_MASK, NORM>(x, M, K, ldx, bcodes, bscales, rcodes, rscales, mask, nm, stream);
+  return launch_dense_or_strided<0, SPM, WRITE_MASK, NORM>(x, M, K, ldx, bcodes, bscales, rcodes, rscales, mask, nm,
+                                                           stream);
+}
+
+template <int SPM>
+hipError_t prep_pattern(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, uint8_t* bcodes, uint8_t* bscales,
+                        uint8_t* rcodes, uint8_t* rscales, uint8_t* mask, Norm nm, int tiled, hipStream_t stream) {
+  if (nm.r) {
+    return mask ? prep_variant<SPM, true, true>(x, M, K, ldx, bcodes, bscales, rcodes, rscales, mask, nm, tiled, stream)
+                : prep_variant<SPM, false, true>(x, M, K, ldx, bcodes, bscales, rcodes, rscales, mask, nm, tiled, stream);
+  }
+  return mask ? prep_variant<SPM, true, false>(x, M, K, ldx, bcodes, bscales, rcodes, rscales, mask, nm, tiled, stream)
+              : prep_variant<SPM, false, false>(x, M, K, ldx, bcodes, bscales, rcodes, rscales, mask, nm, tiled, stream);
 }
 
 }  // namespace
 
 hipError_t launch_prep_mx(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, int sp_n, int sp_m,
                           uint8_t* bcodes, uint8_t* bscales, uint8_t* rcodes, uint8_t* rscales,
-                          uint8_t* mask, int tiled, hipStream_t stream) {
+                          uint8_t* mask, const float* rnorm, const uint16_t* gamma, int tiled,
+                          hipStream_t stream) {
   (void)sp_n;  // n = m/2 for both supported patterns
-  if (tiled) {
-    if (sp_m == 4)
-      return mask ? launch_tiled<0, 4, true>(x, M, K, ldx, bcodes, bscales, rcodes, rscales, mask, stream)
-                  : launch_tiled<0, 4, false>(x, M, K, ldx, bcodes, bscales, rcodes, rscales, mask, stream);
-    return mask ? launch_tiled<0, 8, true>(x, M, K, ldx, bcodes, bscales, rcodes, rscales, mask, stream)
-                : launch_tiled<0, 8, false>(x, M, K, ldx, bcodes, bscales, rcodes, rscales, mask, stream);
-  }
-  if (sp_m == 4) {
-    if (mask)
-      return launch_dense_or_strided<0, 4, true>(x, M, K, ldx, bcodes, bscales, rcodes, rscales, mask, stream);
-    return launch_dense_or_strided<0, 4, false>(x, M, K, ldx, bcodes, bscales, rcodes, rscales, mask, stream);
-  }
-  if (mask)
-    return launch_dense_or_strided<0, 8, true>(x, M, K, ldx, bcodes, bscales, rcodes, rscales, mask, stream);
-  return launch_dense_or_strided<0, 8, false>(x, M, K, ldx, bcodes, bscales, rcodes, rscales, mask, stream);
+  const Norm nm{rnorm, gamma};
+  if (sp_m == 4) return prep_pattern<4>(x, M, K, ldx, bcodes, bscales, rcodes, rscales, mask, nm, tiled, stream);
+  return prep_pattern<8>(x, M, K, ldx, bcodes, bscales, rcodes, rscales, mask, nm, tiled, stream);
 }
 
 hipError_t launch_quant_mx(const uint16_t* x, int64_t rows, int64_t K, int64_t ldx, uint8_t* codes,
                            uint8_t* scales, int tiled, hipStream_t stream) {
+  const Norm none{nullptr, nullptr};
   if (tiled)
-    return launch_tiled<1, 4, false>(x, rows, K, ldx, nullptr, nullptr, codes, scales, nullptr, stream);
-  return launch_dense_or_strided<1, 4, false>(x, rows, K, ldx, nullptr, nullptr, codes, scales, nullptr,
-                                              stream);
+    return launch_tiled<1, 4, false, false>(x, rows, K, ldx, nullptr, nullptr, codes, scales, nullptr, none, stream);
+  return launch_dense_or_strided<1, 4, false, false>(x, rows, K, ldx, nullptr, nullptr, codes, scales, nullptr, none,
+                                                     stream);
 }
 
 }  // namespace sharq

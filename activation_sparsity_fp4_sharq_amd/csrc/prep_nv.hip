@@ -193,12 +193,13 @@ __device__ __forceinline__ uint32_t abs_max8_bits(const float v[8]) {
 // one-work-group launch after each maximum pass reduces its partials into work[0]
 // or work[1]; work-group 0 of the pass after it writes that path's tensor scale
 // (backbone or plain: bts, residual: rts).
-template <int PASS, int MODE, int SPM, bool DENSE_ROWS, bool WRITE_MASK>
+template <int PASS, int MODE, int SPM, bool DENSE_ROWS, bool WRITE_MASK, bool NORM>
 __global__ __launch_bounds__(kThreads) void prep_nv_kernel(
     const uint16_t* __restrict__ x, int64_t ldx, int64_t chunks_per_row, int64_t nchunks,
     uint8_t* __restrict__ bcodes, uint8_t* __restrict__ bscales, uint8_t* __restrict__ rcodes,
     uint8_t* __restrict__ rscales, uint8_t* __restrict__ mask, uint32_t* __restrict__ work,
-    float* __restrict__ bts, float* __restrict__ rts) {
+    float* __restrict__ bts, float* __restrict__ rts, const float* __restrict__ rnorm,
+    const uint16_t* __restrict__ gamma) {
   const int lane = threadIdx.x & 63;
   const int64_t wave = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
   // the maximum passes walk the chunks grid-stride with a bounded grid; the last pass
@@ -235,6 +236,14 @@ __global__ __launch_bounds__(kThreads) void prep_nv_kernel(
           off = row * ldx + (c - row * chunks_per_row) * 8;
         }
         v[u] = *reinterpret_cast<const u32x4*>(x + off);
+        if constexpr (NORM) {
+          // RMS normalization folded in: bf16(fp32(fp32(x * r_row) * g_col))
+          const int64_t row = c / chunks_per_row;
+          const float rr = rnorm[row];
+          const u32x4 g = *reinterpret_cast<const u32x4*>(gamma + (c - row * chunks_per_row) * 8);
+          v[u] = u32x4{rms_scale_pair(v[u][0], g[0], rr), rms_scale_pair(v[u][1], g[1], rr),
+                       rms_scale_pair(v[u][2], g[2], rr), rms_scale_pair(v[u][3], g[3], rr)};
+        }
         if constexpr (PASS == 2 && MODE == 0) {
           bpk_in[u] = *reinterpret_cast<const uint32_t*>(bcodes + c * 4);
           bsb_in[u] = bscales[c >> 1];
@@ -350,40 +359,51 @@ __global__ void nv_empty_kernel(uint32_t* work, float* t0, float* t1) {
   }
 }
 
-template <int MODE, int SPM, bool DENSE, bool WRITE_MASK>
+template <int MODE, int SPM, bool DENSE, bool WRITE_MASK, bool NORM>
 hipError_t run_passes(const uint16_t* x, int64_t ldx, int64_t cpr, int64_t nchunks, uint8_t* bcodes,
                       uint8_t* bscales, float* bts, uint8_t* rcodes, uint8_t* rscales, float* rts, uint8_t* mask,
-                      uint32_t* work, hipStream_t st) {
+                      uint32_t* work, const float* rnorm, const uint16_t* gamma, hipStream_t st) {
   const int64_t per_wg = (kThreads / 64) * 64 * kUnroll;
   const int64_t grid = (nchunks + per_wg - 1) / per_wg;
   const unsigned rgrid = (unsigned)(grid < kMaxGroups ? grid : kMaxGroups);
-  prep_nv_kernel<0, MODE, SPM, DENSE, WRITE_MASK><<<dim3(rgrid), kThreads, 0, st>>>(
-      x, ldx, cpr, nchunks, bcodes, bscales, rcodes, rscales, mask, work, bts, rts);
+  prep_nv_kernel<0, MODE, SPM, DENSE, WRITE_MASK, NORM><<<dim3(rgrid), kThreads, 0, st>>>(
+      x, ldx, cpr, nchunks, bcodes, bscales, rcodes, rscales, mask, work, bts, rts, rnorm, gamma);
   nv_reduce_kernel<<<1, 256, 0, st>>>(work, 0, (int)rgrid);
   if constexpr (MODE == 0) {
-    prep_nv_kernel<1, MODE, SPM, DENSE, WRITE_MASK><<<dim3(rgrid), kThreads, 0, st>>>(
-        x, ldx, cpr, nchunks, bcodes, bscales, rcodes, rscales, mask, work, bts, rts);
+    prep_nv_kernel<1, MODE, SPM, DENSE, WRITE_MASK, NORM><<<dim3(rgrid), kThreads, 0, st>>>(
+        x, ldx, cpr, nchunks, bcodes, bscales, rcodes, rscales, mask, work, bts, rts, rnorm, gamma);
     nv_reduce_kernel<<<1, 256, 0, st>>>(work, 1, (int)rgrid);
   }
-  prep_nv_kernel<2, MODE, SPM, DENSE, WRITE_MASK><<<dim3((unsigned)grid), kThreads, 0, st>>>(
-      x, ldx, cpr, nchunks, bcodes, bscales, rcodes, rscales, mask, work, bts, rts);
+  prep_nv_kernel<2, MODE, SPM, DENSE, WRITE_MASK, NORM><<<dim3((unsigned)grid), kThreads, 0, st>>>(
+      x, ldx, cpr, nchunks, bcodes, bscales, rcodes, rscales, mask, work, bts, rts, rnorm, gamma);
   return hipGetLastError();
 }
 
-template <int MODE, int SPM, bool WRITE_MASK>
+template <int MODE, int SPM, bool WRITE_MASK, bool NORM>
 hipError_t run_nv(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, uint8_t* bcodes, uint8_t* bscales,
                   float* bts, uint8_t* rcodes, uint8_t* rscales, float* rts, uint8_t* mask, uint32_t* work,
-                  hipStream_t st) {
+                  const float* rnorm, const uint16_t* gamma, hipStream_t st) {
   const int64_t cpr = K / 8;
   const int64_t nchunks = M * cpr;
   if (nchunks == 0) {
     nv_empty_kernel<<<1, 64, 0, st>>>(work, bts, rts);
     return hipGetLastError();
   }
-  return ldx == K ? run_passes<MODE, SPM, true, WRITE_MASK>(x, ldx, cpr, nchunks, bcodes, bscales, bts, rcodes,
-                                                            rscales, rts, mask, work, st)
-                  : run_passes<MODE, SPM, false, WRITE_MASK>(x, ldx, cpr, nchunks, bcodes, bscales, bts, rcodes,
-                                                             rscales, rts, mask, work, st);
+  return ldx == K ? run_passes<MODE, SPM, true, WRITE_MASK, NORM>(x, ldx, cpr, nchunks, bcodes, bscales, bts, rcodes,
+                                                                  rscales, rts, mask, work, rnorm, gamma, st)
+                  : run_passes<MODE, SPM, false, WRITE_MASK, NORM>(x, ldx, cpr, nchunks, bcodes, bscales, bts,
+                                                                   rcodes, rscales, rts, mask, work, rnorm, gamma, st);
+}
+
+template <int SPM, bool WRITE_MASK>
+hipError_t run_prep(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, uint8_t* bcodes, uint8_t* bscales,
+                    float* bts, uint8_t* rcodes, uint8_t* rscales, float* rts, uint8_t* mask, uint32_t* work,
+                    const float* rnorm, const uint16_t* gamma, hipStream_t st) {
+  if (rnorm)
+    return run_nv<0, SPM, WRITE_MASK, true>(x, M, K, ldx, bcodes, bscales, bts, rcodes, rscales, rts, mask, work,
+                                            rnorm, gamma, st);
+  return run_nv<0, SPM, WRITE_MASK, false>(x, M, K, ldx, bcodes, bscales, bts, rcodes, rscales, rts, mask, work,
+                                           nullptr, nullptr, st);
 }
 
 }  // namespace
@@ -391,23 +411,23 @@ hipError_t run_nv(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, uint8_t*
 hipError_t launch_prep_nv(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, int sp_n, int sp_m,
                           uint8_t* bcodes, uint8_t* bscales, float* btscale, uint8_t* rcodes,
                           uint8_t* rscales, float* rtscale, uint8_t* mask, uint32_t* work,
-                          hipStream_t stream) {
+                          const float* rnorm, const uint16_t* gamma, hipStream_t stream) {
   (void)sp_n;
   if (sp_m == 4)
-    return mask ? run_nv<0, 4, true>(x, M, K, ldx, bcodes, bscales, btscale, rcodes, rscales, rtscale, mask,
-                                     work, stream)
-                : run_nv<0, 4, false>(x, M, K, ldx, bcodes, bscales, btscale, rcodes, rscales, rtscale,
-                                      mask, work, stream);
-  return mask ? run_nv<0, 8, true>(x, M, K, ldx, bcodes, bscales, btscale, rcodes, rscales, rtscale, mask,
-                                   work, stream)
-              : run_nv<0, 8, false>(x, M, K, ldx, bcodes, bscales, btscale, rcodes, rscales, rtscale, mask,
-                                    work, stream);
+    return mask ? run_prep<4, true>(x, M, K, ldx, bcodes, bscales, btscale, rcodes, rscales, rtscale, mask, work,
+                                    rnorm, gamma, stream)
+                : run_prep<4, false>(x, M, K, ldx, bcodes, bscales, btscale, rcodes, rscales, rtscale, mask, work,
+                                     rnorm, gamma, stream);
+  return mask ? run_prep<8, true>(x, M, K, ldx, bcodes, bscales, btscale, rcodes, rscales, rtscale, mask, work,
+                                  rnorm, gamma, stream)
+              : run_prep<8, false>(x, M, K, ldx, bcodes, bscales, btscale, rcodes, rscales, rtscale, mask, work,
+                                   rnorm, gamma, stream);
 }
 
 hipError_t launch_quant_nv(const uint16_t* x, int64_t rows, int64_t K, int64_t ldx, uint8_t* codes,
                            uint8_t* scales, float* tscale, uint32_t* work, hipStream_t stream) {
-  return run_nv<1, 4, false>(x, rows, K, ldx, nullptr, nullptr, tscale, codes, scales, nullptr, nullptr,
-                             work, stream);
+  return run_nv<1, 4, false, false>(x, rows, K, ldx, nullptr, nullptr, tscale, codes, scales, nullptr, nullptr,
+                                    work, nullptr, nullptr, stream);
 }
 
 }  // namespace sharq

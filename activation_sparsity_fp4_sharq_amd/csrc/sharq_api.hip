@@ -62,6 +62,22 @@ sharq_status check_device() {
 
 sharq_status launched(hipError_t e) { return e == hipSuccess ? SHARQ_OK : SHARQ_E_LAUNCH; }
 
+// The preparation's launch for either format, optionally with the RMS normalization
+// folded in (rnorm / gamma non-NULL).  Arguments were validated by the caller.
+hipError_t enqueue_prep(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, int sp_n, int sp_m, int fmt,
+                        const sharq_fp4* backbone, const sharq_fp4* residual, uint8_t* mask_bits, void* workspace,
+                        const float* rnorm, const uint16_t* gamma, hipStream_t st) {
+  if (fmt == SHARQ_MXFP4)
+    return launch_prep_mx(x, M, K, ldx, sp_n, sp_m, backbone->codes, backbone->scales, residual->codes,
+                          residual->scales, mask_bits, rnorm, gamma, backbone->layout == SHARQ_LAYOUT_TILED, st);
+  return launch_prep_nv(x, M, K, ldx, sp_n, sp_m, backbone->codes, backbone->scales, backbone->tensor_scale,
+                        residual->codes, residual->scales, residual->tensor_scale, mask_bits,
+                        reinterpret_cast<uint32_t*>(workspace), rnorm, gamma, st);
+}
+
+// The row factors of sharq_prep_rmsnorm follow the format's own preparation workspace.
+size_t rms_factor_offset(int fmt) { return fmt == SHARQ_NVFP4 ? round_up(kNvPrepWorkspace, 256) : 0; }
+
 }  // namespace
 
 extern "C" {
@@ -158,14 +174,39 @@ sharq_status sharq_prep(const void* x, int64_t M, int64_t K, int64_t ldx, int sp
   if ((s = check_device()) != SHARQ_OK) return s;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   const uint16_t* xb = reinterpret_cast<const uint16_t*>(x);
-  if (fmt == SHARQ_MXFP4)
-    return launched(launch_prep_mx(xb, M, K, ldx, sp_n, sp_m, backbone->codes, backbone->scales,
-                                   residual->codes, residual->scales, mask_bits,
-                                   backbone->layout == SHARQ_LAYOUT_TILED, st));
-  return launched(launch_prep_nv(xb, M, K, ldx, sp_n, sp_m, backbone->codes, backbone->scales,
-                                 backbone->tensor_scale, residual->codes, residual->scales,
-                                 residual->tensor_scale, mask_bits,
-                                 reinterpret_cast<uint32_t*>(workspace), st));
+  return launched(enqueue_prep(xb, M, K, ldx, sp_n, sp_m, fmt, backbone, residual, mask_bits, workspace, nullptr,
+                               nullptr, st));
+}
+
+size_t sharq_prep_rmsnorm_workspace_bytes(int64_t M, int64_t K, int fmt) {
+  if (M < 0) return 0;
+  return rms_factor_offset(fmt) + (size_t)round_up(M > 0 ? M : 1, 64) * sizeof(float);
+}
+
+sharq_status sharq_prep_rmsnorm(const void* x, int64_t M, int64_t K, int64_t ldx, const void* gamma, float eps,
+                                int sp_n, int sp_m, int fmt, const sharq_fp4* backbone, const sharq_fp4* residual,
+                                uint8_t* mask_bits, void* workspace, size_t workspace_bytes, void* stream) {
+  sharq_status s = check_input(x, M, K, ldx, fmt);
+  if (s != SHARQ_OK) return s;
+  if (!(eps >= 0.0f) || eps > 3.0e38f) return SHARQ_E_SHAPE;  // negative, NaN or infinite
+  if ((s = check_pattern(sp_n, sp_m)) != SHARQ_OK) return s;
+  if ((s = check_payload(backbone, fmt, M)) != SHARQ_OK) return s;
+  if ((s = check_payload(residual, fmt, M)) != SHARQ_OK) return s;
+  if (backbone->layout != residual->layout) return SHARQ_E_FORMAT;
+  if (M > 0 && !gamma) return SHARQ_E_NULL;
+  if (gamma && !aligned16(gamma)) return SHARQ_E_ALIGN;
+  if (mask_bits && (reinterpret_cast<uintptr_t>(mask_bits) & 3u)) return SHARQ_E_ALIGN;
+  const size_t need = sharq_prep_rmsnorm_workspace_bytes(M, K, fmt);
+  if (!workspace || workspace_bytes < need) return SHARQ_E_WORKSPACE;
+  if (!aligned16(workspace)) return SHARQ_E_ALIGN;
+  if ((s = check_device()) != SHARQ_OK) return s;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const uint16_t* xb = reinterpret_cast<const uint16_t*>(x);
+  float* rfac = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + rms_factor_offset(fmt));
+  hipError_t e = launch_row_rms(xb, M, K, ldx, eps, rfac, st);
+  if (e != hipSuccess) return SHARQ_E_LAUNCH;
+  return launched(enqueue_prep(xb, M, K, ldx, sp_n, sp_m, fmt, backbone, residual, mask_bits, workspace, rfac,
+                               reinterpret_cast<const uint16_t*>(gamma), st));
 }
 
 sharq_status sharq_linear(const sharq_fp4* backbone, const sharq_fp4* residual, int64_t M,

@@ -22,7 +22,7 @@ LIB_PATH = os.path.join(_HERE, "libsharq.so")
 
 SYMBOLS = ["sharq_abi_version", "sharq_status_str", "sharq_payload_bytes", "sharq_convert_layout",
            "sharq_prep_workspace_bytes", "sharq_linear_workspace_bytes", "sharq_quantize", "sharq_prep",
-           "sharq_linear", "sharq_forward"]
+           "sharq_prep_rmsnorm_workspace_bytes", "sharq_prep_rmsnorm", "sharq_linear", "sharq_forward"]
 
 
 class SharqFp4(ctypes.Structure):
@@ -67,6 +67,11 @@ def lib():
         L.sharq_prep.restype = ctypes.c_int
         L.sharq_prep.argtypes = [vp, i64, i64, i64, ctypes.c_int, ctypes.c_int, ctypes.c_int, P, P, vp,
                                  vp, sz, vp]
+        L.sharq_prep_rmsnorm_workspace_bytes.restype = sz
+        L.sharq_prep_rmsnorm_workspace_bytes.argtypes = [i64, i64, ctypes.c_int]
+        L.sharq_prep_rmsnorm.restype = ctypes.c_int
+        L.sharq_prep_rmsnorm.argtypes = [vp, i64, i64, i64, vp, ctypes.c_float, ctypes.c_int, ctypes.c_int,
+                                         ctypes.c_int, P, P, vp, vp, sz, vp]
         L.sharq_linear.restype = ctypes.c_int
         L.sharq_linear.argtypes = [P, P, i64, P, i64, i64, ctypes.c_int, vp, i64, ctypes.c_int, vp, sz,
                                    vp]
@@ -187,6 +192,27 @@ def prep(x, n=2, m=4, fmt=MXFP4, want_mask=False, out=None, ws=None, layout=None
     _check("sharq_prep", lib().sharq_prep(_ptr(x), M, K, x.stride(0), n, m, fmt, ctypes.byref(sb),
                                           ctypes.byref(sr), _ptr(mask), _ptr(ws),
                                           0 if ws is None else ws.numel(), _stream(stream)))
+    return bb, rr, mask
+
+
+def prep_rmsnorm(x, gamma, eps=1e-6, n=2, m=4, fmt=MXFP4, want_mask=False, out=None, ws=None, layout=None,
+                 stream=None):
+    """SharQ preparation of RMSNorm(x) * gamma (bf16 gains [K]): returns (backbone,
+    residual, mask_bits or None)."""
+    x = _as_bf16_2d(x)
+    M, K = x.shape
+    if gamma.dtype != torch.bfloat16 or gamma.dim() != 1 or gamma.numel() != K or not gamma.is_contiguous():
+        raise ValueError("gamma must be a contiguous bfloat16 vector of K entries")
+    bb, rr = out if out is not None else (Payload.empty(M, K, fmt, x.device, layout),
+                                          Payload.empty(M, K, fmt, x.device, layout))
+    mask = torch.empty((M, K // 8), dtype=torch.uint8, device=x.device) if want_mask else None
+    if ws is None:
+        ws = workspace(lib().sharq_prep_rmsnorm_workspace_bytes(M, K, fmt), x.device)
+    sb, sr = bb.struct(), rr.struct()
+    _check("sharq_prep_rmsnorm", lib().sharq_prep_rmsnorm(_ptr(x), M, K, x.stride(0), _ptr(gamma), float(eps), n, m,
+                                                          fmt, ctypes.byref(sb), ctypes.byref(sr), _ptr(mask),
+                                                          _ptr(ws), 0 if ws is None else ws.numel(),
+                                                          _stream(stream)))
     return bb, rr, mask
 
 

@@ -61,7 +61,7 @@
 extern "C" {
 #endif
 
-#define SHARQ_ABI_VERSION 2
+#define SHARQ_ABI_VERSION 3
 
 typedef enum sharq_status {
   SHARQ_OK = 0,
@@ -133,7 +133,7 @@ sharq_status sharq_quantize(const void* x, int64_t rows, int64_t K, int64_t ldx,
                             void* stream);
 
 /* The SharQ activation preparation (abstract; "Core claim"; Figure 2's fused
- * preparation kernel, without the layer normalization):
+ * preparation kernel; sharq_prep_rmsnorm below adds the layer normalization):
  *   1. mask: in every group of m consecutive elements along K keep the n with the
  *      largest |x| (compared on the bf16 bits with the sign cleared; on equal
  *      magnitude the lower index wins), so exactly n are kept per group;
@@ -155,6 +155,31 @@ sharq_status sharq_prep(const void* x, int64_t M, int64_t K, int64_t ldx, int sp
                         int fmt, const sharq_fp4* backbone, const sharq_fp4* residual,
                         uint8_t* mask_bits, void* workspace, size_t workspace_bytes,
                         void* stream);
+
+/* Bytes of device workspace sharq_prep_rmsnorm needs: the format's preparation
+ * workspace plus one fp32 row factor per row (rounded up).  Host-only. */
+size_t sharq_prep_rmsnorm_workspace_bytes(int64_t M, int64_t K, int fmt);
+
+/* sharq_prep with the layer normalization folded in, as the pages' fused preparation
+ * does ("Core claim"; abstract: the preparation also takes over the layer
+ * normalization).  The pages do not spell the normalization out; it is read as RMS
+ * normalization with a per-channel gain and no bias, producing the bf16 tensor that
+ * the preparation then decomposes:
+ *   r_i  = fp32( 1 / sqrt( (sum_k x_ik^2) / K + eps ) )   (sum, sqrt, division in fp64)
+ *   y_ik = bf16_rne( fp32( fp32(x_ik * r_i) * gamma_k ) )
+ * and backbone / residual / mask_bits are exactly sharq_prep's outputs for y.
+ *   x, M, K, ldx, sp_n, sp_m, fmt, backbone, residual, mask_bits: as for sharq_prep
+ *   gamma      device bf16 [K] gains, 16-byte aligned (may be NULL only when M == 0)
+ *   eps        >= 0 and finite, else SHARQ_E_SHAPE
+ *   workspace  device, >= sharq_prep_rmsnorm_workspace_bytes(M, K, fmt) bytes, 16-byte
+ *              aligned; holds the row factors between the two launches of the call
+ * The fp64 row sums are exact up to ~K * 2^-53 relative, so the fp32 factor r_i can
+ * differ from an exact evaluation's only when the exact value lies within that margin
+ * of an fp32 rounding boundary. */
+sharq_status sharq_prep_rmsnorm(const void* x, int64_t M, int64_t K, int64_t ldx, const void* gamma,
+                                float eps, int sp_n, int sp_m, int fmt, const sharq_fp4* backbone,
+                                const sharq_fp4* residual, uint8_t* mask_bits, void* workspace,
+                                size_t workspace_bytes, void* stream);
 
 /* The two SharQ GEMMs over one weight payload (abstract: a sparse FP4 GEMM for the
  * backbone, a dense FP4 GEMM for the residual, one FP4 weight payload), summed in

@@ -33,7 +33,7 @@ def test_header_symbols_exported():
 
 def test_version_and_status_strings():
     L = sharq.lib()
-    assert L.sharq_abi_version() == 2
+    assert L.sharq_abi_version() == 3
     for s in range(9):
         assert L.sharq_status_str(s)
     assert L.sharq_status_str(99) == b"unknown status"
@@ -166,3 +166,37 @@ def test_convert_rejects():
     assert L.sharq_convert_layout(ctypes.byref(a), ctypes.byref(b), 4, 64, 1, None) == E_FORMAT
     assert L.sharq_convert_layout(ctypes.byref(a), ctypes.byref(b), 4, 48, 0, None) == E_SHAPE
     assert L.sharq_convert_layout(ctypes.byref(a), ctypes.byref(fp4(codes=None)), 4, 64, 0, None) == E_NULL
+
+
+def prep_norm(x=A, M=4, K=64, ldx=64, gamma=A, eps=1e-6, n=2, m=4, fmt=0, bb=None, rr=None, mask=None, ws=A,
+              wsb=1 << 20):
+    bb = bb if bb is not None else fp4()
+    rr = rr if rr is not None else fp4()
+    return sharq.lib().sharq_prep_rmsnorm(x, M, K, ldx, gamma, eps, n, m, fmt, ctypes.byref(bb), ctypes.byref(rr),
+                                          mask, ws, wsb, None)
+
+
+@pytest.mark.parametrize("kwargs,status", [
+    (dict(gamma=None), E_NULL),
+    (dict(gamma=A + 8), E_ALIGN),
+    (dict(eps=-1.0), E_SHAPE),
+    (dict(eps=float("nan")), E_SHAPE),
+    (dict(eps=float("inf")), E_SHAPE),
+    (dict(ws=None), E_WORKSPACE),
+    (dict(wsb=8), E_WORKSPACE),
+    (dict(ws=A + 4), E_ALIGN),
+    (dict(K=48), E_SHAPE),
+    (dict(n=1), E_PATTERN),
+    (dict(bb=fp4(layout=1)), E_FORMAT),
+])
+def test_prep_rmsnorm_rejects(kwargs, status):
+    assert prep_norm(**kwargs) == status
+
+
+def test_prep_rmsnorm_workspace_and_device():
+    L = sharq.lib()
+    assert L.sharq_prep_rmsnorm_workspace_bytes(100, 64, 0) >= 100 * 4
+    assert L.sharq_prep_rmsnorm_workspace_bytes(100, 64, 1) >= 100 * 4 + L.sharq_prep_workspace_bytes(100, 64, 1)
+    import torch
+    if not torch.cuda.is_available():
+        assert prep_norm() == E_DEVICE

@@ -274,3 +274,49 @@ def test_linear_rejects_mixed_layouts():
     with pytest.raises(sharq.SharqError) as e:
         sharq.linear(bb, rr, w_rm)
     assert e.value.status == 4
+
+
+# ------------------------------------------------------------ RMSNorm folded into the prep
+
+def _gain(K, seed):
+    rng = np.random.default_rng(seed)
+    return f32_to_bf16_bits(rng.normal(1.0, 0.25, K).astype(np.float32))
+
+
+@pytest.mark.parametrize("fmt,layout", FMT_LAYOUTS, ids=FL_IDS)
+@pytest.mark.parametrize("n,m", [(2, 4), (4, 8)])
+@pytest.mark.parametrize("M,K,ldx_pad", [(1, 64, 0), (37, 352, 0), (300, 1024, 64), (128, 4096, 0)])
+def test_prep_rmsnorm_matches_oracle(fmt, layout, n, m, M, K, ldx_pad):
+    """sharq_prep_rmsnorm == oracle.prep(oracle.rmsnorm(x)): masks, codes, scale bytes
+    and tensor scales bit for bit."""
+    print(f"[prep_rmsnorm] fmt={fmt} layout={layout} {n}:{m} M={M} K={K} pad={ldx_pad}", flush=True)
+    xb, _ = make_shape(M, 8, K, seed=M * 7 + K, dist="student_t3", token_sigma=0.8)
+    g = _gain(K, K)
+    eps = 1e-5
+    if ldx_pad:
+        wide = np.zeros((M, K + ldx_pad), np.uint16)
+        wide[:, :K] = xb
+        x = to_dev(wide)[:, :K]
+    else:
+        x = to_dev(xb)
+    bb, rr, mask = sharq.prep_rmsnorm(x, to_dev(g), eps, n, m, fmt, want_mask=True, layout=layout)
+    torch.cuda.synchronize()
+    yb, _ = oracle.rmsnorm(xb, g, eps)
+    ob, orr, omask = oracle.prep(yb, n, m, fmt)
+    assert np.array_equal(mask.cpu().numpy(), omask), "mask bits differ"
+    assert_payload_equal(bb, ob, "backbone")
+    assert_payload_equal(rr, orr, "residual")
+
+
+def test_prep_rmsnorm_workload_full_size():
+    """The prefill workload's activation through the normalized preparation."""
+    w = WORKLOADS["prefill"]
+    print("[prep_rmsnorm] prefill full size", flush=True)
+    xb, _ = make_inputs(w, with_weight=False)
+    g = _gain(w.K, 1)
+    bb, rr, _ = sharq.prep_rmsnorm(to_dev(xb), to_dev(g), 1e-6, w.n, w.m, w.fmt)
+    torch.cuda.synchronize()
+    yb, _ = oracle.rmsnorm(xb, g, 1e-6)
+    ob, orr, _ = oracle.prep(yb, w.n, w.m, w.fmt)
+    assert_payload_equal(bb, ob, "backbone")
+    assert_payload_equal(rr, orr, "residual")
