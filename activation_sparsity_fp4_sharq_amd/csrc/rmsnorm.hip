@@ -22,14 +22,24 @@ __global__ __launch_bounds__(kThreads) void row_rms_kernel(const uint16_t* __res
   if (row >= M) return;  // whole waves only
   const uint16_t* xr = x + row * ldx;
   double ss = 0.0;
-  for (int64_t k = (int64_t)lane * 8; k < K; k += 64 * 8) {
-    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(xr + k));
+  // ordinary (temporal) loads: the preparation re-reads X right after, ideally from
+  // the Infinity Cache; four 16-byte loads in flight per lane
+  constexpr int kUnroll = 4;
+  for (int64_t k0 = (int64_t)lane * 8; k0 < K; k0 += 64 * 8 * kUnroll) {
+    u32x4 v[kUnroll];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const double a = (double)__uint_as_float(v[i] << 16), b = (double)__uint_as_float(v[i] & 0xFFFF0000u);
-      ss = __fma_rn(a, a, ss);
-      ss = __fma_rn(b, b, ss);
+    for (int u = 0; u < kUnroll; ++u) {
+      const int64_t k = k0 + (int64_t)u * 64 * 8;
+      v[u] = k < K ? *reinterpret_cast<const u32x4*>(xr + k) : u32x4{0u, 0u, 0u, 0u};
     }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const double a = (double)__uint_as_float(v[u][i] << 16), b = (double)__uint_as_float(v[u][i] & 0xFFFF0000u);
+        ss = __fma_rn(a, a, ss);
+        ss = __fma_rn(b, b, ss);
+      }
   }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off, 64);

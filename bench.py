@@ -38,6 +38,8 @@ def parse():
     p.add_argument("--workload", default="prefill")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time for the CPU baseline")
+    p.add_argument("--rmsnorm", action="store_true",
+                   help="time the preparation with the RMS normalization folded in (sharq_prep_rmsnorm)")
     p.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                    help="only run a plain device copy of MIB MiB (5 times): the reference dispatch that "
                         "scales hardware byte counters to bytes")
@@ -182,12 +184,22 @@ def main():
         y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
         sets.append((x, weight, bb, rr, y))
     ws = sharq.workspace(max(sharq.lib().sharq_prep_workspace_bytes(M, K, w.fmt),
+                             sharq.lib().sharq_prep_rmsnorm_workspace_bytes(M, K, w.fmt),
                              sharq.lib().sharq_linear_workspace_bytes(M, N, K, w.fmt)), dev)
     stream = torch.cuda.current_stream()
+    # the normalization gain: seeded, around 1 (random-init layer, no checkpoint)
+    gamma = torch.from_numpy(np.random.default_rng(1).normal(1.0, 0.1, K).astype(np.float32)).to(dev)
+    gamma = gamma.to(torch.bfloat16)
+
+    def prep_call(x, bb, rr):
+        if args.rmsnorm:
+            sharq.prep_rmsnorm(x, gamma, 1e-6, w.n, w.m, w.fmt, out=(bb, rr), ws=ws, stream=stream)
+        else:
+            sharq.prep(x, w.n, w.m, w.fmt, out=(bb, rr), ws=ws, stream=stream)
 
     def step(i):
         x, weight, bb, rr, y = sets[i % nsets]
-        sharq.prep(x, w.n, w.m, w.fmt, out=(bb, rr), ws=ws, stream=stream)
+        prep_call(x, bb, rr)
         sharq.linear(bb, rr, weight, sharq.OUT_BF16, y=y, ws=ws, stream=stream)
 
     for i in range(args.warmup):
@@ -204,7 +216,7 @@ def main():
     # per-kernel durations with HIP events on the launch stream (separate pass)
     def prep_only(i):
         x, weight, bb, rr, y = sets[i % nsets]
-        sharq.prep(x, w.n, w.m, w.fmt, out=(bb, rr), ws=ws, stream=stream)
+        prep_call(x, bb, rr)
 
     def linear_only(i):
         x, weight, bb, rr, y = sets[i % nsets]
@@ -245,6 +257,7 @@ def main():
         "config": {"workload": w.name, "M": M, "N": N, "K": K, "pattern": f"{w.n}:{w.m}",
                    "format": "mxfp4" if w.fmt == sharq.MXFP4 else "nvfp4", "input_sets": nsets,
                    "payload_layout": "tiled" if weight0.layout == sharq.TILED else "row-major",
+                   "prep_rmsnorm": bool(args.rmsnorm),
                    "description": w.note},
         "pct_mxfp4_peak": round(100.0 * eff / t_step / 1e12 / PEAK_MXFP4_TFLOPS, 3),
         "roofline": {"bound": "mfma", "kernel": kernel_key.split(":")[0], "achieved": round(ach, 2),
