@@ -8,15 +8,16 @@
 // gfx950's block-scaled FP4 matrix instructions take power-of-two (E8M0) block
 // scales only, and an E2M1 value times an E4M3 scale needs up to 6 significant bits,
 // more than FP8 holds.  The product is, however, exact in fp16 (|v*s| <= 2688,
-// >= 2^-10), so the operands are decoded once per work-group into fp16 while they are
-// staged into LDS, and the contraction runs on v_mfma_f32_32x32x16_f16: every
-// product is exact and only the fp32 summation order differs from exact arithmetic.
-// The two paths keep separate accumulators because their tensor scales differ; the
-// weight tile in LDS is shared by both.
+// >= 2^-10), so the operands are decoded into fp16 and the contraction runs on
+// v_mfma_f32_32x32x16_f16: every product is exact and only the fp32 summation order
+// differs from exact arithmetic.  The two paths keep separate accumulators because
+// their tensor scales differ; the decoded weight operand is shared by both.
 //
 // Tiling: 256 threads (4 waves, 2x2) own a 128x128 output tile (64x64 per wave =
-// 2x2 instructions per path); per 64-element K-step the block decodes A_b, A_r and
-// W (128 rows x 64 fp16 each, rows padded to 144 B) into LDS, double-buffered.
+// 2x2 instructions per path).  For K % 64 == 0 the raw payload is staged through LDS
+// and each wave decodes its operands in registers (linear_nv_stream_kernel); other K
+// take linear_nv_kernel, which decodes each 64-element K-step cooperatively into
+// fp16 LDS tiles (rows padded to 144 B), double-buffered.
 #include <atomic>
 
 #include "sharq_internal.h"
@@ -215,14 +216,21 @@ __global__ __launch_bounds__(kThreads, 1) void linear_nv_kernel(Args a) {
 
 // ---------------------------------------------------------------------------------
 // Streaming variant for K % 64 == 0 (the usual case).  The raw payload -- 32 code
-// bytes and 4 scale bytes per row and 64-element K-step -- goes global -> LDS by
-// LDS-DMA into a 3-slot ring, two K-steps ahead, with no registers in flight; each
-// K-step is then decoded cooperatively (every element once per work-group) into the
-// fp16 tile the matrix instructions read, while the previous tile is consumed.
-// One barrier per K-step:
-//   iteration ks:  DMA of step ks+3 into raw slot ks%3 (decoded in iteration ks-1)
-//                  decode raw step ks+1 -> fp16 buffer (ks+1)%2 | MFMA on buffer ks%2
-//                  own loads of step ks+2 landed (vmcnt 5); barrier
+// bytes and 4 scale bytes per row and 64-element stage -- goes global -> LDS by
+// LDS-DMA into a 3-slot ring, three stages ahead, with no registers in flight.  Each
+// wave then reads the raw bytes of its own 64 A rows and 64 W rows straight into
+// registers and decodes them into matrix-instruction operands there: no fp16 tile in
+// LDS, one barrier per stage, and the decode's vector work of one wave runs beside the
+// matrix instructions of the other wave on its SIMD (two work-groups per CU).
+//
+// K order inside a stage: the matrix instruction's k-slot 8*h + j (h = lane / 32) of
+// sub-step i stands for stage element 32*h + 8*i + j, for A and W alike -- a dot
+// product does not depend on the order of its terms -- so that a lane's four
+// sub-steps read one contiguous 16-byte run of codes (elements 32*h .. 32*h + 31,
+// NVFP4 blocks 2*h and 2*h + 1).
+//   stage s:  raw bytes of stage s+1 -> registers;  16 sub-step pairs of matrix
+//             instructions on stage s (decoded from registers);  own loads of stage
+//             s+2 landed (vmcnt 5);  barrier;  DMA of stage s+4 into slot (s+1)%3
 // Per stage each wave issues 5 loads: 3 of the 12 code pieces (32 rows x 32 B) and 2
 // of the 6 scale pieces (64 rows x 4 B; wave 3 repeats wave 2's), so every wave's
 // count is the same.
@@ -230,14 +238,34 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 constexpr int kRawCodeBytes = 3 * BM * 32;                  // 12 KiB
 constexpr int kRawStageBytes = kRawCodeBytes + 3 * BM * 4;  // + 1.5 KiB of scales
 constexpr int kRawStages = 3;
-constexpr int kRawBytes = kRawStages * kRawStageBytes;
+constexpr int kStreamLds = kRawStages * kRawStageBytes;     // 40.5 KiB
 #define SHARQ_NV_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (7 << 4) | (15 << 8) | (((n) >> 4) << 14))
 
+// Two E4M3 scale bytes (low two bytes of w) -> their exact values as two fp16.  The
+// byte's low seven bits shifted left by seven form an fp16 with the same exponent and
+// mantissa fields, valued at 2^-8 of the E4M3 value (subnormals included: m * 2^-17),
+// and the scaling by 2^8 is exact.
+__device__ __forceinline__ v2h scale_pair(uint32_t w) {
+  const uint32_t bits = ((w & 0x7Fu) << 7) | ((w & 0x7F00u) << 15);
+  v2h s;
+  __builtin_memcpy(&s, &bits, 4);
+  return s * v2h{(_Float16)256.0f, (_Float16)256.0f};
+}
+
+// 8 E2M1 codes (one dword) times a block scale -> one matrix-instruction operand
+__device__ __forceinline__ v8h decode8(uint32_t codes, _Float16 sc) {
+  const v2h s2 = {sc, sc};
+  const v2h p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 0) * s2;  // <= 6 significant bits: exact
+  const v2h p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 1) * s2;
+  const v2h p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 2) * s2;
+  const v2h p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 3) * s2;
+  return v8h{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+}
+
 template <bool OUT_F32>
-__global__ __launch_bounds__(kThreads, 1) void linear_nv_stream_kernel(Args a) {
+__global__ __launch_bounds__(kThreads, 2) void linear_nv_stream_kernel(Args a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  uint8_t* raw = smem;               // kRawStages x [codes: 3 tiles x 128 rows x 32 B][scales: 3 x 128 x 4 B]
-  uint8_t* half = smem + kRawBytes;  // 2 x 3 fp16 tiles
+  uint8_t* raw = smem;  // kRawStages x [codes: 3 tiles x 128 rows x 32 B][scales: 3 x 128 x 4 B]
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -278,7 +306,7 @@ __global__ __launch_bounds__(kThreads, 1) void linear_nv_stream_kernel(Args a) {
   }
   auto dma = [&](int ks) {
     uint8_t* st = raw + (ks % kRawStages) * kRawStageBytes;
-    const int64_t kc = ks < nk ? ks : nk - 1;  // past the end: re-load into a slot nobody decodes
+    const int64_t kc = ks < nk ? ks : nk - 1;  // past the end: re-load into a slot nobody reads
 #pragma unroll
     for (int j = 0; j < 3; ++j)
       __builtin_amdgcn_global_load_lds(csrc[j] + kc * 32, (lds_void_t*)(st + cdst[j]), 16, 0, 0);
@@ -287,34 +315,27 @@ __global__ __launch_bounds__(kThreads, 1) void linear_nv_stream_kernel(Args a) {
       __builtin_amdgcn_global_load_lds(ssrc[j] + kc * 4, (lds_void_t*)(st + sdst[j]), 4, 0, 0);
   };
 
-  // cooperative decode: thread t owns row t/2, 32-element half t%2 of each tile; a
-  // step is 6 units (tile, 16-element block) over raw bytes read up front
-  const int srow = tid >> 1, scc = tid & 1;
-  u32x4 rcodes[3];
-  uint32_t rsc[3];
-  auto read_raw = [&](int ks) {
+  // this lane's six operand rows: A_b and A_r of rows wm*64 + 32*mt + r32, W of rows
+  // wn*64 + 32*nt + r32; raw bytes: 16 code bytes at offset 16*h, two scale bytes
+  int roff[6];
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt) {
+    roff[2 * mt] = wm * 64 + mt * 32 + r32;             // tile 0 (A_b)
+    roff[2 * mt + 1] = BM + wm * 64 + mt * 32 + r32;    // tile 1 (A_r)
+  }
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) roff[4 + nt] = 2 * BM + wn * 64 + nt * 32 + r32;
+  struct Raw {
+    u32x4 codes[6];
+    uint32_t scales[6];
+  };
+  auto read_raw = [&](Raw& r, int ks) {
     const uint8_t* st = raw + (ks % kRawStages) * kRawStageBytes;
 #pragma unroll
-    for (int t = 0; t < 3; ++t) {
-      rcodes[t] = *reinterpret_cast<const u32x4*>(st + t * BM * 32 + srow * 32 + scc * 16);
-      rsc[t] = *reinterpret_cast<const uint16_t*>(st + kRawCodeBytes + t * BM * 4 + srow * 4 + scc * 2);
+    for (int q = 0; q < 6; ++q) {
+      r.codes[q] = *reinterpret_cast<const u32x4*>(st + roff[q] * 32 + h * 16);
+      r.scales[q] = *reinterpret_cast<const uint32_t*>(st + kRawCodeBytes + roff[q] * 4) >> (16 * h);
     }
-  };
-  auto decode_unit = [&](int u, int buf) {
-    const int t = u >> 1, bi = u & 1;
-    v2h d[8];
-    decode16(u32x2{rcodes[t][2 * bi], rcodes[t][2 * bi + 1]}, (rsc[t] >> (8 * bi)) & 0xFFu, d);
-    uint8_t* dst = half + buf * kStageBytes + t * kTileBytes + srow * kRowPitch + (scc * 32 + bi * 16) * 2;
-    u32x4 lo, hi;
-    __builtin_memcpy(&lo, &d[0], 16);
-    __builtin_memcpy(&hi, &d[4], 16);
-    *reinterpret_cast<u32x4*>(dst) = lo;
-    *reinterpret_cast<u32x4*>(dst + 16) = hi;
-  };
-  auto decode = [&](int ks, int buf) {
-    read_raw(ks);
-#pragma unroll
-    for (int u = 0; u < 6; ++u) decode_unit(u, buf);
   };
 
   v16f accb[2][2], accr[2][2];
@@ -325,34 +346,27 @@ __global__ __launch_bounds__(kThreads, 1) void linear_nv_stream_kernel(Args a) {
       accb[i][j] = v16f{};
       accr[i][j] = v16f{};
     }
-  // fp16 fragments of one 16-element sub-step, double-buffered in registers
-  v8h fab[2][2], far[2][2], fw[2][2];
-  auto read_frags = [&](int buf, int s, int slot) {
-    const uint8_t* base = half + buf * kStageBytes;
-    const int col = (16 * s + 8 * h) * 2;
+  auto compute = [&](const Raw& r) {
+    v2h sc[6];
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-      const int row = wm * 64 + mt * 32 + r32;
-      fab[slot][mt] = *reinterpret_cast<const v8h*>(base + row * kRowPitch + col);
-      far[slot][mt] = *reinterpret_cast<const v8h*>(base + kTileBytes + row * kRowPitch + col);
+    for (int q = 0; q < 6; ++q) sc[q] = scale_pair(r.scales[q]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v8h f[6];
+#pragma unroll
+      for (int q = 0; q < 6; ++q) f[q] = decode8(r.codes[q][i], sc[q][i >> 1]);
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+          accb[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f[2 * mt], f[4 + nt], accb[mt][nt], 0, 0, 0);
+          accr[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f[2 * mt + 1], f[4 + nt], accr[mt][nt], 0, 0, 0);
+        }
     }
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      const int row = wn * 64 + nt * 32 + r32;
-      fw[slot][nt] = *reinterpret_cast<const v8h*>(base + 2 * kTileBytes + row * kRowPitch + col);
-    }
-  };
-  auto mma = [&](int slot) {
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
-        accb[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fab[slot][mt], fw[slot][nt], accb[mt][nt], 0, 0, 0);
-        accr[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(far[slot][mt], fw[slot][nt], accr[mt][nt], 0, 0, 0);
-      }
   };
   auto barrier = [&]() {
     __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's raw reads have returned
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
     __builtin_amdgcn_sched_barrier(0);
@@ -361,35 +375,21 @@ __global__ __launch_bounds__(kThreads, 1) void linear_nv_stream_kernel(Args a) {
   dma(0);
   dma(1);
   dma(2);
-  SHARQ_NV_WAIT_VMCNT(10);  // step 0 landed
+  SHARQ_NV_WAIT_VMCNT(5);  // this wave's loads of stages 0 and 1 landed
   barrier();
-  decode(0, 0);
-  SHARQ_NV_WAIT_VMCNT(5);   // step 1 landed
-  barrier();
+  Raw cur, nxt;
+  read_raw(cur, 0);
+  barrier();  // every wave has stage 0 in registers: its slot is free
+  dma(3);
   for (int ks = 0; ks < nk; ++ks) {
-    const int cur = ks & 1, nxt = cur ^ 1;
-    dma(ks + 3);
-    // (in the last iteration this decodes the clamped re-load of the last step into
-    // the idle buffer: wasted once, but the body stays branch-free)
-    read_raw(ks + 1);
-    read_frags(cur, 0, 0);
-    // each sub-step's 8 matrix instructions are issued, then a share of the next
-    // step's decode runs on the vector ALU while they execute
-#pragma unroll
-    for (int s = 0; s < BK / 16; ++s) {
-      if (s + 1 < BK / 16) read_frags(cur, s + 1, (s + 1) & 1);
-      mma(s & 1);
-      __builtin_amdgcn_sched_barrier(0);
-      if (s == 0 || s == 2) {
-        decode_unit(s == 0 ? 0 : 3, nxt);
-        decode_unit(s == 0 ? 1 : 4, nxt);
-      } else {
-        decode_unit(s == 1 ? 2 : 5, nxt);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    SHARQ_NV_WAIT_VMCNT(5);  // this wave's loads of step ks+2 landed
-    barrier();
+    read_raw(nxt, ks + 1);   // past the last stage: a loaded slot, never used
+    __builtin_amdgcn_sched_barrier(0);  // issue the reads first: their latency hides under compute
+    compute(cur);
+    __builtin_amdgcn_sched_barrier(0);
+    SHARQ_NV_WAIT_VMCNT(5);  // this wave's loads of stage ks+2 landed
+    barrier();               // ... everyone's; everyone has stage ks+1 in registers
+    dma(ks + 4);             // into the slot of stage ks+1
+    cur = nxt;
   }
   SHARQ_NV_WAIT_VMCNT(0);
 
@@ -416,18 +416,17 @@ __global__ __launch_bounds__(kThreads, 1) void linear_nv_stream_kernel(Args a) {
 
 template <bool OUT_F32>
 hipError_t launch_stream(const Args& a, hipStream_t stream) {
-  constexpr int kLds = kRawBytes + 2 * kStageBytes;
   static std::atomic<bool> configured[kMaxDevices];
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
   if (dev < 0 || dev >= kMaxDevices || !configured[dev].load(std::memory_order_acquire)) {
     e = hipFuncSetAttribute(reinterpret_cast<const void*>(&linear_nv_stream_kernel<OUT_F32>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, kLds);
+                            hipFuncAttributeMaxDynamicSharedMemorySize, kStreamLds);
     if (e != hipSuccess) return e;
     if (dev >= 0 && dev < kMaxDevices) configured[dev].store(true, std::memory_order_release);
   }
-  linear_nv_stream_kernel<OUT_F32><<<dim3(a.tiles_m * a.tiles_n), dim3(kThreads), kLds, stream>>>(a);
+  linear_nv_stream_kernel<OUT_F32><<<dim3(a.tiles_m * a.tiles_n), dim3(kThreads), kStreamLds, stream>>>(a);
   return hipGetLastError();
 }
 
