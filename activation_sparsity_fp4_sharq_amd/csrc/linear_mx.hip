@@ -121,7 +121,7 @@ __device__ __forceinline__ uint32_t load_scale_dword(const uint8_t* s, int64_t r
   }
 }
 
-template <bool OUT_F32, bool K_ALIGNED>
+template <bool OUT_F32, bool K_ALIGNED, bool DUAL>
 __global__ __launch_bounds__(kThreads, 1) void linear_mx_kernel(Args a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int tid = threadIdx.x;
@@ -149,6 +149,7 @@ __global__ __launch_bounds__(kThreads, 1) void linear_mx_kernel(Args a) {
       const int c = tid + kThreads * (i & 1);  // chunk 0..1023 within its tile
       const int row = c >> 2, col = c & 3;
       const int which = i >> 1;              // 0: A_b, 1: A_r, 2: W
+      if (!DUAL && which == 0) continue;     // one activation operand: A_b absent
       const uint8_t* src = which == 0 ? a.bc : which == 1 ? a.rc : a.wc;
       const int64_t grow = (which == 2 ? n0 : m0) + row;
       const int64_t glim = which == 2 ? a.N : a.M;
@@ -162,7 +163,7 @@ __global__ __launch_bounds__(kThreads, 1) void linear_mx_kernel(Args a) {
       const int row = tid & 255;
       const uint8_t* s = tid < 256 ? a.bs : a.rs;
       const int64_t grow = m0 + row;
-      sstage[0] = grow < a.M ? load_scale_dword<K_ALIGNED>(s, grow, nbk, kstep) : 0u;
+      sstage[0] = grow < a.M && (DUAL || tid >= 256) ? load_scale_dword<K_ALIGNED>(s, grow, nbk, kstep) : 0u;
       const int64_t wrow = n0 + row;
       sstage[1] = (tid < 256 && wrow < a.N) ? load_scale_dword<K_ALIGNED>(a.ws, wrow, nbk, kstep) : 0u;
     }
@@ -175,6 +176,7 @@ __global__ __launch_bounds__(kThreads, 1) void linear_mx_kernel(Args a) {
       const int c = tid + kThreads * (i & 1);
       const int row = c >> 2, col = c & 3;
       const int which = i >> 1;
+      if (!DUAL && which == 0) continue;
       *reinterpret_cast<u32x4*>(base + which * kTileBytes + row * kRowPitch + col * 16) = stage[i];
     }
     uint32_t* sc = reinterpret_cast<uint32_t*>(base + 3 * kTileBytes);
@@ -202,7 +204,7 @@ __global__ __launch_bounds__(kThreads, 1) void linear_mx_kernel(Args a) {
     v4i af[2][2][2];  // [path][mt][substep]
     uint32_t as[2][2];
 #pragma unroll
-    for (int p = 0; p < 2; ++p)
+    for (int p = DUAL ? 0 : 1; p < 2; ++p)
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt) {
         const int row = wm * 64 + mt * 32 + r32;
@@ -222,7 +224,7 @@ __global__ __launch_bounds__(kThreads, 1) void linear_mx_kernel(Args a) {
       ws[nt] = sc[512 + row] >> (16 * h);
     }
 #pragma unroll
-    for (int p = 0; p < 2; ++p)
+    for (int p = DUAL ? 0 : 1; p < 2; ++p)
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
@@ -325,7 +327,7 @@ __device__ __forceinline__ void store_swapped(const Args& a, const v16f (&acc)[M
 // s_waitcnt with only the vector-memory counter constrained (expcnt/lgkmcnt left free).
 #define SHARQ_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (7 << 4) | (15 << 8) | (((n) >> 4) << 14))
 
-template <bool OUT_F32>
+template <bool OUT_F32, bool DUAL>
 __global__ __launch_bounds__(kThreads, 1) void linear_mx_dma_kernel(Args a) {
   extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
   const int tid = threadIdx.x;
@@ -339,15 +341,17 @@ __global__ __launch_bounds__(kThreads, 1) void linear_mx_dma_kernel(Args a) {
   const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
   const int nk = (int)(a.Kp / 128);
 
-  // Each wave fills 6 of the 48 fragments of a stage (A_b, A_r, W x 16): one
-  // contiguous 1 KiB fragment of the tiled payload per load.  Row tiles past the
-  // padded extent are clamped to the last one (computed, never stored).
-  const uint8_t* fsrc[6];
+  // Each wave fills 6 of the 48 fragments of a stage (A_b, A_r, W x 16; 4 of 32
+  // without A_b): one contiguous 1 KiB fragment of the tiled payload per load.  Row
+  // tiles past the padded extent are clamped to the last one (computed, never stored).
+  constexpr int kFragLoads = DUAL ? 6 : 4;
+  constexpr int kOp0 = DUAL ? 0 : 1;  // first activation operand present
+  const uint8_t* fsrc[6];  // (fixed extent: a template-dependent one drops the host launch stub)
   int fdst[6];
 #pragma unroll
-  for (int j = 0; j < 6; ++j) {
-    const int f = wave * 6 + j;
-    const int op = f >> 4, fi = f & 15, rt = fi >> 1, sub = fi & 1;
+  for (int j = 0; j < kFragLoads; ++j) {
+    const int f = wave * kFragLoads + j;
+    const int op = kOp0 + (f >> 4), fi = f & 15, rt = fi >> 1, sub = fi & 1;
     const uint8_t* base = op == 0 ? a.bc : op == 1 ? a.rc : a.wc;
     const int64_t ntiles = (op == 2 ? a.Np : a.Mp) / 32;
     int64_t t = (op == 2 ? n0 : m0) / 32 + rt;
@@ -355,15 +359,16 @@ __global__ __launch_bounds__(kThreads, 1) void linear_mx_dma_kernel(Args a) {
     fsrc[j] = base + (t * (a.Kp / 64) + sub) * kFragBytes + lane * 16;
     fdst[j] = op * kOpTileBytes + fi * kFragBytes;
   }
-  // Scale words: one operand's 256 words per K-step are 1 KiB contiguous; waves 0..2
-  // load one operand each and waves 3..7 repeat wave 2's load (identical bytes to the
-  // same place), so every wave issues the same 7 loads per stage and no branch sits
-  // between them -- the compiler's vmcnt bookkeeping then never degrades to a full wait.
+  // Scale words: one operand's 256 words per K-step are 1 KiB contiguous; the first
+  // waves load one operand each and the others repeat the weight's load (identical
+  // bytes to the same place), so every wave issues the same loads per stage and no
+  // branch sits between them -- the compiler's vmcnt bookkeeping then never degrades
+  // to a full wait.
   const uint8_t* ssrc;
   int64_t sstep;
   int sdst;
   {
-    const int op = wave < 3 ? wave : 2;
+    const int op = (kOp0 + wave < 3) ? kOp0 + wave : 2;
     const uint8_t* base = op == 0 ? a.bs : op == 1 ? a.rs : a.ws;
     const int64_t rp = op == 2 ? a.Np : a.Mp;
     int64_t row = (op == 2 ? n0 : m0) + 4 * lane;
@@ -372,13 +377,13 @@ __global__ __launch_bounds__(kThreads, 1) void linear_mx_dma_kernel(Args a) {
     sstep = rp * 4;
     sdst = 3 * kOpTileBytes + op * 1024;
   }
-  constexpr int kLoads = 7;  // per wave and stage
+  constexpr int kLoads = kFragLoads + 1;  // per wave and stage
   // load j of stage ks (indices past the last K-step re-load the last one into a slot
   // nobody reads again, keeping the count per iteration constant)
   auto issue_one = [&](int j, int ks) {
     uint8_t* st = smem + (ks % kDmaStages) * kDmaStageBytes;
     const int64_t kc = ks < nk ? ks : nk - 1;
-    if (j < 6)
+    if (j < kFragLoads)
       __builtin_amdgcn_global_load_lds(fsrc[j] + kc * 2 * kFragBytes, (lds_void_t*)(st + fdst[j]), 16, 0, 0);
     else
       __builtin_amdgcn_global_load_lds(ssrc + kc * sstep, (lds_void_t*)(st + sdst), 16, 0, 0);
@@ -405,7 +410,7 @@ __global__ __launch_bounds__(kThreads, 1) void linear_mx_dma_kernel(Args a) {
     const uint32_t* sc = reinterpret_cast<const uint32_t*>(st + 3 * kOpTileBytes);
     uint32_t as[2][2], ws[4];
 #pragma unroll
-    for (int p = 0; p < 2; ++p)
+    for (int p = kOp0; p < 2; ++p)
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt) as[p][mt] = sc[p * 256 + wm * 64 + mt * 32 + r32] >> (8 * h);
 #pragma unroll
@@ -414,7 +419,7 @@ __global__ __launch_bounds__(kThreads, 1) void linear_mx_dma_kernel(Args a) {
     for (int sub = 0; sub < 2; ++sub) {
       v4i af[2][2], wf[4];
 #pragma unroll
-      for (int p = 0; p < 2; ++p)
+      for (int p = kOp0; p < 2; ++p)
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt)
           af[p][mt] = *reinterpret_cast<const v4i*>(st + p * kOpTileBytes +
@@ -424,7 +429,7 @@ __global__ __launch_bounds__(kThreads, 1) void linear_mx_dma_kernel(Args a) {
         wf[nt] = *reinterpret_cast<const v4i*>(st + 2 * kOpTileBytes + ((wn * 4 + nt) * 2 + sub) * kFragBytes +
                                                lane * 16);
 #pragma unroll
-      for (int p = 0; p < 2; ++p)
+      for (int p = kOp0; p < 2; ++p)
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
@@ -438,8 +443,9 @@ __global__ __launch_bounds__(kThreads, 1) void linear_mx_dma_kernel(Args a) {
               acc[mt][nt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
                   widen(wf[nt]), widen(af[p][mt]), acc[mt][nt], 4, 4, 2, (int)ws[nt], 2, (int)as[p][mt]);
             // the next-but-one stage's loads, spread through the instructions
-            const int i = sub * 16 + (p * 2 + mt) * 4 + nt;
-            if (i % 4 == 3 && i / 4 < kLoads) issue_one(i / 4, ks + 2);
+            constexpr int kPaths = 2 - kOp0, kEvery = DUAL ? 4 : 3;
+            const int i = sub * 8 * kPaths + ((p - kOp0) * 2 + mt) * 4 + nt;
+            if (i % kEvery == kEvery - 1 && i / kEvery < kLoads) issue_one(i / kEvery, ks + 2);
           }
     }
   }
@@ -450,372 +456,20 @@ __global__ __launch_bounds__(kThreads, 1) void linear_mx_dma_kernel(Args a) {
                                smem + wave * (64 * (256 + kEpiPad)), a.y_aligned);
 }
 
-template <bool OUT_F32>
+template <bool OUT_F32, bool DUAL>
 hipError_t launch_dma(const Args& a, hipStream_t stream) {
   static std::atomic<bool> configured[kMaxDevices];
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
   if (dev < 0 || dev >= kMaxDevices || !configured[dev].load(std::memory_order_acquire)) {
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&linear_mx_dma_kernel<OUT_F32>),
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&linear_mx_dma_kernel<OUT_F32, DUAL>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, kDmaStages * kDmaStageBytes);
     if (e != hipSuccess) return e;
     if (dev >= 0 && dev < kMaxDevices) configured[dev].store(true, std::memory_order_release);
   }
   const int grid = a.tiles_m * a.tiles_n;
-  linear_mx_dma_kernel<OUT_F32><<<dim3(grid), dim3(kThreads), kDmaStages * kDmaStageBytes, stream>>>(a);
-  return hipGetLastError();
-}
-
-// ---------------------------------------------------------------------------------
-// Software-pipelined kernel: 4 waves (one per SIMD), each owning a 128x128 wave tile
-// (4x4 instructions per path and sub-step, 256 fp32 accumulators per lane), so every
-// fragment read from LDS feeds 4 (A) or 8 (W, both paths) instructions.  The fragment
-// reads of the next sub-step are issued while the current sub-step's 32 instructions
-// run, and the next K-step's first fragments are read right after the mid-step
-// barrier, so the matrix pipe never waits on LDS latency.  LDS holds a 3-slot ring
-// of stages in fragment order (as above); a stage's DMA is issued two K-steps ahead.
-//   iteration i:  [A] read sub-step-1 fragments of stage i | 32 MFMA on sub-step 0
-//                 [B] wait own DMA of stage i+1; barrier; DMA stage i+3 into slot i%3
-//                 [C] read sub-step-0 fragments + scales of stage i+1 | 32 MFMA on sub-step 1
-constexpr int kPipeThreads = 256;
-
-struct Frags {
-  v4i a[2][4];  // [path][mt]
-  v4i w[4];     // [nt]
-};
-
-__device__ __forceinline__ void read_frags(Frags& f, const uint8_t* st, int sub, int wm, int wn, int lane) {
-#pragma unroll
-  for (int p = 0; p < 2; ++p)
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-      f.a[p][mt] = *reinterpret_cast<const v4i*>(st + p * kOpTileBytes + ((wm * 4 + mt) * 2 + sub) * kFragBytes +
-                                                 lane * 16);
-#pragma unroll
-  for (int nt = 0; nt < 4; ++nt)
-    f.w[nt] = *reinterpret_cast<const v4i*>(st + 2 * kOpTileBytes + ((wn * 4 + nt) * 2 + sub) * kFragBytes +
-                                            lane * 16);
-}
-
-struct Scales {
-  uint32_t a[2][4], w[4];
-};
-
-__device__ __forceinline__ void read_scales(Scales& sc, const uint8_t* st, int wm, int wn, int r32, int h) {
-  const uint32_t* s = reinterpret_cast<const uint32_t*>(st + 3 * kOpTileBytes);
-#pragma unroll
-  for (int p = 0; p < 2; ++p)
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) sc.a[p][mt] = s[p * 256 + wm * 128 + mt * 32 + r32] >> (8 * h);
-#pragma unroll
-  for (int nt = 0; nt < 4; ++nt) sc.w[nt] = s[512 + wn * 128 + nt * 32 + r32] >> (8 * h);
-}
-
-template <int SUB>
-__device__ __forceinline__ void mma_substep(v16f (&acc)[4][4], const Frags& f, const Scales& sc) {
-#pragma unroll
-  for (int p = 0; p < 2; ++p)
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt)
-        acc[mt][nt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-            widen(f.w[nt]), widen(f.a[p][mt]), acc[mt][nt], 4, 4, 2 * SUB, (int)sc.w[nt], 2 * SUB,
-            (int)sc.a[p][mt]);
-}
-
-template <bool OUT_F32>
-__global__ __launch_bounds__(kPipeThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void linear_mx_pipe_kernel(Args a) {
-  extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
-  const int r32 = lane & 31, h = lane >> 5;
-
-  int tm, tn;
-  tile_of(blockIdx.x, a.tiles_m, a.tiles_n, tm, tn);
-  const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
-  const int nk = (int)(a.Kp / 128);
-
-  // Each wave fills 12 of the 48 fragments of a stage; waves 0..2 also load one
-  // operand's 1 KiB of scale words.
-  const uint8_t* fsrc[12];
-  int fdst[12];
-#pragma unroll
-  for (int j = 0; j < 12; ++j) {
-    const int f = wave * 12 + j;
-    const int op = f >> 4, fi = f & 15, rt = fi >> 1, sub = fi & 1;
-    const uint8_t* base = op == 0 ? a.bc : op == 1 ? a.rc : a.wc;
-    const int64_t ntiles = (op == 2 ? a.Np : a.Mp) / 32;
-    int64_t t = (op == 2 ? n0 : m0) / 32 + rt;
-    t = t < ntiles ? t : ntiles - 1;
-    fsrc[j] = base + (t * (a.Kp / 64) + sub) * kFragBytes + lane * 16;
-    fdst[j] = op * kOpTileBytes + fi * kFragBytes;
-  }
-  const bool scale_wave = wave < 3;
-  const uint8_t* ssrc;
-  int64_t sstep;
-  {
-    const int op = scale_wave ? wave : 0;
-    const uint8_t* base = op == 0 ? a.bs : op == 1 ? a.rs : a.ws;
-    const int64_t rp = op == 2 ? a.Np : a.Mp;
-    int64_t row = (op == 2 ? n0 : m0) + 4 * lane;
-    row = row < rp - 4 ? row : rp - 4;
-    ssrc = base + row * 4;
-    sstep = rp * 4;
-  }
-  const int sdst = 3 * kOpTileBytes + (scale_wave ? wave : 0) * 1024;
-  auto issue = [&](int ks) {
-    uint8_t* st = smem + (ks % kDmaStages) * kDmaStageBytes;
-#pragma unroll
-    for (int j = 0; j < 12; ++j)
-      __builtin_amdgcn_global_load_lds(fsrc[j] + (int64_t)ks * 2 * kFragBytes, (lds_void_t*)(st + fdst[j]), 16, 0, 0);
-    if (scale_wave)
-      __builtin_amdgcn_global_load_lds(ssrc + (int64_t)ks * sstep, (lds_void_t*)(st + sdst), 16, 0, 0);
-  };
-  auto stage_ptr = [&](int ks) { return smem + (ks % kDmaStages) * kDmaStageBytes; };
-
-  v16f acc[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = v16f{};
-
-  // prologue: three stages in flight, wait for the first
-  issue(0);
-  if (nk > 1) issue(1);
-  if (nk > 2) issue(2);
-  // a wave issues L = 12 or 13 loads per stage
-  if (nk > 2) { if (scale_wave) SHARQ_WAIT_VMCNT(26); else SHARQ_WAIT_VMCNT(24); }
-  else if (nk > 1) { if (scale_wave) SHARQ_WAIT_VMCNT(13); else SHARQ_WAIT_VMCNT(12); }
-  else SHARQ_WAIT_VMCNT(0);
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-
-  Frags f0, f1;
-  Scales sc, scn;
-  read_frags(f0, stage_ptr(0), 0, wm, wn, lane);
-  read_scales(sc, stage_ptr(0), wm, wn, r32, h);
-
-  for (int ks = 0; ks < nk; ++ks) {
-    const uint8_t* st = stage_ptr(ks);
-    // [A]
-    read_frags(f1, st, 1, wm, wn, lane);
-    mma_substep<0>(acc, f0, sc);
-    // [B] stage ks+1 complete for every wave; slot ks%3 free for stage ks+3
-    if (ks + 2 < nk) { if (scale_wave) SHARQ_WAIT_VMCNT(13); else SHARQ_WAIT_VMCNT(12); }
-    else SHARQ_WAIT_VMCNT(0);
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-    if (ks + 3 < nk) issue(ks + 3);
-    // [C]
-    if (ks + 1 < nk) {
-      read_frags(f0, stage_ptr(ks + 1), 0, wm, wn, lane);
-      read_scales(scn, stage_ptr(ks + 1), wm, wn, r32, h);
-    }
-    mma_substep<1>(acc, f1, sc);
-    sc = scn;
-  }
-
-  __syncthreads();  // every wave is done with the stage ring; reuse it for the epilogue
-  store_swapped<OUT_F32, 4, 4>(a, acc, m0 + wm * 128, n0 + wn * 128, lane,
-                               smem + wave * (128 * (256 + kEpiPad)), a.y_aligned);
-}
-
-template <bool OUT_F32>
-hipError_t launch_pipe(const Args& a, hipStream_t stream) {
-  static std::atomic<bool> configured[kMaxDevices];
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return e;
-  if (dev < 0 || dev >= kMaxDevices || !configured[dev].load(std::memory_order_acquire)) {
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&linear_mx_pipe_kernel<OUT_F32>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, kDmaStages * kDmaStageBytes);
-    if (e != hipSuccess) return e;
-    if (dev >= 0 && dev < kMaxDevices) configured[dev].store(true, std::memory_order_release);
-  }
-  const int grid = a.tiles_m * a.tiles_n;
-  linear_mx_pipe_kernel<OUT_F32><<<dim3(grid), dim3(kPipeThreads), kDmaStages * kDmaStageBytes, stream>>>(a);
-  return hipGetLastError();
-}
-
-// ---------------------------------------------------------------------------------
-// Streaming kernel (the default for tiled payloads).  4 waves, one per SIMD; wave w
-// owns output rows m0+64w .. +63 and all 256 columns of the work-group tile (2 x 8
-// instructions per path and sub-step, 256 fp32 accumulators per lane), so a weight
-// fragment read from LDS feeds 4 instructions and an activation fragment 8.
-// Everything reaches LDS by DMA: per K-step and wave, its own 8 activation
-// fragments (backbone and residual; tiled fragments are exactly instruction
-// operands) and their scale words into a wave-private region, plus a quarter of the
-// 16 shared weight fragments and of their scale words -- 15 loads, the same for
-// every wave and every iteration (indices past the last K-step are clamped), with
-// no branch between them, so a single constant vmcnt threshold means "the stage I
-// need next has landed" and the compiler never has to add a conservative wait.
-// Three LDS slots; stage i+2 is issued right after the barrier that frees its slot.
-constexpr int kAregThreads = 256;
-constexpr int kSWFrag = 0;                              // 16 weight fragments
-constexpr int kSWScale = 16 * kFragBytes;               // 256 weight scale words
-constexpr int kSAWave = kSWScale + 1024;                // per wave: 8 A fragments + 128 scale words
-constexpr int kSAWaveBytes = 8 * kFragBytes + 512;
-constexpr int kSStageBytes = kSAWave + 4 * kSAWaveBytes;  // 52224
-constexpr int kSSlots = 3;
-constexpr int kAregEpiPitch = 8 * 32 * 2 + kEpiPad;       // bf16 row of a 64x256 wave tile
-constexpr int kAregLds = (4 * 64 * kAregEpiPitch > kSSlots * kSStageBytes) ? 4 * 64 * kAregEpiPitch
-                                                                            : kSSlots * kSStageBytes;
-constexpr int kSLoadsPerStage = 15;
-
-template <bool OUT_F32>
-__global__ __launch_bounds__(kAregThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void linear_mx_areg_kernel(Args a) {
-  extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int r32 = lane & 31, h = lane >> 5;
-
-  int tm, tn;
-  tile_of(blockIdx.x, a.tiles_m, a.tiles_n, tm, tn);
-  const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
-  const int nk = (int)(a.Kp / 128);
-  const int64_t kc_per_rt = a.Kp / 64;
-
-  // ---- load descriptors (per lane source, per wave LDS offset within a stage)
-  const uint8_t* src[10];  // 8 A fragments, 4 W fragments below, scale words separately
-  int dst[10];
-#pragma unroll
-  for (int p = 0; p < 2; ++p)
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-      int64_t t = (m0 + 64 * wave) / 32 + mt;
-      t = t < a.Mp / 32 ? t : a.Mp / 32 - 1;
-      const uint8_t* base = p == 0 ? a.bc : a.rc;
-#pragma unroll
-      for (int sub = 0; sub < 2; ++sub) {
-        const int j = (p * 2 + mt) * 2 + sub;
-        src[j] = base + (t * kc_per_rt + sub) * kFragBytes + lane * 16;
-        dst[j] = kSAWave + wave * kSAWaveBytes + j * kFragBytes;
-      }
-    }
-  const uint8_t* wsrc[4];
-  int wdst[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int fi = wave * 4 + j, nt = fi >> 1, sub = fi & 1;
-    int64_t t = n0 / 32 + nt;
-    t = t < a.Np / 32 ? t : a.Np / 32 - 1;
-    wsrc[j] = a.wc + (t * kc_per_rt + sub) * kFragBytes + lane * 16;
-    wdst[j] = kSWFrag + fi * kFragBytes;
-  }
-  const uint8_t* asrc[2];
-  {
-    int64_t row = m0 + 64 * wave + lane;
-    row = row < a.Mp ? row : a.Mp - 1;
-    asrc[0] = a.bs + row * 4;
-    asrc[1] = a.rs + row * 4;
-  }
-  const uint8_t* wssrc;
-  {
-    int64_t row = n0 + 64 * wave + lane;
-    row = row < a.Np ? row : a.Np - 1;
-    wssrc = a.ws + row * 4;
-  }
-  // Load j (0..14) of stage ks.  The 15 loads of a stage are spread through the
-  // matrix instructions of the current K-step (one after every fourth instruction):
-  // the texture unit takes ~16 cycles per 1 KiB request, and a burst of 60 requests
-  // per work-group would stall every wave for ~1000 cycles at the start of a step.
-  auto issue_one = [&](int j, int ks) {
-    uint8_t* st = smem + (ks % kSSlots) * kSStageBytes;
-    const int64_t kc = ks < nk ? ks : nk - 1;
-    if (j < 8)
-      __builtin_amdgcn_global_load_lds(src[j] + kc * 2 * kFragBytes, (lds_void_t*)(st + dst[j]), 16, 0, 0);
-    else if (j < 12)
-      __builtin_amdgcn_global_load_lds(wsrc[j - 8] + kc * 2 * kFragBytes, (lds_void_t*)(st + wdst[j - 8]), 16, 0, 0);
-    else if (j < 14)
-      __builtin_amdgcn_global_load_lds(asrc[j - 12] + kc * a.Mp * 4,
-                                       (lds_void_t*)(st + kSAWave + wave * kSAWaveBytes + 8 * kFragBytes + (j - 12) * 256),
-                                       4, 0, 0);
-    else
-      __builtin_amdgcn_global_load_lds(wssrc + kc * a.Np * 4, (lds_void_t*)(st + kSWScale + 256 * wave), 4, 0, 0);
-  };
-  auto issue = [&](int ks) {
-#pragma unroll
-    for (int j = 0; j < kSLoadsPerStage; ++j) issue_one(j, ks);
-  };
-
-  v16f acc[2][8];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 8; ++j) acc[i][j] = v16f{};
-
-  issue(0);
-  issue(1);
-  for (int ks = 0; ks < nk; ++ks) {
-    // this wave's loads of stage ks are done when at most one stage's remain
-    SHARQ_WAIT_VMCNT(kSLoadsPerStage);
-    __builtin_amdgcn_s_barrier();  // every wave's stage ks landed; slot (ks+2)%3 is free
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-
-    const uint8_t* st = smem + (ks % kSSlots) * kSStageBytes;
-    const uint8_t* ab = st + kSAWave + wave * kSAWaveBytes;
-    const uint32_t* wsw = reinterpret_cast<const uint32_t*>(st + kSWScale);
-    const uint32_t* asw = reinterpret_cast<const uint32_t*>(ab + 8 * kFragBytes);
-    uint32_t ws[8], as[2][2];
-#pragma unroll
-    for (int nt = 0; nt < 8; ++nt) ws[nt] = wsw[nt * 32 + r32] >> (8 * h);
-#pragma unroll
-    for (int p = 0; p < 2; ++p)
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt) as[p][mt] = asw[p * 64 + mt * 32 + r32] >> (8 * h);
-#pragma unroll
-    for (int sub = 0; sub < 2; ++sub) {
-      v4i af[2][2], wf[8];
-#pragma unroll
-      for (int p = 0; p < 2; ++p)
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
-          af[p][mt] = *reinterpret_cast<const v4i*>(ab + ((p * 2 + mt) * 2 + sub) * kFragBytes + lane * 16);
-#pragma unroll
-      for (int nt = 0; nt < 8; ++nt)
-        wf[nt] = *reinterpret_cast<const v4i*>(st + kSWFrag + (nt * 2 + sub) * kFragBytes + lane * 16);
-#pragma unroll
-      for (int p = 0; p < 2; ++p)
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-          for (int nt = 0; nt < 8; ++nt) {
-            if (sub == 0)
-              acc[mt][nt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                  widen(wf[nt]), widen(af[p][mt]), acc[mt][nt], 4, 4, 0, (int)ws[nt], 0, (int)as[p][mt]);
-            else
-              acc[mt][nt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                  widen(wf[nt]), widen(af[p][mt]), acc[mt][nt], 4, 4, 2, (int)ws[nt], 2, (int)as[p][mt]);
-            const int i = sub * 32 + (p * 2 + mt) * 8 + nt;  // instruction index in the K-step
-            if (i % 4 == 3 && i / 4 < kSLoadsPerStage) issue_one(i / 4, ks + 2);
-          }
-    }
-  }
-  SHARQ_WAIT_VMCNT(0);  // the clamped trailing loads land before LDS is reused
-  __syncthreads();
-  store_swapped<OUT_F32, 2, 8>(a, acc, m0 + 64 * wave, n0, lane, smem + wave * (64 * kAregEpiPitch), a.y_aligned);
-}
-
-template <bool OUT_F32>
-hipError_t launch_areg(const Args& a, hipStream_t stream) {
-  static std::atomic<bool> configured[kMaxDevices];
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return e;
-  if (dev < 0 || dev >= kMaxDevices || !configured[dev].load(std::memory_order_acquire)) {
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&linear_mx_areg_kernel<OUT_F32>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, kAregLds);
-    if (e != hipSuccess) return e;
-    if (dev >= 0 && dev < kMaxDevices) configured[dev].store(true, std::memory_order_release);
-  }
-  linear_mx_areg_kernel<OUT_F32><<<dim3(a.tiles_m * a.tiles_n), dim3(kAregThreads), kAregLds, stream>>>(a);
+  linear_mx_dma_kernel<OUT_F32, DUAL><<<dim3(grid), dim3(kThreads), kDmaStages * kDmaStageBytes, stream>>>(a);
   return hipGetLastError();
 }
 
@@ -832,7 +486,7 @@ hipError_t launch_areg(const Args& a, hipStream_t stream) {
 constexpr int kSmallWaves = 8;
 constexpr int kSmallThreads = 64 * kSmallWaves;
 
-template <bool OUT_F32, int NT, int CH>
+template <bool OUT_F32, int NT, int CH, bool DUAL>
 __global__ __launch_bounds__(kSmallThreads, 1) void linear_mx_small_kernel(Args a) {
   __shared__ float part[kSmallWaves][NT][16][64];
   const int tid = threadIdx.x;
@@ -874,27 +528,29 @@ __global__ __launch_bounds__(kSmallThreads, 1) void linear_mx_small_kernel(Args 
 #pragma unroll
         for (int t = 0; t < NT; ++t)
           wf[j][t][sub] = *reinterpret_cast<const v4i*>(wsrc[t] + (2 * ks + sub) * kFragBytes);
-        bf[j][sub] = *reinterpret_cast<const v4i*>(bsrc + (2 * ks + sub) * kFragBytes);
+        if constexpr (DUAL) bf[j][sub] = *reinterpret_cast<const v4i*>(bsrc + (2 * ks + sub) * kFragBytes);
         rf[j][sub] = *reinterpret_cast<const v4i*>(rsrc + (2 * ks + sub) * kFragBytes);
       }
 #pragma unroll
       for (int t = 0; t < NT; ++t) wsw[j][t] = wssrc[t][ks * a.Np];
-      bsw[j] = bssrc[ks * a.Mp];
+      if constexpr (DUAL) bsw[j] = bssrc[ks * a.Mp];
       rsw[j] = rssrc[ks * a.Mp];
     }
     __builtin_amdgcn_sched_barrier(0);  // keep every load of the chunk ahead of the math
 #pragma unroll
     for (int j = 0; j < CH; ++j) {
       const bool live = c + j < k1;
-      const int bs = (int)(bsw[j] >> (8 * h)), rs = (int)(rsw[j] >> (8 * h));
+      const int bs = DUAL ? (int)(bsw[j] >> (8 * h)) : 0, rs = (int)(rsw[j] >> (8 * h));
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
         const int ws = (int)(wsw[j][t] >> (8 * h));
         const v4i w0 = live ? wf[j][t][0] : v4i{0, 0, 0, 0};
         const v4i w1 = live ? wf[j][t][1] : v4i{0, 0, 0, 0};
-        acc[t] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(widen(w0), widen(bf[j][0]), acc[t], 4, 4, 0, ws, 0, bs);
+        if constexpr (DUAL)
+          acc[t] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(widen(w0), widen(bf[j][0]), acc[t], 4, 4, 0, ws, 0, bs);
         acc[t] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(widen(w0), widen(rf[j][0]), acc[t], 4, 4, 0, ws, 0, rs);
-        acc[t] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(widen(w1), widen(bf[j][1]), acc[t], 4, 4, 2, ws, 2, bs);
+        if constexpr (DUAL)
+          acc[t] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(widen(w1), widen(bf[j][1]), acc[t], 4, 4, 2, ws, 2, bs);
         acc[t] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(widen(w1), widen(rf[j][1]), acc[t], 4, 4, 2, ws, 2, rs);
       }
     }
@@ -921,16 +577,16 @@ __global__ __launch_bounds__(kSmallThreads, 1) void linear_mx_small_kernel(Args 
   }
 }
 
-template <bool OUT_F32>
+template <bool OUT_F32, bool DUAL>
 hipError_t launch_small(const Args& a, hipStream_t stream) {
   constexpr int NT = 2, CH = 4;
   const int64_t tiles = a.Np / 32;
-  linear_mx_small_kernel<OUT_F32, NT, CH>
+  linear_mx_small_kernel<OUT_F32, NT, CH, DUAL>
       <<<dim3((unsigned)((tiles + NT - 1) / NT)), dim3(kSmallThreads), 0, stream>>>(a);
   return hipGetLastError();
 }
 
-template <bool OUT_F32, bool K_ALIGNED>
+template <bool OUT_F32, bool K_ALIGNED, bool DUAL>
 hipError_t launch(const Args& a, hipStream_t stream) {
   // The dynamic-LDS limit is a per-device function attribute; setting it twice is harmless.
   static std::atomic<bool> configured[kMaxDevices];
@@ -938,34 +594,40 @@ hipError_t launch(const Args& a, hipStream_t stream) {
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
   if (dev < 0 || dev >= kMaxDevices || !configured[dev].load(std::memory_order_acquire)) {
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&linear_mx_kernel<OUT_F32, K_ALIGNED>),
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&linear_mx_kernel<OUT_F32, K_ALIGNED, DUAL>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, 2 * kStageBytes);
     if (e != hipSuccess) return e;
     if (dev >= 0 && dev < kMaxDevices) configured[dev].store(true, std::memory_order_release);
   }
   const int grid = a.tiles_m * a.tiles_n;
-  linear_mx_kernel<OUT_F32, K_ALIGNED><<<dim3(grid), dim3(kThreads), 2 * kStageBytes, stream>>>(a);
+  linear_mx_kernel<OUT_F32, K_ALIGNED, DUAL><<<dim3(grid), dim3(kThreads), 2 * kStageBytes, stream>>>(a);
   return hipGetLastError();
+}
+
+template <bool DUAL>
+hipError_t dispatch(const Args& a, bool tiled, bool out_fp32, hipStream_t stream) {
+  if (tiled) {  // all payloads are tiled (checked by the caller)
+    if (a.M <= 32) return out_fp32 ? launch_small<true, DUAL>(a, stream) : launch_small<false, DUAL>(a, stream);
+    return out_fp32 ? launch_dma<true, DUAL>(a, stream) : launch_dma<false, DUAL>(a, stream);
+  }
+  if (a.K % 128 == 0)
+    return out_fp32 ? launch<true, true, DUAL>(a, stream) : launch<false, true, DUAL>(a, stream);
+  return out_fp32 ? launch<true, false, DUAL>(a, stream) : launch<false, false, DUAL>(a, stream);
 }
 
 }  // namespace
 
 size_t linear_mx_workspace(int64_t, int64_t, int64_t) { return 0; }
 
-hipError_t launch_linear_mx(const sharq_fp4& b, const sharq_fp4& r, int64_t M, const sharq_fp4& w,
+hipError_t launch_linear_mx(const sharq_fp4* b, const sharq_fp4& r, int64_t M, const sharq_fp4& w,
                             int64_t N, int64_t K, void* y, int64_t ldy, int out_fp32, void*, size_t,
                             hipStream_t stream) {
   if (M == 0 || N == 0) return hipSuccess;
-  Args a{b.codes, b.scales, r.codes, r.scales, w.codes, w.scales, y, M, N, K, ldy,
+  Args a{b ? b->codes : nullptr, b ? b->scales : nullptr, r.codes, r.scales, w.codes, w.scales, y, M, N, K, ldy,
          (int)((M + BM - 1) / BM), (int)((N + BN - 1) / BN), round_up(M, 32), round_up(N, 32), round_up(K, 128),
          (reinterpret_cast<uintptr_t>(y) & 15u) == 0 && ldy % 8 == 0};
-  if (b.layout == SHARQ_LAYOUT_TILED) {  // all three are tiled (checked by the caller)
-    if (M <= 32) return out_fp32 ? launch_small<true>(a, stream) : launch_small<false>(a, stream);
-    return out_fp32 ? launch_dma<true>(a, stream) : launch_dma<false>(a, stream);
-  }
-  const bool k_aligned = K % 128 == 0;
-  if (out_fp32) return k_aligned ? launch<true, true>(a, stream) : launch<true, false>(a, stream);
-  return k_aligned ? launch<false, true>(a, stream) : launch<false, false>(a, stream);
+  const bool tiled = r.layout == SHARQ_LAYOUT_TILED;
+  return b ? dispatch<true>(a, tiled, out_fp32, stream) : dispatch<false>(a, tiled, out_fp32, stream);
 }
 
 }  // namespace sharq

@@ -91,7 +91,35 @@ __device__ __forceinline__ void decode16(u32x2 codes, uint32_t sbyte, v2h out[8]
   for (int i = 0; i < 8; ++i) out[i] = p[i] * s2;  // <= 6 significant bits: exact
 }
 
-template <bool OUT_F32>
+// Epilogue: Y = S_w (S_b acc_b + S_r acc_r) in fp32, each operation rounded to nearest
+// (with one activation operand: Y = S_w (S_r acc_r), the same value as with a zero
+// backbone); lane holds column r32 of each 32x32 tile and rows 8*(j/4) + 4*h + j%4.
+template <bool OUT_F32, bool DUAL>
+__device__ __forceinline__ void store_tile(const Args& a, const v16f (&accb)[2][2], const v16f (&accr)[2][2],
+                                           int64_t m0, int64_t n0, int wm, int wn, int r32, int h) {
+  const float sb = DUAL ? *a.bt : 0.f, sr = *a.rt, sw = *a.wt;
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      const int64_t col = n0 + wn * 64 + nt * 32 + r32;
+      if (col >= a.N) continue;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int64_t row = m0 + wm * 64 + mt * 32 + 8 * (j >> 2) + 4 * h + (j & 3);
+        if (row < a.M) {
+          const float pr = __fmul_rn(sr, accr[mt][nt][j]);
+          const float v = __fmul_rn(sw, DUAL ? __fadd_rn(__fmul_rn(sb, accb[mt][nt][j]), pr) : pr);
+          if constexpr (OUT_F32)
+            reinterpret_cast<float*>(a.y)[row * a.ldy + col] = v;
+          else
+            reinterpret_cast<uint16_t*>(a.y)[row * a.ldy + col] = f32_to_bf16_rne(v);
+        }
+      }
+    }
+}
+
+template <bool OUT_F32, bool DUAL>
 __global__ __launch_bounds__(kThreads, 1) void linear_nv_kernel(Args a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int tid = threadIdx.x;
@@ -114,7 +142,7 @@ __global__ __launch_bounds__(kThreads, 1) void linear_nv_kernel(Args a) {
 
   auto gload = [&](int ks) {
 #pragma unroll
-    for (int which = 0; which < 3; ++which) {
+    for (int which = DUAL ? 0 : 1; which < 3; ++which) {  // 0: A_b (absent for one operand), 1: A_r, 2: W
       const uint8_t* c = which == 0 ? a.bc : which == 1 ? a.rc : a.wc;
       const uint8_t* s = which == 0 ? a.bs : which == 1 ? a.rs : a.ws;
       const int64_t grow = (which == 2 ? n0 : m0) + srow;
@@ -135,7 +163,7 @@ __global__ __launch_bounds__(kThreads, 1) void linear_nv_kernel(Args a) {
   auto sstore = [&](int buf) {
     uint8_t* base = smem + buf * kStageBytes;
 #pragma unroll
-    for (int which = 0; which < 3; ++which)
+    for (int which = DUAL ? 0 : 1; which < 3; ++which)
 #pragma unroll
       for (int bi = 0; bi < 2; ++bi) {
         v2h d[8];
@@ -173,7 +201,7 @@ __global__ __launch_bounds__(kThreads, 1) void linear_nv_kernel(Args a) {
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt) {
         const int row = wm * 64 + mt * 32 + r32;
-        ab[mt] = *reinterpret_cast<const v8h*>(base + row * kRowPitch + col);
+        if constexpr (DUAL) ab[mt] = *reinterpret_cast<const v8h*>(base + row * kRowPitch + col);
         ar[mt] = *reinterpret_cast<const v8h*>(base + kTileBytes + row * kRowPitch + col);
       }
 #pragma unroll
@@ -185,7 +213,8 @@ __global__ __launch_bounds__(kThreads, 1) void linear_nv_kernel(Args a) {
       for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) {
-          accb[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ab[mt], wf[nt], accb[mt][nt], 0, 0, 0);
+          if constexpr (DUAL)
+            accb[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ab[mt], wf[nt], accb[mt][nt], 0, 0, 0);
           accr[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ar[mt], wf[nt], accr[mt][nt], 0, 0, 0);
         }
     }
@@ -193,25 +222,7 @@ __global__ __launch_bounds__(kThreads, 1) void linear_nv_kernel(Args a) {
     __syncthreads();
   }
 
-  const float sb = *a.bt, sr = *a.rt, sw = *a.wt;
-#pragma unroll
-  for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      const int64_t col = n0 + wn * 64 + nt * 32 + r32;
-      if (col >= a.N) continue;
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int64_t row = m0 + wm * 64 + mt * 32 + 8 * (j >> 2) + 4 * h + (j & 3);
-        if (row < a.M) {
-          const float v = __fmul_rn(sw, __fadd_rn(__fmul_rn(sb, accb[mt][nt][j]), __fmul_rn(sr, accr[mt][nt][j])));
-          if constexpr (OUT_F32)
-            reinterpret_cast<float*>(a.y)[row * a.ldy + col] = v;
-          else
-            reinterpret_cast<uint16_t*>(a.y)[row * a.ldy + col] = f32_to_bf16_rne(v);
-        }
-      }
-    }
+  store_tile<OUT_F32, DUAL>(a, accb, accr, m0, n0, wm, wn, r32, h);
 }
 
 // ---------------------------------------------------------------------------------
@@ -262,7 +273,7 @@ __device__ __forceinline__ v8h decode8(uint32_t codes, _Float16 sc) {
   return v8h{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
 }
 
-template <bool OUT_F32>
+template <bool OUT_F32, bool DUAL>
 __global__ __launch_bounds__(kThreads, 2) void linear_nv_stream_kernel(Args a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   uint8_t* raw = smem;  // kRawStages x [codes: 3 tiles x 128 rows x 32 B][scales: 3 x 128 x 4 B]
@@ -278,13 +289,16 @@ __global__ __launch_bounds__(kThreads, 2) void linear_nv_stream_kernel(Args a) {
   const int64_t kb = a.K / 2, nbk = a.K / 16;
   const int nk = (int)(a.K / BK);
 
-  // this wave's loads: 3 code pieces and 2 scale pieces per stage (rows past the
-  // operand's end re-read its last row; their results are never stored)
-  const uint8_t* csrc[3];
+  // this wave's loads per stage: 3 code pieces and 2 scale pieces (2 and 1 without
+  // A_b; rows past the operand's end re-read its last row, never stored)
+  constexpr int kT0 = DUAL ? 0 : 1;            // first tile present
+  constexpr int kCodeLoads = DUAL ? 3 : 2, kScaleLoads = DUAL ? 2 : 1;
+  constexpr int kLoads = kCodeLoads + kScaleLoads;
+  const uint8_t* csrc[3];  // (fixed extents: template-dependent ones drop the host launch stub)
   int cdst[3];
 #pragma unroll
-  for (int j = 0; j < 3; ++j) {
-    const int piece = 3 * wave + j, t = piece >> 2, part = piece & 3;
+  for (int j = 0; j < kCodeLoads; ++j) {
+    const int piece = kCodeLoads * wave + j, t = kT0 + (piece >> 2), part = piece & 3;
     const uint8_t* base = t == 0 ? a.bc : t == 1 ? a.rc : a.wc;
     const int64_t rows = t == 2 ? a.N : a.M;
     int64_t row = (t == 2 ? n0 : m0) + 32 * part + (lane >> 1);
@@ -295,8 +309,9 @@ __global__ __launch_bounds__(kThreads, 2) void linear_nv_stream_kernel(Args a) {
   const uint8_t* ssrc[2];
   int sdst[2];
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int piece = 2 * (wave < 3 ? wave : 2) + j, t = piece >> 1, part = piece & 1;
+  for (int j = 0; j < kScaleLoads; ++j) {
+    // DUAL: 6 pieces, wave 3 repeats wave 2's; else 4 pieces, one per wave
+    const int piece = DUAL ? 2 * (wave < 3 ? wave : 2) + j : wave, t = kT0 + (piece >> 1), part = piece & 1;
     const uint8_t* base = t == 0 ? a.bs : t == 1 ? a.rs : a.ws;
     const int64_t rows = t == 2 ? a.N : a.M;
     int64_t row = (t == 2 ? n0 : m0) + 64 * part + lane;
@@ -308,10 +323,10 @@ __global__ __launch_bounds__(kThreads, 2) void linear_nv_stream_kernel(Args a) {
     uint8_t* st = raw + (ks % kRawStages) * kRawStageBytes;
     const int64_t kc = ks < nk ? ks : nk - 1;  // past the end: re-load into a slot nobody reads
 #pragma unroll
-    for (int j = 0; j < 3; ++j)
+    for (int j = 0; j < kCodeLoads; ++j)
       __builtin_amdgcn_global_load_lds(csrc[j] + kc * 32, (lds_void_t*)(st + cdst[j]), 16, 0, 0);
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < kScaleLoads; ++j)
       __builtin_amdgcn_global_load_lds(ssrc[j] + kc * 4, (lds_void_t*)(st + sdst[j]), 4, 0, 0);
   };
 
@@ -333,6 +348,7 @@ __global__ __launch_bounds__(kThreads, 2) void linear_nv_stream_kernel(Args a) {
     const uint8_t* st = raw + (ks % kRawStages) * kRawStageBytes;
 #pragma unroll
     for (int q = 0; q < 6; ++q) {
+      if (!DUAL && q < 4 && (q & 1) == 0) continue;  // A_b absent
       r.codes[q] = *reinterpret_cast<const u32x4*>(st + roff[q] * 32 + h * 16);
       r.scales[q] = *reinterpret_cast<const uint32_t*>(st + kRawCodeBytes + roff[q] * 4) >> (16 * h);
     }
@@ -349,17 +365,20 @@ __global__ __launch_bounds__(kThreads, 2) void linear_nv_stream_kernel(Args a) {
   auto compute = [&](const Raw& r) {
     v2h sc[6];
 #pragma unroll
-    for (int q = 0; q < 6; ++q) sc[q] = scale_pair(r.scales[q]);
+    for (int q = 0; q < 6; ++q)
+      if (DUAL || q >= 4 || (q & 1)) sc[q] = scale_pair(r.scales[q]);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       v8h f[6];
 #pragma unroll
-      for (int q = 0; q < 6; ++q) f[q] = decode8(r.codes[q][i], sc[q][i >> 1]);
+      for (int q = 0; q < 6; ++q)
+        if (DUAL || q >= 4 || (q & 1)) f[q] = decode8(r.codes[q][i], sc[q][i >> 1]);
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) {
-          accb[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f[2 * mt], f[4 + nt], accb[mt][nt], 0, 0, 0);
+          if constexpr (DUAL)
+            accb[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f[2 * mt], f[4 + nt], accb[mt][nt], 0, 0, 0);
           accr[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f[2 * mt + 1], f[4 + nt], accr[mt][nt], 0, 0, 0);
         }
     }
@@ -375,7 +394,7 @@ __global__ __launch_bounds__(kThreads, 2) void linear_nv_stream_kernel(Args a) {
   dma(0);
   dma(1);
   dma(2);
-  SHARQ_NV_WAIT_VMCNT(5);  // this wave's loads of stages 0 and 1 landed
+  SHARQ_NV_WAIT_VMCNT(kLoads);  // this wave's loads of stages 0 and 1 landed
   barrier();
   Raw cur, nxt;
   read_raw(cur, 0);
@@ -386,63 +405,47 @@ __global__ __launch_bounds__(kThreads, 2) void linear_nv_stream_kernel(Args a) {
     __builtin_amdgcn_sched_barrier(0);  // issue the reads first: their latency hides under compute
     compute(cur);
     __builtin_amdgcn_sched_barrier(0);
-    SHARQ_NV_WAIT_VMCNT(5);  // this wave's loads of stage ks+2 landed
+    SHARQ_NV_WAIT_VMCNT(kLoads);  // this wave's loads of stage ks+2 landed
     barrier();               // ... everyone's; everyone has stage ks+1 in registers
     dma(ks + 4);             // into the slot of stage ks+1
     cur = nxt;
   }
   SHARQ_NV_WAIT_VMCNT(0);
 
-  const float sb = *a.bt, sr = *a.rt, sw = *a.wt;
-#pragma unroll
-  for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      const int64_t col = n0 + wn * 64 + nt * 32 + r32;
-      if (col >= a.N) continue;
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int64_t row = m0 + wm * 64 + mt * 32 + 8 * (j >> 2) + 4 * h + (j & 3);
-        if (row < a.M) {
-          const float v = __fmul_rn(sw, __fadd_rn(__fmul_rn(sb, accb[mt][nt][j]), __fmul_rn(sr, accr[mt][nt][j])));
-          if constexpr (OUT_F32)
-            reinterpret_cast<float*>(a.y)[row * a.ldy + col] = v;
-          else
-            reinterpret_cast<uint16_t*>(a.y)[row * a.ldy + col] = f32_to_bf16_rne(v);
-        }
-      }
-    }
+  store_tile<OUT_F32, DUAL>(a, accb, accr, m0, n0, wm, wn, r32, h);
 }
 
-template <bool OUT_F32>
-hipError_t launch_stream(const Args& a, hipStream_t stream) {
+// The dynamic-LDS limit is a per-device function attribute, set once per device and
+// kernel instantiation (setting it twice is harmless).
+template <const void* (*KERNEL)()>
+hipError_t configure(int lds_bytes) {
   static std::atomic<bool> configured[kMaxDevices];
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
   if (dev < 0 || dev >= kMaxDevices || !configured[dev].load(std::memory_order_acquire)) {
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&linear_nv_stream_kernel<OUT_F32>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, kStreamLds);
+    e = hipFuncSetAttribute(KERNEL(), hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
     if (e != hipSuccess) return e;
     if (dev >= 0 && dev < kMaxDevices) configured[dev].store(true, std::memory_order_release);
   }
-  linear_nv_stream_kernel<OUT_F32><<<dim3(a.tiles_m * a.tiles_n), dim3(kThreads), kStreamLds, stream>>>(a);
-  return hipGetLastError();
+  return hipSuccess;
 }
+template <bool OUT_F32, bool DUAL>
+const void* stream_kernel() { return reinterpret_cast<const void*>(&linear_nv_stream_kernel<OUT_F32, DUAL>); }
+template <bool OUT_F32, bool DUAL>
+const void* generic_kernel() { return reinterpret_cast<const void*>(&linear_nv_kernel<OUT_F32, DUAL>); }
 
-template <bool OUT_F32>
+template <bool OUT_F32, bool DUAL>
 hipError_t launch(const Args& a, hipStream_t stream) {
-  static std::atomic<bool> configured[kMaxDevices];
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return e;
-  if (dev < 0 || dev >= kMaxDevices || !configured[dev].load(std::memory_order_acquire)) {
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&linear_nv_kernel<OUT_F32>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, 2 * kStageBytes);
-    if (e != hipSuccess) return e;
-    if (dev >= 0 && dev < kMaxDevices) configured[dev].store(true, std::memory_order_release);
+  const dim3 grid(a.tiles_m * a.tiles_n);
+  hipError_t e;
+  if (a.K % BK == 0) {
+    if ((e = configure<stream_kernel<OUT_F32, DUAL>>(kStreamLds)) != hipSuccess) return e;
+    linear_nv_stream_kernel<OUT_F32, DUAL><<<grid, dim3(kThreads), kStreamLds, stream>>>(a);
+  } else {
+    if ((e = configure<generic_kernel<OUT_F32, DUAL>>(2 * kStageBytes)) != hipSuccess) return e;
+    linear_nv_kernel<OUT_F32, DUAL><<<grid, dim3(kThreads), 2 * kStageBytes, stream>>>(a);
   }
-  linear_nv_kernel<OUT_F32><<<dim3(a.tiles_m * a.tiles_n), dim3(kThreads), 2 * kStageBytes, stream>>>(a);
   return hipGetLastError();
 }
 
@@ -450,14 +453,15 @@ hipError_t launch(const Args& a, hipStream_t stream) {
 
 size_t linear_nv_workspace(int64_t, int64_t, int64_t) { return 0; }
 
-hipError_t launch_linear_nv(const sharq_fp4& b, const sharq_fp4& r, int64_t M, const sharq_fp4& w,
+hipError_t launch_linear_nv(const sharq_fp4* b, const sharq_fp4& r, int64_t M, const sharq_fp4& w,
                             int64_t N, int64_t K, void* y, int64_t ldy, int out_fp32, void*, size_t,
                             hipStream_t stream) {
   if (M == 0 || N == 0) return hipSuccess;
-  Args a{b.codes, b.scales, b.tensor_scale, r.codes, r.scales, r.tensor_scale, w.codes, w.scales,
+  Args a{b ? b->codes : nullptr, b ? b->scales : nullptr, b ? b->tensor_scale : nullptr,
+         r.codes, r.scales, r.tensor_scale, w.codes, w.scales,
          w.tensor_scale, y, M, N, K, ldy, (int)((M + BM - 1) / BM), (int)((N + BN - 1) / BN)};
-  if (K % BK == 0) return out_fp32 ? launch_stream<true>(a, stream) : launch_stream<false>(a, stream);
-  return out_fp32 ? launch<true>(a, stream) : launch<false>(a, stream);
+  if (b) return out_fp32 ? launch<true, true>(a, stream) : launch<false, true>(a, stream);
+  return out_fp32 ? launch<true, false>(a, stream) : launch<false, false>(a, stream);
 }
 
 }  // namespace sharq

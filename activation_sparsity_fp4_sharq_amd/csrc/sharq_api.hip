@@ -80,6 +80,39 @@ size_t rms_factor_offset(int fmt) { return fmt == SHARQ_NVFP4 ? round_up(kNvPrep
 
 }  // namespace
 
+// Shared by sharq_linear (backbone != NULL) and sharq_linear_dense (backbone == NULL:
+// one activation payload, passed as `residual`).
+static sharq_status linear_common(const sharq_fp4* backbone, const sharq_fp4* residual, int64_t M,
+                           const sharq_fp4* weight, int64_t N, int64_t K, int fmt, void* y, int64_t ldy,
+                           int out_dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  sharq_status s = check_format(fmt);
+  if (s != SHARQ_OK) return s;
+  if (out_dtype != SHARQ_OUT_BF16 && out_dtype != SHARQ_OUT_FP32) return SHARQ_E_FORMAT;
+  if (M < 0 || N <= 0 || K <= 0 || K % block_of(fmt) || ldy < N) return SHARQ_E_SHAPE;
+  if (M > (int64_t)1 << 31 || N > (int64_t)1 << 30 || K > (int64_t)1 << 30) return SHARQ_E_SHAPE;
+  if ((s = check_payload(weight, fmt, N)) != SHARQ_OK) return s;
+  if (backbone && (s = check_payload(backbone, fmt, M)) != SHARQ_OK) return s;
+  if ((s = check_payload(residual, fmt, M)) != SHARQ_OK) return s;
+  if (residual->layout != weight->layout || (backbone && backbone->layout != residual->layout))
+    return SHARQ_E_FORMAT;
+  if (M > 0) {
+    if (!y) return SHARQ_E_NULL;
+    if (reinterpret_cast<uintptr_t>(y) & (out_dtype == SHARQ_OUT_FP32 ? 3u : 1u)) return SHARQ_E_ALIGN;
+  }
+  const size_t need = sharq_linear_workspace_bytes(M, N, K, fmt);
+  if (need && (!workspace || workspace_bytes < need)) return SHARQ_E_WORKSPACE;
+  if (need && !aligned16(workspace)) return SHARQ_E_ALIGN;
+  if ((s = check_device()) != SHARQ_OK) return s;
+  if (M == 0) return SHARQ_OK;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const int f32 = out_dtype == SHARQ_OUT_FP32;
+  if (fmt == SHARQ_MXFP4)
+    return launched(launch_linear_mx(backbone, *residual, M, *weight, N, K, y, ldy, f32, workspace,
+                                     workspace_bytes, st));
+  return launched(launch_linear_nv(backbone, *residual, M, *weight, N, K, y, ldy, f32, workspace,
+                                   workspace_bytes, st));
+}
+
 extern "C" {
 
 int sharq_abi_version(void) { return SHARQ_ABI_VERSION; }
@@ -212,31 +245,16 @@ sharq_status sharq_prep_rmsnorm(const void* x, int64_t M, int64_t K, int64_t ldx
 sharq_status sharq_linear(const sharq_fp4* backbone, const sharq_fp4* residual, int64_t M,
                           const sharq_fp4* weight, int64_t N, int64_t K, int fmt, void* y, int64_t ldy,
                           int out_dtype, void* workspace, size_t workspace_bytes, void* stream) {
-  sharq_status s = check_format(fmt);
-  if (s != SHARQ_OK) return s;
-  if (out_dtype != SHARQ_OUT_BF16 && out_dtype != SHARQ_OUT_FP32) return SHARQ_E_FORMAT;
-  if (M < 0 || N <= 0 || K <= 0 || K % block_of(fmt) || ldy < N) return SHARQ_E_SHAPE;
-  if (M > (int64_t)1 << 31 || N > (int64_t)1 << 30 || K > (int64_t)1 << 30) return SHARQ_E_SHAPE;
-  if ((s = check_payload(weight, fmt, N)) != SHARQ_OK) return s;
-  if ((s = check_payload(backbone, fmt, M)) != SHARQ_OK) return s;
-  if ((s = check_payload(residual, fmt, M)) != SHARQ_OK) return s;
-  if (backbone->layout != residual->layout || backbone->layout != weight->layout) return SHARQ_E_FORMAT;
-  if (M > 0) {
-    if (!y) return SHARQ_E_NULL;
-    if (reinterpret_cast<uintptr_t>(y) & (out_dtype == SHARQ_OUT_FP32 ? 3u : 1u)) return SHARQ_E_ALIGN;
-  }
-  const size_t need = sharq_linear_workspace_bytes(M, N, K, fmt);
-  if (need && (!workspace || workspace_bytes < need)) return SHARQ_E_WORKSPACE;
-  if (need && !aligned16(workspace)) return SHARQ_E_ALIGN;
-  if ((s = check_device()) != SHARQ_OK) return s;
-  if (M == 0) return SHARQ_OK;
-  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  const int f32 = out_dtype == SHARQ_OUT_FP32;
-  if (fmt == SHARQ_MXFP4)
-    return launched(launch_linear_mx(*backbone, *residual, M, *weight, N, K, y, ldy, f32, workspace,
-                                     workspace_bytes, st));
-  return launched(launch_linear_nv(*backbone, *residual, M, *weight, N, K, y, ldy, f32, workspace,
-                                   workspace_bytes, st));
+  if (!backbone) return SHARQ_E_NULL;  // the one-operand form is sharq_linear_dense
+  return linear_common(backbone, residual, M, weight, N, K, fmt, y, ldy, out_dtype, workspace,
+                       workspace_bytes, stream);
+}
+
+sharq_status sharq_linear_dense(const sharq_fp4* a, int64_t M, const sharq_fp4* weight, int64_t N, int64_t K,
+                                int fmt, void* y, int64_t ldy, int out_dtype, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  return linear_common(nullptr, a, M, weight, N, K, fmt, y, ldy, out_dtype, workspace, workspace_bytes,
+                       stream);
 }
 
 sharq_status sharq_forward(const void* x, int64_t M, int64_t K, int64_t ldx, int sp_n, int sp_m, int fmt,

@@ -34,12 +34,13 @@ hipError_t launch_quant_nv(const uint16_t* x, int64_t rows, int64_t K, int64_t l
                            uint8_t* codes, uint8_t* scales, float* tscale, uint32_t* work,
                            hipStream_t stream);
 
-hipError_t launch_linear_mx(const sharq_fp4& b, const sharq_fp4& r, int64_t M, const sharq_fp4& w,
+// Linear launchers: b == NULL runs one activation operand (Y = R W^T, the backbone path off).
+hipError_t launch_linear_mx(const sharq_fp4* b, const sharq_fp4& r, int64_t M, const sharq_fp4& w,
                             int64_t N, int64_t K, void* y, int64_t ldy, int out_fp32,
                             void* work, size_t work_bytes, hipStream_t stream);
 size_t linear_mx_workspace(int64_t M, int64_t N, int64_t K);
 
-hipError_t launch_linear_nv(const sharq_fp4& b, const sharq_fp4& r, int64_t M, const sharq_fp4& w,
+hipError_t launch_linear_nv(const sharq_fp4* b, const sharq_fp4& r, int64_t M, const sharq_fp4& w,
                             int64_t N, int64_t K, void* y, int64_t ldy, int out_fp32,
                             void* work, size_t work_bytes, hipStream_t stream);
 size_t linear_nv_workspace(int64_t M, int64_t N, int64_t K);

@@ -22,7 +22,8 @@ LIB_PATH = os.path.join(_HERE, "libsharq.so")
 
 SYMBOLS = ["sharq_abi_version", "sharq_status_str", "sharq_payload_bytes", "sharq_convert_layout",
            "sharq_prep_workspace_bytes", "sharq_linear_workspace_bytes", "sharq_quantize", "sharq_prep",
-           "sharq_prep_rmsnorm_workspace_bytes", "sharq_prep_rmsnorm", "sharq_linear", "sharq_forward"]
+           "sharq_prep_rmsnorm_workspace_bytes", "sharq_prep_rmsnorm", "sharq_linear", "sharq_linear_dense",
+           "sharq_forward"]
 
 
 class SharqFp4(ctypes.Structure):
@@ -75,6 +76,8 @@ def lib():
         L.sharq_linear.restype = ctypes.c_int
         L.sharq_linear.argtypes = [P, P, i64, P, i64, i64, ctypes.c_int, vp, i64, ctypes.c_int, vp, sz,
                                    vp]
+        L.sharq_linear_dense.restype = ctypes.c_int
+        L.sharq_linear_dense.argtypes = [P, i64, P, i64, i64, ctypes.c_int, vp, i64, ctypes.c_int, vp, sz, vp]
         L.sharq_forward.restype = ctypes.c_int
         L.sharq_forward.argtypes = [vp, i64, i64, i64, ctypes.c_int, ctypes.c_int, ctypes.c_int, P, P, P,
                                     i64, vp, i64, ctypes.c_int, vp, sz, vp]
@@ -167,12 +170,15 @@ def _as_bf16_2d(x):
     return x
 
 
-def quantize(x, fmt=MXFP4, layout=None, stream=None):
-    """Plain FP4 quantization of a bf16 matrix (a weight payload)."""
+def quantize(x, fmt=MXFP4, layout=None, stream=None, out=None, ws=None):
+    """Plain FP4 quantization of a bf16 matrix (a weight payload, or the activation of
+    a plain FP4 layer)."""
     x = _as_bf16_2d(x)
     rows, K = x.shape
-    out = Payload.empty(rows, K, fmt, x.device, layout)
-    ws = workspace(lib().sharq_prep_workspace_bytes(rows, K, fmt), x.device)
+    if out is None:
+        out = Payload.empty(rows, K, fmt, x.device, layout)
+    if ws is None:
+        ws = workspace(lib().sharq_prep_workspace_bytes(rows, K, fmt), x.device)
     st = out.struct()
     _check("sharq_quantize", lib().sharq_quantize(_ptr(x), rows, K, x.stride(0), fmt, ctypes.byref(st),
                                                   _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream)))
@@ -229,6 +235,22 @@ def linear(backbone, residual, weight, out_dtype=OUT_BF16, y=None, ws=None, stre
     _check("sharq_linear", lib().sharq_linear(ctypes.byref(sb), ctypes.byref(sr), M, ctypes.byref(sw), N, K,
                                               fmt, _ptr(y), y.stride(0), out_dtype, _ptr(ws),
                                               0 if ws is None else ws.numel(), _stream(stream)))
+    return y
+
+
+def linear_dense(a, weight, out_dtype=OUT_BF16, y=None, ws=None, stream=None):
+    """Plain FP4 linear Y = Ahat W^T (no SharQ) on the device; returns Y [M, N]."""
+    fmt = weight.fmt
+    M, K, N = a.rows, a.K, weight.rows
+    dev = weight.codes.device
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.float32 if out_dtype == OUT_FP32 else torch.bfloat16, device=dev)
+    if ws is None:
+        ws = workspace(lib().sharq_linear_workspace_bytes(M, N, K, fmt), dev)
+    sa, sw = a.struct(), weight.struct()
+    _check("sharq_linear_dense", lib().sharq_linear_dense(ctypes.byref(sa), M, ctypes.byref(sw), N, K, fmt, _ptr(y),
+                                                          y.stride(0), out_dtype, _ptr(ws),
+                                                          0 if ws is None else ws.numel(), _stream(stream)))
     return y
 
 

@@ -40,6 +40,9 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time for the CPU baseline")
     p.add_argument("--rmsnorm", action="store_true",
                    help="time the preparation with the RMS normalization folded in (sharq_prep_rmsnorm)")
+    p.add_argument("--compare", action="store_true",
+                   help="also time comparison points at the same shape: torch bf16 and fp8 GEMMs, the "
+                        "library MXFP4 GEMM, and the plain FP4 layer (quantize + one-operand GEMM)")
     p.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                    help="only run a plain device copy of MIB MiB (5 times): the reference dispatch that "
                         "scales hardware byte counters to bytes")
@@ -136,6 +139,76 @@ def back_to_back_seconds(launch, reps, stream):
         cycles *= 4
         if cycles > 1 << 34:
             raise RuntimeError("could not hold the stream long enough to queue the launches")
+
+
+def comparison_points(w, sets, weight_sets, ws, stream, reps, t_prep, t_lin):
+    """Kernel-level comparison at the workload's shape, every point timed like the SharQ
+    kernels (back-to-back launches rotating over the same independent input sets):
+    torch's bf16 GEMM, fp8 GEMM (per-tensor scales) and MXFP4 GEMM (E8M0 block scales;
+    the library's, through torch._scaled_mm), and the plain FP4 layer of this library
+    (sharq_quantize of the activation + sharq_linear_dense, i.e. the SharQ kernels with
+    the backbone path off).  Values are not checked here: the plain FP4 kernels are
+    covered by the parity tests, the torch GEMMs are context."""
+    import torch
+
+    from activation_sparsity_fp4_sharq_amd import sharq
+
+    M, N, K = w.M, w.N, w.K
+    n = len(sets)
+    out = {"shape": [M, N, K], "sharq_gemm_us": round(t_lin * 1e6, 2),
+           "sharq_layer_us": round((t_prep + t_lin) * 1e6, 2)}
+
+    def timed(name, launch):
+        try:
+            out[name] = round(back_to_back_seconds(launch, reps, stream) * 1e6, 2)
+        except Exception as e:  # a torch path this ROCm build lacks: reported, not fatal
+            out[name] = None
+            out[name + "_error"] = repr(e)[:200]
+
+    wb16 = [ws_[0] for ws_ in weight_sets]
+    ys = [torch.empty((M, N), dtype=torch.bfloat16, device=sets[0][0].device) for _ in range(n)]
+    timed("bf16_gemm_us", lambda i: torch.matmul(sets[i % n][0], wb16[i % n].t(), out=ys[i % n]))
+    try:
+        x8 = [s_[0].to(torch.float8_e4m3fn) for s_ in sets]
+        w8 = [t.to(torch.float8_e4m3fn) for t in wb16]
+        one = torch.ones((), device=x8[0].device)
+        timed("fp8_gemm_us", lambda i: torch._scaled_mm(x8[i % n], w8[i % n].t(), scale_a=one, scale_b=one,
+                                                          out_dtype=torch.bfloat16))
+        del x8, w8
+    except Exception as e:
+        out["fp8_gemm_us"], out["fp8_gemm_us_error"] = None, repr(e)[:200]
+    try:
+        dev = sets[0][0].device
+        g = torch.Generator(device=dev)
+        g.manual_seed(3)
+        a4 = [torch.randint(0, 256, (M, K // 2), dtype=torch.uint8, device=dev, generator=g)
+              .view(torch.float4_e2m1fn_x2) for _ in range(n)]
+        b4 = [torch.randint(0, 256, (N, K // 2), dtype=torch.uint8, device=dev, generator=g)
+              .view(torch.float4_e2m1fn_x2) for _ in range(n)]
+        sa = torch.full((M, K // 32), 127, dtype=torch.uint8, device=dev).view(torch.float8_e8m0fnu)
+        sb = torch.full((N, K // 32), 127, dtype=torch.uint8, device=dev).view(torch.float8_e8m0fnu)
+        timed("mxfp4_library_gemm_us", lambda i: torch._scaled_mm(a4[i % n], b4[i % n].t(), scale_a=sa,
+                                                                    scale_b=sb, out_dtype=torch.bfloat16))
+        del a4, b4
+    except Exception as e:
+        out["mxfp4_library_gemm_us"], out["mxfp4_library_gemm_us_error"] = None, repr(e)[:200]
+    acts = [sharq.Payload.empty(M, K, w.fmt, s_[0].device, s_[1].layout) for s_ in sets]
+    quant = lambda i: sharq.quantize(sets[i % n][0], w.fmt, out=acts[i % n], ws=ws, stream=stream)
+    for i in range(n):
+        quant(i)
+    gemm = lambda i: sharq.linear_dense(acts[i % n], sets[i % n][1], sharq.OUT_BF16, y=ys[i % n], ws=ws,
+                                         stream=stream)
+    timed("fp4_quantize_us", quant)
+    timed("fp4_dense_gemm_us", gemm)
+    if out.get("fp4_quantize_us") and out.get("fp4_dense_gemm_us"):
+        out["fp4_layer_us"] = round(out["fp4_quantize_us"] + out["fp4_dense_gemm_us"], 2)
+    lay = out["sharq_layer_us"]
+    for key, name in (("bf16_gemm_us", "sharq_layer_speedup_vs_bf16_gemm"),
+                      ("fp8_gemm_us", "sharq_layer_speedup_vs_fp8_gemm"),
+                      ("fp4_layer_us", "sharq_layer_cost_vs_plain_fp4_layer")):
+        if out.get(key):
+            out[name] = round(out[key] / lay, 3) if "speedup" in name else round(lay / out[key], 3)
+    return out
 
 
 def main():
@@ -272,6 +345,10 @@ def main():
                    "TFLOPS_issued": round(issued / t_lin / 1e12, 2),
                    "pct_peak_issued": round(100.0 * issued / t_lin / 1e12 / gemm_peak, 2)},
     }
+    if args.compare:
+        wsets = [(wt,)] + [(wt.clone(),) for _ in range(nsets - 1)]
+        out["comparison"] = comparison_points(w, [(s_[0], s_[1]) for s_ in sets], wsets, ws, stream,
+                                              args.steps, t_prep, t_lin)
     if not args.no_cpu_baseline:
         cb = cpu_baseline(w, xb, wb, args.cpu_seconds)
         out["cpu_baseline"] = {k: (round(v, 6) if isinstance(v, float) else v) for k, v in cb.items()}

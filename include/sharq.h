@@ -61,7 +61,7 @@
 extern "C" {
 #endif
 
-#define SHARQ_ABI_VERSION 3
+#define SHARQ_ABI_VERSION 4
 
 typedef enum sharq_status {
   SHARQ_OK = 0,
@@ -199,6 +199,19 @@ sharq_status sharq_linear(const sharq_fp4* backbone, const sharq_fp4* residual, 
                           const sharq_fp4* weight, int64_t N, int64_t K, int fmt, void* y,
                           int64_t ldy, int out_dtype, void* workspace, size_t workspace_bytes,
                           void* stream);
+
+/* Plain FP4 linear layer without SharQ: Y = Ahat W^T over one activation payload
+ * (e.g. from sharq_quantize) -- the kernels of sharq_linear with the backbone path
+ * off.  It is the plain FP4 baseline the method is measured against (SharQ,
+ * arXiv 2606.26587: Figure 4 normalizes prefill latency to plain NVFP4; the
+ * summary's speed claims are against FP16 and FP8).
+ *   a                   payload [M, K], same format and layout as weight
+ *   weight, y, ldy, out_dtype, workspace, stream: as for sharq_linear
+ *   NVFP4: Y = S_w (S_a acc) in fp32, each product rounded to nearest.
+ * Errors as for sharq_linear (SHARQ_E_NULL for a NULL payload or y). */
+sharq_status sharq_linear_dense(const sharq_fp4* a, int64_t M, const sharq_fp4* weight, int64_t N,
+                                int64_t K, int fmt, void* y, int64_t ldy, int out_dtype, void* workspace,
+                                size_t workspace_bytes, void* stream);
 
 /* One SharQ linear layer end to end: sharq_prep into the caller's backbone and
  * residual payloads, then sharq_linear, on one stream.  Arguments as above; the

@@ -172,6 +172,13 @@ def linear(backbone, residual, weight, fmt=MXFP4, rows=None):
     return y
 
 
+def linear_dense(a, weight, fmt=MXFP4, rows=None):
+    """Plain FP4 linear Y = Ahat W^T in fp64 (no SharQ decomposition): the GEMM pair
+    above with an all-zero backbone payload, whose every product is an exact zero."""
+    zero = Payload(np.zeros_like(a.codes), np.zeros_like(a.scales), 1.0)
+    return linear(zero, a, weight, fmt, rows)
+
+
 def e2m1_encode(t):
     t = np.ascontiguousarray(t, dtype=np.float32).ravel()
     out = np.zeros(t.size, np.uint8)

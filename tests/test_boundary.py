@@ -33,7 +33,7 @@ def test_header_symbols_exported():
 
 def test_version_and_status_strings():
     L = sharq.lib()
-    assert L.sharq_abi_version() == 3
+    assert L.sharq_abi_version() == 4
     for s in range(9):
         assert L.sharq_status_str(s)
     assert L.sharq_status_str(99) == b"unknown status"
@@ -114,6 +114,38 @@ def test_linear_rejects(kwargs, status):
     assert linear(**kwargs) == status
 
 
+def linear_dense(M=4, N=8, K=64, fmt=0, y=A, ldy=8, out=0, a=None, w=None, ws=None, wsb=0):
+    a = a if a is not None else fp4()
+    w = w if w is not None else fp4()
+    return sharq.lib().sharq_linear_dense(ctypes.byref(a), M, ctypes.byref(w), N, K, fmt, y, ldy, out, ws, wsb,
+                                          None)
+
+
+@pytest.mark.parametrize("kwargs,status", [
+    (dict(y=None), E_NULL),
+    (dict(N=0), E_SHAPE),
+    (dict(K=40), E_SHAPE),
+    (dict(K=40, fmt=1), E_SHAPE),             # not a multiple of 16 (NVFP4)
+    (dict(ldy=4), E_SHAPE),
+    (dict(M=-1), E_SHAPE),
+    (dict(fmt=2), E_FORMAT),
+    (dict(out=2), E_FORMAT),
+    (dict(y=A + 1), E_ALIGN),
+    (dict(a=fp4(codes=None)), E_NULL),
+    (dict(a=fp4(scales=A + 2)), E_ALIGN),
+    (dict(fmt=1, a=fp4(ts=None)), E_NULL),    # NVFP4 needs the activation's tensor scale
+    (dict(a=fp4(layout=1)), E_FORMAT),        # activation and weight layouts differ
+])
+def test_linear_dense_rejects(kwargs, status):
+    assert linear_dense(**kwargs) == status
+
+
+def test_linear_null_backbone_is_rejected():
+    rr, w = fp4(), fp4()
+    assert sharq.lib().sharq_linear(None, ctypes.byref(rr), 4, ctypes.byref(w), 8, 64, 0, A, 8, 0, None, 0,
+                                    None) == E_NULL
+
+
 def test_quantize_rejects():
     L = sharq.lib()
     out = fp4()
@@ -145,6 +177,7 @@ def test_valid_call_without_gfx950_reports_device():
         pytest.skip("a GPU is present; covered by the GPU tests")
     assert prep() == E_DEVICE
     assert linear() == E_DEVICE
+    assert linear_dense() == E_DEVICE
 
 
 def test_payload_bytes():

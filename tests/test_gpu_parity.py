@@ -198,6 +198,48 @@ def test_linear_small_full_compare(fmt, layout, M, N, K):
         assert fro <= TOL
 
 
+@pytest.mark.parametrize("fmt,layout", FMT_LAYOUTS, ids=FL_IDS)
+@pytest.mark.parametrize("M,N,K", [(1, 1, 32), (16, 512, 512), (37, 70, 96), (257, 513, 1056),
+                                   (64, 256, 2048), (520, 300, 384), (33, 96, 640)])
+def test_linear_dense_matches_oracle(fmt, layout, M, N, K):
+    """Plain FP4 linear (the SharQ kernels with the backbone path off)."""
+    print(f"[linear_dense] M={M} N={N} K={K} fmt={fmt} layout={layout}", flush=True)
+    xb, wb = make_shape(M, N, K, seed=3 * M + N + K, dist="laplace", token_sigma=0.3)
+    x, wt = to_dev(xb), to_dev(wb)
+    weight = sharq.quantize(wt, fmt, layout=layout)
+    a = sharq.quantize(x, fmt, layout=layout)
+    y32 = sharq.linear_dense(a, weight, sharq.OUT_FP32)
+    y16 = sharq.linear_dense(a, weight, sharq.OUT_BF16)
+    torch.cuda.synchronize()
+    oa, ow = oracle.quantize(xb, fmt), oracle.quantize(wb, fmt)
+    assert_payload_equal(a, oa, "activation")
+    assert_payload_equal(weight, ow, "weight")
+    yref = oracle.linear_dense(oa, ow, fmt)
+    err = rel_maxnorm(y32.cpu().numpy().astype(np.float64), yref)
+    assert err <= TOL, f"fp32 output max-norm rel err {err}"
+    assert bf16_ulp_check(y16, yref) <= 1
+
+
+@pytest.mark.parametrize("name", ["prefill", "decode", "mlp_down_nvfp4", "dit"])
+def test_linear_dense_workloads_sampled_rows(name):
+    """Plain FP4 linear at the full workload shapes (the comparison point of the benchmark)."""
+    w = WORKLOADS[name]
+    print(f"[linear_dense] {name} M={w.M} N={w.N} K={w.K} fmt={w.fmt}", flush=True)
+    xb, wb = make_inputs(w)
+    x, wt = to_dev(xb), to_dev(wb)
+    weight = sharq.quantize(wt, w.fmt)
+    a = sharq.quantize(x, w.fmt)
+    y32 = sharq.linear_dense(a, weight, sharq.OUT_FP32)
+    torch.cuda.synchronize()
+    oa, ow = oracle.quantize(xb, w.fmt), oracle.quantize(wb, w.fmt)
+    assert_payload_equal(a, oa, "activation")
+    rows = np.unique(np.concatenate([np.arange(min(8, w.M)), np.arange(max(0, w.M - 8), w.M),
+                                     np.linspace(0, w.M - 1, 16).astype(np.int64)]))
+    yref = oracle.linear_dense(oa, ow, w.fmt, rows=rows)
+    err = rel_maxnorm(y32.cpu().numpy()[rows].astype(np.float64), yref)
+    assert err <= TOL, f"{name}: fp32 output max-norm rel err {err}"
+
+
 @pytest.mark.parametrize("name", list(WORKLOADS))
 def test_linear_workloads_sampled_rows(name):
     """Full-size shapes in the benchmark's launch configuration; the oracle computes

@@ -396,6 +396,39 @@ def test_linear_identity_weight_returns_dequantized_sum():
     assert np.array_equal(y, want)
 
 
+@pytest.mark.parametrize("M,N,K", [(1, 1, 32), (3, 4, 64), (2, 3, 96)])
+def test_linear_dense_matches_exact_rationals(M, N, K):
+    rng = np.random.default_rng(20 + K)
+    xb = make_activation(rng, M, K, "laplace", n_out=1, out_scale=20.0)
+    wb = f32_to_bf16_bits(rng.normal(0, 0.02, (N, K)).astype(np.float32))
+    a, w = oracle.quantize(xb), oracle.quantize(wb)
+    y = oracle.linear_dense(a, w)
+    A, W = _frac_decode_mx(a, K), _frac_decode_mx(w, K)
+    for i in range(M):
+        for o in range(N):
+            exact = sum(A[i][k] * W[o][k] for k in range(K))
+            mag = sum(abs(A[i][k] * W[o][k]) for k in range(K))
+            assert abs(Fraction(y[i, o]) - exact) <= Fraction(K + 1) * Fraction(2) ** -53 * mag
+
+
+@pytest.mark.parametrize("fmt", [oracle.MXFP4, oracle.NVFP4])
+def test_linear_dense_identity_weight_returns_dequantized_input(fmt):
+    K = 64
+    rng = np.random.default_rng(21)
+    xb = make_activation(rng, 5, K, "laplace", n_out=2, out_scale=20.0)
+    a = oracle.quantize(xb, fmt)
+    codes = np.zeros((K, K), np.uint8)
+    codes[np.arange(K), np.arange(K)] = 0x2  # E2M1 1.0
+    packed = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+    if fmt == oracle.MXFP4:
+        w = oracle.Payload(packed, np.full((K, K // 32), 127, np.uint8))  # E8M0 2^0
+        want = decode_mx(a.codes, a.scales, K)
+    else:
+        w = oracle.Payload(packed, np.full((K, K // 16), 0x38, np.uint8), 1.0)  # E4M3 1.0
+        want = decode_nv(a.codes, a.scales, a.tscale, K)
+    assert np.array_equal(oracle.linear_dense(a, w, fmt), want)
+
+
 def test_linear_zero_input_and_row_selection():
     K, N = 64, 8
     rng = np.random.default_rng(12)
