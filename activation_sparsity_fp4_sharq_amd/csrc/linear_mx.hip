@@ -265,6 +265,18 @@ constexpr int kDmaStages = 3;
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
+// LDS-DMA through a buffer resource (buffer_load_dwordx4 ... lds): each lane's 16 bytes
+// at `base + voffset` (base wave-uniform) land at LDS `dst + 16 * lane`.  Bytes past
+// `bytes` read as zero.  The buffer form, unlike global_load_lds, leaves the compiler's
+// LDS-read counter exact, so fragment reads that follow are waited for one by one
+// instead of all at once.  Descriptor word 3 is the gfx9-family raw-buffer setting
+// (32-bit data format, no swizzle).
+constexpr int kRsrcWord3 = 0x00020000;
+__device__ __forceinline__ void buffer_lds16(const uint8_t* base, uint32_t bytes, uint8_t* dst, uint32_t voffset) {
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), 0, bytes, kRsrcWord3);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)dst, 16, voffset, 0, 0, 0);
+}
+
 // Epilogue of the tiled kernels.  The weights are the instruction's A operand, so in
 // accumulator acc[mt][nt] lane (r32, h) holds output row (row0 + 32mt + r32) and
 // columns col0 + 32nt + 8g + 4h + {0,1,2,3} in elements 4g..4g+3 -- four consecutive
@@ -356,7 +368,7 @@ __global__ __launch_bounds__(kThreads, 1) void linear_mx_dma_kernel(Args a) {
     const int64_t ntiles = (op == 2 ? a.Np : a.Mp) / 32;
     int64_t t = (op == 2 ? n0 : m0) / 32 + rt;
     t = t < ntiles ? t : ntiles - 1;
-    fsrc[j] = base + (t * (a.Kp / 64) + sub) * kFragBytes + lane * 16;
+    fsrc[j] = base + (t * (a.Kp / 64) + sub) * kFragBytes;  // wave-uniform; lane adds 16 * lane
     fdst[j] = op * kOpTileBytes + fi * kFragBytes;
   }
   // Scale words: one operand's 256 words per K-step are 1 KiB contiguous; the first
@@ -364,17 +376,19 @@ __global__ __launch_bounds__(kThreads, 1) void linear_mx_dma_kernel(Args a) {
   // bytes to the same place), so every wave issues the same loads per stage and no
   // branch sits between them -- the compiler's vmcnt bookkeeping then never degrades
   // to a full wait.
+  // (rows past the padded extent read as zero: the load is bounded to the rows that exist)
   const uint8_t* ssrc;
   int64_t sstep;
+  uint32_t sbytes;
   int sdst;
   {
     const int op = (kOp0 + wave < 3) ? kOp0 + wave : 2;
     const uint8_t* base = op == 0 ? a.bs : op == 1 ? a.rs : a.ws;
     const int64_t rp = op == 2 ? a.Np : a.Mp;
-    int64_t row = (op == 2 ? n0 : m0) + 4 * lane;
-    row = row < rp - 4 ? row : rp - 4;
-    ssrc = base + row * 4;
+    const int64_t row0 = op == 2 ? n0 : m0;
+    ssrc = base + row0 * 4;  // wave-uniform; lane adds 16 * lane (4 rows)
     sstep = rp * 4;
+    sbytes = (uint32_t)((rp - row0) * 4 < 1024 ? (rp - row0) * 4 : 1024);
     sdst = 3 * kOpTileBytes + op * 1024;
   }
   constexpr int kLoads = kFragLoads + 1;  // per wave and stage
@@ -384,9 +398,9 @@ __global__ __launch_bounds__(kThreads, 1) void linear_mx_dma_kernel(Args a) {
     uint8_t* st = smem + (ks % kDmaStages) * kDmaStageBytes;
     const int64_t kc = ks < nk ? ks : nk - 1;
     if (j < kFragLoads)
-      __builtin_amdgcn_global_load_lds(fsrc[j] + kc * 2 * kFragBytes, (lds_void_t*)(st + fdst[j]), 16, 0, 0);
+      buffer_lds16(fsrc[j] + kc * 2 * kFragBytes, kFragBytes, st + fdst[j], 16 * lane);
     else
-      __builtin_amdgcn_global_load_lds(ssrc + kc * sstep, (lds_void_t*)(st + sdst), 16, 0, 0);
+      buffer_lds16(ssrc + kc * sstep, sbytes, st + sdst, 16 * lane);
   };
 
   v16f acc[2][4];
@@ -408,26 +422,33 @@ __global__ __launch_bounds__(kThreads, 1) void linear_mx_dma_kernel(Args a) {
 
     const uint8_t* st = smem + (ks % kDmaStages) * kDmaStageBytes;
     const uint32_t* sc = reinterpret_cast<const uint32_t*>(st + 3 * kOpTileBytes);
+    // every LDS read of the K-step first, in the order of use (scale words, sub-step 0
+    // fragments, sub-step 1 fragments): LDS reads return in order, so sub-step 0 waits
+    // only for its own operands
     uint32_t as[2][2], ws[4];
 #pragma unroll
     for (int p = kOp0; p < 2; ++p)
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt) as[p][mt] = sc[p * 256 + wm * 64 + mt * 32 + r32] >> (8 * h);
+      for (int mt = 0; mt < 2; ++mt) as[p][mt] = sc[p * 256 + wm * 64 + mt * 32 + r32];
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) ws[nt] = sc[512 + wn * 128 + nt * 32 + r32] >> (8 * h);
+    for (int nt = 0; nt < 4; ++nt) ws[nt] = sc[512 + wn * 128 + nt * 32 + r32];
+    v4i af[2][2][2], wf[2][4];  // [sub][path][mt], [sub][nt]
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
-      v4i af[2][2], wf[4];
 #pragma unroll
       for (int p = kOp0; p < 2; ++p)
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt)
-          af[p][mt] = *reinterpret_cast<const v4i*>(st + p * kOpTileBytes +
-                                                    ((wm * 2 + mt) * 2 + sub) * kFragBytes + lane * 16);
+          af[sub][p][mt] = *reinterpret_cast<const v4i*>(st + p * kOpTileBytes +
+                                                         ((wm * 2 + mt) * 2 + sub) * kFragBytes + lane * 16);
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt)
-        wf[nt] = *reinterpret_cast<const v4i*>(st + 2 * kOpTileBytes + ((wn * 4 + nt) * 2 + sub) * kFragBytes +
-                                               lane * 16);
+        wf[sub][nt] = *reinterpret_cast<const v4i*>(st + 2 * kOpTileBytes +
+                                                    ((wn * 4 + nt) * 2 + sub) * kFragBytes + lane * 16);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) {
 #pragma unroll
       for (int p = kOp0; p < 2; ++p)
 #pragma unroll
@@ -438,14 +459,19 @@ __global__ __launch_bounds__(kThreads, 1) void linear_mx_dma_kernel(Args a) {
             // 4 consecutive output columns of one output row (see store_swapped)
             if (sub == 0)
               acc[mt][nt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                  widen(wf[nt]), widen(af[p][mt]), acc[mt][nt], 4, 4, 0, (int)ws[nt], 0, (int)as[p][mt]);
+                  widen(wf[0][nt]), widen(af[0][p][mt]), acc[mt][nt], 4, 4, 0, (int)(ws[nt] >> (8 * h)), 0,
+                  (int)(as[p][mt] >> (8 * h)));
             else
               acc[mt][nt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                  widen(wf[nt]), widen(af[p][mt]), acc[mt][nt], 4, 4, 2, (int)ws[nt], 2, (int)as[p][mt]);
+                  widen(wf[1][nt]), widen(af[1][p][mt]), acc[mt][nt], 4, 4, 2, (int)(ws[nt] >> (8 * h)), 2,
+                  (int)(as[p][mt] >> (8 * h)));
             // the next-but-one stage's loads, spread through the instructions
             constexpr int kPaths = 2 - kOp0, kEvery = DUAL ? 4 : 3;
             const int i = sub * 8 * kPaths + ((p - kOp0) * 2 + mt) * 4 + nt;
-            if (i % kEvery == kEvery - 1 && i / kEvery < kLoads) issue_one(i / kEvery, ks + 2);
+            if (i % kEvery == kEvery - 1 && i / kEvery < kLoads) {
+              issue_one(i / kEvery, ks + 2);
+              __builtin_amdgcn_sched_barrier(0);  // keep the loads spread between the instructions
+            }
           }
     }
   }
