@@ -27,6 +27,7 @@
 // distinct banks) and their scale dwords, double-buffered; one barrier per K-step.
 // Work-groups are renumbered so that consecutive tiles share an XCD (and its L2).
 #include <atomic>
+#include <type_traits>
 
 #include "sharq_internal.h"
 
@@ -409,71 +410,107 @@ __global__ __launch_bounds__(kThreads, 1) void linear_mx_dma_kernel(Args a) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = v16f{};
 
+  // Software pipeline across the K-steps, one barrier per step placed between its two
+  // sub-steps, so the LDS latency of every fragment read hides under matrix work:
+  //   [A] read sub-step 1 fragments of stage ks  |  16 MFMA on sub-step 0 of ks
+  //   [B] own loads of stage ks+1 landed; all reads of stage ks done (lgkmcnt 0);
+  //       barrier: stage ks+1 visible, slot ks%3 free
+  //   [C] read scales + sub-step 0 fragments of ks+1  |  16 MFMA on sub-step 1 of ks,
+  //       with the DMA of stage ks+3 into slot ks%3 spread between them
+  // (stages past the last are clamped re-loads into slots nobody reads)
+  auto read_frags = [&](v4i (&af)[2][2], v4i (&wf)[4], const uint8_t* st, int sub) {
 #pragma unroll
-  for (int j = 0; j < kLoads; ++j) issue_one(j, 0);
+    for (int p = kOp0; p < 2; ++p)
 #pragma unroll
-  for (int j = 0; j < kLoads; ++j) issue_one(j, 1);
-
-  for (int ks = 0; ks < nk; ++ks) {
-    // this wave's loads of stage ks are done when at most one stage's loads remain
-    SHARQ_WAIT_VMCNT(kLoads);
-    __builtin_amdgcn_s_barrier();  // every wave's stage ks landed; slot (ks+2)%3 is free
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-
-    const uint8_t* st = smem + (ks % kDmaStages) * kDmaStageBytes;
+      for (int mt = 0; mt < 2; ++mt)
+        af[p][mt] = *reinterpret_cast<const v4i*>(st + p * kOpTileBytes + ((wm * 2 + mt) * 2 + sub) * kFragBytes +
+                                                  lane * 16);
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt)
+      wf[nt] = *reinterpret_cast<const v4i*>(st + 2 * kOpTileBytes + ((wn * 4 + nt) * 2 + sub) * kFragBytes +
+                                             lane * 16);
+  };
+  auto read_scales = [&](uint32_t (&as)[2][2], uint32_t (&ws)[4], const uint8_t* st) {
     const uint32_t* sc = reinterpret_cast<const uint32_t*>(st + 3 * kOpTileBytes);
-    // every LDS read of the K-step first, in the order of use (scale words, sub-step 0
-    // fragments, sub-step 1 fragments): LDS reads return in order, so sub-step 0 waits
-    // only for its own operands
-    uint32_t as[2][2], ws[4];
 #pragma unroll
     for (int p = kOp0; p < 2; ++p)
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt) as[p][mt] = sc[p * 256 + wm * 64 + mt * 32 + r32];
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) ws[nt] = sc[512 + wn * 128 + nt * 32 + r32];
-    v4i af[2][2][2], wf[2][4];  // [sub][path][mt], [sub][nt]
+  };
+  // 16 matrix instructions of one sub-step; with ISSUE, the loads of stage ld spread
+  // between them (one per kEvery instructions)
+  auto mma = [&](const v4i (&af)[2][2], const v4i (&wf)[4], const uint32_t (&as)[2][2], const uint32_t (&ws)[4],
+                 auto sub_c, auto issue_c, int ld) {
+    constexpr int SUB = decltype(sub_c)::value;
+    constexpr bool ISSUE = decltype(issue_c)::value;
+    constexpr int kPerSub = 8 * (2 - kOp0), kEvery = kPerSub / kLoads;
+    static_assert(kEvery >= 1 && kPerSub / kEvery >= kLoads, "every load of a stage must be issued");
 #pragma unroll
-    for (int sub = 0; sub < 2; ++sub) {
+    for (int p = kOp0; p < 2; ++p)
 #pragma unroll
-      for (int p = kOp0; p < 2; ++p)
+      for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
-          af[sub][p][mt] = *reinterpret_cast<const v4i*>(st + p * kOpTileBytes +
-                                                         ((wm * 2 + mt) * 2 + sub) * kFragBytes + lane * 16);
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt)
-        wf[sub][nt] = *reinterpret_cast<const v4i*>(st + 2 * kOpTileBytes +
-                                                    ((wn * 4 + nt) * 2 + sub) * kFragBytes + lane * 16);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int sub = 0; sub < 2; ++sub) {
-#pragma unroll
-      for (int p = kOp0; p < 2; ++p)
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-          for (int nt = 0; nt < 4; ++nt) {
-            // weights as the instruction's A operand: each lane's accumulators are then
-            // 4 consecutive output columns of one output row (see store_swapped)
-            if (sub == 0)
-              acc[mt][nt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                  widen(wf[0][nt]), widen(af[0][p][mt]), acc[mt][nt], 4, 4, 0, (int)(ws[nt] >> (8 * h)), 0,
-                  (int)(as[p][mt] >> (8 * h)));
-            else
-              acc[mt][nt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                  widen(wf[1][nt]), widen(af[1][p][mt]), acc[mt][nt], 4, 4, 2, (int)(ws[nt] >> (8 * h)), 2,
-                  (int)(as[p][mt] >> (8 * h)));
-            // the next-but-one stage's loads, spread through the instructions
-            constexpr int kPaths = 2 - kOp0, kEvery = DUAL ? 4 : 3;
-            const int i = sub * 8 * kPaths + ((p - kOp0) * 2 + mt) * 4 + nt;
+        for (int nt = 0; nt < 4; ++nt) {
+          // weights as the instruction's A operand: each lane's accumulators are then
+          // 4 consecutive output columns of one output row (see store_swapped)
+          acc[mt][nt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+              widen(wf[nt]), widen(af[p][mt]), acc[mt][nt], 4, 4, 2 * SUB, (int)(ws[nt] >> (8 * h)), 2 * SUB,
+              (int)(as[p][mt] >> (8 * h)));
+          if constexpr (ISSUE) {
+            const int i = ((p - kOp0) * 2 + mt) * 4 + nt;
             if (i % kEvery == kEvery - 1 && i / kEvery < kLoads) {
-              issue_one(i / kEvery, ks + 2);
+              issue_one(i / kEvery, ld);
               __builtin_amdgcn_sched_barrier(0);  // keep the loads spread between the instructions
             }
           }
-    }
+        }
+  };
+
+#pragma unroll
+  for (int j = 0; j < kLoads; ++j) issue_one(j, 0);
+#pragma unroll
+  for (int j = 0; j < kLoads; ++j) issue_one(j, 1);
+#pragma unroll
+  for (int j = 0; j < kLoads; ++j) issue_one(j, 2);
+  SHARQ_WAIT_VMCNT(2 * kLoads);  // this wave's loads of stage 0 landed
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+
+  v4i af0[2][2], wf0[4], af1[2][2], wf1[4];
+  uint32_t as[2][2], ws[4], asn[2][2], wsn[4];
+  read_scales(as, ws, smem);
+  read_frags(af0, wf0, smem, 0);
+  using C0 = std::integral_constant<int, 0>;
+  using C1 = std::integral_constant<int, 1>;
+  using NoIssue = std::integral_constant<bool, false>;
+  using Issue = std::integral_constant<bool, true>;
+  for (int ks = 0; ks < nk; ++ks) {
+    const uint8_t* st = smem + (ks % kDmaStages) * kDmaStageBytes;
+    const uint8_t* nx = smem + ((ks + 1) % kDmaStages) * kDmaStageBytes;
+    // [A]
+    read_frags(af1, wf1, st, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(af0, wf0, as, ws, C0{}, NoIssue{}, 0);
+    // [B]
+    __builtin_amdgcn_sched_barrier(0);
+    SHARQ_WAIT_VMCNT(kLoads);            // this wave's loads of stage ks+1 landed
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's reads of stage ks are done
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    __builtin_amdgcn_sched_barrier(0);
+    // [C]
+    read_scales(asn, wsn, nx);
+    read_frags(af0, wf0, nx, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(af1, wf1, as, ws, C1{}, Issue{}, ks + 3);
+#pragma unroll
+    for (int p = 0; p < 2; ++p)
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) as[p][mt] = asn[p][mt];
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) ws[nt] = wsn[nt];
   }
   SHARQ_WAIT_VMCNT(0);  // trailing loads land before the stage ring is reused
 
