@@ -257,6 +257,15 @@ sharq_status sharq_linear_dense(const sharq_fp4* a, int64_t M, const sharq_fp4* 
                        stream);
 }
 
+sharq_status sharq_clock_probe(int64_t iters, uint64_t* counters, void* stream) {
+  if (!counters) return SHARQ_E_NULL;
+  if (iters < 1 || iters > ((int64_t)1 << 40)) return SHARQ_E_SHAPE;
+  if (reinterpret_cast<uintptr_t>(counters) & 7u) return SHARQ_E_ALIGN;
+  sharq_status s = check_device();
+  if (s != SHARQ_OK) return s;
+  return launched(launch_clock_probe(iters, counters, reinterpret_cast<hipStream_t>(stream)));
+}
+
 sharq_status sharq_forward(const void* x, int64_t M, int64_t K, int64_t ldx, int sp_n, int sp_m, int fmt,
                            const sharq_fp4* backbone, const sharq_fp4* residual, const sharq_fp4* weight,
                            int64_t N, void* y, int64_t ldy, int out_dtype, void* workspace,

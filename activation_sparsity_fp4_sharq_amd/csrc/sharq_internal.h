@@ -45,6 +45,10 @@ hipError_t launch_linear_nv(const sharq_fp4* b, const sharq_fp4& r, int64_t M, c
                             void* work, size_t work_bytes, hipStream_t stream);
 size_t linear_nv_workspace(int64_t M, int64_t N, int64_t K);
 
+// Shader-clock probe: out[0] = shader cycles, out[1] = 100 MHz ticks over one wave's
+// loop of `iters` x 4 FP4 matrix instructions while every CU runs the same loop.
+hipError_t launch_clock_probe(int64_t iters, uint64_t* out, hipStream_t stream);
+
 constexpr size_t kNvPrepWorkspace = 16448;  // 16 + 2 * 2048 dwords: maxima and partials
 constexpr int kMaxDevices = 64;
 

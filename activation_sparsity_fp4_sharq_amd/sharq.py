@@ -23,7 +23,7 @@ LIB_PATH = os.path.join(_HERE, "libsharq.so")
 SYMBOLS = ["sharq_abi_version", "sharq_status_str", "sharq_payload_bytes", "sharq_convert_layout",
            "sharq_prep_workspace_bytes", "sharq_linear_workspace_bytes", "sharq_quantize", "sharq_prep",
            "sharq_prep_rmsnorm_workspace_bytes", "sharq_prep_rmsnorm", "sharq_linear", "sharq_linear_dense",
-           "sharq_forward"]
+           "sharq_clock_probe", "sharq_forward"]
 
 
 class SharqFp4(ctypes.Structure):
@@ -78,6 +78,8 @@ def lib():
                                    vp]
         L.sharq_linear_dense.restype = ctypes.c_int
         L.sharq_linear_dense.argtypes = [P, i64, P, i64, i64, ctypes.c_int, vp, i64, ctypes.c_int, vp, sz, vp]
+        L.sharq_clock_probe.restype = ctypes.c_int
+        L.sharq_clock_probe.argtypes = [i64, vp, vp]
         L.sharq_forward.restype = ctypes.c_int
         L.sharq_forward.argtypes = [vp, i64, i64, i64, ctypes.c_int, ctypes.c_int, ctypes.c_int, P, P, P,
                                     i64, vp, i64, ctypes.c_int, vp, sz, vp]
@@ -252,6 +254,15 @@ def linear_dense(a, weight, out_dtype=OUT_BF16, y=None, ws=None, stream=None):
                                                           y.stride(0), out_dtype, _ptr(ws),
                                                           0 if ws is None else ws.numel(), _stream(stream)))
     return y
+
+
+def clock_probe(iters=20000, device=None, stream=None):
+    """Shader clock (Hz) under FP4 matrix load, from the device's cycle and 100 MHz counters."""
+    dev = device if device is not None else torch.device("cuda", torch.cuda.current_device())
+    out = torch.zeros(4, dtype=torch.int64, device=dev)
+    _check("sharq_clock_probe", lib().sharq_clock_probe(iters, _ptr(out), _stream(stream)))
+    cycles, ticks = (int(v) for v in out[:2].cpu())
+    return cycles / (ticks / 1e8) if ticks > 0 else float("nan")
 
 
 def forward(x, weight, n=2, m=4, out_dtype=OUT_BF16, bufs=None, y=None, ws=None, stream=None):

@@ -61,7 +61,7 @@
 extern "C" {
 #endif
 
-#define SHARQ_ABI_VERSION 4
+#define SHARQ_ABI_VERSION 5
 
 typedef enum sharq_status {
   SHARQ_OK = 0,
@@ -212,6 +212,14 @@ sharq_status sharq_linear(const sharq_fp4* backbone, const sharq_fp4* residual, 
 sharq_status sharq_linear_dense(const sharq_fp4* a, int64_t M, const sharq_fp4* weight, int64_t N,
                                 int64_t K, int fmt, void* y, int64_t ldy, int out_dtype, void* workspace,
                                 size_t workspace_bytes, void* stream);
+
+/* Measurement aid: the shader clock under matrix load.  Every CU runs iters x 4
+ * register-only FP4 matrix instructions per wave; counters (device, 8-byte aligned,
+ * >= 3 uint64) receive [0] the shader-clock cycles and [1] the 100 MHz reference
+ * ticks of one wave's loop (clock = [0] / ([1] / 1e8) Hz) and [2] a value that keeps
+ * the loop from being optimized away.  Errors: NULL counters -> SHARQ_E_NULL; iters
+ * outside [1, 2^40] -> SHARQ_E_SHAPE; misaligned -> SHARQ_E_ALIGN. */
+sharq_status sharq_clock_probe(int64_t iters, uint64_t* counters, void* stream);
 
 /* One SharQ linear layer end to end: sharq_prep into the caller's backbone and
  * residual payloads, then sharq_linear, on one stream.  Arguments as above; the

@@ -33,7 +33,7 @@ def test_header_symbols_exported():
 
 def test_version_and_status_strings():
     L = sharq.lib()
-    assert L.sharq_abi_version() == 4
+    assert L.sharq_abi_version() == 5
     for s in range(9):
         assert L.sharq_status_str(s)
     assert L.sharq_status_str(99) == b"unknown status"
@@ -144,6 +144,13 @@ def test_linear_null_backbone_is_rejected():
     rr, w = fp4(), fp4()
     assert sharq.lib().sharq_linear(None, ctypes.byref(rr), 4, ctypes.byref(w), 8, 64, 0, A, 8, 0, None, 0,
                                     None) == E_NULL
+
+
+def test_clock_probe_rejects():
+    L = sharq.lib()
+    assert L.sharq_clock_probe(100, None, None) == E_NULL
+    assert L.sharq_clock_probe(0, A, None) == E_SHAPE
+    assert L.sharq_clock_probe(100, A + 4, None) == E_ALIGN
 
 
 def test_quantize_rejects():
