@@ -60,6 +60,9 @@ def lib():
         L.oracle_prep.restype = ctypes.c_int
         L.oracle_prep.argtypes = [_u16p, _i64, _i64, _i64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                   _u8p, _u8p, _vp, _u8p, _u8p, _vp, _vp, _vp, _vp]
+        L.oracle_prep_variant.restype = ctypes.c_int
+        L.oracle_prep_variant.argtypes = [_u16p, _i64, _i64, _i64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                          ctypes.c_int, _u8p, _u8p, _vp, _u8p, _u8p, _vp, _vp, _vp, _vp]
         L.oracle_dequant.restype = ctypes.c_int
         L.oracle_dequant.argtypes = [_u8p, _u8p, ctypes.c_float, _i64, _i64, ctypes.c_int, _f64p]
         L.oracle_linear.restype = ctypes.c_int
@@ -122,8 +125,15 @@ def rmsnorm(x_bits, gamma_bits, eps):
     return y, r[:M]
 
 
-def prep(x_bits, n, m, fmt=MXFP4, want_values=False):
-    """SharQ activation preparation.  Returns (backbone, residual, mask_bits[, bhat, resid])."""
+ABLATE_RESIDUAL_UNQUANTIZED = 1
+ABLATE_STATIC_MASK = 2
+ABLATE_NO_RESIDUAL = 3
+
+
+def prep(x_bits, n, m, fmt=MXFP4, want_values=False, variant=0):
+    """SharQ activation preparation.  Returns (backbone, residual, mask_bits[, bhat, resid]).
+    variant: 0 = the method; 1-3 = the ablations of reading R13 (residual against the
+    unquantized sparse values, static mask, no residual)."""
     x_bits = np.ascontiguousarray(x_bits, dtype=np.uint16)
     M, K = x_bits.shape
     bc, bs = _alloc(M, K, fmt)
@@ -133,7 +143,7 @@ def prep(x_bits, n, m, fmt=MXFP4, want_values=False):
     mask = np.zeros((M, K // 8), np.uint8)
     bh = np.zeros((M, K), np.float32) if want_values else None
     rr = np.zeros((M, K), np.float32) if want_values else None
-    rc = lib().oracle_prep(x_bits, M, K, K, n, m, fmt, bc, bs, _ptr(bt), rc_, rs, _ptr(rt),
+    rc = lib().oracle_prep_variant(x_bits, M, K, K, n, m, fmt, variant, bc, bs, _ptr(bt), rc_, rs, _ptr(rt),
                            _ptr(mask), _ptr(bh), _ptr(rr))
     if rc:
         raise ValueError(f"oracle_prep rejected shape {x_bits.shape} pattern {n}:{m} fmt {fmt}")

@@ -38,7 +38,14 @@
  *      mask bit k%8 of byte k/8.
  *   R7 GEMM: Y = Bhat Ŵ^T + Rhat Ŵ^T, each a plain fp64 triple loop over dequantized
  *      values, summed.
- *   R8 normalization absorbed by the preparation ("Core claim" and abstract: the
+ *   R13 ablations (the pages' review asks for them: "What would settle it" and the
+ *      referee's third major comment): variant 1 = residual against the
+ *      unquantized sparse values, R = x - x*keep (exact: x or +0); variant 2 =
+ *      static mask, keep(j) <=> (j mod m) < n for every row and group, the backbone
+ *      block maximum then taken over the kept values as R2 already states; variant
+ *      3 = direct N:M without residual, R = 0 everywhere (so its payload is code 0x0,
+ *      E = -127, and for NVFP4 a tensor scale of 1 by R5).
+ *   R9 normalization absorbed by the preparation ("Core claim" and abstract: the
  *      fused preparation also takes over the layer normalization): RMS normalization
  *      with a per-channel bf16 gain g and no bias, producing the bf16 tensor the
  *      preparation then decomposes:
@@ -269,7 +276,7 @@ static uint16_t f32_to_bf16(float f) {
   return (uint16_t)(u >> 16);
 }
 
-/* R8: RMS normalization of x bf16 [M, ldx] (first K columns) with gain g bf16 [K]
+/* R9: RMS normalization of x bf16 [M, ldx] (first K columns) with gain g bf16 [K]
  * into y bf16 [M, K]; r_out (optional) receives the per-row factors r_i. */
 int oracle_rmsnorm(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, const uint16_t* g, float eps,
                    uint16_t* y, float* r_out) {
@@ -298,12 +305,13 @@ int oracle_rmsnorm(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, const u
  * Outputs: backbone codes/scales/tscale, residual codes/scales/tscale (layouts R6),
  *          optional mask bits [M, K/8]; optional fp32 views of Bhat and R [M, K]
  *          (bhat_out, resid_out; either may be NULL) for the invariant checks. */
-int oracle_prep(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, int n, int m, int fmt,
-                uint8_t* b_codes, uint8_t* b_scales, float* b_tscale,
-                uint8_t* r_codes, uint8_t* r_scales, float* r_tscale,
-                uint8_t* mask_bits, float* bhat_out, float* resid_out) {
+int oracle_prep_variant(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, int n, int m, int fmt,
+                        int variant, uint8_t* b_codes, uint8_t* b_scales, float* b_tscale,
+                        uint8_t* r_codes, uint8_t* r_scales, float* r_tscale,
+                        uint8_t* mask_bits, float* bhat_out, float* resid_out) {
   if (check_shape(M, K, ldx, fmt)) return -1;
   if (!((n == 2 && m == 4) || (n == 4 && m == 8))) return -2;
+  if (variant < 0 || variant > 3) return -2;
   const int B = fmt == ORACLE_MXFP4 ? 32 : 16;
   const int64_t nb = K / B;
 
@@ -313,7 +321,12 @@ int oracle_prep(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, int n, int
   if (!keep || !resid) { free(keep); free(resid); return -3; }
 #pragma omp parallel for schedule(static)
   for (int64_t i = 0; i < M; ++i)
-    for (int64_t g = 0; g < K / m; ++g) mask_group(x + i * ldx + g * m, n, m, keep + i * K + g * m);
+    for (int64_t g = 0; g < K / m; ++g) {
+      if (variant == 2) /* R13: static mask */
+        for (int j = 0; j < m; ++j) keep[i * K + g * m + j] = j < n;
+      else
+        mask_group(x + i * ldx + g * m, n, m, keep + i * K + g * m);
+    }
 
   /* NVFP4 backbone tensor scale: amax over the kept values (R5). */
   float Sb = 1.0f, Sr = 1.0f;
@@ -346,7 +359,9 @@ int oracle_prep(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, int n, int
         put_code(b_codes + i * (K / 2), k0 + j, c[j]);
         bh = fmt == ORACLE_MXFP4 ? mx_dequant(c[j], sb) : nv_dequant(c[j], sb, Sb);
         float xv = bf16_to_f32(x[i * ldx + k0 + j]);
-        float r = xv - bh;
+        float r = xv - bh;                                            /* R4 */
+        if (variant == 1) r = xv - (keep[i * K + k0 + j] ? xv : 0.0f); /* R13: x - x*keep */
+        if (variant == 3) r = 0.0f;                                    /* R13: no residual */
         resid[i * K + k0 + j] = r;
         if (bhat_out) bhat_out[i * K + k0 + j] = bh;
         if (resid_out) resid_out[i * K + k0 + j] = r;
@@ -391,6 +406,14 @@ int oracle_prep(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, int n, int
   free(keep);
   free(resid);
   return 0;
+}
+
+int oracle_prep(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, int n, int m, int fmt,
+                uint8_t* b_codes, uint8_t* b_scales, float* b_tscale,
+                uint8_t* r_codes, uint8_t* r_scales, float* r_tscale,
+                uint8_t* mask_bits, float* bhat_out, float* resid_out) {
+  return oracle_prep_variant(x, M, K, ldx, n, m, fmt, 0, b_codes, b_scales, b_tscale, r_codes, r_scales,
+                             r_tscale, mask_bits, bhat_out, resid_out);
 }
 
 /* Dequantize one FP4 payload row-block into fp64 (exact: every product of an

@@ -565,3 +565,74 @@ def test_rmsnorm_closed_forms():
     z = np.zeros((1, K), np.uint16)
     y, r = oracle.rmsnorm(z, g, 0.25)
     assert r[0] == np.float32(2.0) and np.all(bf16_bits_to_f32(y) == 0.0)
+
+
+# ------------------------------------------------------------ ablation variants (R13)
+
+def _abl_inputs(fmt, M=5, K=256, seed=31):
+    rng = np.random.default_rng(seed)
+    return make_activation(rng, M, K, "laplace", n_out=3, out_scale=20.0)
+
+
+@pytest.mark.parametrize("n,m,byte", [(2, 4, 0x33), (4, 8, 0x0F)])
+@pytest.mark.parametrize("fmt", [oracle.MXFP4, oracle.NVFP4])
+def test_static_mask_is_the_fixed_pattern(n, m, byte, fmt):
+    xb = _abl_inputs(fmt)
+    _, _, mask = oracle.prep(xb, n, m, fmt, variant=oracle.ABLATE_STATIC_MASK)
+    assert np.all(mask == byte)
+
+
+def test_static_mask_scale_comes_from_the_kept_values():
+    # one MX block whose largest magnitude sits at a position the static 2:4 mask drops
+    vals = np.zeros((1, 32), np.float32)
+    vals[0, 0], vals[0, 2] = 1.0, 40.0     # position 2 of its group: dropped statically
+    xb = f32_to_bf16_bits(vals)
+    bb, _, _ = oracle.prep(xb, 2, 4, oracle.MXFP4, variant=oracle.ABLATE_STATIC_MASK)
+    assert bb.scales[0, 0] == 127 + 0 - 2            # floor(log2 1.0) - 2
+    ba, _, _ = oracle.prep(xb, 2, 4, oracle.MXFP4)   # adaptive: 40 kept
+    assert ba.scales[0, 0] == 127 + 5 - 2            # floor(log2 40) = 5
+
+
+@pytest.mark.parametrize("fmt", [oracle.MXFP4, oracle.NVFP4])
+def test_residual_against_unquantized_sparse_values(fmt):
+    xb = _abl_inputs(fmt)
+    K = xb.shape[1]
+    b0, _, mask0 = oracle.prep(xb, 2, 4, fmt)
+    b1, _, mask1, _, r1 = oracle.prep(xb, 2, 4, fmt, want_values=True, variant=oracle.ABLATE_RESIDUAL_UNQUANTIZED)
+    assert np.array_equal(mask0, mask1)
+    assert np.array_equal(b0.codes, b1.codes) and np.array_equal(b0.scales, b1.scales)
+    keep = np.unpackbits(mask1, axis=1, bitorder="little").astype(bool)[:, :K]
+    x = x_values(xb)
+    assert np.array_equal(r1, np.where(keep, 0.0, x).astype(np.float32))
+
+
+@pytest.mark.parametrize("fmt", [oracle.MXFP4, oracle.NVFP4])
+def test_no_residual_variant_is_backbone_only(fmt):
+    xb = _abl_inputs(fmt)
+    b0, _, _ = oracle.prep(xb, 2, 4, fmt)
+    b3, r3, _ = oracle.prep(xb, 2, 4, fmt, variant=oracle.ABLATE_NO_RESIDUAL)
+    assert np.array_equal(b0.codes, b3.codes) and np.array_equal(b0.scales, b3.scales)
+    assert np.all(r3.codes == 0) and np.all(r3.scales == 0)
+    assert r3.tscale == 1.0
+
+
+@pytest.mark.parametrize("name", ["prefill", "dit"])
+def test_ablations_reconstruct_worse_than_the_method(name):
+    """Method sanity (not a pin): on the workload's X, the residual against the
+    quantized backbone reconstructs X better than each ablation and than plain FP4."""
+    w = WORKLOADS[name]
+    xb, _ = make_inputs(w)
+    xb = xb[:256]
+    x = x_values(xb)
+
+    def err(variant):
+        bb, rr, _ = oracle.prep(xb, w.n, w.m, w.fmt, variant=variant)
+        xh = oracle.dequant(bb, w.fmt) + oracle.dequant(rr, w.fmt)
+        return np.linalg.norm(x - xh) / np.linalg.norm(x)
+
+    e0 = err(0)
+    plain = np.linalg.norm(x - oracle.dequant(oracle.quantize(xb, w.fmt), w.fmt)) / np.linalg.norm(x)
+    for v in (oracle.ABLATE_RESIDUAL_UNQUANTIZED, oracle.ABLATE_STATIC_MASK, oracle.ABLATE_NO_RESIDUAL):
+        assert e0 < err(v), (name, v)
+    assert e0 < plain
+
