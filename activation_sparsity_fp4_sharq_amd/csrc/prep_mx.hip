@@ -97,9 +97,13 @@ __device__ __forceinline__ void store_scales(uint8_t* dst, int64_t b, int64_t nb
 // The per-block codec of one lane: 8 consecutive bf16 of a 32-element block (the
 // quad's other three lanes hold the rest).  MODE 0: mask, backbone codes and scale,
 // residual against the dequantized backbone, residual codes and scale.  MODE 1:
-// plain MXFP4 of the 8 values into (rbyte, rpacked).  Every lane of the quad must
-// call it together (the block maxima are quad exchanges).  `keep` (bit j = element
-// j kept) is only computed when a caller uses it.
+// plain MXFP4 of the 8 values into (rbyte, rpacked).  MODEs 2-4 are the ablations
+// of the method's choices: 2 = residual against the unquantized sparse values
+// (R = X - X*mask: the backbone's quantization error is left uncompensated), 3 = a
+// static mask (the first n of every m positions, whatever the input), 4 = no
+// residual (direct N:M sparsity + FP4; the residual payload is all zero).  Every
+// lane of the quad must call it together (the block maxima are quad exchanges).
+// `keep` (bit j = element j kept) is only computed when a caller uses it.
 template <int MODE, int SPM>
 __device__ __forceinline__ void codec_block(const uint32_t w[4], uint32_t& keep, uint32_t& bbyte,
                                             uint32_t& bpacked, uint32_t& rbyte, uint32_t& rpacked) {
@@ -113,27 +117,43 @@ __device__ __forceinline__ void codec_block(const uint32_t w[4], uint32_t& keep,
 
   float r[8];
   keep = 0xFFu; bbyte = 0; bpacked = 0;
-  if constexpr (MODE == 0) {
+  if constexpr (MODE != 1) {
     bool kept[8];
-    keep_mask<SPM>(xf, kept);
+    if constexpr (MODE == 3) {
+      // static: the lane's 8 elements start at a multiple of 8, so element j sits
+      // at position j % SPM of its group
+#pragma unroll
+      for (int j = 0; j < 8; ++j) kept[j] = (j % SPM) < SPM / 2;
+    } else {
+      keep_mask<SPM>(xf, kept);
+    }
     keep = 0;
 #pragma unroll
     for (int j = 0; j < 8; ++j) keep |= (kept[j] ? 1u : 0u) << j;
-    // Backbone block maximum: every group's largest element is kept and the groups
-    // tile the block, so the kept maximum is the block maximum of |x|.
-    const uint32_t bsb = scale_bits_of(quad_max(abs_max8(xf)));
-    bbyte = bsb >> 23;
-    const float bscale = __uint_as_float(bsb);
     // dropped positions become +0, which encodes as code 0x0
     float xm[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) xm[j] = kept[j] ? xf[j] : 0.0f;
+    // Backbone block maximum: with the top-|x| mask every group's largest element is
+    // kept and the groups tile the block, so the kept maximum is the block maximum
+    // of |x|; a static mask needs the maximum of the kept values themselves.
+    const uint32_t bsb = scale_bits_of(quad_max(abs_max8(MODE == 3 ? xm : xf)));
+    bbyte = bsb >> 23;
+    const float bscale = __uint_as_float(bsb);
     bpacked = quant8(xm, bscale);
-    // residual against the dequantized backbone: one fp32 subtraction each
-    float bh[8];
-    dequant8(bpacked, bscale, bh);
+    if constexpr (MODE == 2) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) r[j] = xf[j] - bh[j];
+      for (int j = 0; j < 8; ++j) r[j] = kept[j] ? 0.0f : xf[j];  // x - x*mask, exact
+    } else if constexpr (MODE == 4) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) r[j] = 0.0f;
+    } else {
+      // residual against the dequantized backbone: one fp32 subtraction each
+      float bh[8];
+      dequant8(bpacked, bscale, bh);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) r[j] = xf[j] - bh[j];
+    }
   } else {
 #pragma unroll
     for (int j = 0; j < 8; ++j) r[j] = xf[j];
@@ -160,7 +180,8 @@ __device__ __forceinline__ u32x4 rms_scale8(const u32x4& v, const Norm& nm, int6
 }
 
 // MODE 0: SharQ preparation (mask, backbone, residual).  MODE 1: plain MXFP4
-// quantization of X into (rcodes, rscales) -- used for weight payloads.
+// quantization of X into (rcodes, rscales) -- used for weight payloads.  MODEs 2-4:
+// the ablations (see codec_block).
 template <int MODE, int SPM, bool DENSE_ROWS, bool WRITE_MASK, bool NORM>
 __global__ __launch_bounds__(kThreads) void prep_mx_kernel(
     const uint16_t* __restrict__ x, int64_t ldx, int64_t nbk, int64_t nblocks,
@@ -205,17 +226,17 @@ __global__ __launch_bounds__(kThreads) void prep_mx_kernel(
     const int64_t b0 = base + u * kBlocksPerWave + 4 * (lane >> 4);
     const uint32_t rpk = gather_scales(rbyte);
     uint32_t bpk = 0;
-    if constexpr (MODE == 0) bpk = gather_scales(bbyte);
+    if constexpr (MODE != 1) bpk = gather_scales(bbyte);
 
     if (valid) {
       __builtin_nontemporal_store(rpacked, reinterpret_cast<uint32_t*>(rcodes + b * 16 + q * 4));
-      if constexpr (MODE == 0) {
+      if constexpr (MODE != 1) {
         __builtin_nontemporal_store(bpacked, reinterpret_cast<uint32_t*>(bcodes + b * 16 + q * 4));
         if constexpr (WRITE_MASK) mask[b * 4 + q] = (uint8_t)keep;
       }
     }
     store_scales(rscales, b0, nblocks, lane, rpk);
-    if constexpr (MODE == 0) store_scales(bscales, b0, nblocks, lane, bpk);
+    if constexpr (MODE != 1) store_scales(bscales, b0, nblocks, lane, bpk);
   }
 }
 
@@ -277,7 +298,7 @@ __global__ __launch_bounds__(kThreads) void prep_mx_tiled_kernel(
     codec_block<MODE, SPM>(w, keep, bbyte, bpacked, rbyte, rpacked);
     my[u * 64 + lane] = rpacked;  // = slot (u, k), dword q
     rword |= rbyte << (8 * u);
-    if constexpr (MODE == 0) {
+    if constexpr (MODE != 1) {
       myb[u * 64 + lane] = bpacked;
       bword |= bbyte << (8 * u);
       if constexpr (WRITE_MASK)
@@ -291,11 +312,11 @@ __global__ __launch_bounds__(kThreads) void prep_mx_tiled_kernel(
   const int su = lane >> 4;
   const int off = (su >> 1) * 1024 + (su & 1) * 512 + (int)(((r0 & 31) + (lane & 15)) * 16);
   __builtin_nontemporal_store(reinterpret_cast<const u32x4*>(my)[lane], reinterpret_cast<u32x4*>(rcodes + frag0 + off));
-  if constexpr (MODE == 0)
+  if constexpr (MODE != 1)
     __builtin_nontemporal_store(reinterpret_cast<const u32x4*>(myb)[lane], reinterpret_cast<u32x4*>(bcodes + frag0 + off));
   if (q == 0) {
     reinterpret_cast<uint32_t*>(rscales)[ks * Mp + r] = rword;
-    if constexpr (MODE == 0) reinterpret_cast<uint32_t*>(bscales)[ks * Mp + r] = bword;
+    if constexpr (MODE != 1) reinterpret_cast<uint32_t*>(bscales)[ks * Mp + r] = bword;
   }
 }
 
@@ -338,24 +359,43 @@ hipError_t launch_dense_or_strided(const uint16_t* x, int64_t M, int64_t K, int6
 
 
 // Dispatch over the compile-time variants: pattern, mask output, normalization, layout.
-template <int SPM, bool WRITE_MASK, bool NORM>
+template <int MODE, int SPM, bool WRITE_MASK, bool NORM>
 hipError_t prep_variant(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, uint8_t* bcodes, uint8_t* bscales,
                         uint8_t* rcodes, uint8_t* rscales, uint8_t* mask, Norm nm, int tiled, hipStream_t stream) {
   if (tiled)
-    return launch_tiled<0, SPM, WRITE_MASK, NORM>(x, M, K, ldx, bcodes, bscales, rcodes, rscales, mask, nm, stream);
-  return launch_dense_or_strided<0, SPM, WRITE_MASK, NORM>(x, M, K, ldx, bcodes, bscales, rcodes, rscales, mask, nm,
-                                                           stream);
+    return launch_tiled<MODE, SPM, WRITE_MASK, NORM>(x, M, K, ldx, bcodes, bscales, rcodes, rscales, mask, nm, stream);
+  return launch_dense_or_strided<MODE, SPM, WRITE_MASK, NORM>(x, M, K, ldx, bcodes, bscales, rcodes, rscales, mask,
+                                                              nm, stream);
+}
+
+// The ablations (MODEs 2-4), without normalization.
+template <int SPM>
+hipError_t prep_ablation(int variant, const uint16_t* x, int64_t M, int64_t K, int64_t ldx, uint8_t* bcodes,
+                         uint8_t* bscales, uint8_t* rcodes, uint8_t* rscales, uint8_t* mask, int tiled,
+                         hipStream_t stream) {
+  const Norm none{nullptr, nullptr};
+  switch (variant) {
+    case SHARQ_ABLATE_RESIDUAL_UNQUANTIZED:
+      return mask ? prep_variant<2, SPM, true, false>(x, M, K, ldx, bcodes, bscales, rcodes, rscales, mask, none, tiled, stream)
+                  : prep_variant<2, SPM, false, false>(x, M, K, ldx, bcodes, bscales, rcodes, rscales, mask, none, tiled, stream);
+    case SHARQ_ABLATE_STATIC_MASK:
+      return mask ? prep_variant<3, SPM, true, false>(x, M, K, ldx, bcodes, bscales, rcodes, rscales, mask, none, tiled, stream)
+                  : prep_variant<3, SPM, false, false>(x, M, K, ldx, bcodes, bscales, rcodes, rscales, mask, none, tiled, stream);
+    default:  // SHARQ_ABLATE_NO_RESIDUAL
+      return mask ? prep_variant<4, SPM, true, false>(x, M, K, ldx, bcodes, bscales, rcodes, rscales, mask, none, tiled, stream)
+                  : prep_variant<4, SPM, false, false>(x, M, K, ldx, bcodes, bscales, rcodes, rscales, mask, none, tiled, stream);
+  }
 }
 
 template <int SPM>
 hipError_t prep_pattern(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, uint8_t* bcodes, uint8_t* bscales,
                         uint8_t* rcodes, uint8_t* rscales, uint8_t* mask, Norm nm, int tiled, hipStream_t stream) {
   if (nm.r) {
-    return mask ? prep_variant<SPM, true, true>(x, M, K, ldx, bcodes, bscales, rcodes, rscales, mask, nm, tiled, stream)
-                : prep_variant<SPM, false, true>(x, M, K, ldx, bcodes, bscales, rcodes, rscales, mask, nm, tiled, stream);
+    return mask ? prep_variant<0, SPM, true, true>(x, M, K, ldx, bcodes, bscales, rcodes, rscales, mask, nm, tiled, stream)
+                : prep_variant<0, SPM, false, true>(x, M, K, ldx, bcodes, bscales, rcodes, rscales, mask, nm, tiled, stream);
   }
-  return mask ? prep_variant<SPM, true, false>(x, M, K, ldx, bcodes, bscales, rcodes, rscales, mask, nm, tiled, stream)
-              : prep_variant<SPM, false, false>(x, M, K, ldx, bcodes, bscales, rcodes, rscales, mask, nm, tiled, stream);
+  return mask ? prep_variant<0, SPM, true, false>(x, M, K, ldx, bcodes, bscales, rcodes, rscales, mask, nm, tiled, stream)
+              : prep_variant<0, SPM, false, false>(x, M, K, ldx, bcodes, bscales, rcodes, rscales, mask, nm, tiled, stream);
 }
 
 }  // namespace
@@ -368,6 +408,13 @@ hipError_t launch_prep_mx(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, 
   const Norm nm{rnorm, gamma};
   if (sp_m == 4) return prep_pattern<4>(x, M, K, ldx, bcodes, bscales, rcodes, rscales, mask, nm, tiled, stream);
   return prep_pattern<8>(x, M, K, ldx, bcodes, bscales, rcodes, rscales, mask, nm, tiled, stream);
+}
+
+hipError_t launch_prep_mx_ablation(int variant, const uint16_t* x, int64_t M, int64_t K, int64_t ldx, int sp_m,
+                                   uint8_t* bcodes, uint8_t* bscales, uint8_t* rcodes, uint8_t* rscales,
+                                   uint8_t* mask, int tiled, hipStream_t stream) {
+  if (sp_m == 4) return prep_ablation<4>(variant, x, M, K, ldx, bcodes, bscales, rcodes, rscales, mask, tiled, stream);
+  return prep_ablation<8>(variant, x, M, K, ldx, bcodes, bscales, rcodes, rscales, mask, tiled, stream);
 }
 
 hipError_t launch_quant_mx(const uint16_t* x, int64_t rows, int64_t K, int64_t ldx, uint8_t* codes,

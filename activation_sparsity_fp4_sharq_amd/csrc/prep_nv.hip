@@ -189,10 +189,22 @@ __device__ __forceinline__ uint32_t abs_max8_bits(const float v[8]) {
 
 // PASS 0: amax|X| partials.  PASS 1 (MODE 0): backbone written, amax|R| partials.
 // PASS 2: MODE 0 writes the residual from X and the written backbone; MODE 1 (plain
-// NVFP4 quantization, used for weights) quantizes X into (rcodes, rscales).  A
+// NVFP4 quantization, used for weights) quantizes X into (rcodes, rscales).  MODEs
+// 2-4 are the ablations of the method's choices: 2 = residual against the
+// unquantized sparse values (R = X - X*mask), 3 = a static mask (the first n of
+// every m positions; the backbone maxima are then those of the kept values), 4 = no
+// residual (all-zero residual payload, tensor scale 1).  A
 // one-work-group launch after each maximum pass reduces its partials into work[0]
 // or work[1]; work-group 0 of the pass after it writes that path's tensor scale
 // (backbone or plain: bts, residual: rts).
+// static mask of the lane's 8 elements (they start at a multiple of 8, so element j
+// sits at position j % SPM of its group)
+template <int SPM>
+__device__ __forceinline__ void static_mask(bool kept[8]) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) kept[j] = (j % SPM) < SPM / 2;
+}
+
 template <int PASS, int MODE, int SPM, bool DENSE_ROWS, bool WRITE_MASK, bool NORM>
 __global__ __launch_bounds__(kThreads) void prep_nv_kernel(
     const uint16_t* __restrict__ x, int64_t ldx, int64_t chunks_per_row, int64_t nchunks,
@@ -212,7 +224,7 @@ __global__ __launch_bounds__(kThreads) void prep_nv_kernel(
     pb = path_scale(work[0]);
     if (blockIdx.x == 0 && threadIdx.x == 0 && (PASS == 1 || MODE == 1) && bts) *bts = pb.S;
   }
-  if constexpr (PASS == 2 && MODE == 0) {
+  if constexpr (PASS == 2 && MODE != 1) {
     pr = path_scale(work[1]);
     if (blockIdx.x == 0 && threadIdx.x == 0 && rts) *rts = pr.S;
   }
@@ -244,7 +256,7 @@ __global__ __launch_bounds__(kThreads) void prep_nv_kernel(
           v[u] = u32x4{rms_scale_pair(v[u][0], g[0], rr), rms_scale_pair(v[u][1], g[1], rr),
                        rms_scale_pair(v[u][2], g[2], rr), rms_scale_pair(v[u][3], g[3], rr)};
         }
-        if constexpr (PASS == 2 && MODE == 0) {
+        if constexpr (PASS == 2 && (MODE == 0 || MODE == 3)) {
           bpk_in[u] = *reinterpret_cast<const uint32_t*>(bcodes + c * 4);
           bsb_in[u] = bscales[c >> 1];
         }
@@ -257,7 +269,16 @@ __global__ __launch_bounds__(kThreads) void prep_nv_kernel(
       const bool valid = c < nchunks;
       float xf[8];
       unpack8(v[u], xf);
-      const uint32_t xmax = abs_max8_bits(xf);
+      uint32_t xmax = abs_max8_bits(xf);
+      if constexpr (MODE == 3 && PASS <= 1) {
+        // static mask: the backbone's maxima are those of the kept values
+        bool kept[8];
+        static_mask<SPM>(kept);
+        float kv[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) kv[j] = kept[j] ? xf[j] : 0.0f;
+        xmax = abs_max8_bits(kv);
+      }
       if constexpr (PASS == 0) {
         run_max = umax(run_max, xmax);
         continue;
@@ -275,10 +296,12 @@ __global__ __launch_bounds__(kThreads) void prep_nv_kernel(
         continue;
       } else {
         float r[8], bh[8];
+        bool kept[8];
         if constexpr (PASS == 1) {
-          // mask and backbone (the block maximum of the kept values is that of X)
-          bool kept[8];
-          keep_mask<SPM>(xf, kept);
+          // mask and backbone (with the top-|x| mask the block maximum of the kept
+          // values is that of X; the static mask's xmax is already the kept one)
+          if constexpr (MODE == 3) static_mask<SPM>(kept);
+          else keep_mask<SPM>(xf, kept);
           float kv[8];
 #pragma unroll
           for (int j = 0; j < 8; ++j) kv[j] = kept[j] ? xf[j] : 0.0f;  // dropped: +0 -> code 0x0
@@ -297,13 +320,23 @@ __global__ __launch_bounds__(kThreads) void prep_nv_kernel(
             }
           }
           store_scale_words(bscales, g0, nblocks, lane, pk);
-        } else {
+        } else if constexpr (MODE == 0 || MODE == 3) {
           // the backbone as written by pass 1
           const float d = __fmul_rn(e4m3_value(bsb_in[u]), pb.S);
           nv_dequant(bpk_in[u], d, bh);
+        } else if constexpr (MODE == 2) {
+          keep_mask<SPM>(xf, kept);  // the same mask as pass 1's
         }
+        if constexpr (MODE == 2) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) r[j] = __fsub_rn(xf[j], bh[j]);
+          for (int j = 0; j < 8; ++j) r[j] = kept[j] ? 0.0f : xf[j];  // x - x*mask, exact
+        } else if constexpr (MODE == 4) {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) r[j] = 0.0f;
+        } else {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) r[j] = __fsub_rn(xf[j], bh[j]);
+        }
         const uint32_t rmax = abs_max8_bits(r);
         if constexpr (PASS == 1) {
           run_max = umax(run_max, rmax);
@@ -369,7 +402,7 @@ hipError_t run_passes(const uint16_t* x, int64_t ldx, int64_t cpr, int64_t nchun
   prep_nv_kernel<0, MODE, SPM, DENSE, WRITE_MASK, NORM><<<dim3(rgrid), kThreads, 0, st>>>(
       x, ldx, cpr, nchunks, bcodes, bscales, rcodes, rscales, mask, work, bts, rts, rnorm, gamma);
   nv_reduce_kernel<<<1, 256, 0, st>>>(work, 0, (int)rgrid);
-  if constexpr (MODE == 0) {
+  if constexpr (MODE != 1) {
     prep_nv_kernel<1, MODE, SPM, DENSE, WRITE_MASK, NORM><<<dim3(rgrid), kThreads, 0, st>>>(
         x, ldx, cpr, nchunks, bcodes, bscales, rcodes, rscales, mask, work, bts, rts, rnorm, gamma);
     nv_reduce_kernel<<<1, 256, 0, st>>>(work, 1, (int)rgrid);
@@ -422,6 +455,38 @@ hipError_t launch_prep_nv(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, 
                                   rnorm, gamma, stream)
               : run_prep<8, false>(x, M, K, ldx, bcodes, bscales, btscale, rcodes, rscales, rtscale, mask, work,
                                    rnorm, gamma, stream);
+}
+
+template <int SPM, bool WRITE_MASK>
+hipError_t run_ablation(int variant, const uint16_t* x, int64_t M, int64_t K, int64_t ldx, uint8_t* bcodes,
+                        uint8_t* bscales, float* bts, uint8_t* rcodes, uint8_t* rscales, float* rts, uint8_t* mask,
+                        uint32_t* work, hipStream_t st) {
+  switch (variant) {
+    case SHARQ_ABLATE_RESIDUAL_UNQUANTIZED:
+      return run_nv<2, SPM, WRITE_MASK, false>(x, M, K, ldx, bcodes, bscales, bts, rcodes, rscales, rts, mask, work,
+                                               nullptr, nullptr, st);
+    case SHARQ_ABLATE_STATIC_MASK:
+      return run_nv<3, SPM, WRITE_MASK, false>(x, M, K, ldx, bcodes, bscales, bts, rcodes, rscales, rts, mask, work,
+                                               nullptr, nullptr, st);
+    default:  // SHARQ_ABLATE_NO_RESIDUAL
+      return run_nv<4, SPM, WRITE_MASK, false>(x, M, K, ldx, bcodes, bscales, bts, rcodes, rscales, rts, mask, work,
+                                               nullptr, nullptr, st);
+  }
+}
+
+hipError_t launch_prep_nv_ablation(int variant, const uint16_t* x, int64_t M, int64_t K, int64_t ldx, int sp_m,
+                                   uint8_t* bcodes, uint8_t* bscales, float* btscale, uint8_t* rcodes,
+                                   uint8_t* rscales, float* rtscale, uint8_t* mask, uint32_t* work,
+                                   hipStream_t stream) {
+  if (sp_m == 4)
+    return mask ? run_ablation<4, true>(variant, x, M, K, ldx, bcodes, bscales, btscale, rcodes, rscales, rtscale,
+                                        mask, work, stream)
+                : run_ablation<4, false>(variant, x, M, K, ldx, bcodes, bscales, btscale, rcodes, rscales, rtscale,
+                                         mask, work, stream);
+  return mask ? run_ablation<8, true>(variant, x, M, K, ldx, bcodes, bscales, btscale, rcodes, rscales, rtscale,
+                                      mask, work, stream)
+              : run_ablation<8, false>(variant, x, M, K, ldx, bcodes, bscales, btscale, rcodes, rscales, rtscale,
+                                       mask, work, stream);
 }
 
 hipError_t launch_quant_nv(const uint16_t* x, int64_t rows, int64_t K, int64_t ldx, uint8_t* codes,

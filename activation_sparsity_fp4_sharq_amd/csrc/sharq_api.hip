@@ -211,6 +211,49 @@ sharq_status sharq_prep(const void* x, int64_t M, int64_t K, int64_t ldx, int sp
                                nullptr, st));
 }
 
+sharq_status sharq_prep_ablation(const void* x, int64_t M, int64_t K, int64_t ldx, int sp_n, int sp_m, int fmt,
+                                 int variant, const sharq_fp4* backbone, const sharq_fp4* residual,
+                                 uint8_t* mask_bits, void* workspace, size_t workspace_bytes, void* stream) {
+  sharq_status s = check_input(x, M, K, ldx, fmt);
+  if (s != SHARQ_OK) return s;
+  if ((s = check_pattern(sp_n, sp_m)) != SHARQ_OK) return s;
+  if (variant != SHARQ_ABLATE_RESIDUAL_UNQUANTIZED && variant != SHARQ_ABLATE_STATIC_MASK &&
+      variant != SHARQ_ABLATE_NO_RESIDUAL)
+    return SHARQ_E_FORMAT;
+  if ((s = check_payload(backbone, fmt, M)) != SHARQ_OK) return s;
+  if ((s = check_payload(residual, fmt, M)) != SHARQ_OK) return s;
+  if (backbone->layout != residual->layout) return SHARQ_E_FORMAT;
+  if (mask_bits && (reinterpret_cast<uintptr_t>(mask_bits) & 3u)) return SHARQ_E_ALIGN;
+  const size_t need = sharq_prep_workspace_bytes(M, K, fmt);
+  if (need && (!workspace || workspace_bytes < need)) return SHARQ_E_WORKSPACE;
+  if (need && !aligned16(workspace)) return SHARQ_E_ALIGN;
+  if ((s = check_device()) != SHARQ_OK) return s;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const uint16_t* xb = reinterpret_cast<const uint16_t*>(x);
+  if (fmt == SHARQ_MXFP4)
+    return launched(launch_prep_mx_ablation(variant, xb, M, K, ldx, sp_m, backbone->codes, backbone->scales,
+                                            residual->codes, residual->scales, mask_bits,
+                                            backbone->layout == SHARQ_LAYOUT_TILED, st));
+  return launched(launch_prep_nv_ablation(variant, xb, M, K, ldx, sp_m, backbone->codes, backbone->scales,
+                                          backbone->tensor_scale, residual->codes, residual->scales,
+                                          residual->tensor_scale, mask_bits, reinterpret_cast<uint32_t*>(workspace),
+                                          st));
+}
+
+sharq_status sharq_dequantize(const sharq_fp4* p, int64_t rows, int64_t K, int fmt, float* out, int64_t ldo,
+                              void* stream) {
+  sharq_status s = check_format(fmt);
+  if (s != SHARQ_OK) return s;
+  if (rows < 0 || K <= 0 || K % block_of(fmt) || ldo < K) return SHARQ_E_SHAPE;
+  if (rows > (int64_t)1 << 31 || K > (int64_t)1 << 30 || rows * (K / 8) > ((int64_t)1 << 39)) return SHARQ_E_SHAPE;
+  if ((s = check_payload(p, fmt, rows)) != SHARQ_OK) return s;
+  if (rows > 0 && !out) return SHARQ_E_NULL;
+  if (reinterpret_cast<uintptr_t>(out) & 3u) return SHARQ_E_ALIGN;
+  if ((s = check_device()) != SHARQ_OK) return s;
+  if (rows == 0) return SHARQ_OK;
+  return launched(launch_dequantize(*p, rows, K, fmt, out, ldo, reinterpret_cast<hipStream_t>(stream)));
+}
+
 size_t sharq_prep_rmsnorm_workspace_bytes(int64_t M, int64_t K, int fmt) {
   if (M < 0) return 0;
   return rms_factor_offset(fmt) + (size_t)round_up(M > 0 ? M : 1, 64) * sizeof(float);

@@ -16,6 +16,17 @@ hipError_t launch_prep_mx(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, 
                           int sp_m, uint8_t* bcodes, uint8_t* bscales, uint8_t* rcodes,
                           uint8_t* rscales, uint8_t* mask, const float* rnorm, const uint16_t* gamma,
                           int tiled, hipStream_t stream);
+// The ablation variants of the preparation (sharq_ablation), without normalization.
+hipError_t launch_prep_mx_ablation(int variant, const uint16_t* x, int64_t M, int64_t K, int64_t ldx, int sp_m,
+                                   uint8_t* bcodes, uint8_t* bscales, uint8_t* rcodes, uint8_t* rscales,
+                                   uint8_t* mask, int tiled, hipStream_t stream);
+hipError_t launch_prep_nv_ablation(int variant, const uint16_t* x, int64_t M, int64_t K, int64_t ldx, int sp_m,
+                                   uint8_t* bcodes, uint8_t* bscales, float* btscale, uint8_t* rcodes,
+                                   uint8_t* rscales, float* rtscale, uint8_t* mask, uint32_t* work,
+                                   hipStream_t stream);
+// fp32 values of a payload (row-major or tiled MXFP4; row-major NVFP4).
+hipError_t launch_dequantize(const sharq_fp4& p, int64_t rows, int64_t K, int fmt, float* out, int64_t ldo,
+                             hipStream_t stream);
 hipError_t launch_quant_mx(const uint16_t* x, int64_t rows, int64_t K, int64_t ldx,
                            uint8_t* codes, uint8_t* scales, int tiled, hipStream_t stream);
 hipError_t launch_convert_mx(const sharq_fp4& src, const sharq_fp4& dst, int64_t rows, int64_t K,

@@ -23,7 +23,7 @@ LIB_PATH = os.path.join(_HERE, "libsharq.so")
 SYMBOLS = ["sharq_abi_version", "sharq_status_str", "sharq_payload_bytes", "sharq_convert_layout",
            "sharq_prep_workspace_bytes", "sharq_linear_workspace_bytes", "sharq_quantize", "sharq_prep",
            "sharq_prep_rmsnorm_workspace_bytes", "sharq_prep_rmsnorm", "sharq_linear", "sharq_linear_dense",
-           "sharq_clock_probe", "sharq_forward"]
+           "sharq_clock_probe", "sharq_prep_ablation", "sharq_dequantize", "sharq_forward"]
 
 
 class SharqFp4(ctypes.Structure):
@@ -78,6 +78,11 @@ def lib():
                                    vp]
         L.sharq_linear_dense.restype = ctypes.c_int
         L.sharq_linear_dense.argtypes = [P, i64, P, i64, i64, ctypes.c_int, vp, i64, ctypes.c_int, vp, sz, vp]
+        L.sharq_prep_ablation.restype = ctypes.c_int
+        L.sharq_prep_ablation.argtypes = [vp, i64, i64, i64, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                          P, P, vp, vp, sz, vp]
+        L.sharq_dequantize.restype = ctypes.c_int
+        L.sharq_dequantize.argtypes = [P, i64, i64, ctypes.c_int, vp, i64, vp]
         L.sharq_clock_probe.restype = ctypes.c_int
         L.sharq_clock_probe.argtypes = [i64, vp, vp]
         L.sharq_forward.restype = ctypes.c_int
@@ -254,6 +259,37 @@ def linear_dense(a, weight, out_dtype=OUT_BF16, y=None, ws=None, stream=None):
                                                           y.stride(0), out_dtype, _ptr(ws),
                                                           0 if ws is None else ws.numel(), _stream(stream)))
     return y
+
+
+ABLATE_RESIDUAL_UNQUANTIZED = 1
+ABLATE_STATIC_MASK = 2
+ABLATE_NO_RESIDUAL = 3
+
+
+def prep_ablation(x, variant, n=2, m=4, fmt=MXFP4, want_mask=False, out=None, ws=None, layout=None, stream=None):
+    """sharq_prep with one of the ablations (ABLATE_*): returns (backbone, residual, mask_bits or None)."""
+    x = _as_bf16_2d(x)
+    M, K = x.shape
+    bb, rr = out if out is not None else (Payload.empty(M, K, fmt, x.device, layout),
+                                          Payload.empty(M, K, fmt, x.device, layout))
+    mask = torch.empty((M, K // 8), dtype=torch.uint8, device=x.device) if want_mask else None
+    if ws is None:
+        ws = workspace(lib().sharq_prep_workspace_bytes(M, K, fmt), x.device)
+    sb, sr = bb.struct(), rr.struct()
+    _check("sharq_prep_ablation", lib().sharq_prep_ablation(_ptr(x), M, K, x.stride(0), n, m, fmt, variant,
+                                                            ctypes.byref(sb), ctypes.byref(sr), _ptr(mask), _ptr(ws),
+                                                            0 if ws is None else ws.numel(), _stream(stream)))
+    return bb, rr, mask
+
+
+def dequantize(p, out=None, stream=None):
+    """fp32 values [rows, K] of a payload, on the device."""
+    if out is None:
+        out = torch.empty((p.rows, p.K), dtype=torch.float32, device=p.codes.device)
+    st = p.struct()
+    _check("sharq_dequantize", lib().sharq_dequantize(ctypes.byref(st), p.rows, p.K, p.fmt, _ptr(out), out.stride(0),
+                                                      _stream(stream)))
+    return out
 
 
 def clock_probe(iters=20000, device=None, stream=None):

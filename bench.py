@@ -46,6 +46,10 @@ def parse():
     p.add_argument("--compare", action="store_true",
                    help="also time comparison points at the same shape: torch bf16 and fp8 GEMMs, the "
                         "library MXFP4 GEMM, and the plain FP4 layer (quantize + one-operand GEMM)")
+    p.add_argument("--ablation", action="store_true",
+                   help="also report the reconstruction error ||X - (Bhat + Rhat)|| / ||X|| of the method, its "
+                        "ablations (residual against the unquantized sparse values, static mask, no residual) "
+                        "and plain FP4, on the workload's X, with each preparation's time")
     p.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                    help="only run a plain device copy of MIB MiB (5 times): the reference dispatch that "
                         "scales hardware byte counters to bytes")
@@ -221,6 +225,49 @@ def comparison_points(w, sets, weight_sets, ws, stream, reps, t_prep, t_lin):
     return out
 
 
+def ablation_report(w, x, ws, stream, reps):
+    """Reconstruction error of each preparation on the workload's X, computed on the
+    device from sharq_dequantize (fp32 values, fp64 sums), and each preparation's
+    back-to-back time."""
+    import torch
+
+    from activation_sparsity_fp4_sharq_amd import sharq
+
+    M, K = w.M, w.K
+    xf = x.double()
+    xnorm = torch.linalg.vector_norm(xf).item()
+    bb = sharq.Payload.empty(M, K, w.fmt, x.device)
+    rr = sharq.Payload.empty(M, K, w.fmt, x.device)
+    d0 = torch.empty((M, K), dtype=torch.float32, device=x.device)
+    d1 = torch.empty((M, K), dtype=torch.float32, device=x.device)
+
+    def rel_err(b, r):
+        sharq.dequantize(b, out=d0, stream=stream)
+        xh = d0.double()
+        if r is not None:
+            sharq.dequantize(r, out=d1, stream=stream)
+            xh = xh + d1.double()
+        return torch.linalg.vector_norm(xf - xh).item() / xnorm
+
+    out = {"x_rows": M, "x_cols": K, "metric": "||X - Xhat||_F / ||X||_F"}
+    variants = [("sharq", 0), ("residual_vs_unquantized_sparse", sharq.ABLATE_RESIDUAL_UNQUANTIZED),
+                ("static_mask", sharq.ABLATE_STATIC_MASK), ("no_residual_direct_nm", sharq.ABLATE_NO_RESIDUAL)]
+    for name, v in variants:
+        if v == 0:
+            launch = lambda i: sharq.prep(x, w.n, w.m, w.fmt, out=(bb, rr), ws=ws, stream=stream)
+        else:
+            launch = lambda i, v=v: sharq.prep_ablation(x, v, w.n, w.m, w.fmt, out=(bb, rr), ws=ws, stream=stream)
+        launch(0)
+        e = rel_err(bb, rr)
+        t = back_to_back_seconds(launch, reps, stream)
+        out[name] = {"rel_err": round(e, 6), "prep_us": round(t * 1e6, 2)}
+    launch = lambda i: sharq.quantize(x, w.fmt, out=rr, ws=ws, stream=stream)
+    launch(0)
+    out["plain_fp4"] = {"rel_err": round(rel_err(rr, None), 6),
+                        "prep_us": round(back_to_back_seconds(launch, reps, stream) * 1e6, 2)}
+    return out
+
+
 def main():
     args = parse()
     if args.calibrate_copy:
@@ -375,6 +422,8 @@ def main():
                    "TFLOPS_issued": round(issued / t_lin / 1e12, 2),
                    "pct_peak_issued": round(100.0 * issued / t_lin / 1e12 / gemm_peak, 2)},
     }
+    if args.ablation:
+        out["ablation"] = ablation_report(w, x0, ws, stream, args.steps)
     if args.compare:
         wsets = [(wt,)] + [(wt.clone(),) for _ in range(nsets - 1)]
         out["comparison"] = comparison_points(w, [(s_[0], s_[1]) for s_ in sets], wsets, ws, stream,

@@ -61,7 +61,7 @@
 extern "C" {
 #endif
 
-#define SHARQ_ABI_VERSION 5
+#define SHARQ_ABI_VERSION 6
 
 typedef enum sharq_status {
   SHARQ_OK = 0,
@@ -155,6 +155,42 @@ sharq_status sharq_prep(const void* x, int64_t M, int64_t K, int64_t ldx, int sp
                         int fmt, const sharq_fp4* backbone, const sharq_fp4* residual,
                         uint8_t* mask_bits, void* workspace, size_t workspace_bytes,
                         void* stream);
+
+/* The ablations of the method's choices named by the pages' review ("What would
+ * settle it": the residual against the unquantized sparse values; the referee's
+ * third major comment on Table 2 and Section 5.1: a static mask, and direct N:M
+ * sparsity on the unquantized activations), as preparation variants:
+ *   SHARQ_ABLATE_RESIDUAL_UNQUANTIZED  residual R = X - X*mask (the dropped values
+ *                                      only: the backbone's FP4 error is left in)
+ *   SHARQ_ABLATE_STATIC_MASK           mask = the first n of every m positions for
+ *                                      every row (backbone block scales over the kept
+ *                                      values); residual against the dequantized backbone
+ *   SHARQ_ABLATE_NO_RESIDUAL           direct N:M + FP4: backbone as sharq_prep, the
+ *                                      residual payload all zero (codes 0x0, scale
+ *                                      bytes 0, NVFP4 tensor scale 1) */
+typedef enum sharq_ablation {
+  SHARQ_ABLATE_RESIDUAL_UNQUANTIZED = 1,
+  SHARQ_ABLATE_STATIC_MASK = 2,
+  SHARQ_ABLATE_NO_RESIDUAL = 3
+} sharq_ablation;
+
+/* sharq_prep with one of the ablations above (arguments, layouts, workspace and
+ * errors as for sharq_prep; a variant outside the enum -> SHARQ_E_FORMAT).  For
+ * measurement and comparison only: the method itself is sharq_prep. */
+sharq_status sharq_prep_ablation(const void* x, int64_t M, int64_t K, int64_t ldx, int sp_n, int sp_m,
+                                 int fmt, int variant, const sharq_fp4* backbone, const sharq_fp4* residual,
+                                 uint8_t* mask_bits, void* workspace, size_t workspace_bytes, void* stream);
+
+/* The values an FP4 payload encodes, as fp32: out[i * ldo + k] = E2M1(code) * 2^(E-127)
+ * (MXFP4, exact) or E2M1(code) * E4M3(scale) * tensor_scale rounded once to fp32
+ * (NVFP4; the first product is exact).  For checking reconstructions (X against
+ * Bhat + Rhat).
+ *   p        payload [rows, K] in either layout (tiled: MXFP4)
+ *   out      device fp32 [rows, ldo], ldo >= K, 4-byte aligned
+ * Errors as for sharq_quantize's shape and payload checks; out == NULL with
+ * rows > 0 -> SHARQ_E_NULL. */
+sharq_status sharq_dequantize(const sharq_fp4* p, int64_t rows, int64_t K, int fmt, float* out, int64_t ldo,
+                              void* stream);
 
 /* Bytes of device workspace sharq_prep_rmsnorm needs: the format's preparation
  * workspace plus one fp32 row factor per row (rounded up).  Host-only. */

@@ -33,7 +33,7 @@ def test_header_symbols_exported():
 
 def test_version_and_status_strings():
     L = sharq.lib()
-    assert L.sharq_abi_version() == 5
+    assert L.sharq_abi_version() == 6
     for s in range(9):
         assert L.sharq_status_str(s)
     assert L.sharq_status_str(99) == b"unknown status"
@@ -144,6 +144,37 @@ def test_linear_null_backbone_is_rejected():
     rr, w = fp4(), fp4()
     assert sharq.lib().sharq_linear(None, ctypes.byref(rr), 4, ctypes.byref(w), 8, 64, 0, A, 8, 0, None, 0,
                                     None) == E_NULL
+
+
+def test_prep_ablation_rejects():
+    L = sharq.lib()
+    bb, rr = fp4(), fp4()
+
+    def call(variant=1, fmt=0, n=2, m=4, x=A, K=64, ws=None, wsb=0):
+        return L.sharq_prep_ablation(x, 4, K, K, n, m, fmt, variant, ctypes.byref(bb), ctypes.byref(rr), None, ws,
+                                     wsb, None)
+    assert call(variant=0) == E_FORMAT     # the method itself is sharq_prep
+    assert call(variant=4) == E_FORMAT
+    assert call(n=3) == E_PATTERN
+    assert call(x=None) == E_NULL
+    assert call(K=48) == E_SHAPE
+    assert call(fmt=1) == E_WORKSPACE
+    import torch
+    if not torch.cuda.is_available():
+        for v in (1, 2, 3):
+            assert call(variant=v) == E_DEVICE
+
+
+def test_dequantize_rejects():
+    L = sharq.lib()
+    p = fp4()
+    assert L.sharq_dequantize(ctypes.byref(p), 4, 64, 0, None, 64, None) == E_NULL
+    assert L.sharq_dequantize(ctypes.byref(p), 4, 48, 0, A, 64, None) == E_SHAPE
+    assert L.sharq_dequantize(ctypes.byref(p), 4, 64, 0, A, 32, None) == E_SHAPE    # ldo < K
+    assert L.sharq_dequantize(ctypes.byref(p), 4, 64, 0, A + 2, 64, None) == E_ALIGN
+    assert L.sharq_dequantize(ctypes.byref(p), 4, 64, 3, A, 64, None) == E_FORMAT
+    q = fp4(layout=1)
+    assert L.sharq_dequantize(ctypes.byref(q), 4, 64, 1, A, 64, None) == E_FORMAT  # tiled NVFP4
 
 
 def test_clock_probe_rejects():

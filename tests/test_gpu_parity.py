@@ -362,3 +362,57 @@ def test_prep_rmsnorm_workload_full_size():
     ob, orr, _ = oracle.prep(yb, w.n, w.m, w.fmt)
     assert_payload_equal(bb, ob, "backbone")
     assert_payload_equal(rr, orr, "residual")
+
+
+# ------------------------------------------------------------------ ablations and dequantization
+
+ABLATIONS = [sharq.ABLATE_RESIDUAL_UNQUANTIZED, sharq.ABLATE_STATIC_MASK, sharq.ABLATE_NO_RESIDUAL]
+
+
+@pytest.mark.parametrize("fmt,layout", FMT_LAYOUTS, ids=FL_IDS)
+@pytest.mark.parametrize("variant", ABLATIONS)
+@pytest.mark.parametrize("n,m", [(2, 4), (4, 8)])
+@pytest.mark.parametrize("M,K,ldx_pad", [(1, 64, 0), (37, 352, 0), (300, 1024, 64)])
+def test_prep_ablation_matches_oracle(fmt, layout, variant, n, m, M, K, ldx_pad):
+    print(f"[prep_ablation] variant={variant} {n}:{m} M={M} K={K} fmt={fmt} layout={layout}", flush=True)
+    rng = np.random.default_rng(M * 7 + K + variant)
+    from activation_sparsity_fp4_sharq_amd.workloads import make_activation
+    xb = make_activation(rng, M, K, "laplace", n_out=max(1, K // 64), out_scale=20.0)
+    if ldx_pad:
+        wide = np.zeros((M, K + ldx_pad), np.uint16)
+        wide[:, :K] = xb
+        x = to_dev(wide)[:, :K]
+    else:
+        x = to_dev(xb)
+    bb, rr, mask = sharq.prep_ablation(x, variant, n, m, fmt, want_mask=True, layout=layout)
+    torch.cuda.synchronize()
+    ob, orr, omask = oracle.prep(xb, n, m, fmt, variant=variant)
+    assert np.array_equal(mask.cpu().numpy(), omask), "mask bits differ"
+    assert_payload_equal(bb, ob, "backbone")
+    assert_payload_equal(rr, orr, "residual")
+
+
+@pytest.mark.parametrize("variant", ABLATIONS)
+def test_prep_ablation_full_size_prefill(variant):
+    w = WORKLOADS["prefill"]
+    print(f"[prep_ablation] prefill variant={variant}", flush=True)
+    xb, _ = make_inputs(w)
+    bb, rr, _ = sharq.prep_ablation(to_dev(xb), variant, w.n, w.m, w.fmt)
+    torch.cuda.synchronize()
+    ob, orr, _ = oracle.prep(xb, w.n, w.m, w.fmt, variant=variant)
+    assert_payload_equal(bb, ob, "backbone")
+    assert_payload_equal(rr, orr, "residual")
+
+
+@pytest.mark.parametrize("fmt,layout", FMT_LAYOUTS, ids=FL_IDS)
+@pytest.mark.parametrize("rows,K", [(1, 32), (37, 96), (300, 1056), (64, 4096)])
+def test_dequantize_matches_oracle(fmt, layout, rows, K):
+    if fmt == sharq.NVFP4 and K % 16:
+        pytest.skip("not an NVFP4 shape")
+    print(f"[dequantize] rows={rows} K={K} fmt={fmt} layout={layout}", flush=True)
+    xb, _ = make_shape(rows, 8, K, seed=rows + K, dist="laplace", token_sigma=0.3)
+    p = sharq.quantize(to_dev(xb), fmt, layout=layout)
+    got = sharq.dequantize(p).cpu().numpy()
+    torch.cuda.synchronize()
+    want = oracle.dequant(oracle.quantize(xb, fmt), fmt).astype(np.float32)  # exact values, one rounding
+    assert np.array_equal(got, want)
