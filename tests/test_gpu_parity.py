@@ -416,3 +416,9 @@ def test_dequantize_matches_oracle(fmt, layout, rows, K):
     torch.cuda.synchronize()
     want = oracle.dequant(oracle.quantize(xb, fmt), fmt).astype(np.float32)  # exact values, one rounding
     assert np.array_equal(got, want)
+
+
+def test_clock_probe_reports_a_plausible_clock():
+    print("[clock_probe]", flush=True)
+    hz = sharq.clock_probe(20000)
+    assert 0.5e9 < hz < 3.5e9, hz
