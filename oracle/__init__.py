@@ -63,6 +63,10 @@ def lib():
         L.oracle_prep_variant.restype = ctypes.c_int
         L.oracle_prep_variant.argtypes = [_u16p, _i64, _i64, _i64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                           ctypes.c_int, _u8p, _u8p, _vp, _u8p, _u8p, _vp, _vp, _vp, _vp]
+        L.oracle_silu.restype = ctypes.c_float
+        L.oracle_silu.argtypes = [ctypes.c_float]
+        L.oracle_swiglu.restype = ctypes.c_int
+        L.oracle_swiglu.argtypes = [_u16p, _i64, _i64, _i64, _u16p]
         L.oracle_dequant.restype = ctypes.c_int
         L.oracle_dequant.argtypes = [_u8p, _u8p, ctypes.c_float, _i64, _i64, ctypes.c_int, _f64p]
         L.oracle_linear.restype = ctypes.c_int
@@ -107,6 +111,22 @@ def quantize(x_bits, fmt=MXFP4):
     if rc:
         raise ValueError(f"oracle_quantize rejected shape {x_bits.shape} fmt {fmt}")
     return Payload(codes, scales, ts[0])
+
+
+def silu(g):
+    """silu(g) in fp32 by reading R14 (scalar)."""
+    return float(lib().oracle_silu(float(g)))
+
+
+def swiglu(gate_up_bits, I):
+    """bf16 h [M, I] = bf16(fp32(silu(gate) * up)) of gate_up [M, ld >= 2I] (gate in
+    columns [0, I), up in [I, 2I)), reading R14."""
+    gu = np.ascontiguousarray(gate_up_bits, dtype=np.uint16)
+    M, ld = gu.shape
+    h = np.zeros((M, I), np.uint16)
+    if lib().oracle_swiglu(gu, M, I, ld, h):
+        raise ValueError("oracle_swiglu rejected its arguments")
+    return h
 
 
 def rmsnorm(x_bits, gamma_bits, eps):

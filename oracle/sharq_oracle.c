@@ -45,6 +45,16 @@
  *      block maximum then taken over the kept values as R2 already states; variant
  *      3 = direct N:M without residual, R = 0 everywhere (so its payload is code 0x0,
  *      E = -127, and for NVFP4 a tensor scale of 1 by R5).
+ *   R14 SwiGLU between an MLP block's gate/up and down projections (the second
+ *      workload of the benchmark; the pages name Llama-3.1-8B's layers but give no
+ *      arithmetic for them): h = bf16_rne(fp32(silu(g) * u)), silu(g) = fp32(g /
+ *      fp32(1 + e)), e = exp(-g) in fp32 by Cody and Waite's range reduction
+ *      (Software Manual for the Elementary Functions, 1980): t = -g clamped to
+ *      [-150, 150], n = rint(fp32(t * log2 e)), r = fp32(fp32(t - n * ln2_hi) -
+ *      n * ln2_lo) with ln2_hi = 0x1.62e4p-1 (15 bits, so n * ln2_hi is exact) and
+ *      ln2_lo = fp32(ln 2 - ln2_hi), p = the degree-7 Taylor polynomial of e^r in
+ *      Horner form with fp32(1/k!) coefficients, e = p * 2^n.  Every operation is one
+ *      fp32 rounding, in this order, with no contraction.
  *   R9 normalization absorbed by the preparation ("Core claim" and abstract: the
  *      fused preparation also takes over the layer normalization): RMS normalization
  *      with a per-channel bf16 gain g and no bias, producing the bf16 tensor the
@@ -296,6 +306,47 @@ int oracle_rmsnorm(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, const u
       y[i * K + k] = f32_to_bf16(u);
     }
   }
+  return 0;
+}
+
+/* R14: e^(-g) and silu(g) in fp32. */
+static float swiglu_exp_neg(float g) {
+  float t = -g;
+  if (t > 150.0f) t = 150.0f;
+  if (t < -150.0f) t = -150.0f;
+  const float log2e = 0x1.715476p+0f;   /* fp32(log2(e)) */
+  const float ln2_hi = 0x1.62e4p-1f;    /* ln 2 to 15 significant bits */
+  const float ln2_lo = 0x1.7f7d1cp-20f; /* fp32(ln 2 - ln2_hi) */
+  const float n = rintf(t * log2e);
+  const float r = (t - n * ln2_hi) - n * ln2_lo;
+  /* e^r = sum_k r^k / k!, k = 0..7 */
+  float p = 0x1.a01a02p-13f;            /* 1/5040 */
+  p = p * r + 0x1.6c16c2p-10f;          /* 1/720 */
+  p = p * r + 0x1.111112p-7f;           /* 1/120 */
+  p = p * r + 0x1.555556p-5f;           /* 1/24 */
+  p = p * r + 0x1.555556p-3f;           /* 1/6 */
+  p = p * r + 0.5f;
+  p = p * r + 1.0f;
+  p = p * r + 1.0f;
+  return ldexpf(p, (int)n);
+}
+
+float oracle_silu(float g) {
+  const float d = 1.0f + swiglu_exp_neg(g);
+  return g / d;
+}
+
+/* R14: gate_up bf16 [M, ld] holds gate in columns [0, I) and up in [I, 2I) of each
+ * row; h bf16 [M, I] = bf16_rne(fp32(silu(gate) * up)). */
+int oracle_swiglu(const uint16_t* gu, int64_t M, int64_t I, int64_t ld, uint16_t* h) {
+  if (M < 0 || I <= 0 || ld < 2 * I) return -1;
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < M; ++i)
+    for (int64_t k = 0; k < I; ++k) {
+      const float g = bf16_to_f32(gu[i * ld + k]);
+      const float u = bf16_to_f32(gu[i * ld + I + k]);
+      h[i * I + k] = f32_to_bf16(oracle_silu(g) * u);
+    }
   return 0;
 }
 

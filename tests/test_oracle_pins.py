@@ -636,3 +636,46 @@ def test_ablations_reconstruct_worse_than_the_method(name):
         assert e0 < err(v), (name, v)
     assert e0 < plain
 
+
+# ------------------------------------------------------------ SwiGLU (R14)
+
+def test_silu_matches_the_mathematics_over_every_bf16_in_range():
+    """Every finite bf16 g with |g| <= 100: fp32 silu within 4 fp32 ulps of silu computed in
+    fp64 from math.exp (the reading fixes the fp32 algorithm; this bounds its error)."""
+    import math
+    bits = np.arange(0, 1 << 16, dtype=np.uint32).astype(np.uint16)
+    with np.errstate(invalid="ignore"):
+        g = bf16_bits_to_f32(bits).astype(np.float64)
+    g = g[np.isfinite(g) & (np.abs(g) <= 100.0)]
+    got = np.array([oracle.silu(v) for v in g[::7]], np.float64)
+    ref = np.array([v / (1.0 + math.exp(-v)) for v in g[::7]])
+    ulp = np.spacing(np.abs(ref).astype(np.float32)).astype(np.float64)
+    tiny = np.abs(ref) < 1e-30
+    assert np.all(np.abs(got - ref)[~tiny] <= 4 * ulp[~tiny])
+
+
+def test_silu_closed_forms():
+    assert oracle.silu(0.0) == 0.0
+    for g in (150.0, 1000.0, 3.0e38):
+        assert oracle.silu(g) == np.float32(g)           # e^-g underflows to 0
+    for g in (-150.0, -1000.0):
+        assert oracle.silu(g) == 0.0                     # e^-g overflows: -0
+    # silu(g) - silu(-g) = g (the logistic's symmetry), up to fp32 rounding
+    for g in (0.5, 1.25, 3.0, 7.5):
+        assert abs(oracle.silu(g) - oracle.silu(-g) - g) <= 4 * np.spacing(np.float32(g))
+
+
+def test_swiglu_layout_and_special_inputs():
+    rng = np.random.default_rng(40)
+    M, I = 3, 64
+    g = rng.normal(0, 3, (M, I)).astype(np.float32)
+    gu = np.zeros((M, 2 * I + 16), np.uint16)           # padded rows: ld > 2I
+    gu[:, :I] = f32_to_bf16_bits(g)
+    gu[:, I:2 * I] = f32_to_bf16_bits(np.ones((M, I), np.float32))  # up = 1
+    h = oracle.swiglu(gu, I)
+    want = np.array([[oracle.silu(v) for v in row] for row in bf16_bits_to_f32(gu[:, :I])], np.float32)
+    assert np.array_equal(h, f32_to_bf16_bits(want))
+    gu[:, I:2 * I] = 0                                   # up = +0: h = +-0
+    h0 = bf16_bits_to_f32(oracle.swiglu(gu, I))
+    assert np.all(h0 == 0.0)
+
