@@ -94,5 +94,40 @@ __device__ __forceinline__ uint32_t rms_scale_pair(uint32_t w, uint32_t gw, floa
   return bf16_rne_bits(y0) | (bf16_rne_bits(y1) << 16);
 }
 
+// Input transforms the preparation kernels can apply to the loaded bf16 values.
+constexpr int kXfNone = 0;    // X as given
+constexpr int kXfRms = 1;     // RMS normalization with a bf16 gain (rms_scale_pair)
+constexpr int kXfSwiglu = 2;  // SwiGLU of a gate/up pair (swiglu_pair)
+
+// SwiGLU: h = bf16(fp32(silu(g) * u)), silu(g) = fp32(g / fp32(1 + e)), e = e^-g in
+// fp32 by Cody and Waite's range reduction (t = -g clamped to [-150, 150],
+// n = rint(t log2 e), r = (t - n ln2_hi) - n ln2_lo with a 15-bit ln2_hi so that
+// n ln2_hi is exact) and the degree-7 Taylor polynomial of e^r, scaled by 2^n.  Every
+// operation is one rounding in a fixed order, so the value is reproducible bit for bit.
+__device__ __forceinline__ float silu_f32(float g) {
+  float t = -g;
+  t = t > 150.0f ? 150.0f : t;
+  t = t < -150.0f ? -150.0f : t;
+  const float n = __builtin_rintf(__fmul_rn(t, 0x1.715476p+0f));
+  const float r = __fsub_rn(__fsub_rn(t, __fmul_rn(n, 0x1.62e4p-1f)), __fmul_rn(n, 0x1.7f7d1cp-20f));
+  float p = 0x1.a01a02p-13f;                        // 1/7!
+  p = __fadd_rn(__fmul_rn(p, r), 0x1.6c16c2p-10f);  // 1/6!
+  p = __fadd_rn(__fmul_rn(p, r), 0x1.111112p-7f);   // 1/5!
+  p = __fadd_rn(__fmul_rn(p, r), 0x1.555556p-5f);   // 1/4!
+  p = __fadd_rn(__fmul_rn(p, r), 0x1.555556p-3f);   // 1/3!
+  p = __fadd_rn(__fmul_rn(p, r), 0.5f);
+  p = __fadd_rn(__fmul_rn(p, r), 1.0f);
+  p = __fadd_rn(__fmul_rn(p, r), 1.0f);
+  const float e = ldexpf(p, (int)n);
+  return __fdiv_rn(g, __fadd_rn(1.0f, e));
+}
+
+// Two bf16 gates and two bf16 ups (packed) -> two bf16 SwiGLU values (packed).
+__device__ __forceinline__ uint32_t swiglu_pair(uint32_t gw, uint32_t uw) {
+  const float h0 = __fmul_rn(silu_f32(__uint_as_float(gw << 16)), __uint_as_float(uw << 16));
+  const float h1 = __fmul_rn(silu_f32(__uint_as_float(gw & 0xFFFF0000u)), __uint_as_float(uw & 0xFFFF0000u));
+  return bf16_rne_bits(h0) | (bf16_rne_bits(h1) << 16);
+}
+
 }  // namespace codec
 }  // namespace sharq

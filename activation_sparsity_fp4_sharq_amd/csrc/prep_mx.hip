@@ -165,12 +165,16 @@ __device__ __forceinline__ void codec_block(const uint32_t w[4], uint32_t& keep,
   rpacked = quant8(r, __uint_as_float(rsb));
 }
 
-// Optional RMS normalization applied to the loaded bf16 values (NORM): per-row
+// Optional RMS normalization applied to the loaded bf16 values (XF == kXfRms): per-row
 // factors r[M] and per-channel bf16 gains g[K] (see rms_scale_pair).
 struct Norm {
   const float* r;
   const uint16_t* g;
 };
+
+__device__ __forceinline__ u32x4 swiglu8(const u32x4& g, const u32x4& u) {
+  return u32x4{swiglu_pair(g[0], u[0]), swiglu_pair(g[1], u[1]), swiglu_pair(g[2], u[2]), swiglu_pair(g[3], u[3])};
+}
 
 __device__ __forceinline__ u32x4 rms_scale8(const u32x4& v, const Norm& nm, int64_t row, int64_t col) {
   const float r = nm.r[row];
@@ -182,7 +186,7 @@ __device__ __forceinline__ u32x4 rms_scale8(const u32x4& v, const Norm& nm, int6
 // MODE 0: SharQ preparation (mask, backbone, residual).  MODE 1: plain MXFP4
 // quantization of X into (rcodes, rscales) -- used for weight payloads.  MODEs 2-4:
 // the ablations (see codec_block).
-template <int MODE, int SPM, bool DENSE_ROWS, bool WRITE_MASK, bool NORM>
+template <int MODE, int SPM, bool DENSE_ROWS, bool WRITE_MASK, int XF>
 __global__ __launch_bounds__(kThreads) void prep_mx_kernel(
     const uint16_t* __restrict__ x, int64_t ldx, int64_t nbk, int64_t nblocks,
     uint8_t* __restrict__ bcodes, uint8_t* __restrict__ bscales, uint8_t* __restrict__ rcodes,
@@ -206,7 +210,10 @@ __global__ __launch_bounds__(kThreads) void prep_mx_kernel(
         off = row * ldx + (b - row * nbk) * 32 + q * 8;
       }
       v[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(x + off));
-      if constexpr (NORM) {
+      if constexpr (XF == kXfSwiglu) {  // gate at off, up K columns further in the same row
+        v[u] = swiglu8(v[u], __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(x + off + nbk * 32)));
+      }
+      if constexpr (XF == kXfRms) {
         const int64_t row = b / nbk;
         v[u] = rms_scale8(v[u], nm, row, (b - row * nbk) * 32 + q * 8);
       }
@@ -248,7 +255,7 @@ __global__ __launch_bounds__(kThreads) void prep_mx_kernel(
 // contiguous bytes.  Rows >= M and blocks >= K/32 are processed as zeros, which
 // writes the layout's zero padding.  The grid is (K-step groups of 4, row groups):
 // a work-group's 4 waves take 4 consecutive K-steps of the same 16 rows.
-template <int MODE, int SPM, bool WRITE_MASK, bool NORM>
+template <int MODE, int SPM, bool WRITE_MASK, int XF>
 __global__ __launch_bounds__(kThreads) void prep_mx_tiled_kernel(
     const uint16_t* __restrict__ x, int64_t M, int64_t K, int64_t ldx, int64_t Mp, int64_t Kp,
     int64_t rg0, uint8_t* __restrict__ bcodes, uint8_t* __restrict__ bscales,
@@ -271,7 +278,9 @@ __global__ __launch_bounds__(kThreads) void prep_mx_tiled_kernel(
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       v[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(xrow + lane_off + u * 32));
-      if constexpr (NORM) v[u] = rms_scale8(v[u], nm, r, ks * 128 + u * 32 + q * 8);
+      if constexpr (XF == kXfSwiglu)
+        v[u] = swiglu8(v[u], __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(xrow + lane_off + u * 32 + K)));
+      if constexpr (XF == kXfRms) v[u] = rms_scale8(v[u], nm, r, ks * 128 + u * 32 + q * 8);
     }
   } else {
 #pragma unroll
@@ -279,7 +288,9 @@ __global__ __launch_bounds__(kThreads) void prep_mx_tiled_kernel(
       v[u] = u32x4{0u, 0u, 0u, 0u};
       if (r < M && ks * 4 + u < nbk) {
         v[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(xrow + lane_off + u * 32));
-        if constexpr (NORM) v[u] = rms_scale8(v[u], nm, r, ks * 128 + u * 32 + q * 8);
+        if constexpr (XF == kXfSwiglu)
+          v[u] = swiglu8(v[u], __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(xrow + lane_off + u * 32 + K)));
+        if constexpr (XF == kXfRms) v[u] = rms_scale8(v[u], nm, r, ks * 128 + u * 32 + q * 8);
       }
     }
   }
@@ -320,7 +331,7 @@ __global__ __launch_bounds__(kThreads) void prep_mx_tiled_kernel(
   }
 }
 
-template <int MODE, int SPM, bool WRITE_MASK, bool NORM>
+template <int MODE, int SPM, bool WRITE_MASK, int XF>
 hipError_t launch_tiled(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, uint8_t* bcodes,
                         uint8_t* bscales, uint8_t* rcodes, uint8_t* rscales, uint8_t* mask, Norm nm,
                         hipStream_t stream) {
@@ -331,7 +342,7 @@ hipError_t launch_tiled(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, ui
   constexpr int64_t kMaxGridY = 65535;
   for (int64_t rg0 = 0; rg0 < nrg; rg0 += kMaxGridY) {
     const int64_t gy = nrg - rg0 < kMaxGridY ? nrg - rg0 : kMaxGridY;
-    prep_mx_tiled_kernel<MODE, SPM, WRITE_MASK, NORM><<<dim3((unsigned)gx, (unsigned)gy), dim3(kThreads), 0, stream>>>(
+    prep_mx_tiled_kernel<MODE, SPM, WRITE_MASK, XF><<<dim3((unsigned)gx, (unsigned)gy), dim3(kThreads), 0, stream>>>(
         x, M, K, ldx, Mp, Kp, rg0, bcodes, bscales, rcodes, rscales, mask, nm);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -339,7 +350,7 @@ hipError_t launch_tiled(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, ui
   return hipSuccess;
 }
 
-template <int MODE, int SPM, bool WRITE_MASK, bool NORM>
+template <int MODE, int SPM, bool WRITE_MASK, int XF>
 hipError_t launch_dense_or_strided(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
                                    uint8_t* bcodes, uint8_t* bscales, uint8_t* rcodes,
                                    uint8_t* rscales, uint8_t* mask, Norm nm, hipStream_t stream) {
@@ -349,22 +360,22 @@ hipError_t launch_dense_or_strided(const uint16_t* x, int64_t M, int64_t K, int6
   const int64_t per_wg = (kThreads / 64) * kBlocksPerWave * kUnroll;
   const int64_t grid = (nblocks + per_wg - 1) / per_wg;
   if (ldx == K)
-    prep_mx_kernel<MODE, SPM, true, WRITE_MASK, NORM><<<dim3((unsigned)grid), dim3(kThreads), 0, stream>>>(
+    prep_mx_kernel<MODE, SPM, true, WRITE_MASK, XF><<<dim3((unsigned)grid), dim3(kThreads), 0, stream>>>(
         x, ldx, nbk, nblocks, bcodes, bscales, rcodes, rscales, mask, nm);
   else
-    prep_mx_kernel<MODE, SPM, false, WRITE_MASK, NORM><<<dim3((unsigned)grid), dim3(kThreads), 0, stream>>>(
+    prep_mx_kernel<MODE, SPM, false, WRITE_MASK, XF><<<dim3((unsigned)grid), dim3(kThreads), 0, stream>>>(
         x, ldx, nbk, nblocks, bcodes, bscales, rcodes, rscales, mask, nm);
   return hipGetLastError();
 }
 
 
 // Dispatch over the compile-time variants: pattern, mask output, normalization, layout.
-template <int MODE, int SPM, bool WRITE_MASK, bool NORM>
+template <int MODE, int SPM, bool WRITE_MASK, int XF>
 hipError_t prep_variant(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, uint8_t* bcodes, uint8_t* bscales,
                         uint8_t* rcodes, uint8_t* rscales, uint8_t* mask, Norm nm, int tiled, hipStream_t stream) {
   if (tiled)
-    return launch_tiled<MODE, SPM, WRITE_MASK, NORM>(x, M, K, ldx, bcodes, bscales, rcodes, rscales, mask, nm, stream);
-  return launch_dense_or_strided<MODE, SPM, WRITE_MASK, NORM>(x, M, K, ldx, bcodes, bscales, rcodes, rscales, mask,
+    return launch_tiled<MODE, SPM, WRITE_MASK, XF>(x, M, K, ldx, bcodes, bscales, rcodes, rscales, mask, nm, stream);
+  return launch_dense_or_strided<MODE, SPM, WRITE_MASK, XF>(x, M, K, ldx, bcodes, bscales, rcodes, rscales, mask,
                                                               nm, stream);
 }
 
@@ -376,38 +387,42 @@ hipError_t prep_ablation(int variant, const uint16_t* x, int64_t M, int64_t K, i
   const Norm none{nullptr, nullptr};
   switch (variant) {
     case SHARQ_ABLATE_RESIDUAL_UNQUANTIZED:
-      return mask ? prep_variant<2, SPM, true, false>(x, M, K, ldx, bcodes, bscales, rcodes, rscales, mask, none, tiled, stream)
-                  : prep_variant<2, SPM, false, false>(x, M, K, ldx, bcodes, bscales, rcodes, rscales, mask, none, tiled, stream);
+      return mask ? prep_variant<2, SPM, true, kXfNone>(x, M, K, ldx, bcodes, bscales, rcodes, rscales, mask, none, tiled, stream)
+                  : prep_variant<2, SPM, false, kXfNone>(x, M, K, ldx, bcodes, bscales, rcodes, rscales, mask, none, tiled, stream);
     case SHARQ_ABLATE_STATIC_MASK:
-      return mask ? prep_variant<3, SPM, true, false>(x, M, K, ldx, bcodes, bscales, rcodes, rscales, mask, none, tiled, stream)
-                  : prep_variant<3, SPM, false, false>(x, M, K, ldx, bcodes, bscales, rcodes, rscales, mask, none, tiled, stream);
+      return mask ? prep_variant<3, SPM, true, kXfNone>(x, M, K, ldx, bcodes, bscales, rcodes, rscales, mask, none, tiled, stream)
+                  : prep_variant<3, SPM, false, kXfNone>(x, M, K, ldx, bcodes, bscales, rcodes, rscales, mask, none, tiled, stream);
     default:  // SHARQ_ABLATE_NO_RESIDUAL
-      return mask ? prep_variant<4, SPM, true, false>(x, M, K, ldx, bcodes, bscales, rcodes, rscales, mask, none, tiled, stream)
-                  : prep_variant<4, SPM, false, false>(x, M, K, ldx, bcodes, bscales, rcodes, rscales, mask, none, tiled, stream);
+      return mask ? prep_variant<4, SPM, true, kXfNone>(x, M, K, ldx, bcodes, bscales, rcodes, rscales, mask, none, tiled, stream)
+                  : prep_variant<4, SPM, false, kXfNone>(x, M, K, ldx, bcodes, bscales, rcodes, rscales, mask, none, tiled, stream);
   }
 }
 
 template <int SPM>
 hipError_t prep_pattern(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, uint8_t* bcodes, uint8_t* bscales,
-                        uint8_t* rcodes, uint8_t* rscales, uint8_t* mask, Norm nm, int tiled, hipStream_t stream) {
-  if (nm.r) {
-    return mask ? prep_variant<0, SPM, true, true>(x, M, K, ldx, bcodes, bscales, rcodes, rscales, mask, nm, tiled, stream)
-                : prep_variant<0, SPM, false, true>(x, M, K, ldx, bcodes, bscales, rcodes, rscales, mask, nm, tiled, stream);
-  }
-  return mask ? prep_variant<0, SPM, true, false>(x, M, K, ldx, bcodes, bscales, rcodes, rscales, mask, nm, tiled, stream)
-              : prep_variant<0, SPM, false, false>(x, M, K, ldx, bcodes, bscales, rcodes, rscales, mask, nm, tiled, stream);
+                        uint8_t* rcodes, uint8_t* rscales, uint8_t* mask, Norm nm, int xf, int tiled,
+                        hipStream_t stream) {
+  if (xf == kXfRms)
+    return mask ? prep_variant<0, SPM, true, kXfRms>(x, M, K, ldx, bcodes, bscales, rcodes, rscales, mask, nm, tiled, stream)
+                : prep_variant<0, SPM, false, kXfRms>(x, M, K, ldx, bcodes, bscales, rcodes, rscales, mask, nm, tiled, stream);
+  if (xf == kXfSwiglu)
+    return mask ? prep_variant<0, SPM, true, kXfSwiglu>(x, M, K, ldx, bcodes, bscales, rcodes, rscales, mask, nm, tiled, stream)
+                : prep_variant<0, SPM, false, kXfSwiglu>(x, M, K, ldx, bcodes, bscales, rcodes, rscales, mask, nm, tiled, stream);
+  return mask ? prep_variant<0, SPM, true, kXfNone>(x, M, K, ldx, bcodes, bscales, rcodes, rscales, mask, nm, tiled, stream)
+              : prep_variant<0, SPM, false, kXfNone>(x, M, K, ldx, bcodes, bscales, rcodes, rscales, mask, nm, tiled, stream);
 }
 
 }  // namespace
 
 hipError_t launch_prep_mx(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, int sp_n, int sp_m,
                           uint8_t* bcodes, uint8_t* bscales, uint8_t* rcodes, uint8_t* rscales,
-                          uint8_t* mask, const float* rnorm, const uint16_t* gamma, int tiled,
+                          uint8_t* mask, const float* rnorm, const uint16_t* gamma, int swiglu, int tiled,
                           hipStream_t stream) {
   (void)sp_n;  // n = m/2 for both supported patterns
   const Norm nm{rnorm, gamma};
-  if (sp_m == 4) return prep_pattern<4>(x, M, K, ldx, bcodes, bscales, rcodes, rscales, mask, nm, tiled, stream);
-  return prep_pattern<8>(x, M, K, ldx, bcodes, bscales, rcodes, rscales, mask, nm, tiled, stream);
+  const int xf = swiglu ? kXfSwiglu : rnorm ? kXfRms : kXfNone;
+  if (sp_m == 4) return prep_pattern<4>(x, M, K, ldx, bcodes, bscales, rcodes, rscales, mask, nm, xf, tiled, stream);
+  return prep_pattern<8>(x, M, K, ldx, bcodes, bscales, rcodes, rscales, mask, nm, xf, tiled, stream);
 }
 
 hipError_t launch_prep_mx_ablation(int variant, const uint16_t* x, int64_t M, int64_t K, int64_t ldx, int sp_m,
@@ -421,8 +436,8 @@ hipError_t launch_quant_mx(const uint16_t* x, int64_t rows, int64_t K, int64_t l
                            uint8_t* scales, int tiled, hipStream_t stream) {
   const Norm none{nullptr, nullptr};
   if (tiled)
-    return launch_tiled<1, 4, false, false>(x, rows, K, ldx, nullptr, nullptr, codes, scales, nullptr, none, stream);
-  return launch_dense_or_strided<1, 4, false, false>(x, rows, K, ldx, nullptr, nullptr, codes, scales, nullptr, none,
+    return launch_tiled<1, 4, false, kXfNone>(x, rows, K, ldx, nullptr, nullptr, codes, scales, nullptr, none, stream);
+  return launch_dense_or_strided<1, 4, false, kXfNone>(x, rows, K, ldx, nullptr, nullptr, codes, scales, nullptr, none,
                                                      stream);
 }
 

@@ -205,7 +205,7 @@ __device__ __forceinline__ void static_mask(bool kept[8]) {
   for (int j = 0; j < 8; ++j) kept[j] = (j % SPM) < SPM / 2;
 }
 
-template <int PASS, int MODE, int SPM, bool DENSE_ROWS, bool WRITE_MASK, bool NORM>
+template <int PASS, int MODE, int SPM, bool DENSE_ROWS, bool WRITE_MASK, int XF>
 __global__ __launch_bounds__(kThreads) void prep_nv_kernel(
     const uint16_t* __restrict__ x, int64_t ldx, int64_t chunks_per_row, int64_t nchunks,
     uint8_t* __restrict__ bcodes, uint8_t* __restrict__ bscales, uint8_t* __restrict__ rcodes,
@@ -248,7 +248,12 @@ __global__ __launch_bounds__(kThreads) void prep_nv_kernel(
           off = row * ldx + (c - row * chunks_per_row) * 8;
         }
         v[u] = *reinterpret_cast<const u32x4*>(x + off);
-        if constexpr (NORM) {
+        if constexpr (XF == kXfSwiglu) {  // gate at off, up K columns further in the same row
+          const u32x4 up = *reinterpret_cast<const u32x4*>(x + off + chunks_per_row * 8);
+          v[u] = u32x4{swiglu_pair(v[u][0], up[0]), swiglu_pair(v[u][1], up[1]), swiglu_pair(v[u][2], up[2]),
+                       swiglu_pair(v[u][3], up[3])};
+        }
+        if constexpr (XF == kXfRms) {
           // RMS normalization folded in: bf16(fp32(fp32(x * r_row) * g_col))
           const int64_t row = c / chunks_per_row;
           const float rr = rnorm[row];
@@ -392,27 +397,27 @@ __global__ void nv_empty_kernel(uint32_t* work, float* t0, float* t1) {
   }
 }
 
-template <int MODE, int SPM, bool DENSE, bool WRITE_MASK, bool NORM>
+template <int MODE, int SPM, bool DENSE, bool WRITE_MASK, int XF>
 hipError_t run_passes(const uint16_t* x, int64_t ldx, int64_t cpr, int64_t nchunks, uint8_t* bcodes,
                       uint8_t* bscales, float* bts, uint8_t* rcodes, uint8_t* rscales, float* rts, uint8_t* mask,
                       uint32_t* work, const float* rnorm, const uint16_t* gamma, hipStream_t st) {
   const int64_t per_wg = (kThreads / 64) * 64 * kUnroll;
   const int64_t grid = (nchunks + per_wg - 1) / per_wg;
   const unsigned rgrid = (unsigned)(grid < kMaxGroups ? grid : kMaxGroups);
-  prep_nv_kernel<0, MODE, SPM, DENSE, WRITE_MASK, NORM><<<dim3(rgrid), kThreads, 0, st>>>(
+  prep_nv_kernel<0, MODE, SPM, DENSE, WRITE_MASK, XF><<<dim3(rgrid), kThreads, 0, st>>>(
       x, ldx, cpr, nchunks, bcodes, bscales, rcodes, rscales, mask, work, bts, rts, rnorm, gamma);
   nv_reduce_kernel<<<1, 256, 0, st>>>(work, 0, (int)rgrid);
   if constexpr (MODE != 1) {
-    prep_nv_kernel<1, MODE, SPM, DENSE, WRITE_MASK, NORM><<<dim3(rgrid), kThreads, 0, st>>>(
+    prep_nv_kernel<1, MODE, SPM, DENSE, WRITE_MASK, XF><<<dim3(rgrid), kThreads, 0, st>>>(
         x, ldx, cpr, nchunks, bcodes, bscales, rcodes, rscales, mask, work, bts, rts, rnorm, gamma);
     nv_reduce_kernel<<<1, 256, 0, st>>>(work, 1, (int)rgrid);
   }
-  prep_nv_kernel<2, MODE, SPM, DENSE, WRITE_MASK, NORM><<<dim3((unsigned)grid), kThreads, 0, st>>>(
+  prep_nv_kernel<2, MODE, SPM, DENSE, WRITE_MASK, XF><<<dim3((unsigned)grid), kThreads, 0, st>>>(
       x, ldx, cpr, nchunks, bcodes, bscales, rcodes, rscales, mask, work, bts, rts, rnorm, gamma);
   return hipGetLastError();
 }
 
-template <int MODE, int SPM, bool WRITE_MASK, bool NORM>
+template <int MODE, int SPM, bool WRITE_MASK, int XF>
 hipError_t run_nv(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, uint8_t* bcodes, uint8_t* bscales,
                   float* bts, uint8_t* rcodes, uint8_t* rscales, float* rts, uint8_t* mask, uint32_t* work,
                   const float* rnorm, const uint16_t* gamma, hipStream_t st) {
@@ -422,21 +427,24 @@ hipError_t run_nv(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, uint8_t*
     nv_empty_kernel<<<1, 64, 0, st>>>(work, bts, rts);
     return hipGetLastError();
   }
-  return ldx == K ? run_passes<MODE, SPM, true, WRITE_MASK, NORM>(x, ldx, cpr, nchunks, bcodes, bscales, bts, rcodes,
+  return ldx == K ? run_passes<MODE, SPM, true, WRITE_MASK, XF>(x, ldx, cpr, nchunks, bcodes, bscales, bts, rcodes,
                                                                   rscales, rts, mask, work, rnorm, gamma, st)
-                  : run_passes<MODE, SPM, false, WRITE_MASK, NORM>(x, ldx, cpr, nchunks, bcodes, bscales, bts,
+                  : run_passes<MODE, SPM, false, WRITE_MASK, XF>(x, ldx, cpr, nchunks, bcodes, bscales, bts,
                                                                    rcodes, rscales, rts, mask, work, rnorm, gamma, st);
 }
 
 template <int SPM, bool WRITE_MASK>
 hipError_t run_prep(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, uint8_t* bcodes, uint8_t* bscales,
                     float* bts, uint8_t* rcodes, uint8_t* rscales, float* rts, uint8_t* mask, uint32_t* work,
-                    const float* rnorm, const uint16_t* gamma, hipStream_t st) {
-  if (rnorm)
-    return run_nv<0, SPM, WRITE_MASK, true>(x, M, K, ldx, bcodes, bscales, bts, rcodes, rscales, rts, mask, work,
-                                            rnorm, gamma, st);
-  return run_nv<0, SPM, WRITE_MASK, false>(x, M, K, ldx, bcodes, bscales, bts, rcodes, rscales, rts, mask, work,
-                                           nullptr, nullptr, st);
+                    const float* rnorm, const uint16_t* gamma, int xf, hipStream_t st) {
+  if (xf == kXfRms)
+    return run_nv<0, SPM, WRITE_MASK, kXfRms>(x, M, K, ldx, bcodes, bscales, bts, rcodes, rscales, rts, mask, work,
+                                              rnorm, gamma, st);
+  if (xf == kXfSwiglu)
+    return run_nv<0, SPM, WRITE_MASK, kXfSwiglu>(x, M, K, ldx, bcodes, bscales, bts, rcodes, rscales, rts, mask,
+                                                 work, nullptr, nullptr, st);
+  return run_nv<0, SPM, WRITE_MASK, kXfNone>(x, M, K, ldx, bcodes, bscales, bts, rcodes, rscales, rts, mask, work,
+                                             nullptr, nullptr, st);
 }
 
 }  // namespace
@@ -444,35 +452,39 @@ hipError_t run_prep(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, uint8_
 hipError_t launch_prep_nv(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, int sp_n, int sp_m,
                           uint8_t* bcodes, uint8_t* bscales, float* btscale, uint8_t* rcodes,
                           uint8_t* rscales, float* rtscale, uint8_t* mask, uint32_t* work,
-                          const float* rnorm, const uint16_t* gamma, hipStream_t stream) {
+                          const float* rnorm, const uint16_t* gamma, int swiglu, hipStream_t stream) {
   (void)sp_n;
+  const int xf = swiglu ? kXfSwiglu : rnorm ? kXfRms : kXfNone;
   if (sp_m == 4)
     return mask ? run_prep<4, true>(x, M, K, ldx, bcodes, bscales, btscale, rcodes, rscales, rtscale, mask, work,
-                                    rnorm, gamma, stream)
+                                    rnorm, gamma, xf, stream)
                 : run_prep<4, false>(x, M, K, ldx, bcodes, bscales, btscale, rcodes, rscales, rtscale, mask, work,
-                                     rnorm, gamma, stream);
+                                     rnorm, gamma, xf, stream);
   return mask ? run_prep<8, true>(x, M, K, ldx, bcodes, bscales, btscale, rcodes, rscales, rtscale, mask, work,
-                                  rnorm, gamma, stream)
+                                  rnorm, gamma, xf, stream)
               : run_prep<8, false>(x, M, K, ldx, bcodes, bscales, btscale, rcodes, rscales, rtscale, mask, work,
-                                   rnorm, gamma, stream);
+                                   rnorm, gamma, xf, stream);
 }
 
+namespace {
 template <int SPM, bool WRITE_MASK>
 hipError_t run_ablation(int variant, const uint16_t* x, int64_t M, int64_t K, int64_t ldx, uint8_t* bcodes,
                         uint8_t* bscales, float* bts, uint8_t* rcodes, uint8_t* rscales, float* rts, uint8_t* mask,
                         uint32_t* work, hipStream_t st) {
   switch (variant) {
     case SHARQ_ABLATE_RESIDUAL_UNQUANTIZED:
-      return run_nv<2, SPM, WRITE_MASK, false>(x, M, K, ldx, bcodes, bscales, bts, rcodes, rscales, rts, mask, work,
+      return run_nv<2, SPM, WRITE_MASK, kXfNone>(x, M, K, ldx, bcodes, bscales, bts, rcodes, rscales, rts, mask, work,
                                                nullptr, nullptr, st);
     case SHARQ_ABLATE_STATIC_MASK:
-      return run_nv<3, SPM, WRITE_MASK, false>(x, M, K, ldx, bcodes, bscales, bts, rcodes, rscales, rts, mask, work,
+      return run_nv<3, SPM, WRITE_MASK, kXfNone>(x, M, K, ldx, bcodes, bscales, bts, rcodes, rscales, rts, mask, work,
                                                nullptr, nullptr, st);
     default:  // SHARQ_ABLATE_NO_RESIDUAL
-      return run_nv<4, SPM, WRITE_MASK, false>(x, M, K, ldx, bcodes, bscales, bts, rcodes, rscales, rts, mask, work,
+      return run_nv<4, SPM, WRITE_MASK, kXfNone>(x, M, K, ldx, bcodes, bscales, bts, rcodes, rscales, rts, mask, work,
                                                nullptr, nullptr, st);
   }
 }
+
+}  // namespace
 
 hipError_t launch_prep_nv_ablation(int variant, const uint16_t* x, int64_t M, int64_t K, int64_t ldx, int sp_m,
                                    uint8_t* bcodes, uint8_t* bscales, float* btscale, uint8_t* rcodes,
@@ -491,7 +503,7 @@ hipError_t launch_prep_nv_ablation(int variant, const uint16_t* x, int64_t M, in
 
 hipError_t launch_quant_nv(const uint16_t* x, int64_t rows, int64_t K, int64_t ldx, uint8_t* codes,
                            uint8_t* scales, float* tscale, uint32_t* work, hipStream_t stream) {
-  return run_nv<1, 4, false, false>(x, rows, K, ldx, nullptr, nullptr, tscale, codes, scales, nullptr, nullptr,
+  return run_nv<1, 4, false, kXfNone>(x, rows, K, ldx, nullptr, nullptr, tscale, codes, scales, nullptr, nullptr,
                                     work, nullptr, nullptr, stream);
 }
 

@@ -66,13 +66,14 @@ sharq_status launched(hipError_t e) { return e == hipSuccess ? SHARQ_OK : SHARQ_
 // folded in (rnorm / gamma non-NULL).  Arguments were validated by the caller.
 hipError_t enqueue_prep(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, int sp_n, int sp_m, int fmt,
                         const sharq_fp4* backbone, const sharq_fp4* residual, uint8_t* mask_bits, void* workspace,
-                        const float* rnorm, const uint16_t* gamma, hipStream_t st) {
+                        const float* rnorm, const uint16_t* gamma, int swiglu, hipStream_t st) {
   if (fmt == SHARQ_MXFP4)
     return launch_prep_mx(x, M, K, ldx, sp_n, sp_m, backbone->codes, backbone->scales, residual->codes,
-                          residual->scales, mask_bits, rnorm, gamma, backbone->layout == SHARQ_LAYOUT_TILED, st);
+                          residual->scales, mask_bits, rnorm, gamma, swiglu, backbone->layout == SHARQ_LAYOUT_TILED,
+                          st);
   return launch_prep_nv(x, M, K, ldx, sp_n, sp_m, backbone->codes, backbone->scales, backbone->tensor_scale,
                         residual->codes, residual->scales, residual->tensor_scale, mask_bits,
-                        reinterpret_cast<uint32_t*>(workspace), rnorm, gamma, st);
+                        reinterpret_cast<uint32_t*>(workspace), rnorm, gamma, swiglu, st);
 }
 
 // The row factors of sharq_prep_rmsnorm follow the format's own preparation workspace.
@@ -208,7 +209,27 @@ sharq_status sharq_prep(const void* x, int64_t M, int64_t K, int64_t ldx, int sp
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   const uint16_t* xb = reinterpret_cast<const uint16_t*>(x);
   return launched(enqueue_prep(xb, M, K, ldx, sp_n, sp_m, fmt, backbone, residual, mask_bits, workspace, nullptr,
-                               nullptr, st));
+                               nullptr, 0, st));
+}
+
+sharq_status sharq_prep_swiglu(const void* gate_up, int64_t M, int64_t I, int64_t ld, int sp_n, int sp_m, int fmt,
+                               const sharq_fp4* backbone, const sharq_fp4* residual, uint8_t* mask_bits,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+  sharq_status s = check_input(gate_up, M, I, ld, fmt);
+  if (s != SHARQ_OK) return s;
+  if (ld < 2 * I) return SHARQ_E_SHAPE;
+  if ((s = check_pattern(sp_n, sp_m)) != SHARQ_OK) return s;
+  if ((s = check_payload(backbone, fmt, M)) != SHARQ_OK) return s;
+  if ((s = check_payload(residual, fmt, M)) != SHARQ_OK) return s;
+  if (backbone->layout != residual->layout) return SHARQ_E_FORMAT;
+  if (mask_bits && (reinterpret_cast<uintptr_t>(mask_bits) & 3u)) return SHARQ_E_ALIGN;
+  const size_t need = sharq_prep_workspace_bytes(M, I, fmt);
+  if (need && (!workspace || workspace_bytes < need)) return SHARQ_E_WORKSPACE;
+  if (need && !aligned16(workspace)) return SHARQ_E_ALIGN;
+  if ((s = check_device()) != SHARQ_OK) return s;
+  return launched(enqueue_prep(reinterpret_cast<const uint16_t*>(gate_up), M, I, ld, sp_n, sp_m, fmt, backbone,
+                               residual, mask_bits, workspace, nullptr, nullptr, 1,
+                               reinterpret_cast<hipStream_t>(stream)));
 }
 
 sharq_status sharq_prep_ablation(const void* x, int64_t M, int64_t K, int64_t ldx, int sp_n, int sp_m, int fmt,
@@ -282,7 +303,7 @@ sharq_status sharq_prep_rmsnorm(const void* x, int64_t M, int64_t K, int64_t ldx
   hipError_t e = launch_row_rms(xb, M, K, ldx, eps, rfac, st);
   if (e != hipSuccess) return SHARQ_E_LAUNCH;
   return launched(enqueue_prep(xb, M, K, ldx, sp_n, sp_m, fmt, backbone, residual, mask_bits, workspace, rfac,
-                               reinterpret_cast<const uint16_t*>(gamma), st));
+                               reinterpret_cast<const uint16_t*>(gamma), 0, st));
 }
 
 sharq_status sharq_linear(const sharq_fp4* backbone, const sharq_fp4* residual, int64_t M,

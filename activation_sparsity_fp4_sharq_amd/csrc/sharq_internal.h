@@ -12,10 +12,12 @@ namespace sharq {
 // `tiled` selects the output layout (SHARQ_LAYOUT_TILED when non-zero).
 // rnorm / gamma: optional RMS normalization folded into the preparation (both NULL
 // for none): per-row factors r[M] (from launch_row_rms) and per-channel bf16 gains g[K].
+// swiglu != 0: the preparation's input is SwiGLU(gate, up) of x's rows, gate in
+// columns [0, K) and up in [K, 2K) (ldx >= 2K).
 hipError_t launch_prep_mx(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, int sp_n,
                           int sp_m, uint8_t* bcodes, uint8_t* bscales, uint8_t* rcodes,
                           uint8_t* rscales, uint8_t* mask, const float* rnorm, const uint16_t* gamma,
-                          int tiled, hipStream_t stream);
+                          int swiglu, int tiled, hipStream_t stream);
 // The ablation variants of the preparation (sharq_ablation), without normalization.
 hipError_t launch_prep_mx_ablation(int variant, const uint16_t* x, int64_t M, int64_t K, int64_t ldx, int sp_m,
                                    uint8_t* bcodes, uint8_t* bscales, uint8_t* rcodes, uint8_t* rscales,
@@ -37,7 +39,8 @@ inline int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
 hipError_t launch_prep_nv(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, int sp_n,
                           int sp_m, uint8_t* bcodes, uint8_t* bscales, float* btscale,
                           uint8_t* rcodes, uint8_t* rscales, float* rtscale, uint8_t* mask,
-                          uint32_t* work, const float* rnorm, const uint16_t* gamma, hipStream_t stream);
+                          uint32_t* work, const float* rnorm, const uint16_t* gamma, int swiglu,
+                          hipStream_t stream);
 // r_out[i] = fp32(1 / sqrt(sum_k x_ik^2 / K + eps)) for the M rows of x.
 hipError_t launch_row_rms(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, float eps, float* r_out,
                           hipStream_t stream);

@@ -23,7 +23,8 @@ LIB_PATH = os.path.join(_HERE, "libsharq.so")
 SYMBOLS = ["sharq_abi_version", "sharq_status_str", "sharq_payload_bytes", "sharq_convert_layout",
            "sharq_prep_workspace_bytes", "sharq_linear_workspace_bytes", "sharq_quantize", "sharq_prep",
            "sharq_prep_rmsnorm_workspace_bytes", "sharq_prep_rmsnorm", "sharq_linear", "sharq_linear_dense",
-           "sharq_clock_probe", "sharq_prep_ablation", "sharq_dequantize", "sharq_forward"]
+           "sharq_clock_probe", "sharq_prep_ablation", "sharq_dequantize", "sharq_prep_swiglu",
+           "sharq_forward"]
 
 
 class SharqFp4(ctypes.Structure):
@@ -78,6 +79,9 @@ def lib():
                                    vp]
         L.sharq_linear_dense.restype = ctypes.c_int
         L.sharq_linear_dense.argtypes = [P, i64, P, i64, i64, ctypes.c_int, vp, i64, ctypes.c_int, vp, sz, vp]
+        L.sharq_prep_swiglu.restype = ctypes.c_int
+        L.sharq_prep_swiglu.argtypes = [vp, i64, i64, i64, ctypes.c_int, ctypes.c_int, ctypes.c_int, P, P, vp, vp,
+                                        sz, vp]
         L.sharq_prep_ablation.restype = ctypes.c_int
         L.sharq_prep_ablation.argtypes = [vp, i64, i64, i64, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                           P, P, vp, vp, sz, vp]
@@ -259,6 +263,26 @@ def linear_dense(a, weight, out_dtype=OUT_BF16, y=None, ws=None, stream=None):
                                                           y.stride(0), out_dtype, _ptr(ws),
                                                           0 if ws is None else ws.numel(), _stream(stream)))
     return y
+
+
+def prep_swiglu(gate_up, I, n=2, m=4, fmt=MXFP4, want_mask=False, out=None, ws=None, layout=None, stream=None):
+    """SharQ preparation of h = SwiGLU(gate, up) for gate_up bf16 [M, ld >= 2I] (gate in
+    columns [0, I), up in [I, 2I)): returns (backbone, residual, mask_bits or None)."""
+    if gate_up.dtype != torch.bfloat16 or gate_up.dim() != 2 or gate_up.stride(1) != 1:
+        raise ValueError("gate_up must be a 2-D bf16 tensor with unit column stride")
+    M = gate_up.shape[0]
+    if gate_up.shape[1] < 2 * I:
+        raise ValueError("gate_up needs at least 2*I columns")
+    bb, rr = out if out is not None else (Payload.empty(M, I, fmt, gate_up.device, layout),
+                                          Payload.empty(M, I, fmt, gate_up.device, layout))
+    mask = torch.empty((M, I // 8), dtype=torch.uint8, device=gate_up.device) if want_mask else None
+    if ws is None:
+        ws = workspace(lib().sharq_prep_workspace_bytes(M, I, fmt), gate_up.device)
+    sb, sr = bb.struct(), rr.struct()
+    _check("sharq_prep_swiglu", lib().sharq_prep_swiglu(_ptr(gate_up), M, I, gate_up.stride(0), n, m, fmt,
+                                                        ctypes.byref(sb), ctypes.byref(sr), _ptr(mask), _ptr(ws),
+                                                        0 if ws is None else ws.numel(), _stream(stream)))
+    return bb, rr, mask
 
 
 ABLATE_RESIDUAL_UNQUANTIZED = 1

@@ -175,3 +175,45 @@ def adversarial_activation(M, K, seed=0):
             sign = np.where(rng.random(32) < 0.5, np.float32(-1), np.float32(1))
             x[i, b * 32:(b + 1) * 32] = blk * sign
     return f32_to_bf16_bits(x)
+
+
+@dataclass(frozen=True)
+class MlpBlock:
+    """A Llama-3.1-8B-shaped MLP block (hidden H, intermediate I) over M tokens:
+    gate/up projection (one linear over the concatenated [gate; up] weights, N = 2I),
+    SwiGLU, down projection (K = I), each projection a SharQ layer."""
+    name: str
+    M: int
+    H: int
+    I: int
+    n: int
+    m: int
+    fmt: int
+    dist: str = "normal"
+    out_frac: float = 0.01
+    out_scale: float = 20.0
+    w_std: float = 0.02
+    seed: int = 0
+    note: str = field(default="", compare=False)
+
+    def flops_effective(self) -> float:
+        return 2.0 * self.M * self.H * (2 * self.I) + 2.0 * self.M * self.I * self.H
+
+
+MLP_BLOCKS = {
+    "mlp_block": MlpBlock("mlp_block", 2048, 4096, 14336, 2, 4, MXFP4,
+                          note="X[2048,4096] N(0,1), 1% outlier channels x20; W_gate_up[28672,4096], "
+                               "W_down[4096,14336] N(0,0.02); SwiGLU; 2:4; MXFP4"),
+    "mlp_block_small": MlpBlock("mlp_block_small", 64, 512, 1024, 2, 4, MXFP4,
+                                note="the same recipe at a size the oracle finishes in seconds"),
+}
+
+
+def make_mlp_inputs(b: MlpBlock):
+    """Draw order: X [M,H] (distribution, outlier channels), then W_gate_up [2I,H], then
+    W_down [H,I], all from numpy.random.default_rng(seed); returns bf16 bits."""
+    rng = np.random.default_rng(b.seed)
+    x = make_activation(rng, b.M, b.H, b.dist, int(round(b.out_frac * b.H)), b.out_scale)
+    wgu = f32_to_bf16_bits(rng.normal(0.0, b.w_std, (2 * b.I, b.H)).astype(np.float32))
+    wd = f32_to_bf16_bits(rng.normal(0.0, b.w_std, (b.H, b.I)).astype(np.float32))
+    return x, wgu, wd

@@ -268,6 +268,112 @@ def ablation_report(w, x, ws, stream, reps):
     return out
 
 
+def run_mlp_block(args):
+    """One Llama-shaped MLP block per step, every projection a SharQ layer:
+    sharq_prep(X) -> sharq_linear over [W_gate; W_up] (N = 2I) -> sharq_prep_swiglu
+    (SwiGLU folded into the down projection's preparation) -> sharq_linear over W_down."""
+    import numpy as np
+    import torch
+
+    from activation_sparsity_fp4_sharq_amd import sharq
+    from activation_sparsity_fp4_sharq_amd.workloads import MLP_BLOCKS, make_mlp_inputs
+
+    b = MLP_BLOCKS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    M, H, I = b.M, b.H, b.I
+    to_dev = lambda bits: torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
+    xb, wgub, wdb = make_mlp_inputs(b)
+    x0 = to_dev(xb)
+    wgu0 = sharq.quantize(to_dev(wgub), b.fmt)
+    wd0 = sharq.quantize(to_dev(wdb), b.fmt)
+    blk = sharq.BLOCK[b.fmt]
+    pay = lambda rows, k: rows * k // 2 + rows * k // blk
+    per_set = M * H * 2 + 2 * pay(M, H) + pay(2 * I, H) + M * 2 * I * 2 + 2 * pay(M, I) + pay(H, I) + M * H * 2
+    nsets = max(2, min(16, -(-2 * INFINITY_CACHE_BYTES // per_set)))
+    clone = lambda p: sharq.Payload(p.codes.clone(), p.scales.clone(), p.tensor_scale.clone(), p.fmt, p.layout,
+                                    p.rows, p.K)
+    sets = []
+    for i in range(nsets):
+        sets.append(dict(x=x0 if i == 0 else x0.clone(), wgu=wgu0 if i == 0 else clone(wgu0),
+                         wd=wd0 if i == 0 else clone(wd0),
+                         b1=sharq.Payload.empty(M, H, b.fmt, dev), r1=sharq.Payload.empty(M, H, b.fmt, dev),
+                         gu=torch.empty((M, 2 * I), dtype=torch.bfloat16, device=dev),
+                         b2=sharq.Payload.empty(M, I, b.fmt, dev), r2=sharq.Payload.empty(M, I, b.fmt, dev),
+                         y=torch.empty((M, H), dtype=torch.bfloat16, device=dev)))
+    ws = sharq.workspace(max(sharq.lib().sharq_prep_workspace_bytes(M, max(H, I), b.fmt),
+                             sharq.lib().sharq_linear_workspace_bytes(M, 2 * I, max(H, I), b.fmt)), dev)
+    stream = torch.cuda.current_stream()
+
+    def prep1(i):
+        s_ = sets[i % nsets]
+        sharq.prep(s_["x"], b.n, b.m, b.fmt, out=(s_["b1"], s_["r1"]), ws=ws, stream=stream)
+
+    def lin1(i):
+        s_ = sets[i % nsets]
+        sharq.linear(s_["b1"], s_["r1"], s_["wgu"], sharq.OUT_BF16, y=s_["gu"], ws=ws, stream=stream)
+
+    def prep2(i):
+        s_ = sets[i % nsets]
+        sharq.prep_swiglu(s_["gu"], I, b.n, b.m, b.fmt, out=(s_["b2"], s_["r2"]), ws=ws, stream=stream)
+
+    def lin2(i):
+        s_ = sets[i % nsets]
+        sharq.linear(s_["b2"], s_["r2"], s_["wd"], sharq.OUT_BF16, y=s_["y"], ws=ws, stream=stream)
+
+    def step(i):
+        prep1(i)
+        lin1(i)
+        prep2(i)
+        lin2(i)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    t_step = (time.perf_counter() - t0) / args.steps
+    t = {name: back_to_back_seconds(fn, args.steps, stream)
+         for name, fn in (("prep", prep1), ("linear_gate_up", lin1), ("prep_swiglu", prep2), ("linear_down", lin2))}
+
+    # the unfused alternative for the SwiGLU step: torch's silu * mul into a bf16 H, then sharq_prep
+    hbuf = torch.empty((M, I), dtype=torch.bfloat16, device=dev)
+
+    def unfused(i):
+        s_ = sets[i % nsets]
+        torch.mul(torch.nn.functional.silu(s_["gu"][:, :I]), s_["gu"][:, I:], out=hbuf)
+        sharq.prep(hbuf, b.n, b.m, b.fmt, out=(s_["b2"], s_["r2"]), ws=ws, stream=stream)
+    t_unfused = back_to_back_seconds(unfused, args.steps, stream)
+    sclk = sharq.clock_probe(20000, dev, stream)
+
+    eff = b.flops_effective()
+    alg1 = 2.0 * M * (2 * I) * H * (1.0 + b.n / b.m)
+    ach = alg1 / t["linear_gate_up"] / 1e12
+    out = {
+        "metric": "SharQ MLP block effective TFLOPS (2*M*H*2I + 2*M*I*H)/t",
+        "value": round(eff / t_step / 1e12, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(t_step * 1e3, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "mxfp4" if b.fmt == sharq.MXFP4 else "nvfp4 (fp16 matrix cores)",
+        "data": "synthetic",
+        "config": {"workload": b.name, "M": M, "H": H, "I": I, "pattern": f"{b.n}:{b.m}", "input_sets": nsets,
+                   "description": b.note},
+        "roofline": {"bound": "mfma", "kernel": "linear_mx (gate/up)", "achieved": round(ach, 2),
+                     "peak": PEAK_MXFP4_TFLOPS, "unit": "TFLOP/s", "frac": round(ach / PEAK_MXFP4_TFLOPS, 4),
+                     "traffic": None, "flops_per_launch": alg1,
+                     "flop_convention": "algorithmic 2MNK(1+n/m)",
+                     "sclk_ghz": round(sclk / 1e9, 3)},
+        "kernels_us": {k: round(v * 1e6, 2) for k, v in t.items()},
+        "swiglu_unfused_us": round(t_unfused * 1e6, 2),
+        "swiglu_fusion_saving_us": round((t_unfused - t["prep_swiglu"]) * 1e6, 2),
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.calibrate_copy:
@@ -278,6 +384,11 @@ def main():
         print(json.dumps({"error": "this benchmark runs on exactly one GPU; the SharQ layer is timed on "
                                    "one MI355X (multi-GPU sharding is design only)", "n_gpus": args.gpus}))
         sys.exit(2)
+
+    from activation_sparsity_fp4_sharq_amd.workloads import MLP_BLOCKS
+    if args.workload in MLP_BLOCKS:
+        run_mlp_block(args)
+        return
 
     import numpy as np
     import torch

@@ -61,7 +61,7 @@
 extern "C" {
 #endif
 
-#define SHARQ_ABI_VERSION 6
+#define SHARQ_ABI_VERSION 7
 
 typedef enum sharq_status {
   SHARQ_OK = 0,
@@ -155,6 +155,28 @@ sharq_status sharq_prep(const void* x, int64_t M, int64_t K, int64_t ldx, int sp
                         int fmt, const sharq_fp4* backbone, const sharq_fp4* residual,
                         uint8_t* mask_bits, void* workspace, size_t workspace_bytes,
                         void* stream);
+
+/* The preparation of an MLP block's down projection with its SwiGLU activation
+ * folded in: the input is h = SwiGLU(gate, up), formed from each row's gate and up
+ * halves while they are loaded and never stored, then prepared exactly as
+ * sharq_prep prepares X (SharQ, arXiv 2606.26587: Figure 2's fused preparation takes
+ * over the element-wise work in front of the GEMMs; the benchmark's MLP block
+ * workload chains two SharQ layers around it).
+ *   h = bf16(fp32(silu(g) * u)), silu(g) = fp32(g / fp32(1 + e)), e = e^-g in fp32
+ *   by Cody and Waite's range reduction (t = -g clamped to [-150, 150],
+ *   n = rint(t log2 e), r = (t - n ln2_hi) - n ln2_lo with a 15-bit ln2_hi) and the
+ *   degree-7 Taylor polynomial of e^r times 2^n -- every operation one fp32
+ *   rounding in a fixed order, so h is reproducible bit for bit.
+ *   gate_up  device bf16 [M, ld]: gate in columns [0, I), up in [I, 2I) of each row
+ *            (the output of one linear over the concatenated gate and up weights);
+ *            16-byte aligned, ld % 8 == 0, ld >= 2I
+ *   I        the intermediate size (the down projection's K): > 0, multiple of 32
+ *            (MXFP4) or 16 (NVFP4)
+ *   other arguments, outputs, workspace (sharq_prep_workspace_bytes(M, I, fmt)) and
+ *   errors as for sharq_prep; ld < 2I -> SHARQ_E_SHAPE. */
+sharq_status sharq_prep_swiglu(const void* gate_up, int64_t M, int64_t I, int64_t ld, int sp_n, int sp_m,
+                               int fmt, const sharq_fp4* backbone, const sharq_fp4* residual,
+                               uint8_t* mask_bits, void* workspace, size_t workspace_bytes, void* stream);
 
 /* The ablations of the method's choices named by the pages' review ("What would
  * settle it": the residual against the unquantized sparse values; the referee's

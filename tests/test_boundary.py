@@ -33,7 +33,7 @@ def test_header_symbols_exported():
 
 def test_version_and_status_strings():
     L = sharq.lib()
-    assert L.sharq_abi_version() == 6
+    assert L.sharq_abi_version() == 7
     for s in range(9):
         assert L.sharq_status_str(s)
     assert L.sharq_status_str(99) == b"unknown status"
@@ -163,6 +163,23 @@ def test_prep_ablation_rejects():
     if not torch.cuda.is_available():
         for v in (1, 2, 3):
             assert call(variant=v) == E_DEVICE
+
+
+def test_prep_swiglu_rejects():
+    L = sharq.lib()
+    bb, rr = fp4(), fp4()
+
+    def call(x=A, M=4, I=64, ld=128, n=2, m=4, fmt=0, ws=None, wsb=0):
+        return L.sharq_prep_swiglu(x, M, I, ld, n, m, fmt, ctypes.byref(bb), ctypes.byref(rr), None, ws, wsb, None)
+    assert call(ld=120) == E_SHAPE        # ld < 2I
+    assert call(I=48) == E_SHAPE          # not a multiple of 32 (MXFP4)
+    assert call(x=None) == E_NULL
+    assert call(ld=132) == E_ALIGN        # rows not 16-byte aligned
+    assert call(m=8, n=2) == E_PATTERN
+    assert call(fmt=1) == E_WORKSPACE
+    import torch
+    if not torch.cuda.is_available():
+        assert call() == E_DEVICE
 
 
 def test_dequantize_rejects():

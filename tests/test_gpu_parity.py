@@ -422,3 +422,71 @@ def test_clock_probe_reports_a_plausible_clock():
     print("[clock_probe]", flush=True)
     hz = sharq.clock_probe(20000)
     assert 0.5e9 < hz < 3.5e9, hz
+
+
+# ------------------------------------------------------------------ SwiGLU-fused preparation
+
+def _gate_up(M, I, pad, seed):
+    rng = np.random.default_rng(seed)
+    g = rng.normal(0.0, 3.0, (M, I)) * rng.lognormal(0.0, 0.5, (M, 1))
+    u = rng.normal(0.0, 1.0, (M, I))
+    gu = np.zeros((M, 2 * I + pad), np.uint16)
+    gu[:, :I] = f32_to_bf16_bits(g.astype(np.float32))
+    gu[:, I:2 * I] = f32_to_bf16_bits(u.astype(np.float32))
+    return gu
+
+
+@pytest.mark.parametrize("fmt,layout", FMT_LAYOUTS, ids=FL_IDS)
+@pytest.mark.parametrize("n,m", [(2, 4), (4, 8)])
+@pytest.mark.parametrize("M,I,pad", [(1, 64, 0), (37, 352, 16), (300, 1024, 0)])
+def test_prep_swiglu_matches_oracle(fmt, layout, n, m, M, I, pad):
+    print(f"[prep_swiglu] {n}:{m} M={M} I={I} pad={pad} fmt={fmt} layout={layout}", flush=True)
+    gu = _gate_up(M, I, pad, seed=M + I + pad)
+    bb, rr, mask = sharq.prep_swiglu(to_dev(gu), I, n, m, fmt, want_mask=True, layout=layout)
+    torch.cuda.synchronize()
+    h = oracle.swiglu(gu, I)
+    ob, orr, omask = oracle.prep(h, n, m, fmt)
+    assert np.array_equal(mask.cpu().numpy(), omask), "mask bits differ"
+    assert_payload_equal(bb, ob, "backbone")
+    assert_payload_equal(rr, orr, "residual")
+
+
+def test_prep_swiglu_full_size_mlp():
+    """The MLP block's down-projection preparation at its full shape (M=2048, I=14336)."""
+    print("[prep_swiglu] M=2048 I=14336", flush=True)
+    M, I = 2048, 14336
+    gu = _gate_up(M, I, 0, seed=5)
+    bb, rr, _ = sharq.prep_swiglu(to_dev(gu), I, 2, 4, sharq.MXFP4, layout=sharq.TILED)
+    torch.cuda.synchronize()
+    ob, orr, _ = oracle.prep(oracle.swiglu(gu, I), 2, 4, sharq.MXFP4)
+    assert_payload_equal(bb, ob, "backbone")
+    assert_payload_equal(rr, orr, "residual")
+
+
+def test_mlp_block_chain_matches_oracle():
+    """The MLP block (prep -> gate/up linear -> SwiGLU-fused prep -> down linear) stage by
+    stage; each oracle stage takes the GPU's previous output, so what is unique is compared:
+    payloads bit for bit, GEMM outputs within the tolerance."""
+    from activation_sparsity_fp4_sharq_amd.workloads import MLP_BLOCKS, make_mlp_inputs
+    b = MLP_BLOCKS["mlp_block_small"]
+    print(f"[mlp_block] M={b.M} H={b.H} I={b.I}", flush=True)
+    xb, wgub, wdb = make_mlp_inputs(b)
+    wgu = sharq.quantize(to_dev(wgub), b.fmt)
+    wd = sharq.quantize(to_dev(wdb), b.fmt)
+    b1, r1, _ = sharq.prep(to_dev(xb), b.n, b.m, b.fmt)
+    gu = sharq.linear(b1, r1, wgu, sharq.OUT_BF16)
+    b2, r2, _ = sharq.prep_swiglu(gu, b.I, b.n, b.m, b.fmt)
+    y32 = sharq.linear(b2, r2, wd, sharq.OUT_FP32)
+    torch.cuda.synchronize()
+    ob1, or1, _ = oracle.prep(xb, b.n, b.m, b.fmt)
+    assert_payload_equal(b1, ob1, "backbone 1")
+    assert_payload_equal(r1, or1, "residual 1")
+    ref_gu = oracle.linear(ob1, or1, oracle.quantize(wgub, b.fmt), b.fmt)
+    assert bf16_ulp_check(gu, ref_gu) <= 1
+    gu_bits = gu.cpu().view(torch.int16).numpy().view(np.uint16)
+    ob2, or2, _ = oracle.prep(oracle.swiglu(gu_bits, b.I), b.n, b.m, b.fmt)
+    assert_payload_equal(b2, ob2, "backbone 2")
+    assert_payload_equal(r2, or2, "residual 2")
+    yref = oracle.linear(ob2, or2, oracle.quantize(wdb, b.fmt), b.fmt)
+    err = rel_maxnorm(y32.cpu().numpy().astype(np.float64), yref)
+    assert err <= TOL, err
