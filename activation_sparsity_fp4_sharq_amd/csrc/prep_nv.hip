@@ -373,11 +373,21 @@ __global__ __launch_bounds__(kThreads) void prep_nv_kernel(
   }
 }
 
-// work[slot] = max of the `n` partials of a maximum pass (one work-group).
+// work[slot] = max of the `n` partials of a maximum pass (one work-group).  Every
+// thread issues its kMaxGroups / 256 loads before using any (a fixed, unrolled count:
+// a strided loop over n would wait for each load in turn).
 __global__ void nv_reduce_kernel(uint32_t* work, int slot, int n) {
   __shared__ uint32_t red[256];
+  constexpr int kPer = kMaxGroups / 256;
+  uint32_t v[kPer];
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int i = j * 256 + (int)threadIdx.x;
+    v[j] = i < n ? work[kPartialBase + slot * kMaxGroups + i] : 0u;
+  }
   uint32_t m = 0;
-  for (int i = threadIdx.x; i < n; i += 256) m = umax(m, work[kPartialBase + slot * kMaxGroups + i]);
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) m = umax(m, v[j]);
   red[threadIdx.x] = m;
   __syncthreads();
   for (int w = 128; w > 0; w >>= 1) {
