@@ -20,12 +20,17 @@
 // scale byte for sub-step s is byte s of (row's 4 scale bytes >> 16h), selected by
 // the instruction's op_sel.
 //
-// Tiling: 512 threads (8 waves, 2 per SIMD) own a 256x256 output tile; waves form a
-// 4 (M) x 2 (N) grid of 64x128 wave tiles = 2x4 instructions per path and sub-step.
-// Per 128-element K-step the block stages A_b, A_r, W tiles (256 rows x 64 B each,
-// rows padded to 80 B so that 16-byte LDS reads of 32 consecutive rows hit
-// distinct banks) and their scale dwords, double-buffered; one barrier per K-step.
-// Work-groups are renumbered so that consecutive tiles share an XCD (and its L2).
+// Three kernels share the instruction and the 256x256 output tile: the pipelined
+// LDS-DMA kernel for tiled payloads (the layout the preparation writes), a small-M
+// kernel for tiled payloads with M <= 32 (decode: a weight stream), and a generic
+// register-staged kernel for row-major payloads.  The generic kernel: 512 threads (8
+// waves, 2 per SIMD) form a 4 (M) x 2 (N) grid of 64x128 wave tiles = 2x4
+// instructions per path and sub-step; per 128-element K-step the block stages A_b,
+// A_r, W tiles (256 rows x 64 B each, rows padded to 80 B so that 16-byte LDS reads of
+// 32 consecutive rows hit distinct banks) and their scale dwords, double-buffered; one
+// barrier per K-step.  Work-groups are renumbered so that consecutive tiles share an
+// XCD (and its L2).  With one activation operand (sharq_linear_dense) every kernel
+// skips the backbone path.
 #include <atomic>
 #include <type_traits>
 
@@ -244,12 +249,12 @@ __global__ __launch_bounds__(kThreads, 1) void linear_mx_kernel(Args a) {
 }
 
 // ---------------------------------------------------------------------------------
-// Pipelined kernel for K % 128 == 0 (every shape the benchmarks use).
+// Pipelined kernel for tiled payloads (K padded to 128 by the layout).
 //
-// Same tiling and instruction as above, but the operands travel global -> LDS by the
-// gfx950 LDS-DMA loads (global_load_lds_dwordx4 / _dword) instead of through
-// registers, into a 3-deep ring of stages, so the loads for K-step i+2 are in flight
-// while K-step i computes.  Each operand tile is stored in LDS in *fragment order*:
+// Same tiling and instruction as above, but the operands travel global -> LDS by
+// LDS-DMA (buffer_load_dwordx4 ... lds) instead of through registers, into a 3-deep
+// ring of stages, so the loads of later K-steps are in flight while a K-step
+// computes (the schedule is described at the loop).  Each operand tile is stored in LDS in *fragment order*:
 // 16 fragments of 1 KiB (8 row-tiles of 32 rows x 2 sub-steps), fragment byte
 // 16*lane holding exactly the 16 bytes lane `lane` feeds the instruction.  A DMA
 // load writes 64 lanes x 16 B contiguously, so one load fills one fragment (each
@@ -257,8 +262,8 @@ __global__ __launch_bounds__(kThreads, 1) void linear_mx_kernel(Args a) {
 // 16*lane reads it back with no bank conflicts.  Sub-step s, lane half h takes the
 // 16-byte chunk 2s+h of the row's 64-byte K-step, so a load reads 32 contiguous
 // bytes per row; the scale byte of chunk 2s+h is byte 2s of (row scale word >> 8h),
-// op_sel 0 or 2.  Rows past M (or N) are clamped to the last row: they are loaded
-// and computed but never stored.
+// op_sel 0 or 2.  Row tiles past the padded extent are clamped to the last one and
+// scale words past it read as zero: loaded and computed, never stored.
 constexpr int kFragBytes = 1024;
 constexpr int kOpTileBytes = 16 * kFragBytes;                   // 256 rows x 128 K
 constexpr int kDmaStageBytes = 3 * kOpTileBytes + 3 * 256 * 4;  // + scale words
