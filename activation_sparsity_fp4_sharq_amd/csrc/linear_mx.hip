@@ -43,6 +43,7 @@ typedef int v8i __attribute__((ext_vector_type(8)));
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int BM = 256, BN = 256, BKB = 64;  // tile rows, tile cols, bytes of K per step (128 elements)
 constexpr int kThreads = 512;
@@ -556,7 +557,8 @@ constexpr int kSmallThreads = 64 * kSmallWaves;
 
 template <bool OUT_F32, int NT, int CH, bool DUAL>
 __global__ __launch_bounds__(kSmallThreads, 1) void linear_mx_small_kernel(Args a) {
-  __shared__ float part[kSmallWaves][NT][16][64];
+  // partial tiles, [wave][tile][group g][lane]: lane's accumulators 4g..4g+3 as one float4
+  __shared__ f32x4 part[kSmallWaves][NT][4][64];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -626,22 +628,37 @@ __global__ __launch_bounds__(kSmallThreads, 1) void linear_mx_small_kernel(Args 
 #pragma unroll
   for (int t = 0; t < NT; ++t)
 #pragma unroll
-    for (int j = 0; j < 16; ++j) part[wave][t][j][lane] = acc[t][j];
+    for (int g = 0; g < 4; ++g)
+      part[wave][t][g][lane] = f32x4{acc[t][4 * g], acc[t][4 * g + 1], acc[t][4 * g + 2], acc[t][4 * g + 3]};
   __syncthreads();
-  // reduction over the 8 waves, one output per thread per pass, columns fastest
-  for (int q = tid; q < NT * 32 * 32; q += kSmallThreads) {
-    const int row = q / (32 * NT), colw = q - row * (32 * NT);
-    const int t = colw >> 5, cc = colw & 31;
-    const int j = 4 * (cc >> 3) + (cc & 3), src_lane = row + 32 * ((cc >> 2) & 1);
-    const int64_t col = (tn0 + t) * 32 + cc;
+  // reduction over the 8 waves: one float4 (4 consecutive outputs of one row) per thread
+  // and pass, consecutive threads on consecutive 16-byte LDS words (no bank conflicts).
+  // Accumulator element 4g+i of lane (r32, h) is output row r32, column 8g + 4h + i.
+  for (int q = tid; q < NT * 4 * 64; q += kSmallThreads) {
+    const int t = q >> 8, g = (q >> 6) & 3, l = q & 63;
+    const int row = l & 31;
+    const int64_t col = (tn0 + t) * 32 + 8 * g + 4 * (l >> 5);
     if (row >= a.M || col >= a.N) continue;
-    float v = 0.f;
+    f32x4 v = part[0][t][g][l];
 #pragma unroll
-    for (int w = 0; w < kSmallWaves; ++w) v += part[w][t][j][src_lane];
-    if constexpr (OUT_F32)
-      reinterpret_cast<float*>(a.y)[row * a.ldy + col] = v;
-    else
-      reinterpret_cast<uint16_t*>(a.y)[row * a.ldy + col] = f32_to_bf16_rne(v);
+    for (int w = 1; w < kSmallWaves; ++w) v += part[w][t][g][l];
+    if constexpr (OUT_F32) {
+      float* yp = reinterpret_cast<float*>(a.y) + row * a.ldy + col;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (col + i < a.N) yp[i] = v[i];
+    } else {
+      uint16_t* yp = reinterpret_cast<uint16_t*>(a.y) + row * a.ldy + col;
+      if (a.y_aligned && col + 4 <= a.N) {  // 16-byte aligned Y, ldy % 8 == 0, col % 4 == 0: an 8-byte store
+        const uint32_t lo = f32_to_bf16_rne(v[0]) | ((uint32_t)f32_to_bf16_rne(v[1]) << 16);
+        const uint32_t hi = f32_to_bf16_rne(v[2]) | ((uint32_t)f32_to_bf16_rne(v[3]) << 16);
+        *reinterpret_cast<uint2*>(yp) = make_uint2(lo, hi);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (col + i < a.N) yp[i] = f32_to_bf16_rne(v[i]);
+      }
+    }
   }
 }
 
