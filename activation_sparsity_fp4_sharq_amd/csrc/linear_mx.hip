@@ -579,6 +579,7 @@ __global__ __launch_bounds__(kSmallThreads, 1) void linear_mx_small_kernel(Args 
     wsrc[t] = a.wc + tn * kc_per_rt * kFragBytes + lane * 16;
     wssrc[t] = reinterpret_cast<const uint32_t*>(a.ws) + tn * 32 + r32;
   }
+  const bool arow = r32 < a.M;
   const uint8_t* bsrc = a.bc + lane * 16;  // activation row tile 0
   const uint8_t* rsrc = a.rc + lane * 16;
   const uint32_t* bssrc = reinterpret_cast<const uint32_t*>(a.bs) + r32;
@@ -598,8 +599,9 @@ __global__ __launch_bounds__(kSmallThreads, 1) void linear_mx_small_kernel(Args 
 #pragma unroll
         for (int t = 0; t < NT; ++t)
           wf[j][t][sub] = *reinterpret_cast<const v4i*>(wsrc[t] + (2 * ks + sub) * kFragBytes);
-        if constexpr (DUAL) bf[j][sub] = *reinterpret_cast<const v4i*>(bsrc + (2 * ks + sub) * kFragBytes);
-        rf[j][sub] = *reinterpret_cast<const v4i*>(rsrc + (2 * ks + sub) * kFragBytes);
+        // activation rows past M are zero padding in the payload: those lanes load nothing
+        if constexpr (DUAL) bf[j][sub] = arow ? *reinterpret_cast<const v4i*>(bsrc + (2 * ks + sub) * kFragBytes) : v4i{};
+        rf[j][sub] = arow ? *reinterpret_cast<const v4i*>(rsrc + (2 * ks + sub) * kFragBytes) : v4i{};
       }
 #pragma unroll
       for (int t = 0; t < NT; ++t) wsw[j][t] = wssrc[t][ks * a.Np];
