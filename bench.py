@@ -4,8 +4,8 @@
 
 A step is the whole hot path over one batch: sharq_prep (mask, FP4 backbone,
 residual against the dequantized backbone, FP4 residual) then sharq_linear (backbone
-GEMM + residual GEMM into one fp32 tile, bf16 output), on synthetic inputs already
-resident in HBM.  Steps rotate over several independent input sets whose combined
+GEMM + residual GEMM into one fp32 tile, bf16 output), issued as one sharq_forward call
+on synthetic inputs already resident in HBM.  Steps rotate over several independent input sets whose combined
 footprint exceeds the 256 MB Infinity Cache, so no step reads a cache-warm input.
 
 Prints one JSON line.  `value` is the effective throughput 2*M*N*K / t_step
@@ -40,6 +40,9 @@ def parse():
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", default="prefill")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--graph", action="store_true",
+                   help="issue each timed step as the replay of one HIP graph holding its launches "
+                        "(default: the library's calls, eagerly)")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time for the CPU baseline")
     p.add_argument("--rmsnorm", action="store_true",
                    help="time the preparation with the RMS normalization folded in (sharq_prep_rmsnorm)")
@@ -153,6 +156,28 @@ def back_to_back_seconds(launch, reps, stream):
         cycles *= 4
         if cycles > 1 << 34:
             raise RuntimeError("could not hold the stream long enough to queue the launches")
+
+
+def step_runner(step, nsets, graph):
+    """How the timed loop issues step i: eagerly (the library's calls), or by replaying one
+    HIP graph per input set that holds that step's launches (captured once, before timing;
+    the library allocates nothing and records no memset, so a replay is the same
+    launches).  Measured on this torch build, a graph replay costs the host more than the
+    eager calls it replaces, so eager is the default."""
+    import torch
+
+    if not graph:
+        return step, "eager"
+    step(0)  # one eager call first: per-device kernel attributes are set outside capture
+    torch.cuda.synchronize()
+    graphs = []
+    for i in range(nsets):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step(i)
+        graphs.append(g)
+    torch.cuda.synchronize()
+    return (lambda i: graphs[i % nsets].replay()), "hip_graph_per_step"
 
 
 def comparison_points(w, sets, weight_sets, ws, stream, reps, t_prep, t_lin):
@@ -307,19 +332,19 @@ def run_mlp_block(args):
 
     def prep1(i):
         s_ = sets[i % nsets]
-        sharq.prep(s_["x"], b.n, b.m, b.fmt, out=(s_["b1"], s_["r1"]), ws=ws, stream=stream)
+        sharq.prep(s_["x"], b.n, b.m, b.fmt, out=(s_["b1"], s_["r1"]), ws=ws)
 
     def lin1(i):
         s_ = sets[i % nsets]
-        sharq.linear(s_["b1"], s_["r1"], s_["wgu"], sharq.OUT_BF16, y=s_["gu"], ws=ws, stream=stream)
+        sharq.linear(s_["b1"], s_["r1"], s_["wgu"], sharq.OUT_BF16, y=s_["gu"], ws=ws)
 
     def prep2(i):
         s_ = sets[i % nsets]
-        sharq.prep_swiglu(s_["gu"], I, b.n, b.m, b.fmt, out=(s_["b2"], s_["r2"]), ws=ws, stream=stream)
+        sharq.prep_swiglu(s_["gu"], I, b.n, b.m, b.fmt, out=(s_["b2"], s_["r2"]), ws=ws)
 
     def lin2(i):
         s_ = sets[i % nsets]
-        sharq.linear(s_["b2"], s_["r2"], s_["wd"], sharq.OUT_BF16, y=s_["y"], ws=ws, stream=stream)
+        sharq.linear(s_["b2"], s_["r2"], s_["wd"], sharq.OUT_BF16, y=s_["y"], ws=ws)
 
     def step(i):
         prep1(i)
@@ -327,12 +352,13 @@ def run_mlp_block(args):
         prep2(i)
         lin2(i)
 
+    run, launch_mode = step_runner(step, nsets, args.graph)
     for i in range(args.warmup):
-        step(i)
+        run(i)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(i)
+        run(i)
     torch.cuda.synchronize()
     t_step = (time.perf_counter() - t0) / args.steps
     t = {name: back_to_back_seconds(fn, args.steps, stream)
@@ -361,7 +387,7 @@ def run_mlp_block(args):
         "dtype": "mxfp4" if b.fmt == sharq.MXFP4 else "nvfp4 (fp16 matrix cores)",
         "data": "synthetic",
         "config": {"workload": b.name, "M": M, "H": H, "I": I, "pattern": f"{b.n}:{b.m}", "input_sets": nsets,
-                   "description": b.note},
+                   "launch": launch_mode, "description": b.note},
         "roofline": {"bound": "mfma", "kernel": "linear_mx (gate/up)", "achieved": round(ach, 2),
                      "peak": PEAK_MXFP4_TFLOPS, "unit": "TFLOP/s", "frac": round(ach / PEAK_MXFP4_TFLOPS, 4),
                      "traffic": None, "flops_per_launch": alg1,
@@ -434,23 +460,27 @@ def main():
 
     def prep_call(x, bb, rr):
         if args.rmsnorm:
-            sharq.prep_rmsnorm(x, gamma, 1e-6, w.n, w.m, w.fmt, out=(bb, rr), ws=ws, stream=stream)
+            sharq.prep_rmsnorm(x, gamma, 1e-6, w.n, w.m, w.fmt, out=(bb, rr), ws=ws)
         else:
-            sharq.prep(x, w.n, w.m, w.fmt, out=(bb, rr), ws=ws, stream=stream)
+            sharq.prep(x, w.n, w.m, w.fmt, out=(bb, rr), ws=ws)
 
     def step(i):
         x, weight, bb, rr, y = sets[i % nsets]
-        prep_call(x, bb, rr)
-        sharq.linear(bb, rr, weight, sharq.OUT_BF16, y=y, ws=ws, stream=stream)
+        if args.rmsnorm:
+            prep_call(x, bb, rr)
+            sharq.linear(bb, rr, weight, sharq.OUT_BF16, y=y, ws=ws)
+        else:  # sharq_forward: the preparation and the fused linear from one call
+            sharq.forward(x, weight, w.n, w.m, sharq.OUT_BF16, bufs=(bb, rr), y=y, ws=ws)
 
+    run, launch_mode = step_runner(step, nsets, args.graph)
     for i in range(args.warmup):
-        step(i)
+        run(i)
     torch.cuda.synchronize()
 
     # timed region: exactly K steps, bracketed by synchronize
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(i)
+        run(i)
     torch.cuda.synchronize()
     t_step = (time.perf_counter() - t0) / args.steps
 
@@ -461,7 +491,7 @@ def main():
 
     def linear_only(i):
         x, weight, bb, rr, y = sets[i % nsets]
-        sharq.linear(bb, rr, weight, sharq.OUT_BF16, y=y, ws=ws, stream=stream)
+        sharq.linear(bb, rr, weight, sharq.OUT_BF16, y=y, ws=ws)
 
     t_prep = back_to_back_seconds(prep_only, args.steps, stream)
     t_lin = back_to_back_seconds(linear_only, args.steps, stream)
@@ -520,7 +550,7 @@ def main():
         "config": {"workload": w.name, "M": M, "N": N, "K": K, "pattern": f"{w.n}:{w.m}",
                    "format": "mxfp4" if w.fmt == sharq.MXFP4 else "nvfp4", "input_sets": nsets,
                    "payload_layout": "tiled" if weight0.layout == sharq.TILED else "row-major",
-                   "prep_rmsnorm": bool(args.rmsnorm),
+                   "prep_rmsnorm": bool(args.rmsnorm), "launch": launch_mode,
                    "description": w.note},
         "pct_mxfp4_peak": round(100.0 * eff / t_step / 1e12 / PEAK_MXFP4_TFLOPS, 3),
         "roofline": roofline,
