@@ -179,7 +179,7 @@ def run_linear(xb, wb, n, m, fmt, layout=None):
 @pytest.mark.parametrize("fmt,layout", FMT_LAYOUTS, ids=FL_IDS)
 @pytest.mark.parametrize("M,N,K", [(1, 1, 32), (16, 512, 512), (37, 70, 96), (300, 260, 160),
                                    (257, 513, 1056), (64, 256, 2048), (520, 300, 384),
-                                   (32, 1000, 4224), (7, 96, 640), (33, 96, 640)])
+                                   (32, 1000, 4224), (7, 96, 640), (33, 96, 640), (20, 200, 384)])
 def test_linear_small_full_compare(fmt, layout, M, N, K):
     print(f"[linear] M={M} N={N} K={K} fmt={fmt} layout={layout}", flush=True)
     xb, wb = make_shape(M, N, K, seed=M + N + K, dist="laplace", token_sigma=0.3)
