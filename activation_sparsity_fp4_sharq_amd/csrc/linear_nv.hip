@@ -94,19 +94,20 @@ __device__ __forceinline__ void decode16(u32x2 codes, uint32_t sbyte, v2h out[8]
 // Epilogue: Y = S_w (S_b acc_b + S_r acc_r) in fp32, each operation rounded to nearest
 // (with one activation operand: Y = S_w (S_r acc_r), the same value as with a zero
 // backbone); lane holds column r32 of each 32x32 tile and rows 8*(j/4) + 4*h + j%4.
-template <bool OUT_F32, bool DUAL>
-__device__ __forceinline__ void store_tile(const Args& a, const v16f (&accb)[2][2], const v16f (&accr)[2][2],
-                                           int64_t m0, int64_t n0, int wm, int wn, int r32, int h) {
+// row0 / col0: the wave's first output row and column (2 x NT instruction tiles).
+template <bool OUT_F32, bool DUAL, int NT>
+__device__ __forceinline__ void store_tile(const Args& a, const v16f (&accb)[2][NT], const v16f (&accr)[2][NT],
+                                           int64_t row0, int64_t col0, int r32, int h) {
   const float sb = DUAL ? *a.bt : 0.f, sr = *a.rt, sw = *a.wt;
 #pragma unroll
   for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      const int64_t col = n0 + wn * 64 + nt * 32 + r32;
+    for (int nt = 0; nt < NT; ++nt) {
+      const int64_t col = col0 + nt * 32 + r32;
       if (col >= a.N) continue;
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
-        const int64_t row = m0 + wm * 64 + mt * 32 + 8 * (j >> 2) + 4 * h + (j & 3);
+        const int64_t row = row0 + mt * 32 + 8 * (j >> 2) + 4 * h + (j & 3);
         if (row < a.M) {
           const float pr = __fmul_rn(sr, accr[mt][nt][j]);
           const float v = __fmul_rn(sw, DUAL ? __fadd_rn(__fmul_rn(sb, accb[mt][nt][j]), pr) : pr);
@@ -222,7 +223,7 @@ __global__ __launch_bounds__(kThreads, 1) void linear_nv_kernel(Args a) {
     __syncthreads();
   }
 
-  store_tile<OUT_F32, DUAL>(a, accb, accr, m0, n0, wm, wn, r32, h);
+  store_tile<OUT_F32, DUAL, 2>(a, accb, accr, m0 + wm * 64, n0 + wn * 64, r32, h);
 }
 
 // ---------------------------------------------------------------------------------
@@ -412,7 +413,248 @@ __global__ __launch_bounds__(kThreads, 2) void linear_nv_stream_kernel(Args a) {
   }
   SHARQ_NV_WAIT_VMCNT(0);
 
-  store_tile<OUT_F32, DUAL>(a, accb, accr, m0, n0, wm, wn, r32, h);
+  store_tile<OUT_F32, DUAL, 2>(a, accb, accr, m0 + wm * 64, n0 + wn * 64, r32, h);
+}
+
+// ---------------------------------------------------------------------------------
+// Wide variant (both activation paths, K % 64 == 0, enough output tiles to fill the
+// chip).  The same raw-payload streaming and register decode as the streaming kernel,
+// with a 64x128 tile per wave (2 x 4 instructions per path) and one wave per SIMD: a
+// wave decodes 2 x 64 activation rows and 128 weight rows per stage for 64 matrix
+// instructions, a third less vector work per instruction than at 64x64, and its 256
+// accumulators sit in the accumulation registers, so the wave's decode of the next
+// sub-step issues between its own matrix instructions.  4 waves (2 x 2) own a
+// 128 x 256 output tile; the ring holds 4 stages of 18 KiB.
+//
+// Stage layout (rows of 32 code bytes, then one scale word per row, same row order):
+// rows 0-127 A_b, 128-255 A_r, 256-511 W.  Per stage each wave loads 4 of the 16
+// code pieces (32 rows, 1 KiB) and 2 of the 8 scale pieces (64 rows, 256 B).
+constexpr int kWideBM = 128, kWideBN = 256;
+constexpr int kWideRows = 2 * kWideBM + kWideBN;                 // 512
+constexpr int kWideCodeBytes = kWideRows * 32;                   // 16 KiB
+constexpr int kWideStageBytes = kWideCodeBytes + kWideRows * 4;  // + 2 KiB of scales
+constexpr int kWideStages = 4;
+constexpr int kWideLds = kWideStages * kWideStageBytes;          // 72 KiB
+constexpr int kWideMinTiles = 256;
+
+template <bool OUT_F32>
+__global__ __launch_bounds__(kThreads, 1) void linear_nv_wide_kernel(Args a) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int r32 = lane & 31, h = lane >> 5;
+
+  int tm, tn;
+  tile_of(blockIdx.x, a.tiles_m, a.tiles_n, tm, tn);
+  const int64_t m0 = (int64_t)tm * kWideBM, n0 = (int64_t)tn * kWideBN;
+  const int64_t kb = a.K / 2, nbk = a.K / 16;
+  const int nk = (int)(a.K / BK);
+
+  // this wave's loads per stage (rows past an operand's end re-read its last row,
+  // never stored)
+  constexpr int kCodeLoads = 4, kScaleLoads = 2, kLoads = kCodeLoads + kScaleLoads;
+  const uint8_t* csrc[kCodeLoads];
+  int cdst[kCodeLoads];
+#pragma unroll
+  for (int j = 0; j < kCodeLoads; ++j) {
+    const int piece = kCodeLoads * wave + j;    // 0..15, 32 stage rows each
+    const int srow = 32 * piece + (lane >> 1);  // stage row of this lane's 16 bytes
+    const int t = srow < kWideBM ? 0 : srow < 2 * kWideBM ? 1 : 2;
+    const uint8_t* base = t == 0 ? a.bc : t == 1 ? a.rc : a.wc;
+    const int64_t rows = t == 2 ? a.N : a.M;
+    int64_t row = t == 2 ? n0 + (srow - 2 * kWideBM) : m0 + (srow - t * kWideBM);
+    row = row < rows ? row : rows - 1;
+    csrc[j] = base + row * kb + (lane & 1) * 16;
+    cdst[j] = piece * 1024;
+  }
+  const uint8_t* ssrc[kScaleLoads];
+  int sdst[kScaleLoads];
+#pragma unroll
+  for (int j = 0; j < kScaleLoads; ++j) {
+    const int piece = kScaleLoads * wave + j;  // 0..7, 64 stage rows each
+    const int srow = 64 * piece + lane;
+    const int t = srow < kWideBM ? 0 : srow < 2 * kWideBM ? 1 : 2;
+    const uint8_t* base = t == 0 ? a.bs : t == 1 ? a.rs : a.ws;
+    const int64_t rows = t == 2 ? a.N : a.M;
+    int64_t row = t == 2 ? n0 + (srow - 2 * kWideBM) : m0 + (srow - t * kWideBM);
+    row = row < rows ? row : rows - 1;
+    ssrc[j] = base + row * nbk;
+    sdst[j] = kWideCodeBytes + piece * 256;
+  }
+  auto dma = [&](int ks) {
+    uint8_t* st = smem + (ks % kWideStages) * kWideStageBytes;
+    const int64_t kc = ks < nk ? ks : nk - 1;  // past the end: re-load into a slot nobody reads
+#pragma unroll
+    for (int j = 0; j < kCodeLoads; ++j)
+      __builtin_amdgcn_global_load_lds(csrc[j] + kc * 32, (lds_void_t*)(st + cdst[j]), 16, 0, 0);
+#pragma unroll
+    for (int j = 0; j < kScaleLoads; ++j)
+      __builtin_amdgcn_global_load_lds(ssrc[j] + kc * 4, (lds_void_t*)(st + sdst[j]), 4, 0, 0);
+  };
+
+  // this lane's eight operand rows in the stage: A_b / A_r rows wm*64 + 32*mt + r32
+  // (q = 2*mt + path), W rows wn*128 + 32*nt + r32 (q = 4 + nt)
+  int roff[8];
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt) {
+    roff[2 * mt] = wm * 64 + mt * 32 + r32;
+    roff[2 * mt + 1] = kWideBM + wm * 64 + mt * 32 + r32;
+  }
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt) roff[4 + nt] = 2 * kWideBM + wn * 128 + nt * 32 + r32;
+  struct Raw {
+    u32x4 codes[8];
+    uint32_t scales[8];
+  };
+  auto read_raw = [&](Raw& r, int ks) {
+    const uint8_t* st = smem + (ks % kWideStages) * kWideStageBytes;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      r.codes[q] = *reinterpret_cast<const u32x4*>(st + roff[q] * 32 + h * 16);
+      r.scales[q] = *reinterpret_cast<const uint32_t*>(st + kWideCodeBytes + roff[q] * 4);  // 4 blocks
+    }
+  };
+
+  // accumulators [mt][nt] hold W-tile x A-tile products (weights as the instruction's A
+  // operand): lane (r32, h) holds output row 32*mt + r32 and the 4 consecutive columns
+  // 32*nt + 8*g + 4*h + {0..3} in elements 4g..4g+3
+  v16f accb[2][4], accr[2][4];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      accb[i][j] = v16f{};
+      accr[i][j] = v16f{};
+    }
+  // Sub-step i of a stage: 16 instructions on operands decoded during sub-step i-1 (for
+  // sub-step 0, during the previous stage's sub-step 3), while the next sub-step's
+  // eight operands are decoded one per two instructions.
+  v8h f[2][8];
+  v2h sc[8];
+  auto compute = [&](const Raw& r, const Raw& rn) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const v8h(&c)[8] = f[i & 1];
+      v8h(&n)[8] = f[(i + 1) & 1];
+      v2h scn[8];
+      if (i == 3) {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) scn[q] = scale_pair(rn.scales[q] >> (16 * h));  // blocks 2h, 2h+1
+      }
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int mt = j >> 3, path = (j >> 2) & 1, nt = j & 3;
+        if (path == 0)
+          accb[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(c[4 + nt], c[2 * mt], accb[mt][nt], 0, 0, 0);
+        else
+          accr[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(c[4 + nt], c[2 * mt + 1], accr[mt][nt], 0, 0, 0);
+        if (j & 1) {
+          const int q = j >> 1;
+          n[q] = i < 3 ? decode8(r.codes[q][i + 1], sc[q][(i + 1) >> 1]) : decode8(rn.codes[q][0], scn[q][0]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (i == 3) {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) sc[q] = scn[q];
+      }
+    }
+  };
+  auto barrier = [&]() {
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's raw reads have returned
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // one K-step: stage ks in `cur`, stage ks+1 read into `nxt` (past the last stage: a
+  // loaded slot, decoded and never used)
+  auto step = [&](const Raw& cur, Raw& nxt, int ks) {
+    read_raw(nxt, ks + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(cur, nxt);
+    __builtin_amdgcn_sched_barrier(0);
+    SHARQ_NV_WAIT_VMCNT((kWideStages - 2) * kLoads);  // this wave's loads of stage ks+2 landed
+    barrier();                  // ... everyone's; everyone has stage ks+1 in registers
+    dma(ks + kWideStages + 1);  // into the slot of stage ks+1
+  };
+
+  // at the top of step ks: stages ks and ks+1 landed and visible to all waves, stage
+  // ks in registers with its sub-step 0 decoded, this wave's loads of stages ks+2 ..
+  // ks+4 in flight
+#pragma unroll
+  for (int s = 0; s < kWideStages; ++s) dma(s);
+  SHARQ_NV_WAIT_VMCNT((kWideStages - 2) * kLoads);  // this wave's loads of stages 0 and 1 landed
+  barrier();
+  Raw ra, rb;
+  read_raw(ra, 0);
+  barrier();  // every wave has stage 0 in registers: its slot is free
+  dma(kWideStages);
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    sc[q] = scale_pair(ra.scales[q] >> (16 * h));
+    f[0][q] = decode8(ra.codes[q][0], sc[q][0]);
+  }
+  for (int ks = 0; ks < nk; ++ks) {
+    step(ra, rb, ks);
+    ra = rb;
+  }
+  SHARQ_NV_WAIT_VMCNT(0);
+  __syncthreads();  // the ring is free: the epilogue stages the output tile in it
+
+  // Epilogue: Y = S_w (S_b acc_b + S_r acc_r), each operation rounded to nearest.  A
+  // wave whose 64x128 tile lies inside Y (bf16, 16-byte aligned rows) writes it to its
+  // own LDS region and stores whole 16-byte row runs; others store element by element.
+  const float sb = *a.bt, sr = *a.rt, sw = *a.wt;
+  const int64_t row0 = m0 + wm * 64, col0 = n0 + wn * 128;
+  const bool fast = !OUT_F32 && row0 + 64 <= a.M && col0 + 128 <= a.N &&
+                    (reinterpret_cast<uintptr_t>(a.y) & 15u) == 0 && a.ldy % 8 == 0;
+  if (fast) {
+    constexpr int pitch = 128 * 2 + 16;
+    uint8_t* lds = smem + wave * (64 * pitch);
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          uint16_t o[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int e = 4 * g + i;
+            o[i] = f32_to_bf16_rne(
+                __fmul_rn(sw, __fadd_rn(__fmul_rn(sb, accb[mt][nt][e]), __fmul_rn(sr, accr[mt][nt][e]))));
+          }
+          *reinterpret_cast<u32x2*>(lds + (mt * 32 + r32) * pitch + (nt * 32 + 8 * g + 4 * h) * 2) =
+              u32x2{o[0] | ((uint32_t)o[1] << 16), o[2] | ((uint32_t)o[3] << 16)};
+        }
+    const int lr = lane >> 4, lc = lane & 15;  // 16 lanes per 256-byte row, 4 rows per pass
+#pragma unroll
+    for (int it = 0; it < 16; ++it) {
+      const int row = 4 * it + lr;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(lds + row * pitch + lc * 16);
+      *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(a.y) + (row0 + row) * a.ldy + col0 + lc * 8) = v;
+    }
+    return;
+  }
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int64_t row = row0 + mt * 32 + r32;
+        const int64_t col = col0 + nt * 32 + 8 * (e >> 2) + 4 * h + (e & 3);
+        if (row >= a.M || col >= a.N) continue;
+        const float v =
+            __fmul_rn(sw, __fadd_rn(__fmul_rn(sb, accb[mt][nt][e]), __fmul_rn(sr, accr[mt][nt][e])));
+        if constexpr (OUT_F32)
+          reinterpret_cast<float*>(a.y)[row * a.ldy + col] = v;
+        else
+          reinterpret_cast<uint16_t*>(a.y)[row * a.ldy + col] = f32_to_bf16_rne(v);
+      }
 }
 
 // The dynamic-LDS limit is a per-device function attribute, set once per device and
@@ -434,11 +676,25 @@ template <bool OUT_F32, bool DUAL>
 const void* stream_kernel() { return reinterpret_cast<const void*>(&linear_nv_stream_kernel<OUT_F32, DUAL>); }
 template <bool OUT_F32, bool DUAL>
 const void* generic_kernel() { return reinterpret_cast<const void*>(&linear_nv_kernel<OUT_F32, DUAL>); }
+template <bool OUT_F32>
+const void* wide_kernel() { return reinterpret_cast<const void*>(&linear_nv_wide_kernel<OUT_F32>); }
 
 template <bool OUT_F32, bool DUAL>
 hipError_t launch(const Args& a, hipStream_t stream) {
   const dim3 grid(a.tiles_m * a.tiles_n);
   hipError_t e;
+  if constexpr (DUAL) {
+    // the wide tiles when they still give every CU one
+    const int64_t wtm = (a.M + kWideBM - 1) / kWideBM, wtn = (a.N + kWideBN - 1) / kWideBN;
+    if (a.K % BK == 0 && wtm * wtn >= kWideMinTiles) {
+      Args w = a;
+      w.tiles_m = (int)wtm;
+      w.tiles_n = (int)wtn;
+      if ((e = configure<wide_kernel<OUT_F32>>(kWideLds)) != hipSuccess) return e;
+      linear_nv_wide_kernel<OUT_F32><<<dim3((unsigned)(wtm * wtn)), dim3(kThreads), kWideLds, stream>>>(w);
+      return hipGetLastError();
+    }
+  }
   if (a.K % BK == 0) {
     if ((e = configure<stream_kernel<OUT_F32, DUAL>>(kStreamLds)) != hipSuccess) return e;
     linear_nv_stream_kernel<OUT_F32, DUAL><<<grid, dim3(kThreads), kStreamLds, stream>>>(a);
