@@ -529,20 +529,17 @@ __global__ __launch_bounds__(kThreads, 1) void linear_nv_wide_kernel(Args a) {
       accr[i][j] = v16f{};
     }
   // Sub-step i of a stage: 16 instructions on operands decoded during sub-step i-1 (for
-  // sub-step 0, during the previous stage's sub-step 3), while the next sub-step's
-  // eight operands are decoded one per two instructions.
+  // sub-step 0, during the previous stage's sub-step 3).  After every instruction the
+  // wave issues half of the decode of one of the next sub-step's eight operands (two
+  // conversions and two scale products: vector work that fits under one instruction),
+  // and during sub-step 2 the next stage's block scales as well.
   v8h f[2][8];
-  v2h sc[8];
+  v2h sc[8], scn[8];
   auto compute = [&](const Raw& r, const Raw& rn) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const v8h(&c)[8] = f[i & 1];
       v8h(&n)[8] = f[(i + 1) & 1];
-      v2h scn[8];
-      if (i == 3) {
-#pragma unroll
-        for (int q = 0; q < 8; ++q) scn[q] = scale_pair(rn.scales[q] >> (16 * h));  // blocks 2h, 2h+1
-      }
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
         const int mt = j >> 3, path = (j >> 2) & 1, nt = j & 3;
@@ -550,10 +547,21 @@ __global__ __launch_bounds__(kThreads, 1) void linear_nv_wide_kernel(Args a) {
           accb[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(c[4 + nt], c[2 * mt], accb[mt][nt], 0, 0, 0);
         else
           accr[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(c[4 + nt], c[2 * mt + 1], accr[mt][nt], 0, 0, 0);
-        if (j & 1) {
-          const int q = j >> 1;
-          n[q] = i < 3 ? decode8(r.codes[q][i + 1], sc[q][(i + 1) >> 1]) : decode8(rn.codes[q][0], scn[q][0]);
-        }
+        // half (two dwords) of operand q of the next sub-step
+        const int q = j >> 1, half = j & 1;
+        const uint32_t codes = i < 3 ? r.codes[q][i + 1] : rn.codes[q][0];
+        const _Float16 s1 = i < 3 ? sc[q][(i + 1) >> 1] : scn[q][0];
+        const v2h s2 = {s1, s1};
+        // (the byte selector must be a literal)
+        const v2h p0 = (half ? __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 2)
+                             : __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 0)) * s2;  // exact
+        const v2h p1 = (half ? __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 3)
+                             : __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 1)) * s2;
+        n[q][4 * half] = p0[0];
+        n[q][4 * half + 1] = p0[1];
+        n[q][4 * half + 2] = p1[0];
+        n[q][4 * half + 3] = p1[1];
+        if (i == 2 && half) scn[q] = scale_pair(rn.scales[q] >> (16 * h));  // blocks 2h, 2h+1
         __builtin_amdgcn_sched_barrier(0);
       }
       if (i == 3) {
