@@ -483,15 +483,19 @@ __global__ __launch_bounds__(kThreads, 1) void linear_nv_wide_kernel(Args a) {
     ssrc[j] = base + row * nbk;
     sdst[j] = kWideCodeBytes + piece * 256;
   }
-  auto dma = [&](int ks) {
+  // load j (< kLoads) of stage ks (past the end: re-load into a slot nobody reads)
+  auto dma_one = [&](int j, int ks) {
     uint8_t* st = smem + (ks % kWideStages) * kWideStageBytes;
-    const int64_t kc = ks < nk ? ks : nk - 1;  // past the end: re-load into a slot nobody reads
-#pragma unroll
-    for (int j = 0; j < kCodeLoads; ++j)
+    const int64_t kc = ks < nk ? ks : nk - 1;
+    if (j < kCodeLoads)
       __builtin_amdgcn_global_load_lds(csrc[j] + kc * 32, (lds_void_t*)(st + cdst[j]), 16, 0, 0);
+    else
+      __builtin_amdgcn_global_load_lds(ssrc[j - kCodeLoads] + kc * 4, (lds_void_t*)(st + sdst[j - kCodeLoads]), 4,
+                                       0, 0);
+  };
+  auto dma = [&](int ks) {
 #pragma unroll
-    for (int j = 0; j < kScaleLoads; ++j)
-      __builtin_amdgcn_global_load_lds(ssrc[j] + kc * 4, (lds_void_t*)(st + sdst[j]), 4, 0, 0);
+    for (int j = 0; j < kLoads; ++j) dma_one(j, ks);
   };
 
   // this lane's eight operand rows in the stage: A_b / A_r rows wm*64 + 32*mt + r32
@@ -508,13 +512,14 @@ __global__ __launch_bounds__(kThreads, 1) void linear_nv_wide_kernel(Args a) {
     u32x4 codes[8];
     uint32_t scales[8];
   };
-  auto read_raw = [&](Raw& r, int ks) {
+  auto read_one = [&](Raw& r, int q, int ks) {
     const uint8_t* st = smem + (ks % kWideStages) * kWideStageBytes;
+    r.codes[q] = *reinterpret_cast<const u32x4*>(st + roff[q] * 32 + h * 16);
+    r.scales[q] = *reinterpret_cast<const uint32_t*>(st + kWideCodeBytes + roff[q] * 4);  // 4 blocks
+  };
+  auto read_raw = [&](Raw& r, int ks) {
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      r.codes[q] = *reinterpret_cast<const u32x4*>(st + roff[q] * 32 + h * 16);
-      r.scales[q] = *reinterpret_cast<const uint32_t*>(st + kWideCodeBytes + roff[q] * 4);  // 4 blocks
-    }
+    for (int q = 0; q < 8; ++q) read_one(r, q, ks);
   };
 
   // accumulators [mt][nt] hold W-tile x A-tile products (weights as the instruction's A
@@ -531,11 +536,12 @@ __global__ __launch_bounds__(kThreads, 1) void linear_nv_wide_kernel(Args a) {
   // Sub-step i of a stage: 16 instructions on operands decoded during sub-step i-1 (for
   // sub-step 0, during the previous stage's sub-step 3).  After every instruction the
   // wave issues half of the decode of one of the next sub-step's eight operands (two
-  // conversions and two scale products: vector work that fits under one instruction),
-  // and during sub-step 2 the next stage's block scales as well.
+  // conversions and two scale products: vector work that fits under one instruction);
+  // during sub-step 0 also this stage's share of the ring loads (stage ks+4) and the
+  // LDS reads of stage ks+1, during sub-step 2 the next stage's block scales.
   v8h f[2][8];
   v2h sc[8], scn[8];
-  auto compute = [&](const Raw& r, const Raw& rn) {
+  auto compute = [&](const Raw& r, Raw& rn, int ks) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const v8h(&c)[8] = f[i & 1];
@@ -562,6 +568,8 @@ __global__ __launch_bounds__(kThreads, 1) void linear_nv_wide_kernel(Args a) {
         n[q][4 * half + 2] = p1[0];
         n[q][4 * half + 3] = p1[1];
         if (i == 2 && half) scn[q] = scale_pair(rn.scales[q] >> (16 * h));  // blocks 2h, 2h+1
+        if (i == 0 && j < kLoads) dma_one(j, ks + kWideStages);  // into the slot of stage ks
+        if (i == 0 && j >= kLoads && j < kLoads + 8) read_one(rn, j - kLoads, ks + 1);
         __builtin_amdgcn_sched_barrier(0);
       }
       if (i == 3) {
@@ -577,21 +585,18 @@ __global__ __launch_bounds__(kThreads, 1) void linear_nv_wide_kernel(Args a) {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
     __builtin_amdgcn_sched_barrier(0);
   };
-  // one K-step: stage ks in `cur`, stage ks+1 read into `nxt` (past the last stage: a
-  // loaded slot, decoded and never used)
+  // one K-step: stage ks in `cur`, stage ks+1 read into `nxt` during it (past the last
+  // stage: a loaded slot, decoded and never used)
   auto step = [&](const Raw& cur, Raw& nxt, int ks) {
-    read_raw(nxt, ks + 1);
-    __builtin_amdgcn_sched_barrier(0);
-    compute(cur, nxt);
+    compute(cur, nxt, ks);
     __builtin_amdgcn_sched_barrier(0);
     SHARQ_NV_WAIT_VMCNT((kWideStages - 2) * kLoads);  // this wave's loads of stage ks+2 landed
-    barrier();                  // ... everyone's; everyone has stage ks+1 in registers
-    dma(ks + kWideStages + 1);  // into the slot of stage ks+1
+    barrier();  // ... everyone's; everyone has stage ks+1 in registers (its slot is free)
   };
 
   // at the top of step ks: stages ks and ks+1 landed and visible to all waves, stage
-  // ks in registers with its sub-step 0 decoded, this wave's loads of stages ks+2 ..
-  // ks+4 in flight
+  // ks in registers with its sub-step 0 decoded and its slot free, this wave's loads
+  // of stages ks+2 and ks+3 in flight (step ks adds those of stage ks+4)
 #pragma unroll
   for (int s = 0; s < kWideStages; ++s) dma(s);
   SHARQ_NV_WAIT_VMCNT((kWideStages - 2) * kLoads);  // this wave's loads of stages 0 and 1 landed
@@ -599,7 +604,6 @@ __global__ __launch_bounds__(kThreads, 1) void linear_nv_wide_kernel(Args a) {
   Raw ra, rb;
   read_raw(ra, 0);
   barrier();  // every wave has stage 0 in registers: its slot is free
-  dma(kWideStages);
 #pragma unroll
   for (int q = 0; q < 8; ++q) {
     sc[q] = scale_pair(ra.scales[q] >> (16 * h));
