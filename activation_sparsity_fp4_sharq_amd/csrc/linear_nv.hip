@@ -13,11 +13,12 @@
 // differs from exact arithmetic.  The two paths keep separate accumulators because
 // their tensor scales differ; the decoded weight operand is shared by both.
 //
-// Tiling: 256 threads (4 waves, 2x2) own a 128x128 output tile (64x64 per wave =
-// 2x2 instructions per path).  For K % 64 == 0 the raw payload is staged through LDS
-// and each wave decodes its operands in registers (linear_nv_stream_kernel); other K
-// take linear_nv_kernel, which decodes each 64-element K-step cooperatively into
-// fp16 LDS tiles (rows padded to 144 B), double-buffered.
+// Tiling: 256 threads (4 waves, 2x2).  For K % 64 == 0 the raw payload is staged
+// through LDS and each wave decodes its operands in registers: with both paths and at
+// least 256 output tiles of 128x256, linear_nv_wide_kernel (64x128 per wave, one wave
+// per SIMD); otherwise linear_nv_stream_kernel (128x128 tiles, 64x64 per wave, two
+// work-groups per CU).  Other K take linear_nv_kernel, which decodes each 64-element
+// K-step cooperatively into fp16 LDS tiles (rows padded to 144 B), double-buffered.
 #include <atomic>
 
 #include "sharq_internal.h"
