@@ -308,6 +308,32 @@ def test_linear_deterministic_and_guarded():
     assert np.array_equal(res[0], res[1])
 
 
+@pytest.mark.parametrize("fmt", [sharq.MXFP4, sharq.NVFP4], ids=["mx", "nv"])
+def test_linear_large_tiles_strided_output(fmt):
+    """The large-M kernels' bf16 epilogues (LDS-staged 16-byte row stores where a wave's
+    tile lies inside Y and rows are 16-byte aligned, element stores elsewhere) with a row
+    pitch padded to a multiple of 8, with an odd pitch, and with ragged M and N: the same
+    values as the contiguous output, nothing written past a row's N columns or past Y."""
+    M, N, K = 2040, 4090, 128
+    print(f"[linear] strided bf16 output M={M} N={N} K={K} fmt={fmt}", flush=True)
+    xb, wb = make_shape(M, N, K, seed=91)
+    weight = sharq.quantize(to_dev(wb), fmt)
+    bb, rr, _ = sharq.prep(to_dev(xb), 2, 4, fmt)
+    ref = sharq.linear(bb, rr, weight, sharq.OUT_BF16)
+    torch.cuda.synchronize()
+    ref = ref.view(torch.int16).cpu().numpy()
+    for ld in (N + 6, N + 3):
+        big = torch.full(((M + 1) * ld,), -1, dtype=torch.int16, device=DEV)  # 0xFFFF: a bf16 NaN
+        y = big.view(torch.bfloat16)[:M * ld].view(M, ld)[:, :N]  # row pitch ld
+        sharq.linear(bb, rr, weight, sharq.OUT_BF16, y=y)
+        torch.cuda.synchronize()
+        out = big.cpu().numpy()
+        assert np.all(out[M * ld:] == -1), f"ld={ld}: write past the output"
+        rows = out[:M * ld].reshape(M, ld)
+        assert np.all(rows[:, N:] == -1), f"ld={ld}: write into the row padding"
+        assert np.array_equal(rows[:, :N], ref), f"ld={ld}: values differ from the contiguous output"
+
+
 # ------------------------------------------------------------------ layouts
 
 @pytest.mark.parametrize("rows,K", [(1, 32), (37, 96), (300, 1056), (64, 4096)])
