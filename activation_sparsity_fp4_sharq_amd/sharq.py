@@ -325,6 +325,56 @@ def clock_probe(iters=20000, device=None, stream=None):
     return cycles / (ticks / 1e8) if ticks > 0 else float("nan")
 
 
+_raw = None
+
+
+def _raw_lib():
+    """The library through a second handle with no argtypes: calls pass ctypes instances
+    through unconverted (for pre-marshalled calls)."""
+    global _raw
+    if _raw is None:
+        lib()  # checks presence and the ABI
+        _raw = ctypes.CDLL(LIB_PATH)
+    return _raw
+
+
+def bind_forward(x, weight, n=2, m=4, out_dtype=OUT_BF16, bufs=None, y=None, ws=None, stream=None):
+    """`forward` with its arguments marshalled once: returns a zero-argument callable that
+    issues the same sharq_forward on the same buffers and stream (one foreign call per
+    invocation, for launch-bound shapes such as decode).  The callable keeps the buffers
+    alive; its `outputs` attribute is (y, (backbone, residual)).  A non-zero status raises
+    SharqError at the call."""
+    x = _as_bf16_2d(x)
+    fmt = weight.fmt
+    M, K = x.shape
+    N = weight.rows
+    bb, rr = bufs if bufs is not None else (Payload.empty(M, K, fmt, x.device, weight.layout),
+                                            Payload.empty(M, K, fmt, x.device, weight.layout))
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.float32 if out_dtype == OUT_FP32 else torch.bfloat16,
+                        device=x.device)
+    if ws is None:
+        need = max(lib().sharq_prep_workspace_bytes(M, K, fmt), lib().sharq_linear_workspace_bytes(M, N, K, fmt))
+        ws = workspace(need, x.device)
+    sb, sr, sw = bb.struct(), rr.struct(), weight.struct()
+    i64, ci = ctypes.c_int64, ctypes.c_int
+    args = (ctypes.c_void_p(x.data_ptr()), i64(M), i64(K), i64(x.stride(0)), ci(n), ci(m), ci(fmt),
+            ctypes.byref(sb), ctypes.byref(sr), ctypes.byref(sw), i64(N), ctypes.c_void_p(y.data_ptr()),
+            i64(y.stride(0)), ci(out_dtype), _ptr(ws), ctypes.c_size_t(0 if ws is None else ws.numel()),
+            _stream(stream))
+    fn = _raw_lib().sharq_forward
+    keep = (x, weight, bb, rr, y, ws, sb, sr, sw)
+
+    def call():
+        status = fn(*args)
+        if status != 0:
+            _check("sharq_forward", status)
+
+    call.outputs = (y, (bb, rr))
+    call._keep = keep
+    return call
+
+
 def forward(x, weight, n=2, m=4, out_dtype=OUT_BF16, bufs=None, y=None, ws=None, stream=None):
     """One SharQ linear layer: prep then both GEMMs, on one stream."""
     x = _as_bf16_2d(x)

@@ -134,3 +134,26 @@ def test_mlp_block_graph_replays_match_eager():
 
     check_replays(step, payload_tensors(b1) + payload_tensors(r1) + [gu] + payload_tensors(b2)
                   + payload_tensors(r2) + [y])
+
+
+@pytest.mark.parametrize("M,N,K,fmt", [(16, 512, 512, sharq.MXFP4), (300, 384, 640, sharq.MXFP4),
+                                       (130, 256, 512, sharq.NVFP4)])
+def test_bind_forward_matches_forward(M, N, K, fmt):
+    """The pre-marshalled sharq_forward call gives the same payloads and output as
+    `forward`, on every invocation."""
+    print(f"[bind] M={M} N={N} K={K} fmt={fmt}", flush=True)
+    xb, wb = make_shape(M, N, K, seed=3 * M + K)
+    x = to_dev(xb)
+    w = sharq.quantize(to_dev(wb), fmt)
+    y_ref, (b_ref, r_ref) = sharq.forward(x, w)
+    torch.cuda.synchronize()
+    want = snapshot(payload_tensors(b_ref) + payload_tensors(r_ref) + [y_ref])
+    call = sharq.bind_forward(x, w)
+    y, (bb, rr) = call.outputs
+    outs = payload_tensors(bb) + payload_tensors(rr) + [y]
+    for rep in range(3):
+        spoil(outs)
+        call()
+        torch.cuda.synchronize()
+        for i, (got, ref) in enumerate(zip(outs, want)):
+            assert torch.equal(got.view(torch.uint8), ref.view(torch.uint8)), f"call {rep}: output {i} differs"
