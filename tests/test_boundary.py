@@ -288,3 +288,17 @@ def test_prep_rmsnorm_workspace_and_device():
     import torch
     if not torch.cuda.is_available():
         assert prep_norm() == E_DEVICE
+
+
+def test_binding_fails_loudly_without_the_library(monkeypatch):
+    """No fallback: with the shared library absent every entry of the binding raises
+    (there is no CPU path to fall back to)."""
+    monkeypatch.setattr(sharq, "LIB_PATH", os.path.join(ROOT, "no_such_dir", "libsharq.so"))
+    monkeypatch.setattr(sharq, "_lib", None)
+    monkeypatch.setattr(sharq, "_raw", None)
+    with pytest.raises(RuntimeError, match="missing"):
+        sharq.lib()
+    with pytest.raises(RuntimeError, match="missing"):
+        sharq._raw_lib()
+    with pytest.raises(RuntimeError, match="missing"):
+        sharq.payload_sizes(16, 64, sharq.MXFP4, sharq.TILED)
