@@ -309,19 +309,24 @@ def test_linear_deterministic_and_guarded():
 
 
 @pytest.mark.parametrize("fmt", [sharq.MXFP4, sharq.NVFP4], ids=["mx", "nv"])
-def test_linear_large_tiles_strided_output(fmt):
+@pytest.mark.parametrize("M,N,K", [(2040, 4090, 128), (1930, 3850, 64)])
+def test_linear_large_tiles_strided_output(fmt, M, N, K):
     """The large-M kernels' bf16 epilogues (LDS-staged 16-byte row stores where a wave's
     tile lies inside Y and rows are 16-byte aligned, element stores elsewhere) with a row
     pitch padded to a multiple of 8, with an odd pitch, and with ragged M and N: the same
-    values as the contiguous output, nothing written past a row's N columns or past Y."""
-    M, N, K = 2040, 4090, 128
+    values as the contiguous output, nothing written past a row's N columns or past Y.
+    (1930 x 3850 leaves whole waves of the last row and column tiles outside Y; K = 64 is
+    a single K-step.)"""
     print(f"[linear] strided bf16 output M={M} N={N} K={K} fmt={fmt}", flush=True)
     xb, wb = make_shape(M, N, K, seed=91)
     weight = sharq.quantize(to_dev(wb), fmt)
     bb, rr, _ = sharq.prep(to_dev(xb), 2, 4, fmt)
-    ref = sharq.linear(bb, rr, weight, sharq.OUT_BF16)
+    y16 = sharq.linear(bb, rr, weight, sharq.OUT_BF16)
     torch.cuda.synchronize()
-    ref = ref.view(torch.int16).cpu().numpy()
+    ob, orr, _ = oracle.prep(xb, 2, 4, fmt)
+    ow = oracle.quantize(wb, fmt)
+    assert bf16_bound_check(y16, oracle.linear(ob, orr, ow, fmt), abs_linear(ob, orr, ow, fmt), K) <= 1.0
+    ref = y16.view(torch.int16).cpu().numpy()
     for ld in (N + 6, N + 3):
         big = torch.full(((M + 1) * ld,), -1, dtype=torch.int16, device=DEV)  # 0xFFFF: a bf16 NaN
         y = big.view(torch.bfloat16)[:M * ld].view(M, ld)[:, :N]  # row pitch ld
