@@ -129,11 +129,17 @@ def cpu_baseline(w, xb, wb, target_s):
     }
 
 
-def back_to_back_seconds(launch, reps, stream):
-    """Average device time of one launch, from HIP events on the launch stream around
-    `reps` consecutive launches.  A spin kernel holds the stream while the host queues
-    them, so the events bracket back-to-back execution rather than host submission
-    gaps (which would otherwise dominate for microsecond kernels)."""
+def back_to_back_seconds(launch, reps, stream, passes=3):
+    """Device time of one launch: the median over `passes` passes of the average from HIP
+    events on the launch stream around `reps` consecutive launches.  A spin kernel holds
+    the stream while the host queues them, so the events bracket back-to-back execution
+    rather than host submission gaps (which would otherwise dominate for microsecond
+    kernels)."""
+    times = sorted(_one_pass_seconds(launch, reps, stream) for _ in range(passes))
+    return times[len(times) // 2]
+
+
+def _one_pass_seconds(launch, reps, stream):
     import torch
 
     cycles = 1 << 23
