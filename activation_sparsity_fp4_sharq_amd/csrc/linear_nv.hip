@@ -437,6 +437,7 @@ constexpr int kWideStageBytes = kWideCodeBytes + kWideRows * 4;  // + 2 KiB of s
 constexpr int kWideStages = 4;
 constexpr int kWideLds = kWideStages * kWideStageBytes;          // 72 KiB
 constexpr int kWideMinTiles = 256;
+constexpr int kRsrcWord3 = 0x00020000;  // buffer resource word 3: raw (unswizzled) 32-bit data
 
 template <bool OUT_F32>
 __global__ __launch_bounds__(kThreads, 1) void linear_nv_wide_kernel(Args a) {
@@ -456,7 +457,11 @@ __global__ __launch_bounds__(kThreads, 1) void linear_nv_wide_kernel(Args a) {
   // this wave's loads per stage (rows past an operand's end re-read its last row,
   // never stored)
   constexpr int kCodeLoads = 4, kScaleLoads = 2, kLoads = kCodeLoads + kScaleLoads;
-  const uint8_t* csrc[kCodeLoads];
+  // sources as buffer resources (base, byte extent) and per-lane offsets: with buffer
+  // loads the compiler tracks the LDS-read counter in order, so a use of one LDS read
+  // waits for that read only (after global_load_lds it waits for all of them)
+  const uint8_t* cbase[kCodeLoads];
+  uint32_t cbytes[kCodeLoads], coff[kCodeLoads];
   int cdst[kCodeLoads];
 #pragma unroll
   for (int j = 0; j < kCodeLoads; ++j) {
@@ -467,10 +472,13 @@ __global__ __launch_bounds__(kThreads, 1) void linear_nv_wide_kernel(Args a) {
     const int64_t rows = t == 2 ? a.N : a.M;
     int64_t row = t == 2 ? n0 + (srow - 2 * kWideBM) : m0 + (srow - t * kWideBM);
     row = row < rows ? row : rows - 1;
-    csrc[j] = base + row * kb + (lane & 1) * 16;
+    cbase[j] = base;
+    cbytes[j] = (uint32_t)(rows * kb);
+    coff[j] = (uint32_t)(row * kb + (lane & 1) * 16);
     cdst[j] = piece * 1024;
   }
-  const uint8_t* ssrc[kScaleLoads];
+  const uint8_t* sbase[kScaleLoads];
+  uint32_t sbytes[kScaleLoads], soff[kScaleLoads];
   int sdst[kScaleLoads];
 #pragma unroll
   for (int j = 0; j < kScaleLoads; ++j) {
@@ -481,18 +489,26 @@ __global__ __launch_bounds__(kThreads, 1) void linear_nv_wide_kernel(Args a) {
     const int64_t rows = t == 2 ? a.N : a.M;
     int64_t row = t == 2 ? n0 + (srow - 2 * kWideBM) : m0 + (srow - t * kWideBM);
     row = row < rows ? row : rows - 1;
-    ssrc[j] = base + row * nbk;
+    sbase[j] = base;
+    sbytes[j] = (uint32_t)(rows * nbk);
+    soff[j] = (uint32_t)(row * nbk);
     sdst[j] = kWideCodeBytes + piece * 256;
   }
   // load j (< kLoads) of stage ks (past the end: re-load into a slot nobody reads)
   auto dma_one = [&](int j, int ks) {
     uint8_t* st = smem + (ks % kWideStages) * kWideStageBytes;
     const int64_t kc = ks < nk ? ks : nk - 1;
-    if (j < kCodeLoads)
-      __builtin_amdgcn_global_load_lds(csrc[j] + kc * 32, (lds_void_t*)(st + cdst[j]), 16, 0, 0);
-    else
-      __builtin_amdgcn_global_load_lds(ssrc[j - kCodeLoads] + kc * 4, (lds_void_t*)(st + sdst[j - kCodeLoads]), 4,
-                                       0, 0);
+    if (j < kCodeLoads) {
+      const __amdgpu_buffer_rsrc_t rs =
+          __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(cbase[j]), 0, cbytes[j], kRsrcWord3);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(st + cdst[j]), 16, coff[j] + (uint32_t)kc * 32, 0, 0,
+                                               0);
+    } else {
+      const int t = j - kCodeLoads;
+      const __amdgpu_buffer_rsrc_t rs =
+          __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(sbase[t]), 0, sbytes[t], kRsrcWord3);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(st + sdst[t]), 4, soff[t] + (uint32_t)kc * 4, 0, 0, 0);
+    }
   };
   auto dma = [&](int ks) {
 #pragma unroll
@@ -538,15 +554,19 @@ __global__ __launch_bounds__(kThreads, 1) void linear_nv_wide_kernel(Args a) {
   // sub-step 0, during the previous stage's sub-step 3).  After every instruction the
   // wave issues half of the decode of one of the next sub-step's eight operands (two
   // conversions and two scale products: vector work that fits under one instruction);
-  // during sub-step 0 also this stage's share of the ring loads (stage ks+4) and the
-  // LDS reads of stage ks+1, during sub-step 2 the next stage's block scales.
+  // during sub-step 0 also this stage's share of the ring loads (stage ks+4).  One set
+  // of raw registers serves all stages: operand q's bytes of stage ks are last used by
+  // the decode in sub-step 2, right after which the same registers receive stage ks+1's
+  // bytes from LDS; sub-step 3 turns them into the next stage's block scales and its
+  // first operands.
   v8h f[2][8];
   v2h sc[8], scn[8];
-  auto compute = [&](const Raw& r, Raw& rn, int ks) {
+  auto compute = [&](Raw& r, int ks) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const v8h(&c)[8] = f[i & 1];
       v8h(&n)[8] = f[(i + 1) & 1];
+      if (i == 3) scn[0] = scale_pair(r.scales[0] >> (16 * h));  // blocks 2h, 2h+1 of stage ks+1
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
         const int mt = j >> 3, path = (j >> 2) & 1, nt = j & 3;
@@ -554,9 +574,9 @@ __global__ __launch_bounds__(kThreads, 1) void linear_nv_wide_kernel(Args a) {
           accb[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(c[4 + nt], c[2 * mt], accb[mt][nt], 0, 0, 0);
         else
           accr[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(c[4 + nt], c[2 * mt + 1], accr[mt][nt], 0, 0, 0);
-        // half (two dwords) of operand q of the next sub-step
+        // half (two dwords) of operand q of the next sub-step (sub-step 3: of stage ks+1)
         const int q = j >> 1, half = j & 1;
-        const uint32_t codes = i < 3 ? r.codes[q][i + 1] : rn.codes[q][0];
+        const uint32_t codes = r.codes[q][(i + 1) & 3];
         const _Float16 s1 = i < 3 ? sc[q][(i + 1) >> 1] : scn[q][0];
         const v2h s2 = {s1, s1};
         // (the byte selector must be a literal)
@@ -568,9 +588,10 @@ __global__ __launch_bounds__(kThreads, 1) void linear_nv_wide_kernel(Args a) {
         n[q][4 * half + 1] = p0[1];
         n[q][4 * half + 2] = p1[0];
         n[q][4 * half + 3] = p1[1];
-        if (i == 2 && half) scn[q] = scale_pair(rn.scales[q] >> (16 * h));  // blocks 2h, 2h+1
         if (i == 0 && j < kLoads) dma_one(j, ks + kWideStages);  // into the slot of stage ks
-        if (i == 0 && j >= kLoads && j < kLoads + 8) read_one(rn, j - kLoads, ks + 1);
+        // stage ks+1 replaces stage ks in operand q's registers once q's last decode is issued
+        if (i == 2 && half) read_one(r, q, ks + 1);
+        if (i == 3 && half && q < 7) scn[q + 1] = scale_pair(r.scales[q + 1] >> (16 * h));
         __builtin_amdgcn_sched_barrier(0);
       }
       if (i == 3) {
@@ -586,10 +607,10 @@ __global__ __launch_bounds__(kThreads, 1) void linear_nv_wide_kernel(Args a) {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
     __builtin_amdgcn_sched_barrier(0);
   };
-  // one K-step: stage ks in `cur`, stage ks+1 read into `nxt` during it (past the last
-  // stage: a loaded slot, decoded and never used)
-  auto step = [&](const Raw& cur, Raw& nxt, int ks) {
-    compute(cur, nxt, ks);
+  // one K-step: stage ks in `r` on entry, stage ks+1 on exit (past the last stage: a
+  // loaded slot, decoded and never used)
+  auto step = [&](Raw& r, int ks) {
+    compute(r, ks);
     __builtin_amdgcn_sched_barrier(0);
     SHARQ_NV_WAIT_VMCNT((kWideStages - 2) * kLoads);  // this wave's loads of stage ks+2 landed
     barrier();  // ... everyone's; everyone has stage ks+1 in registers (its slot is free)
@@ -602,7 +623,7 @@ __global__ __launch_bounds__(kThreads, 1) void linear_nv_wide_kernel(Args a) {
   for (int s = 0; s < kWideStages; ++s) dma(s);
   SHARQ_NV_WAIT_VMCNT((kWideStages - 2) * kLoads);  // this wave's loads of stages 0 and 1 landed
   barrier();
-  Raw ra, rb;
+  Raw ra;
   read_raw(ra, 0);
   barrier();  // every wave has stage 0 in registers: its slot is free
 #pragma unroll
@@ -610,10 +631,7 @@ __global__ __launch_bounds__(kThreads, 1) void linear_nv_wide_kernel(Args a) {
     sc[q] = scale_pair(ra.scales[q] >> (16 * h));
     f[0][q] = decode8(ra.codes[q][0], sc[q][0]);
   }
-  for (int ks = 0; ks < nk; ++ks) {
-    step(ra, rb, ks);
-    ra = rb;
-  }
+  for (int ks = 0; ks < nk; ++ks) step(ra, ks);
   SHARQ_NV_WAIT_VMCNT(0);
   __syncthreads();  // the ring is free: the epilogue stages the output tile in it
 
@@ -699,7 +717,9 @@ hipError_t launch(const Args& a, hipStream_t stream) {
   if constexpr (DUAL) {
     // the wide tiles when they still give every CU one
     const int64_t wtm = (a.M + kWideBM - 1) / kWideBM, wtn = (a.N + kWideBN - 1) / kWideBN;
-    if (a.K % BK == 0 && wtm * wtn >= kWideMinTiles) {
+    // (buffer offsets are 32-bit: every payload below 2 GiB)
+    const bool small = (a.M > a.N ? a.M : a.N) * (a.K / 2) < ((int64_t)1 << 31);
+    if (a.K % BK == 0 && wtm * wtn >= kWideMinTiles && small) {
       Args w = a;
       w.tiles_m = (int)wtm;
       w.tiles_n = (int)wtn;
