@@ -322,9 +322,11 @@ __global__ __launch_bounds__(kThreads) void prep_mx_tiled_kernel(
   const int64_t frag0 = ((r0 >> 5) * (Kp / 64) + 2 * ks) * 1024;
   const int su = lane >> 4;
   const int off = (su >> 1) * 1024 + (su & 1) * 512 + (int)(((r0 & 31) + (lane & 15)) * 16);
-  __builtin_nontemporal_store(reinterpret_cast<const u32x4*>(my)[lane], reinterpret_cast<u32x4*>(rcodes + frag0 + off));
+  // ordinary (cached) stores: the GEMM reads these payloads next (measured: non-temporal
+  // stores here cost the 32760x3072 preparation about 4 %)
+  *reinterpret_cast<u32x4*>(rcodes + frag0 + off) = reinterpret_cast<const u32x4*>(my)[lane];
   if constexpr (MODE != 1)
-    __builtin_nontemporal_store(reinterpret_cast<const u32x4*>(myb)[lane], reinterpret_cast<u32x4*>(bcodes + frag0 + off));
+    *reinterpret_cast<u32x4*>(bcodes + frag0 + off) = reinterpret_cast<const u32x4*>(myb)[lane];
   if (q == 0) {
     reinterpret_cast<uint32_t*>(rscales)[ks * Mp + r] = rword;
     if constexpr (MODE != 1) reinterpret_cast<uint32_t*>(bscales)[ks * Mp + r] = bword;
