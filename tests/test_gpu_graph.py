@@ -157,3 +157,33 @@ def test_bind_forward_matches_forward(M, N, K, fmt):
         torch.cuda.synchronize()
         for i, (got, ref) in enumerate(zip(outs, want)):
             assert torch.equal(got.view(torch.uint8), ref.view(torch.uint8)), f"call {rep}: output {i} differs"
+
+
+def test_two_streams_concurrently_match_sequential():
+    """Two steps on two streams at once (different inputs, their own buffers and
+    workspaces) give the same bytes as each step alone: the library keeps no state
+    between calls beyond per-device kernel attributes."""
+    print("[streams] two concurrent steps", flush=True)
+    cases = [(300, 512, 640, sharq.MXFP4), (130, 256, 512, sharq.NVFP4)]
+    runs = []
+    for M, N, K, fmt in cases:
+        xb, wb = make_shape(M, N, K, seed=M * 7 + K)
+        x = to_dev(xb)
+        w = sharq.quantize(to_dev(wb), fmt)
+        y, (bb, rr) = sharq.forward(x, w, n=2, m=4)
+        torch.cuda.synchronize()
+        want = snapshot(payload_tensors(bb) + payload_tensors(rr) + [y])
+        runs.append((x, w, bb, rr, y, want))
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    for rep in range(3):
+        for x, w, bb, rr, y, want in runs:
+            spoil(payload_tensors(bb) + payload_tensors(rr) + [y])
+        torch.cuda.synchronize()
+        for (x, w, bb, rr, y, want), s in zip(runs, streams):
+            with torch.cuda.stream(s):
+                sharq.forward(x, w, n=2, m=4, bufs=(bb, rr), y=y)
+        torch.cuda.synchronize()
+        for i, (x, w, bb, rr, y, want) in enumerate(runs):
+            outs = payload_tensors(bb) + payload_tensors(rr) + [y]
+            for j, (got, ref) in enumerate(zip(outs, want)):
+                assert torch.equal(got.view(torch.uint8), ref.view(torch.uint8)), f"rep {rep}: case {i} output {j}"
