@@ -81,6 +81,28 @@ size_t rms_factor_offset(int fmt) { return fmt == SHARQ_NVFP4 ? round_up(kNvPrep
 
 }  // namespace
 
+// Every check of sharq_forward (both halves), before anything is enqueued; *need receives
+// the workspace both halves need.
+static sharq_status check_forward(const void* x, int64_t M, int64_t K, int64_t ldx, int sp_n, int sp_m, int fmt,
+                                  const sharq_fp4* backbone, const sharq_fp4* residual, const sharq_fp4* weight,
+                                  int64_t N, void* y, int64_t ldy, int out_dtype, size_t* need) {
+  sharq_status s = check_input(x, M, K, ldx, fmt);
+  if (s != SHARQ_OK) return s;
+  if ((s = check_pattern(sp_n, sp_m)) != SHARQ_OK) return s;
+  if (out_dtype != SHARQ_OUT_BF16 && out_dtype != SHARQ_OUT_FP32) return SHARQ_E_FORMAT;
+  if (N <= 0 || ldy < N || N > (int64_t)1 << 30) return SHARQ_E_SHAPE;
+  if ((s = check_payload(backbone, fmt, M)) != SHARQ_OK) return s;
+  if ((s = check_payload(residual, fmt, M)) != SHARQ_OK) return s;
+  if ((s = check_payload(weight, fmt, N)) != SHARQ_OK) return s;
+  if (backbone->layout != residual->layout || backbone->layout != weight->layout) return SHARQ_E_FORMAT;
+  if (M > 0 && !y) return SHARQ_E_NULL;
+  if (reinterpret_cast<uintptr_t>(y) & (out_dtype == SHARQ_OUT_FP32 ? 3u : 1u)) return SHARQ_E_ALIGN;
+  const size_t np = sharq_prep_workspace_bytes(M, K, fmt);
+  const size_t nl = sharq_linear_workspace_bytes(M, N, K, fmt);
+  *need = np > nl ? np : nl;
+  return SHARQ_OK;
+}
+
 // Shared by sharq_linear (backbone != NULL) and sharq_linear_dense (backbone == NULL:
 // one activation payload, passed as `residual`).
 static sharq_status linear_common(const sharq_fp4* backbone, const sharq_fp4* residual, int64_t M,
@@ -334,21 +356,10 @@ sharq_status sharq_forward(const void* x, int64_t M, int64_t K, int64_t ldx, int
                            const sharq_fp4* backbone, const sharq_fp4* residual, const sharq_fp4* weight,
                            int64_t N, void* y, int64_t ldy, int out_dtype, void* workspace,
                            size_t workspace_bytes, void* stream) {
-  // validate the linear half first so that nothing is enqueued when it would fail
-  sharq_status s = check_input(x, M, K, ldx, fmt);
+  size_t need = 0;
+  sharq_status s = check_forward(x, M, K, ldx, sp_n, sp_m, fmt, backbone, residual, weight, N, y, ldy, out_dtype,
+                                 &need);
   if (s != SHARQ_OK) return s;
-  if ((s = check_pattern(sp_n, sp_m)) != SHARQ_OK) return s;
-  if (out_dtype != SHARQ_OUT_BF16 && out_dtype != SHARQ_OUT_FP32) return SHARQ_E_FORMAT;
-  if (N <= 0 || ldy < N || N > (int64_t)1 << 30) return SHARQ_E_SHAPE;
-  if ((s = check_payload(backbone, fmt, M)) != SHARQ_OK) return s;
-  if ((s = check_payload(residual, fmt, M)) != SHARQ_OK) return s;
-  if ((s = check_payload(weight, fmt, N)) != SHARQ_OK) return s;
-  if (backbone->layout != residual->layout || backbone->layout != weight->layout) return SHARQ_E_FORMAT;
-  if (M > 0 && !y) return SHARQ_E_NULL;
-  if (reinterpret_cast<uintptr_t>(y) & (out_dtype == SHARQ_OUT_FP32 ? 3u : 1u)) return SHARQ_E_ALIGN;
-  size_t need = sharq_prep_workspace_bytes(M, K, fmt);
-  const size_t need_lin = sharq_linear_workspace_bytes(M, N, K, fmt);
-  if (need_lin > need) need = need_lin;
   if (need && (!workspace || workspace_bytes < need)) return SHARQ_E_WORKSPACE;
   if (need && !aligned16(workspace)) return SHARQ_E_ALIGN;
   s = sharq_prep(x, M, K, ldx, sp_n, sp_m, fmt, backbone, residual, nullptr, workspace, workspace_bytes,

@@ -38,17 +38,26 @@ class SharqError(RuntimeError):
         self.status = status
 
 
+ABI_VERSION = 7  # the SHARQ_ABI_VERSION of include/sharq.h this binding marshals for
+
 _lib = None
 
 
 def lib():
-    """Load libsharq.so (built in-tree by build.py); raise if it is absent."""
+    """Load libsharq.so (built in-tree by build.py); raise if it is absent or was built
+    for another ABI version than this binding's."""
     global _lib
     if _lib is None:
         if not os.path.exists(LIB_PATH):
             raise RuntimeError(f"{LIB_PATH} is missing: build it with "
                                "`python -m activation_sparsity_fp4_sharq_amd.build`")
         L = ctypes.CDLL(LIB_PATH)
+        L.sharq_abi_version.restype = ctypes.c_int
+        L.sharq_abi_version.argtypes = []
+        found = L.sharq_abi_version()
+        if found != ABI_VERSION:
+            raise RuntimeError(f"{LIB_PATH} has ABI version {found}, this binding expects {ABI_VERSION}: "
+                               "rebuild the library")
         i64, vp, sz = ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t
         P = ctypes.POINTER(SharqFp4)
         L.sharq_abi_version.restype = ctypes.c_int
@@ -122,6 +131,80 @@ def default_layout(fmt):
     return TILED if fmt == MXFP4 else ROWMAJOR
 
 
+# ------------------------------------------------------------------ argument checks
+# The C ABI receives raw pointers and cannot see buffer sizes, dtypes or devices, so the
+# binding checks every buffer it passes before the foreign call (ValueError, nothing
+# enqueued).
+
+_REQUIRE_CUDA = True  # tensors must live on a GPU (the CPU tests of these checks lift it)
+
+
+def _host_payload_sizes(rows, K, fmt, layout):
+    """(codes bytes, scales bytes) of a payload, from the layouts of include/sharq.h."""
+    if layout == TILED:
+        rp, kp = -(-rows // 32) * 32, -(-K // 128) * 128
+        return rp * kp // 2, rp * kp // 32
+    return rows * K // 2, rows * K // BLOCK[fmt]
+
+
+def _check_device(t, dev, what):
+    if _REQUIRE_CUDA and not t.is_cuda:
+        raise ValueError(f"{what} must be a CUDA tensor")
+    if dev is not None and t.device != dev:
+        raise ValueError(f"{what} is on {t.device}, expected {dev}")
+
+
+def _check_payload(p, fmt, rows, K, dev, what):
+    if not isinstance(p, Payload):
+        raise ValueError(f"{what} must be a Payload")
+    if p.fmt != fmt:
+        raise ValueError(f"{what} has format {p.fmt}, expected {fmt}")
+    if p.rows != rows or p.K != K:
+        raise ValueError(f"{what} is [{p.rows}, {p.K}], expected [{rows}, {K}]")
+    if p.layout not in (ROWMAJOR, TILED) or (p.layout == TILED and fmt != MXFP4):
+        raise ValueError(f"{what} has an invalid layout {p.layout} for format {fmt}")
+    if fmt not in BLOCK or K <= 0 or K % BLOCK[fmt] or rows < 0:
+        raise ValueError(f"{what}: invalid shape [{rows}, {K}] for format {fmt}")
+    cb, sb = _host_payload_sizes(rows, K, fmt, p.layout)
+    for t, need, name in ((p.codes, cb, "codes"), (p.scales, sb, "scales")):
+        if t.dtype != torch.uint8 or not t.is_contiguous():
+            raise ValueError(f"{what}.{name} must be a contiguous uint8 tensor")
+        if t.numel() < need:
+            raise ValueError(f"{what}.{name} holds {t.numel()} bytes, needs {need}")
+        _check_device(t, dev, f"{what}.{name}")
+    ts = p.tensor_scale
+    if ts is None or ts.dtype != torch.float32 or ts.numel() < 1:
+        raise ValueError(f"{what}.tensor_scale must be a float32 tensor of at least one element")
+    _check_device(ts, dev, f"{what}.tensor_scale")
+
+
+def _check_output(y, M, N, out_dtype, dev):
+    want = {OUT_FP32: torch.float32, OUT_BF16: torch.bfloat16}.get(out_dtype)
+    if want is None:
+        raise ValueError(f"unknown out_dtype {out_dtype}")
+    if y.dtype != want:
+        raise ValueError(f"y has dtype {y.dtype}, out_dtype {out_dtype} writes {want}")
+    if y.dim() != 2 or tuple(y.shape) != (M, N):
+        raise ValueError(f"y has shape {tuple(y.shape)}, expected ({M}, {N})")
+    if M > 0 and y.stride(1) != 1:
+        raise ValueError("y must have a unit column stride")
+    if M > 1 and y.stride(0) < N:
+        raise ValueError("y rows overlap (row stride < N)")
+    _check_device(y, dev, "y")
+
+
+def _check_workspace(ws, need, dev):
+    if need == 0 and ws is None:
+        return
+    if ws is None:
+        raise ValueError(f"a workspace of {need} bytes is required")
+    if ws.dtype != torch.uint8 or not ws.is_contiguous():
+        raise ValueError("the workspace must be a contiguous uint8 tensor")
+    if ws.numel() < need:
+        raise ValueError(f"the workspace holds {ws.numel()} bytes, needs {need}")
+    _check_device(ws, dev, "workspace")
+
+
 class Payload:
     """Device FP4 tensor [rows, K]: flat uint8 codes and scales in `layout`, plus a
     float32 tensor scale (NVFP4)."""
@@ -146,6 +229,7 @@ class Payload:
 
     def convert(self, layout, stream=None):
         """This payload in another layout (a new payload; on-device re-layout)."""
+        _check_payload(self, self.fmt, self.rows, self.K, self.codes.device, "payload")
         out = Payload.empty(self.rows, self.K, self.fmt, self.codes.device, layout)
         src, dst = self.struct(), out.struct()
         _check("sharq_convert_layout", lib().sharq_convert_layout(ctypes.byref(src), ctypes.byref(dst), self.rows,
@@ -174,11 +258,22 @@ def workspace(nbytes, device):
 
 
 def _as_bf16_2d(x):
-    if x.dtype != torch.bfloat16 or x.dim() != 2 or not x.is_cuda:
-        raise ValueError("expected a 2-D bfloat16 CUDA tensor")
+    if x.dtype != torch.bfloat16 or x.dim() != 2:
+        raise ValueError("expected a 2-D bfloat16 tensor")
+    _check_device(x, None, "x")
     if x.stride(1) != 1:
         raise ValueError("the last dimension must be contiguous")
     return x
+
+
+def _prep_outputs(out, M, K, fmt, dev, layout):
+    bb, rr = out if out is not None else (Payload.empty(M, K, fmt, dev, layout),
+                                          Payload.empty(M, K, fmt, dev, layout))
+    _check_payload(bb, fmt, M, K, dev, "backbone")
+    _check_payload(rr, fmt, M, K, dev, "residual")
+    if bb.layout != rr.layout:
+        raise ValueError("backbone and residual must share a layout")
+    return bb, rr
 
 
 def quantize(x, fmt=MXFP4, layout=None, stream=None, out=None, ws=None):
@@ -188,8 +283,11 @@ def quantize(x, fmt=MXFP4, layout=None, stream=None, out=None, ws=None):
     rows, K = x.shape
     if out is None:
         out = Payload.empty(rows, K, fmt, x.device, layout)
+    _check_payload(out, fmt, rows, K, x.device, "out")
+    need = lib().sharq_prep_workspace_bytes(rows, K, fmt)
     if ws is None:
-        ws = workspace(lib().sharq_prep_workspace_bytes(rows, K, fmt), x.device)
+        ws = workspace(need, x.device)
+    _check_workspace(ws, need, x.device)
     st = out.struct()
     _check("sharq_quantize", lib().sharq_quantize(_ptr(x), rows, K, x.stride(0), fmt, ctypes.byref(st),
                                                   _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream)))
@@ -200,11 +298,12 @@ def prep(x, n=2, m=4, fmt=MXFP4, want_mask=False, out=None, ws=None, layout=None
     """SharQ activation preparation: returns (backbone, residual, mask_bits or None)."""
     x = _as_bf16_2d(x)
     M, K = x.shape
-    bb, rr = out if out is not None else (Payload.empty(M, K, fmt, x.device, layout),
-                                          Payload.empty(M, K, fmt, x.device, layout))
+    bb, rr = _prep_outputs(out, M, K, fmt, x.device, layout)
     mask = torch.empty((M, K // 8), dtype=torch.uint8, device=x.device) if want_mask else None
+    need = lib().sharq_prep_workspace_bytes(M, K, fmt)
     if ws is None:
-        ws = workspace(lib().sharq_prep_workspace_bytes(M, K, fmt), x.device)
+        ws = workspace(need, x.device)
+    _check_workspace(ws, need, x.device)
     sb, sr = bb.struct(), rr.struct()
     _check("sharq_prep", lib().sharq_prep(_ptr(x), M, K, x.stride(0), n, m, fmt, ctypes.byref(sb),
                                           ctypes.byref(sr), _ptr(mask), _ptr(ws),
@@ -220,11 +319,13 @@ def prep_rmsnorm(x, gamma, eps=1e-6, n=2, m=4, fmt=MXFP4, want_mask=False, out=N
     M, K = x.shape
     if gamma.dtype != torch.bfloat16 or gamma.dim() != 1 or gamma.numel() != K or not gamma.is_contiguous():
         raise ValueError("gamma must be a contiguous bfloat16 vector of K entries")
-    bb, rr = out if out is not None else (Payload.empty(M, K, fmt, x.device, layout),
-                                          Payload.empty(M, K, fmt, x.device, layout))
+    _check_device(gamma, x.device, "gamma")
+    bb, rr = _prep_outputs(out, M, K, fmt, x.device, layout)
     mask = torch.empty((M, K // 8), dtype=torch.uint8, device=x.device) if want_mask else None
+    need = lib().sharq_prep_rmsnorm_workspace_bytes(M, K, fmt)
     if ws is None:
-        ws = workspace(lib().sharq_prep_rmsnorm_workspace_bytes(M, K, fmt), x.device)
+        ws = workspace(need, x.device)
+    _check_workspace(ws, need, x.device)
     sb, sr = bb.struct(), rr.struct()
     _check("sharq_prep_rmsnorm", lib().sharq_prep_rmsnorm(_ptr(x), M, K, x.stride(0), _ptr(gamma), float(eps), n, m,
                                                           fmt, ctypes.byref(sb), ctypes.byref(sr), _ptr(mask),
@@ -238,10 +339,18 @@ def linear(backbone, residual, weight, out_dtype=OUT_BF16, y=None, ws=None, stre
     fmt = weight.fmt
     M, K, N = backbone.rows, backbone.K, weight.rows
     dev = weight.codes.device
+    _check_payload(weight, fmt, N, K, dev, "weight")
+    _check_payload(backbone, fmt, M, K, dev, "backbone")
+    _check_payload(residual, fmt, M, K, dev, "residual")
+    if not backbone.layout == residual.layout == weight.layout:
+        raise ValueError("backbone, residual and weight must share a layout")
     if y is None:
         y = torch.empty((M, N), dtype=torch.float32 if out_dtype == OUT_FP32 else torch.bfloat16, device=dev)
+    _check_output(y, M, N, out_dtype, dev)
+    need = lib().sharq_linear_workspace_bytes(M, N, K, fmt)
     if ws is None:
-        ws = workspace(lib().sharq_linear_workspace_bytes(M, N, K, fmt), dev)
+        ws = workspace(need, dev)
+    _check_workspace(ws, need, dev)
     sb, sr, sw = backbone.struct(), residual.struct(), weight.struct()
     _check("sharq_linear", lib().sharq_linear(ctypes.byref(sb), ctypes.byref(sr), M, ctypes.byref(sw), N, K,
                                               fmt, _ptr(y), y.stride(0), out_dtype, _ptr(ws),
@@ -254,10 +363,17 @@ def linear_dense(a, weight, out_dtype=OUT_BF16, y=None, ws=None, stream=None):
     fmt = weight.fmt
     M, K, N = a.rows, a.K, weight.rows
     dev = weight.codes.device
+    _check_payload(weight, fmt, N, K, dev, "weight")
+    _check_payload(a, fmt, M, K, dev, "a")
+    if a.layout != weight.layout:
+        raise ValueError("a and weight must share a layout")
     if y is None:
         y = torch.empty((M, N), dtype=torch.float32 if out_dtype == OUT_FP32 else torch.bfloat16, device=dev)
+    _check_output(y, M, N, out_dtype, dev)
+    need = lib().sharq_linear_workspace_bytes(M, N, K, fmt)
     if ws is None:
-        ws = workspace(lib().sharq_linear_workspace_bytes(M, N, K, fmt), dev)
+        ws = workspace(need, dev)
+    _check_workspace(ws, need, dev)
     sa, sw = a.struct(), weight.struct()
     _check("sharq_linear_dense", lib().sharq_linear_dense(ctypes.byref(sa), M, ctypes.byref(sw), N, K, fmt, _ptr(y),
                                                           y.stride(0), out_dtype, _ptr(ws),
@@ -270,14 +386,16 @@ def prep_swiglu(gate_up, I, n=2, m=4, fmt=MXFP4, want_mask=False, out=None, ws=N
     columns [0, I), up in [I, 2I)): returns (backbone, residual, mask_bits or None)."""
     if gate_up.dtype != torch.bfloat16 or gate_up.dim() != 2 or gate_up.stride(1) != 1:
         raise ValueError("gate_up must be a 2-D bf16 tensor with unit column stride")
+    _check_device(gate_up, None, "gate_up")
     M = gate_up.shape[0]
     if gate_up.shape[1] < 2 * I:
         raise ValueError("gate_up needs at least 2*I columns")
-    bb, rr = out if out is not None else (Payload.empty(M, I, fmt, gate_up.device, layout),
-                                          Payload.empty(M, I, fmt, gate_up.device, layout))
+    bb, rr = _prep_outputs(out, M, I, fmt, gate_up.device, layout)
     mask = torch.empty((M, I // 8), dtype=torch.uint8, device=gate_up.device) if want_mask else None
+    need = lib().sharq_prep_workspace_bytes(M, I, fmt)
     if ws is None:
-        ws = workspace(lib().sharq_prep_workspace_bytes(M, I, fmt), gate_up.device)
+        ws = workspace(need, gate_up.device)
+    _check_workspace(ws, need, gate_up.device)
     sb, sr = bb.struct(), rr.struct()
     _check("sharq_prep_swiglu", lib().sharq_prep_swiglu(_ptr(gate_up), M, I, gate_up.stride(0), n, m, fmt,
                                                         ctypes.byref(sb), ctypes.byref(sr), _ptr(mask), _ptr(ws),
@@ -294,11 +412,12 @@ def prep_ablation(x, variant, n=2, m=4, fmt=MXFP4, want_mask=False, out=None, ws
     """sharq_prep with one of the ablations (ABLATE_*): returns (backbone, residual, mask_bits or None)."""
     x = _as_bf16_2d(x)
     M, K = x.shape
-    bb, rr = out if out is not None else (Payload.empty(M, K, fmt, x.device, layout),
-                                          Payload.empty(M, K, fmt, x.device, layout))
+    bb, rr = _prep_outputs(out, M, K, fmt, x.device, layout)
     mask = torch.empty((M, K // 8), dtype=torch.uint8, device=x.device) if want_mask else None
+    need = lib().sharq_prep_workspace_bytes(M, K, fmt)
     if ws is None:
-        ws = workspace(lib().sharq_prep_workspace_bytes(M, K, fmt), x.device)
+        ws = workspace(need, x.device)
+    _check_workspace(ws, need, x.device)
     sb, sr = bb.struct(), rr.struct()
     _check("sharq_prep_ablation", lib().sharq_prep_ablation(_ptr(x), M, K, x.stride(0), n, m, fmt, variant,
                                                             ctypes.byref(sb), ctypes.byref(sr), _ptr(mask), _ptr(ws),
@@ -308,8 +427,11 @@ def prep_ablation(x, variant, n=2, m=4, fmt=MXFP4, want_mask=False, out=None, ws
 
 def dequantize(p, out=None, stream=None):
     """fp32 values [rows, K] of a payload, on the device."""
+    dev = p.codes.device
+    _check_payload(p, p.fmt, p.rows, p.K, dev, "payload")
     if out is None:
-        out = torch.empty((p.rows, p.K), dtype=torch.float32, device=p.codes.device)
+        out = torch.empty((p.rows, p.K), dtype=torch.float32, device=dev)
+    _check_output(out, p.rows, p.K, OUT_FP32, dev)
     st = p.struct()
     _check("sharq_dequantize", lib().sharq_dequantize(ctypes.byref(st), p.rows, p.K, p.fmt, _ptr(out), out.stride(0),
                                                       _stream(stream)))
@@ -325,6 +447,29 @@ def clock_probe(iters=20000, device=None, stream=None):
     return cycles / (ticks / 1e8) if ticks > 0 else float("nan")
 
 
+def _forward_args(x, weight, out_dtype, bufs, y, ws, with_workspace=True):
+    """Buffers of one forward call, allocated where absent and checked (no workspace when
+    with_workspace is false)."""
+    x = _as_bf16_2d(x)
+    fmt = weight.fmt
+    M, K = x.shape
+    N = weight.rows
+    dev = x.device
+    _check_payload(weight, fmt, N, K, dev, "weight")
+    bb, rr = _prep_outputs(bufs, M, K, fmt, dev, weight.layout)
+    if bb.layout != weight.layout:
+        raise ValueError("the activation payloads and the weight must share a layout")
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.float32 if out_dtype == OUT_FP32 else torch.bfloat16, device=dev)
+    _check_output(y, M, N, out_dtype, dev)
+    if with_workspace:
+        need = max(lib().sharq_prep_workspace_bytes(M, K, fmt), lib().sharq_linear_workspace_bytes(M, N, K, fmt))
+        if ws is None:
+            ws = workspace(need, dev)
+        _check_workspace(ws, need, dev)
+    return x, bb, rr, y, ws, M, K, N, fmt
+
+
 _raw = None
 
 
@@ -333,7 +478,7 @@ def _raw_lib():
     through unconverted (for pre-marshalled calls)."""
     global _raw
     if _raw is None:
-        lib()  # checks presence and the ABI
+        lib()  # checks presence and the ABI version
         _raw = ctypes.CDLL(LIB_PATH)
     return _raw
 
@@ -344,18 +489,7 @@ def bind_forward(x, weight, n=2, m=4, out_dtype=OUT_BF16, bufs=None, y=None, ws=
     invocation, for launch-bound shapes such as decode).  The callable keeps the buffers
     alive; its `outputs` attribute is (y, (backbone, residual)).  A non-zero status raises
     SharqError at the call."""
-    x = _as_bf16_2d(x)
-    fmt = weight.fmt
-    M, K = x.shape
-    N = weight.rows
-    bb, rr = bufs if bufs is not None else (Payload.empty(M, K, fmt, x.device, weight.layout),
-                                            Payload.empty(M, K, fmt, x.device, weight.layout))
-    if y is None:
-        y = torch.empty((M, N), dtype=torch.float32 if out_dtype == OUT_FP32 else torch.bfloat16,
-                        device=x.device)
-    if ws is None:
-        need = max(lib().sharq_prep_workspace_bytes(M, K, fmt), lib().sharq_linear_workspace_bytes(M, N, K, fmt))
-        ws = workspace(need, x.device)
+    x, bb, rr, y, ws, M, K, N, fmt = _forward_args(x, weight, out_dtype, bufs, y, ws)
     sb, sr, sw = bb.struct(), rr.struct(), weight.struct()
     i64, ci = ctypes.c_int64, ctypes.c_int
     args = (ctypes.c_void_p(x.data_ptr()), i64(M), i64(K), i64(x.stride(0)), ci(n), ci(m), ci(fmt),
@@ -377,21 +511,11 @@ def bind_forward(x, weight, n=2, m=4, out_dtype=OUT_BF16, bufs=None, y=None, ws=
 
 def forward(x, weight, n=2, m=4, out_dtype=OUT_BF16, bufs=None, y=None, ws=None, stream=None):
     """One SharQ linear layer: prep then both GEMMs, on one stream."""
-    x = _as_bf16_2d(x)
-    fmt = weight.fmt
-    M, K = x.shape
-    N = weight.rows
-    bb, rr = bufs if bufs is not None else (Payload.empty(M, K, fmt, x.device, weight.layout),
-                                            Payload.empty(M, K, fmt, x.device, weight.layout))
-    if y is None:
-        y = torch.empty((M, N), dtype=torch.float32 if out_dtype == OUT_FP32 else torch.bfloat16,
-                        device=x.device)
-    if ws is None:
-        need = max(lib().sharq_prep_workspace_bytes(M, K, fmt), lib().sharq_linear_workspace_bytes(M, N, K, fmt))
-        ws = workspace(need, x.device)
+    x, bb, rr, y, ws, M, K, N, fmt = _forward_args(x, weight, out_dtype, bufs, y, ws)
     sb, sr, sw = bb.struct(), rr.struct(), weight.struct()
     _check("sharq_forward", lib().sharq_forward(_ptr(x), M, K, x.stride(0), n, m, fmt, ctypes.byref(sb),
                                                 ctypes.byref(sr), ctypes.byref(sw), N, _ptr(y), y.stride(0),
                                                 out_dtype, _ptr(ws), 0 if ws is None else ws.numel(),
                                                 _stream(stream)))
     return y, (bb, rr)
+

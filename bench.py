@@ -1,6 +1,6 @@
 """Benchmark: one SharQ linear layer (preparation + both FP4 GEMMs) per step on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload prefill]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload dit]
 
 A step is the whole hot path over one batch: sharq_prep (mask, FP4 backbone,
 residual against the dequantized backbone, FP4 residual) then sharq_linear (backbone
@@ -38,7 +38,9 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
-    p.add_argument("--workload", default="prefill")
+    p.add_argument("--workload", default="dit",
+                   help="tiny | decode | prefill | mlp_down_nvfp4 | dit (default: the long-sequence DiT-like "
+                        "layer, 32760x3072x3072, the largest single-GPU workload, timed end to end) | mlp_block")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--graph", action="store_true",
                    help="issue each timed step as the replay of one HIP graph holding its launches "
@@ -114,6 +116,17 @@ def cpu_baseline(w, xb, wb, target_s):
             break
         rows = min(w.M, max(rows * 2, int(rows * target_s / max(total, 1e-3) / 2)))
     flops = 2.0 * rows * w.N * w.K
+    # one thread on a small slice of the same rows: the oracle's single-core rate
+    threads = oracle.threads()
+    rows1 = max(1, min(rows, 16))
+    oracle.set_threads(1)
+    try:
+        t3 = time.perf_counter()
+        ob1, or1, _ = oracle.prep(xb[:rows1], w.n, w.m, w.fmt)
+        oracle.linear(ob1, or1, ow, w.fmt)
+        t_single = time.perf_counter() - t3
+    finally:
+        oracle.set_threads(threads)
     model = None
     try:
         with open("/proc/cpuinfo") as f:
@@ -121,7 +134,9 @@ def cpu_baseline(w, xb, wb, target_s):
     except OSError:
         pass
     return {
-        "value": flops / total / 1e12, "unit": "TFLOP/s", "cores": oracle.threads(), "kind": "oracle",
+        "value": flops / total / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+        "single_thread": {"value": 2.0 * rows1 * w.N * w.K / t_single / 1e12, "unit": "TFLOP/s",
+                          "rows": rows1, "seconds": t_single},
         "cpu_model": model,
         "sample": f"{rows} of {w.M} rows of the {w.name} workload: oracle prep {t1 - t0:.3f} s + fp64 "
                   f"two-GEMM linear {t2 - t1:.3f} s (weight quantization {t_wq:.2f} s excluded)",
@@ -582,6 +597,15 @@ def main():
         wsets = [(wt,)] + [(wt.clone(),) for _ in range(nsets - 1)]
         out["comparison"] = comparison_points(w, [(s_[0], s_[1]) for s_ in sets], wsets, ws, stream,
                                               args.steps, t_prep, t_lin)
+    # the stated targets: preparation >= 70 % of HBM bandwidth and the fused linear >= 50 % of
+    # the matrix peak on the prefill-sized workloads (the latter only reachable as issued-MFMA
+    # utilization: gfx950 has no sparse FP4 instruction, so the backbone runs zero-filled)
+    if w.name in ("prefill", "mlp_down_nvfp4", "dit"):
+        p_hbm = out["prep"]["pct_hbm"]
+        p_iss = out["linear"]["pct_peak_issued"]
+        out["targets"] = {"prep_pct_hbm": {"target": 70.0, "measured": p_hbm, "met": p_hbm >= 70.0},
+                          "linear_pct_peak_issued": {"target": 50.0, "measured": p_iss, "met": p_iss >= 50.0,
+                                                     "peak": gemm_peak}}
     if not args.no_cpu_baseline:
         cb = cpu_baseline(w, xb, wb, args.cpu_seconds)
         out["cpu_baseline"] = {k: (round(v, 6) if isinstance(v, float) else v) for k, v in cb.items()}

@@ -118,8 +118,8 @@ size_t sharq_prep_workspace_bytes(int64_t rows, int64_t K, int fmt);
 size_t sharq_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, int fmt);
 
 /* Plain FP4 quantization (no mask, no residual) of a bf16 matrix -- how a weight
- * payload W is produced (the pages pre-quantize the weights once; "share a single
- * FP4 weight payload", abstract).  Each block is quantized as the residual blocks
+ * payload W is produced (the pages quantize the weights once, and both GEMMs of the
+ * abstract read that one FP4 weight payload).  Each block is quantized as the residual blocks
  * of sharq_prep are: MXFP4 E8M0 exponent floor(log2 amax) - 2 and E2M1
  * round-to-nearest-even with saturation; NVFP4 with a tensor scale amax/2688.
  *   x       device bf16 [rows, ldx], first K columns used; 16-byte aligned, ldx % 8 == 0
@@ -279,9 +279,13 @@ sharq_status sharq_linear_dense(const sharq_fp4* a, int64_t M, const sharq_fp4* 
  * outside [1, 2^40] -> SHARQ_E_SHAPE; misaligned -> SHARQ_E_ALIGN. */
 sharq_status sharq_clock_probe(int64_t iters, uint64_t* counters, void* stream);
 
-/* One SharQ linear layer end to end: sharq_prep into the caller's backbone and
- * residual payloads, then sharq_linear, on one stream.  Arguments as above; the
- * workspace must cover both calls (max of the two *_workspace_bytes values). */
+/* One SharQ linear layer end to end (SharQ, arXiv 2606.26587: the abstract's
+ * decomposition as one layer; Figure 2's dataflow of the fused preparation feeding the
+ * sparse-backbone and dense-residual GEMMs over one weight payload): sharq_prep into
+ * the caller's backbone and residual payloads, then sharq_linear, on one stream.
+ * Arguments as above; the workspace must cover both calls (max of the two
+ * *_workspace_bytes values).  Errors: every argument of both calls is validated before
+ * the first launch, so on error nothing is enqueued. */
 sharq_status sharq_forward(const void* x, int64_t M, int64_t K, int64_t ldx, int sp_n, int sp_m,
                            int fmt, const sharq_fp4* backbone, const sharq_fp4* residual,
                            const sharq_fp4* weight, int64_t N, void* y, int64_t ldy,

@@ -530,6 +530,16 @@ void oracle_e4m3_encode_array(const float* q, int64_t n, uint8_t* out) {
   for (int64_t i = 0; i < n; ++i) out[i] = oracle_e4m3_encode(q[i]);
 }
 
+/* Thread count of the row loops (timing of the CPU baseline only; results do not
+ * depend on it). */
+void oracle_set_threads(int n) {
+#ifdef _OPENMP
+  if (n > 0) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}
+
 int oracle_omp_threads(void) {
 #ifdef _OPENMP
   return omp_get_max_threads();

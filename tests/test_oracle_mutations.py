@@ -1,0 +1,142 @@
+"""The NVFP4 worked examples pin reading R5's fp32 steps: each test below plants
+one plausible deviation from R5 in a temporary copy of the oracle's C source
+(on the CPU), builds it, and checks that a stored worked example then fails.
+
+R5 (NVFP4 with per-path tensor scales; SharQ, arXiv 2606.26587, abstract: the
+method runs on NVFP4 and names path-specific scale views): S = fp32(amax/2688),
+q = fp32(amax_blk / fp32(6 S)), s = E4M3(q), d = fp32(s S),
+code = E2M1(fp32(x / d)), Bhat = fp32(v d), R = fp32(x - Bhat).
+The stored values come from tests/golden/hand_examples.json; none of them was
+produced by the oracle.
+"""
+import ctypes
+import json
+import os
+import shutil
+import subprocess
+
+import numpy as np
+import pytest
+
+from activation_sparsity_fp4_sharq_amd.workloads import bf16_bits_to_f32, f32_to_bf16_bits
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(os.path.dirname(HERE), "oracle", "sharq_oracle.c")
+GOLDEN = os.path.join(HERE, "golden", "hand_examples.json")
+
+# (name, text of R5's step in the oracle, the same step with the deviation)
+MUTATIONS = [
+    ("6S unrounded", "  float q = amax / six_s;",
+     "  float q = (float)((double)amax / (6.0 * (double)S));"),
+    ("division reordered as (amax/6)/S", "  float q = amax / six_s;",
+     "  float q = (amax / 6.0f) / S;"),
+    ("q unrounded before E4M3", "  uint8_t sb = oracle_e4m3_encode(q);",
+     "  uint8_t sb = oracle_e4m3_encode_exact((double)amax / (double)six_s);"),
+    ("d unrounded", "      float t = v[i] / d;",
+     "      float t = (float)((double)v[i] / (oracle_e4m3_value(sb) * (double)S));"),
+    ("x/d unrounded (fp64 quotient)", "      codes[i] = oracle_e2m1_encode((double)t);",
+     "      codes[i] = oracle_e2m1_encode((double)v[i] / (double)d); (void)t;"),
+    ("R by fused multiply-add", "        float r = xv - bh;",
+     "        float r = fmt == ORACLE_MXFP4 ? xv - bh : fmaf(-(float)oracle_e2m1_value(c[j]),"
+     " (float)oracle_e4m3_value(sb) * Sb, xv);"),
+]
+
+# an E4M3 encoder of an unrounded quotient, for the "q unrounded" deviation
+EXACT_ENCODER = r"""
+static uint8_t oracle_e4m3_encode_exact(double q) {
+  if (!(q > 0.0)) return 0;
+  if (q >= 448.0) return 0x7E;
+  int e2;
+  (void)frexp(q, &e2);
+  int e = e2 - 1;
+  double step = (e < -6) ? ldexp(1.0, -9) : ldexp(1.0, e - 3);
+  double v = nearbyint(q / step) * step;
+  if (v >= 448.0) return 0x7E;
+  if (v == 0.0) return 0;
+  (void)frexp(v, &e2);
+  e = e2 - 1;
+  if (e < -6) return (uint8_t)(v / ldexp(1.0, -9));
+  return (uint8_t)(((e + 7) << 3) | (int)((v / ldexp(1.0, e) - 1.0) * 8.0));
+}
+"""
+
+
+def _nv_examples():
+    with open(GOLDEN) as f:
+        return [e for e in json.load(f)["examples"] if e["fmt"] == "nvfp4"]
+
+
+def _num(v):
+    return -0.0 if v == "-0" else float(v)
+
+
+def _build_variant(tmp_path, old, new):
+    text = open(SRC).read()
+    assert text.count(old) == 1, f"the step {old!r} must occur once in the oracle"
+    text = text.replace(old, new)
+    text = text.replace("/* ---------------------------------------------------------- block quantizers */",
+                        EXACT_ENCODER + "\n/* block quantizers */")
+    src = tmp_path / "oracle_variant.c"
+    src.write_text(text)
+    lib = tmp_path / "liboracle_variant.so"
+    subprocess.run(["gcc", "-O2", "-std=c99", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared",
+                    "-w", "-o", str(lib), str(src), "-lm"], check=True)
+    L = ctypes.CDLL(str(lib))
+    u8p = np.ctypeslib.ndpointer(np.uint8, flags="C_CONTIGUOUS")
+    u16p = np.ctypeslib.ndpointer(np.uint16, flags="C_CONTIGUOUS")
+    vp = ctypes.c_void_p
+    i64 = ctypes.c_int64
+    ci = ctypes.c_int
+    L.oracle_prep_variant.restype = ci
+    L.oracle_prep_variant.argtypes = [u16p, i64, i64, i64, ci, ci, ci, ci, u8p, u8p, vp, u8p, u8p, vp, vp, vp,
+                                      vp]
+    return L
+
+
+def _outputs(L, ex):
+    x = np.array([_num(v) for v in ex["x"]], np.float32)[None, :]
+    xb = f32_to_bf16_bits(x)
+    assert np.array_equal(bf16_bits_to_f32(xb), x)
+    K = x.shape[1]
+    bc = np.zeros((1, K // 2), np.uint8)
+    bs = np.zeros((1, K // 16), np.uint8)
+    rc = np.zeros_like(bc)
+    rs = np.zeros_like(bs)
+    bt = np.ones(1, np.float32)
+    rt = np.ones(1, np.float32)
+    resid = np.zeros((1, K), np.float32)
+    ptr = lambda a: a.ctypes.data_as(ctypes.c_void_p)
+    rcode = L.oracle_prep_variant(xb, 1, K, K, ex["n"], ex["m"], 1, 0, bc, bs, ptr(bt), rc, rs, ptr(rt), None,
+                                  None, ptr(resid))
+    assert rcode == 0
+
+    def unpack(p):
+        out = np.empty(K, np.uint8)
+        out[0::2] = p[0] & 15
+        out[1::2] = p[0] >> 4
+        return out.tolist()
+
+    want_r = np.array([_num(v) for v in ex["residual"]], np.float32)
+    return {
+        "backbone_codes": unpack(bc) == ex["backbone_codes"],
+        "backbone_scales": bs[0].tolist() == ex["backbone_scales"],
+        "residual_codes": unpack(rc) == ex["residual_codes"],
+        "residual_scales": rs[0].tolist() == ex["residual_scales"],
+        "tensor_scales": bt[0] == ex["backbone_tensor_scale"] and rt[0] == ex["residual_tensor_scale"],
+        "residual": np.array_equal(resid[0].view(np.uint32), want_r.view(np.uint32)),
+    }
+
+
+@pytest.mark.skipif(shutil.which("gcc") is None, reason="needs gcc to build the oracle variants")
+def test_unmodified_copy_reproduces_every_nv_example(tmp_path):
+    L = _build_variant(tmp_path, "  float q = amax / six_s;", "  float q = amax / six_s;")
+    for ex in _nv_examples():
+        assert all(_outputs(L, ex).values()), ex["name"]
+
+
+@pytest.mark.skipif(shutil.which("gcc") is None, reason="needs gcc to build the oracle variants")
+@pytest.mark.parametrize("name,old,new", MUTATIONS, ids=[m[0] for m in MUTATIONS])
+def test_nv_examples_catch_a_deviation_from_r5(tmp_path, name, old, new):
+    L = _build_variant(tmp_path, old, new)
+    failed = {ex["name"]: [k for k, ok in _outputs(L, ex).items() if not ok] for ex in _nv_examples()}
+    assert any(failed.values()), f"no worked example detects: {name}"
