@@ -7,6 +7,7 @@ output every element within one bf16 ulp of the oracle plus that bound, and a Fr
 relative error <= 2e-3.  Inputs come from the seeded generators only; the worked examples
 of tests/golden/hand_examples.json are compared with their stored (hand-derived) values.
 """
+import ctypes
 import json
 import os
 
@@ -361,7 +362,7 @@ def test_linear_deterministic_and_guarded():
     for _ in range(2):
         ld = N + 8
         big = torch.full(((M + 2) * ld,), float("nan"), dtype=torch.float32, device=DEV)
-        y = big[:M * ld].view(M, ld)
+        y = big[:M * ld].view(M, ld)[:, :N]  # an (M, N) view with row pitch ld
         sharq.linear(bb, rr, weight, sharq.OUT_FP32, y=y)
         torch.cuda.synchronize()
         out = big.cpu().numpy()
@@ -428,9 +429,15 @@ def test_linear_rejects_mixed_layouts():
     x, wt = to_dev(xb), to_dev(wb)
     w_rm = sharq.quantize(wt, sharq.MXFP4, layout=sharq.ROWMAJOR)
     bb, rr, _ = sharq.prep(x, 2, 4, sharq.MXFP4, layout=sharq.TILED)
-    with pytest.raises(sharq.SharqError) as e:
+    with pytest.raises(ValueError, match="layout"):  # the binding's check
         sharq.linear(bb, rr, w_rm)
-    assert e.value.status == 4
+    # and the library's own, through the C ABI
+    y = torch.empty((64, 64), dtype=torch.bfloat16, device=DEV)
+    sb, sr, sw = bb.struct(), rr.struct(), w_rm.struct()
+    status = sharq.lib().sharq_linear(ctypes.byref(sb), ctypes.byref(sr), 64, ctypes.byref(sw), 64, 128,
+                                      sharq.MXFP4, ctypes.c_void_p(y.data_ptr()), 64, sharq.OUT_BF16, None, 0,
+                                      ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    assert status == 4  # SHARQ_E_FORMAT
 
 
 # ------------------------------------------------------------ RMSNorm folded into the prep
