@@ -3,11 +3,40 @@
 // runs before anything is enqueued; no exception crosses the ABI.
 #include <string.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "sharq_internal.h"
 
 using namespace sharq;
 
+// Scratch of sharq_forward_noalloc: file-scope device memory, one copy per GPU the
+// library runs on, held until the process ends.  Host code never uses this name as an
+// address: each device's copy is resolved once with hipGetSymbolAddress (below).
+static __device__ __align__(256) uint8_t scratch[SHARQ_NOALLOC_SCRATCH_BYTES];
+
 namespace {
+
+// The device address of `scratch` on the current device (nullptr if it cannot be
+// resolved).  Resolved once per device, with that device current; later calls read
+// the cached address.
+void* scratch_address(int dev) {
+  static std::atomic<void*> cached[kMaxDevices];
+  static std::mutex lock;
+  if (dev < 0 || dev >= kMaxDevices) return nullptr;
+  void* p = cached[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  std::lock_guard<std::mutex> guard(lock);
+  p = cached[dev].load(std::memory_order_relaxed);
+  if (!p) {
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) {
+      (void)hipGetLastError();  // leave no sticky error for the caller's next call
+      return nullptr;
+    }
+    cached[dev].store(p, std::memory_order_release);
+  }
+  return p;
+}
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -367,6 +396,23 @@ sharq_status sharq_forward(const void* x, int64_t M, int64_t K, int64_t ldx, int
   if (s != SHARQ_OK) return s;
   return sharq_linear(backbone, residual, M, weight, N, K, fmt, y, ldy, out_dtype, workspace,
                       workspace_bytes, stream);
+}
+
+sharq_status sharq_forward_noalloc(const void* x, int64_t M, int64_t K, int64_t ldx, int sp_n, int sp_m, int fmt,
+                                   const sharq_fp4* backbone, const sharq_fp4* residual, const sharq_fp4* weight,
+                                   int64_t N, void* y, int64_t ldy, int out_dtype, void* stream) {
+  size_t need = 0;
+  sharq_status s = check_forward(x, M, K, ldx, sp_n, sp_m, fmt, backbone, residual, weight, N, y, ldy, out_dtype,
+                                 &need);
+  if (s != SHARQ_OK) return s;
+  if (need > SHARQ_NOALLOC_SCRATCH_BYTES) return SHARQ_E_WORKSPACE;  // beyond the fixed scratch
+  if ((s = check_device()) != SHARQ_OK) return s;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return SHARQ_E_DEVICE;
+  void* ws = scratch_address(dev);
+  if (!ws) return SHARQ_E_DEVICE;
+  return sharq_forward(x, M, K, ldx, sp_n, sp_m, fmt, backbone, residual, weight, N, y, ldy, out_dtype, ws,
+                       SHARQ_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 }  // extern "C"

@@ -64,6 +64,7 @@ size_t linear_nv_workspace(int64_t M, int64_t N, int64_t K);
 hipError_t launch_clock_probe(int64_t iters, uint64_t* out, hipStream_t stream);
 
 constexpr size_t kNvPrepWorkspace = 16448;  // 16 + 2 * 2048 dwords: maxima and partials
+static_assert(SHARQ_NOALLOC_SCRATCH_BYTES >= kNvPrepWorkspace, "the fixed scratch must cover the preparation");
 constexpr int kMaxDevices = 64;
 
 }  // namespace sharq

@@ -24,7 +24,7 @@ SYMBOLS = ["sharq_abi_version", "sharq_status_str", "sharq_payload_bytes", "shar
            "sharq_prep_workspace_bytes", "sharq_linear_workspace_bytes", "sharq_quantize", "sharq_prep",
            "sharq_prep_rmsnorm_workspace_bytes", "sharq_prep_rmsnorm", "sharq_linear", "sharq_linear_dense",
            "sharq_clock_probe", "sharq_prep_ablation", "sharq_dequantize", "sharq_prep_swiglu",
-           "sharq_forward"]
+           "sharq_forward", "sharq_forward_noalloc"]
 
 
 class SharqFp4(ctypes.Structure):
@@ -38,7 +38,7 @@ class SharqError(RuntimeError):
         self.status = status
 
 
-ABI_VERSION = 7  # the SHARQ_ABI_VERSION of include/sharq.h this binding marshals for
+ABI_VERSION = 8  # the SHARQ_ABI_VERSION of include/sharq.h this binding marshals for
 
 _lib = None
 
@@ -101,6 +101,9 @@ def lib():
         L.sharq_forward.restype = ctypes.c_int
         L.sharq_forward.argtypes = [vp, i64, i64, i64, ctypes.c_int, ctypes.c_int, ctypes.c_int, P, P, P,
                                     i64, vp, i64, ctypes.c_int, vp, sz, vp]
+        L.sharq_forward_noalloc.restype = ctypes.c_int
+        L.sharq_forward_noalloc.argtypes = [vp, i64, i64, i64, ctypes.c_int, ctypes.c_int, ctypes.c_int, P, P, P,
+                                            i64, vp, i64, ctypes.c_int, vp]
         _lib = L
     return _lib
 
@@ -519,3 +522,14 @@ def forward(x, weight, n=2, m=4, out_dtype=OUT_BF16, bufs=None, y=None, ws=None,
                                                 _stream(stream)))
     return y, (bb, rr)
 
+
+def forward_noalloc(x, weight, n=2, m=4, out_dtype=OUT_BF16, bufs=None, y=None, stream=None):
+    """`forward` through sharq_forward_noalloc: the library's fixed per-device scratch in
+    place of a workspace (the caller still passes, or here lets the binding allocate,
+    the inputs and outputs).  Calls on one GPU share that scratch: do not overlap them."""
+    x, bb, rr, y, _, M, K, N, fmt = _forward_args(x, weight, out_dtype, bufs, y, None, with_workspace=False)
+    sb, sr, sw = bb.struct(), rr.struct(), weight.struct()
+    _check("sharq_forward_noalloc", lib().sharq_forward_noalloc(_ptr(x), M, K, x.stride(0), n, m, fmt,
+                                                                ctypes.byref(sb), ctypes.byref(sr), ctypes.byref(sw),
+                                                                N, _ptr(y), y.stride(0), out_dtype, _stream(stream)))
+    return y, (bb, rr)

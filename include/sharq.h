@@ -61,7 +61,7 @@
 extern "C" {
 #endif
 
-#define SHARQ_ABI_VERSION 7
+#define SHARQ_ABI_VERSION 8
 
 typedef enum sharq_status {
   SHARQ_OK = 0,
@@ -290,6 +290,26 @@ sharq_status sharq_forward(const void* x, int64_t M, int64_t K, int64_t ldx, int
                            int fmt, const sharq_fp4* backbone, const sharq_fp4* residual,
                            const sharq_fp4* weight, int64_t N, void* y, int64_t ldy,
                            int out_dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation): sharq_forward without a workspace
+ * argument.  Its scratch (the NVFP4 preparation's partial and tensor maxima) is a fixed
+ * array of SHARQ_NOALLOC_SCRATCH_BYTES bytes in the library's own device memory, one
+ * copy per GPU, held until the process ends; the first call on a device resolves that
+ * device's copy.  Nothing is allocated or freed, by the library or by any library it
+ * calls.
+ *   Arguments, outputs and errors as for sharq_forward; a shape whose workspace would
+ *   exceed the scratch -> SHARQ_E_WORKSPACE (no shape does today: the preparation's
+ *   workspace is a constant and the GEMMs need none); the scratch cannot be resolved on
+ *   the current device -> SHARQ_E_DEVICE.
+ *   Every call on one GPU shares that GPU's scratch, which keeps the last call's
+ *   contents (a call writes every scratch word before it reads it): calls that overlap
+ *   on one GPU, on any streams, race. */
+#define SHARQ_NOALLOC_SCRATCH_BYTES 16640
+sharq_status sharq_forward_noalloc(const void* x, int64_t M, int64_t K, int64_t ldx, int sp_n, int sp_m,
+                                   int fmt, const sharq_fp4* backbone, const sharq_fp4* residual,
+                                   const sharq_fp4* weight, int64_t N, void* y, int64_t ldy, int out_dtype,
+                                   void* stream);
 
 #ifdef __cplusplus
 }

@@ -33,7 +33,7 @@ def test_header_symbols_exported():
 
 def test_version_and_status_strings():
     L = sharq.lib()
-    assert L.sharq_abi_version() == 7
+    assert L.sharq_abi_version() == 8
     for s in range(9):
         assert L.sharq_status_str(s)
     assert L.sharq_status_str(99) == b"unknown status"
@@ -302,3 +302,21 @@ def test_binding_fails_loudly_without_the_library(monkeypatch):
         sharq._raw_lib()
     with pytest.raises(RuntimeError, match="missing"):
         sharq.payload_sizes(16, 64, sharq.MXFP4, sharq.TILED)
+
+
+def test_forward_noalloc_rejects_before_launch():
+    """The allocation-free forward validates like sharq_forward before it touches the device."""
+    L = sharq.lib()
+    bb, rr, w = fp4(), fp4(), fp4()
+
+    def call(**kw):
+        a = dict(x=A, M=4, K=64, ldx=64, n=2, m=4, fmt=0, N=8, y=A, ldy=8, out=0)
+        a.update(kw)
+        return L.sharq_forward_noalloc(a["x"], a["M"], a["K"], a["ldx"], a["n"], a["m"], a["fmt"], ctypes.byref(bb),
+                                       ctypes.byref(rr), ctypes.byref(w), a["N"], a["y"], a["ldy"], a["out"], None)
+    assert call(ldy=4) == E_SHAPE
+    assert call(out=9) == E_FORMAT
+    assert call(n=1) == E_PATTERN
+    assert call(y=None) == E_NULL
+    assert call(fmt=7) == E_FORMAT
+    assert call() == E_DEVICE  # valid arguments, no gfx950 in this process
