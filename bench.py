@@ -46,6 +46,9 @@ def parse():
                    help="issue each timed step as the replay of one HIP graph holding its launches "
                         "(default: the library's calls, eagerly)")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time for the CPU baseline")
+    p.add_argument("--settle-ms", type=float, default=400.0,
+                   help="untimed steps for this long before the warm-up, so the timed steps see the clock "
+                        "the part holds under sustained load (0: none)")
     p.add_argument("--rmsnorm", action="store_true",
                    help="time the preparation with the RMS normalization folded in (sharq_prep_rmsnorm)")
     p.add_argument("--compare", action="store_true",
@@ -177,6 +180,23 @@ def _one_pass_seconds(launch, reps, stream):
         cycles *= 4
         if cycles > 1 << 34:
             raise RuntimeError("could not hold the stream long enough to queue the launches")
+
+
+def settle(run, ms):
+    """Untimed steps for about `ms` milliseconds: the part's clock ramps over the first
+    ~100 ms of sustained matrix load (a cold first measurement reads 10-20 % slow), and
+    a deployed layer runs in that steady state.  Returns the number of steps issued."""
+    import torch
+
+    if ms <= 0:
+        return 0
+    n, t0 = 0, time.perf_counter()
+    while (time.perf_counter() - t0) * 1e3 < ms:
+        for _ in range(8):
+            run(n)
+            n += 1
+        torch.cuda.synchronize()
+    return n
 
 
 def step_runner(step, nsets, graph):
@@ -374,6 +394,7 @@ def run_mlp_block(args):
         lin2(i)
 
     run, launch_mode = step_runner(step, nsets, args.graph)
+    settle_steps = settle(run, args.settle_ms)
     for i in range(args.warmup):
         run(i)
     torch.cuda.synchronize()
@@ -408,7 +429,8 @@ def run_mlp_block(args):
         "dtype": "mxfp4" if b.fmt == sharq.MXFP4 else "nvfp4 (fp16 matrix cores)",
         "data": "synthetic",
         "config": {"workload": b.name, "M": M, "H": H, "I": I, "pattern": f"{b.n}:{b.m}", "input_sets": nsets,
-                   "launch": launch_mode, "description": b.note},
+                   "launch": launch_mode, "settle": {"ms": args.settle_ms, "steps": settle_steps},
+                   "description": b.note},
         "roofline": {"bound": "mfma", "kernel": "linear_mx (gate/up)", "achieved": round(ach, 2),
                      "peak": PEAK_MXFP4_TFLOPS, "unit": "TFLOP/s", "frac": round(ach / PEAK_MXFP4_TFLOPS, 4),
                      "traffic": None, "flops_per_launch": alg1,
@@ -501,6 +523,7 @@ def main():
             sharq.forward(x, weight, w.n, w.m, sharq.OUT_BF16, bufs=(bb, rr), y=y, ws=ws)
 
     run, launch_mode = step_runner(step, nsets, args.graph)
+    settle_steps = settle(run, args.settle_ms)
     for i in range(args.warmup):
         run(i)
     torch.cuda.synchronize()
@@ -579,6 +602,7 @@ def main():
                    "format": "mxfp4" if w.fmt == sharq.MXFP4 else "nvfp4", "input_sets": nsets,
                    "payload_layout": "tiled" if weight0.layout == sharq.TILED else "row-major",
                    "prep_rmsnorm": bool(args.rmsnorm), "launch": launch_mode,
+                   "settle": {"ms": args.settle_ms, "steps": settle_steps},
                    "description": w.note},
         "pct_mxfp4_peak": round(100.0 * eff / t_step / 1e12 / PEAK_MXFP4_TFLOPS, 3),
         "roofline": roofline,

@@ -192,6 +192,26 @@ def test_prep_hand_examples(ex):
                 assert np.float32(ts) == np.float32(ex[pre + "_tensor_scale"]), pre
 
 
+@pytest.mark.parametrize("M,K,n,m", [(2048, 14336, 2, 4), (2049, 14336, 2, 4), (4096, 8192, 4, 8), (1, 16, 2, 4),
+                                     (3000, 96, 2, 4)])
+def test_prep_nvfp4_full_sizes_reuse_workspace(M, K, n, m):
+    """The NVFP4 preparation at and around the MLP down-projection size, with both
+    patterns and tiny and ragged shapes: bit-exact, and a second call with the same
+    workspace (first filled with 0xA5) reproduces every byte -- each call writes every
+    workspace word it reads before reading it."""
+    print(f"[prep] nvfp4 M={M} K={K} {n}:{m}", flush=True)
+    xb, _ = make_shape(M, 8, K, seed=M + K, dist="laplace", out_frac=0.01, out_scale=20.0)
+    x = to_dev(xb)
+    ws = torch.full((sharq.lib().sharq_prep_workspace_bytes(M, K, sharq.NVFP4),), 0xA5, dtype=torch.uint8,
+                    device=DEV)
+    ob, orr, _ = oracle.prep(xb, n, m, sharq.NVFP4)
+    for _ in range(2):
+        bb, rr, _ = sharq.prep(x, n, m, sharq.NVFP4, ws=ws)
+        torch.cuda.synchronize()
+        assert_payload_equal(bb, ob, "backbone")
+        assert_payload_equal(rr, orr, "residual")
+
+
 @pytest.mark.parametrize("fmt", [sharq.MXFP4, sharq.NVFP4])
 def test_prep_empty_and_zero(fmt):
     print(f"[prep] empty/zero fmt={fmt}", flush=True)
