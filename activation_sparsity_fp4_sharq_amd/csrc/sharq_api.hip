@@ -381,6 +381,26 @@ sharq_status sharq_clock_probe(int64_t iters, uint64_t* counters, void* stream) 
   return launched(launch_clock_probe(iters, counters, reinterpret_cast<hipStream_t>(stream)));
 }
 
+sharq_status sharq_matrix_rate_probe(int form, int64_t iters, uint64_t* counters, void* stream) {
+  if (form != 0 && form != 1) return SHARQ_E_FORMAT;
+  if (!counters) return SHARQ_E_NULL;
+  if (iters < 1 || iters > ((int64_t)1 << 40)) return SHARQ_E_SHAPE;
+  if (reinterpret_cast<uintptr_t>(counters) & 7u) return SHARQ_E_ALIGN;
+  sharq_status s = check_device();
+  if (s != SHARQ_OK) return s;
+  return launched(launch_matrix_rate_probe(form, iters, counters, reinterpret_cast<hipStream_t>(stream)));
+}
+
+sharq_status sharq_stream_probe(const void* src, int64_t read_bytes, void* dst, int64_t write_bytes, void* stream) {
+  if (read_bytes < 0 || write_bytes < 0 || read_bytes % 16 || write_bytes % 16) return SHARQ_E_SHAPE;
+  if ((read_bytes > 0 && !src) || (write_bytes > 0 && !dst)) return SHARQ_E_NULL;
+  if (!aligned16(src) || !aligned16(dst)) return SHARQ_E_ALIGN;
+  if (read_bytes / 16 > ((int64_t)1 << 40) || write_bytes / 16 > ((int64_t)1 << 40)) return SHARQ_E_SHAPE;
+  sharq_status s = check_device();
+  if (s != SHARQ_OK) return s;
+  return launched(launch_stream_probe(src, read_bytes, dst, write_bytes, reinterpret_cast<hipStream_t>(stream)));
+}
+
 sharq_status sharq_forward(const void* x, int64_t M, int64_t K, int64_t ldx, int sp_n, int sp_m, int fmt,
                            const sharq_fp4* backbone, const sharq_fp4* residual, const sharq_fp4* weight,
                            int64_t N, void* y, int64_t ldy, int out_dtype, void* workspace,

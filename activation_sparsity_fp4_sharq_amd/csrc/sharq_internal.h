@@ -62,6 +62,9 @@ size_t linear_nv_workspace(int64_t M, int64_t N, int64_t K);
 // Shader-clock probe: out[0] = shader cycles, out[1] = 100 MHz ticks over one wave's
 // loop of `iters` x 4 FP4 matrix instructions while every CU runs the same loop.
 hipError_t launch_clock_probe(int64_t iters, uint64_t* out, hipStream_t stream);
+hipError_t launch_matrix_rate_probe(int form, int64_t iters, uint64_t* out, hipStream_t stream);
+hipError_t launch_stream_probe(const void* src, int64_t read_bytes, void* dst, int64_t write_bytes,
+                               hipStream_t stream);
 
 constexpr size_t kNvPrepWorkspace = 16448;  // 16 + 2 * 2048 dwords: maxima and partials
 static_assert(SHARQ_NOALLOC_SCRATCH_BYTES >= kNvPrepWorkspace, "the fixed scratch must cover the preparation");

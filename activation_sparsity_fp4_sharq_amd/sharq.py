@@ -24,7 +24,7 @@ SYMBOLS = ["sharq_abi_version", "sharq_status_str", "sharq_payload_bytes", "shar
            "sharq_prep_workspace_bytes", "sharq_linear_workspace_bytes", "sharq_quantize", "sharq_prep",
            "sharq_prep_rmsnorm_workspace_bytes", "sharq_prep_rmsnorm", "sharq_linear", "sharq_linear_dense",
            "sharq_clock_probe", "sharq_prep_ablation", "sharq_dequantize", "sharq_prep_swiglu",
-           "sharq_forward", "sharq_forward_noalloc"]
+           "sharq_forward", "sharq_forward_noalloc", "sharq_matrix_rate_probe", "sharq_stream_probe"]
 
 
 class SharqFp4(ctypes.Structure):
@@ -38,7 +38,7 @@ class SharqError(RuntimeError):
         self.status = status
 
 
-ABI_VERSION = 8  # the SHARQ_ABI_VERSION of include/sharq.h this binding marshals for
+ABI_VERSION = 9  # the SHARQ_ABI_VERSION of include/sharq.h this binding marshals for
 
 _lib = None
 
@@ -101,6 +101,10 @@ def lib():
         L.sharq_forward.restype = ctypes.c_int
         L.sharq_forward.argtypes = [vp, i64, i64, i64, ctypes.c_int, ctypes.c_int, ctypes.c_int, P, P, P,
                                     i64, vp, i64, ctypes.c_int, vp, sz, vp]
+        L.sharq_matrix_rate_probe.restype = ctypes.c_int
+        L.sharq_matrix_rate_probe.argtypes = [ctypes.c_int, i64, vp, vp]
+        L.sharq_stream_probe.restype = ctypes.c_int
+        L.sharq_stream_probe.argtypes = [vp, i64, vp, i64, vp]
         L.sharq_forward_noalloc.restype = ctypes.c_int
         L.sharq_forward_noalloc.argtypes = [vp, i64, i64, i64, ctypes.c_int, ctypes.c_int, ctypes.c_int, P, P, P,
                                             i64, vp, i64, ctypes.c_int, vp]
@@ -471,6 +475,26 @@ def _forward_args(x, weight, out_dtype, bufs, y, ws, with_workspace=True):
             ws = workspace(need, dev)
         _check_workspace(ws, need, dev)
     return x, bb, rr, y, ws, M, K, N, fmt
+
+
+def matrix_rate_probe(form, iters=20000, device=None, stream=None):
+    """Issue rate of a matrix-instruction form (0: dense scaled FP4 32x32x64, 1: 2:4-sparse
+    fp8 32x32x64): returns (cycles per instruction per SIMD, shader clock in Hz)."""
+    dev = device if device is not None else torch.device("cuda", torch.cuda.current_device())
+    out = torch.zeros(4, dtype=torch.int64, device=dev)
+    _check("sharq_matrix_rate_probe", lib().sharq_matrix_rate_probe(form, iters, _ptr(out), _stream(stream)))
+    cycles, ticks = (int(v) for v in out[:2].cpu())
+    return cycles / (iters * 8), (cycles / (ticks / 1e8) if ticks > 0 else float("nan"))
+
+
+def stream_probe(src, read_bytes, dst, write_bytes, stream=None):
+    """A plain read of read_bytes of src and write of write_bytes of dst (uint8 CUDA tensors)."""
+    for t, n, what in ((src, read_bytes, "src"), (dst, write_bytes, "dst")):
+        if t.dtype != torch.uint8 or not t.is_contiguous() or t.numel() < n:
+            raise ValueError(f"{what} must be a contiguous uint8 tensor of at least {n} bytes")
+        _check_device(t, src.device, what)
+    _check("sharq_stream_probe", lib().sharq_stream_probe(_ptr(src), read_bytes, _ptr(dst), write_bytes,
+                                                          _stream(stream)))
 
 
 _raw = None

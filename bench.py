@@ -528,12 +528,17 @@ def main():
         run(i)
     torch.cuda.synchronize()
 
-    # timed region: exactly K steps, bracketed by synchronize
+    # timed region: exactly K steps, bracketed by synchronize; two HIP events on the launch
+    # stream bracket it too (device time per step, nothing between the kernels)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
+    ev0.record(stream)
     for i in range(args.steps):
         run(i)
+    ev1.record(stream)
     torch.cuda.synchronize()
     t_step = (time.perf_counter() - t0) / args.steps
+    t_step_dev = ev0.elapsed_time(ev1) * 1e-3 / args.steps
 
     # per-kernel durations with HIP events on the launch stream (separate pass)
     def prep_only(i):
@@ -544,8 +549,33 @@ def main():
         x, weight, bb, rr, y = sets[i % nsets]
         sharq.linear(bb, rr, weight, sharq.OUT_BF16, y=y, ws=ws)
 
+    # Per-kernel durations.  The preparation: HIP events around back-to-back launches over
+    # the input sets.  The fused GEMM: its average inside the timed steps, i.e. the device
+    # time per step minus the preparation's.  (Events between the two kernels would
+    # perturb them -- each marker adds a dispatch gap of several microseconds and the GEMM
+    # runs slower after it -- and the GEMM launched back to back with itself runs hotter,
+    # so slower, than alternating with the memory-bound preparation as in the steps.)
     t_prep = back_to_back_seconds(prep_only, args.steps, stream)
-    t_lin = back_to_back_seconds(linear_only, args.steps, stream)
+    t_lin_iso = back_to_back_seconds(linear_only, args.steps, stream)
+    # (a host-bound step -- decode -- leaves the device idle between steps, so there the
+    # difference overstates the kernel; the smaller of the two is the kernel's time)
+    t_lin_in_step = t_step_dev - t_prep
+    t_lin = min(t_lin_in_step, t_lin_iso)
+    # the streaming ceiling at the preparation's byte counts: a plain read of X's bytes and
+    # write of the two payloads' bytes with the same access shape, over the same input sets
+    sinks = [torch.empty(pay_bytes, dtype=torch.uint8, device=dev) for _ in range(nsets)]
+    srcs = [s_[0].view(torch.uint8).view(-1) for s_ in sets]
+    t_stream = back_to_back_seconds(
+        lambda i: sharq.stream_probe(srcs[i % nsets], act_bytes, sinks[i % nsets], pay_bytes, stream=stream),
+        args.steps, stream)
+    del sinks
+    # the two matrix-instruction forms a sparse backbone can take (the backbone form is
+    # chosen by this measurement): cycles per instruction per SIMD, same dense shape
+    forms = {}
+    for form, name in ((0, "dense_scaled_fp4_32x32x64_zero_filled"), (1, "sparse_2of4_fp8_32x32x64_compressed")):
+        cpi, hz = sharq.matrix_rate_probe(form, 20000, dev, stream)
+        forms[name] = {"cycles_per_instr_per_simd": round(cpi, 2), "sclk_ghz": round(hz / 1e9, 3),
+                       "dense_equiv_TFLOPS": round(1024 * 2 * 32 * 32 * 64 / cpi * hz / 1e12, 1)}
     # the shader clock under matrix load, right after the timed passes (the published
     # peaks assume 2.4 GHz; the part holds less under sustained matrix work)
     sclk = sharq.clock_probe(20000, dev, stream)
@@ -608,8 +638,21 @@ def main():
         "roofline": roofline,
         "prep": {"ms": round(t_prep * 1e3, 4), "GB_s": round(prep_bytes / t_prep / 1e9, 1),
                  "pct_hbm": round(100.0 * prep_bytes / t_prep / 1e9 / PEAK_HBM_GBS, 2),
-                 "bytes_per_launch": prep_bytes, "traffic": prep_traffic},
+                 "bytes_per_launch": prep_bytes, "traffic": prep_traffic,
+                 "stream_ceiling": {"kernel": "sharq_stream_probe", "read_bytes": act_bytes, "write_bytes": pay_bytes,
+                                    "ms": round(t_stream * 1e3, 4),
+                                    "GB_s": round((act_bytes + pay_bytes) / t_stream / 1e9, 1),
+                                    "pct_hbm": round(100.0 * (act_bytes + pay_bytes) / t_stream / 1e9 / PEAK_HBM_GBS, 2),
+                                    "prep_vs_ceiling": round(t_stream / t_prep, 3)}},
+        "backbone_forms": forms,
         "sclk_ghz_under_mfma_load": round(sclk / 1e9, 3) if sclk == sclk else None,
+        "kernel_timing": {"step_device_ms": round(t_step_dev * 1e3, 4),
+                          "prep": "HIP events around back-to-back launches on the launch stream",
+                          "linear": ("device time per timed step (HIP events around the timed region) minus prep.ms"
+                                     if t_lin_in_step <= t_lin_iso else
+                                     "HIP events around back-to-back launches (the steps are host-bound)"),
+                          "linear_in_step_ms": round(t_lin_in_step * 1e3, 4),
+                          "linear_back_to_back_ms": round(t_lin_iso * 1e3, 4)},
         "linear": {"ms": round(t_lin * 1e3, 4), "TFLOPS_effective": round(eff / t_lin / 1e12, 2),
                    "TFLOPS_algorithmic": round(alg / t_lin / 1e12, 2),
                    "TFLOPS_issued": round(issued / t_lin / 1e12, 2),

@@ -61,7 +61,7 @@
 extern "C" {
 #endif
 
-#define SHARQ_ABI_VERSION 8
+#define SHARQ_ABI_VERSION 9
 
 typedef enum sharq_status {
   SHARQ_OK = 0,
@@ -278,6 +278,30 @@ sharq_status sharq_linear_dense(const sharq_fp4* a, int64_t M, const sharq_fp4* 
  * the loop from being optimized away.  Errors: NULL counters -> SHARQ_E_NULL; iters
  * outside [1, 2^40] -> SHARQ_E_SHAPE; misaligned -> SHARQ_E_ALIGN. */
 sharq_status sharq_clock_probe(int64_t iters, uint64_t* counters, void* stream);
+
+/* Measurement aid: the issue rate of the two matrix-instruction forms a sparse FP4
+ * backbone can take on gfx950 (the backbone form is chosen by this measurement; the
+ * pages' backbone GEMM is sparse, and gfx950 has no sparse FP4 instruction):
+ *   form 0  dense block-scaled FP4 32x32x64 (v_mfma_scale_f32_32x32x64_f8f6f4) on a
+ *           zero-filled backbone
+ *   form 1  2:4-sparse fp8 32x32x64 (v_smfmac_f32_32x32x64_fp8_fp8) on a compressed
+ *           backbone (FP4 values are exact in fp8)
+ * Both perform 32 x 32 x 64 multiply-adds of the dense operand shape per instruction.
+ * Every CU runs 4 waves (one per SIMD) of iters x 8 register-only instructions in eight
+ * independent chains; counters (device, 8-byte aligned, >= 3 uint64) receive [0] the
+ * shader cycles and [1] the 100 MHz ticks of one wave's loop, [2] a value that keeps
+ * the loop alive; cycles per instruction per SIMD = [0] / (iters * 8).  Errors: form not 0/1 -> SHARQ_E_FORMAT,
+ * otherwise as for sharq_clock_probe. */
+sharq_status sharq_matrix_rate_probe(int form, int64_t iters, uint64_t* counters, void* stream);
+
+/* Measurement aid: the streaming ceiling of a memory pattern like the preparation's --
+ * read read_bytes of src (non-temporal 16-byte loads) and write write_bytes of dst
+ * (16-byte stores), four chunks per lane, no arithmetic.  Timing it at a preparation's
+ * byte counts bounds what that preparation can reach.
+ *   src, dst     device, 16-byte aligned (NULL allowed for a zero byte count)
+ *   read_bytes, write_bytes  >= 0, multiples of 16, else SHARQ_E_SHAPE
+ *   dst's contents afterwards are unspecified. */
+sharq_status sharq_stream_probe(const void* src, int64_t read_bytes, void* dst, int64_t write_bytes, void* stream);
 
 /* One SharQ linear layer end to end (SharQ, arXiv 2606.26587: the abstract's
  * decomposition as one layer; Figure 2's dataflow of the fused preparation feeding the

@@ -33,7 +33,7 @@ def test_header_symbols_exported():
 
 def test_version_and_status_strings():
     L = sharq.lib()
-    assert L.sharq_abi_version() == 8
+    assert L.sharq_abi_version() == 9
     for s in range(9):
         assert L.sharq_status_str(s)
     assert L.sharq_status_str(99) == b"unknown status"
@@ -320,3 +320,16 @@ def test_forward_noalloc_rejects_before_launch():
     assert call(y=None) == E_NULL
     assert call(fmt=7) == E_FORMAT
     assert call() == E_DEVICE  # valid arguments, no gfx950 in this process
+
+
+def test_measurement_probes_reject():
+    L = sharq.lib()
+    assert L.sharq_matrix_rate_probe(2, 10, A, None) == E_FORMAT
+    assert L.sharq_matrix_rate_probe(0, 10, None, None) == E_NULL
+    assert L.sharq_matrix_rate_probe(1, 0, A, None) == E_SHAPE
+    assert L.sharq_matrix_rate_probe(0, 10, A + 4, None) == E_ALIGN
+    assert L.sharq_stream_probe(A, 17, A, 16, None) == E_SHAPE
+    assert L.sharq_stream_probe(None, 16, A, 16, None) == E_NULL
+    assert L.sharq_stream_probe(A + 8, 16, A, 16, None) == E_ALIGN
+    assert L.sharq_stream_probe(A, 16, A, 16, None) == E_DEVICE
+

@@ -275,7 +275,7 @@ def run_linear(xb, wb, n, m, fmt, layout=None):
 @pytest.mark.parametrize("M,N,K", [(1, 1, 32), (16, 512, 512), (37, 70, 96), (300, 260, 160),
                                    (257, 513, 1056), (64, 256, 2048), (520, 300, 384),
                                    (32, 1000, 4224), (7, 96, 640), (33, 96, 640), (20, 200, 384),
-                                   (2000, 4000, 512)])
+                                   (2000, 4000, 512), (4200, 4100, 256)])
 def test_linear_small_full_compare(fmt, layout, M, N, K):
     print(f"[linear] M={M} N={N} K={K} fmt={fmt} layout={layout}", flush=True)
     xb, wb = make_shape(M, N, K, seed=M + N + K, dist="laplace", token_sigma=0.3)
@@ -393,7 +393,7 @@ def test_linear_deterministic_and_guarded():
 
 
 @pytest.mark.parametrize("fmt", [sharq.MXFP4, sharq.NVFP4], ids=["mx", "nv"])
-@pytest.mark.parametrize("M,N,K", [(2040, 4090, 128), (1930, 3850, 64)])
+@pytest.mark.parametrize("M,N,K", [(2040, 4090, 128), (1930, 3850, 64), (4400, 4090, 128)])
 def test_linear_large_tiles_strided_output(fmt, M, N, K):
     """The large-M kernels' bf16 epilogues (LDS-staged 16-byte row stores where a wave's
     tile lies inside Y and rows are 16-byte aligned, element stores elsewhere) with a row
@@ -558,6 +558,31 @@ def test_dequantize_matches_oracle(fmt, layout, rows, K):
     torch.cuda.synchronize()
     want = oracle.dequant(oracle.quantize(xb, fmt), fmt).astype(np.float32)  # exact values, one rounding
     assert np.array_equal(got, want)
+
+
+def test_stream_probe_moves_the_bytes():
+    """The streaming probe (a measurement aid) reads and writes exactly what it is asked:
+    chunk c of the output is chunk c of the input xor c, nothing past write_bytes."""
+    print("[stream_probe]", flush=True)
+    n_r, n_w = 16 * 5000, 16 * 3001
+    src = torch.randint(0, 256, (n_r,), dtype=torch.uint8, device=DEV)
+    dst = torch.zeros(n_w + 4096, dtype=torch.uint8, device=DEV)
+    sharq.stream_probe(src, n_r, dst, n_w)
+    torch.cuda.synchronize()
+    s32 = src.view(torch.int32).cpu().numpy().reshape(-1, 4).astype(np.uint32)
+    d32 = dst.view(torch.int32).cpu().numpy().astype(np.uint32)
+    want = s32[: n_w // 16].copy()
+    want[:, 0] ^= np.arange(n_w // 16, dtype=np.uint32)
+    want[:, 1:] ^= np.arange(n_w // 16, dtype=np.uint32)[:, None]
+    assert np.array_equal(d32[: n_w // 4].reshape(-1, 4), want)
+    assert np.all(d32[n_w // 4:] == 0)
+
+
+def test_matrix_rate_probe_is_plausible():
+    print("[matrix_rate_probe]", flush=True)
+    for form in (0, 1):
+        cpi, hz = sharq.matrix_rate_probe(form, 20000)
+        assert 4 < cpi < 512 and 0.5e9 < hz < 3.5e9, (form, cpi, hz)
 
 
 def test_clock_probe_reports_a_plausible_clock():
