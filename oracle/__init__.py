@@ -76,6 +76,8 @@ def lib():
         L.oracle_linear.argtypes = [_u8p, _u8p, ctypes.c_float, _u8p, _u8p, ctypes.c_float, _i64,
                                     _u8p, _u8p, ctypes.c_float, _i64, _i64, ctypes.c_int, _vp, _i64,
                                     _f64p]
+        L.oracle_row_sumsq.restype = ctypes.c_int
+        L.oracle_row_sumsq.argtypes = [_u16p, _i64, _i64, _i64, _f64p]
         L.oracle_rmsnorm.restype = ctypes.c_int
         L.oracle_rmsnorm.argtypes = [_u16p, _i64, _i64, _i64, _u16p, ctypes.c_float, _u16p, _vp]
         L.oracle_omp_threads.restype = ctypes.c_int
@@ -132,6 +134,16 @@ def swiglu(gate_up_bits, I):
     if lib().oracle_swiglu(gu, M, I, ld, h):
         raise ValueError("oracle_swiglu rejected its arguments")
     return h
+
+
+def row_sumsq(x_bits):
+    """fp64 sums of squares of the rows of a bf16 matrix, in reading R9's order."""
+    x_bits = np.ascontiguousarray(x_bits, dtype=np.uint16)
+    M, K = x_bits.shape
+    out = np.zeros(max(M, 1), np.float64)
+    if lib().oracle_row_sumsq(x_bits, M, K, K, out):
+        raise ValueError("oracle_row_sumsq rejected its arguments")
+    return out[:M]
 
 
 def rmsnorm(x_bits, gamma_bits, eps):

@@ -59,9 +59,12 @@
  *      fused preparation also takes over the layer normalization): RMS normalization
  *      with a per-channel bf16 gain g and no bias, producing the bf16 tensor the
  *      preparation then decomposes:
- *        r_i = fp32( 1 / sqrt( (sum_k x_ik^2) / K + eps ) )   (sum, mean, sqrt and
- *              division in fp64; the sum of squares of bf16 values is exact to ~1e-16)
- *        y_ik = bf16_rne( fp32( fp32(x_ik * r_i) * g_k ) ).
+ *        r_i = fp32( 1 / sqrt( S_i / K + eps ) )   (mean, sqrt and division in fp64)
+ *        y_ik = bf16_rne( fp32( fp32(x_ik * r_i) * g_k ) ),
+ *      S_i the row's sum of squares in fp64 in a fixed order: each run of 8 elements
+ *      summed in index order, the run sums added in a balanced binary tree (see
+ *      row_sumsq) -- an order any split of the row into aligned power-of-two pieces
+ *      reproduces exactly.
  *
  * Compile: gcc -O2 -ffp-contract=off -fno-fast-math -fopenmp -shared -fPIC.
  * The row loops carry an OpenMP pragma; every output element has a fixed
@@ -286,6 +289,41 @@ static uint16_t f32_to_bf16(float f) {
   return (uint16_t)(u >> 16);
 }
 
+/* R9: the sum of squares of one row of K bf16 values.  Each square is exact in fp64
+ * (a bf16 has 8 significant bits).  The squares of each run of 8 consecutive elements
+ * are added in index order; the run sums are then added pairwise in a balanced binary
+ * tree over the run index -- the sequence of runs zero-padded to a power of two, then
+ * halved level by level, element 2j + (element 2j + 1).  (A short last run holds the
+ * leftover elements; adding the exact zeros of the padding changes no value.) */
+static double row_sumsq(const uint16_t* xr, int64_t K) {
+  const int64_t n = (K + 7) / 8;
+  int64_t p = 1;
+  while (p < n) p *= 2;
+  double* v = (double*)calloc((size_t)p, sizeof(double));
+  if (!v) return NAN;
+  for (int64_t j = 0; j < n; ++j) {
+    double s = 0.0;
+    for (int64_t k = 8 * j; k < 8 * j + 8 && k < K; ++k) {
+      const double a = (double)bf16_to_f32(xr[k]);
+      s = s + a * a;
+    }
+    v[j] = s;
+  }
+  for (int64_t w = p; w > 1; w /= 2)
+    for (int64_t j = 0; j < w / 2; ++j) v[j] = v[2 * j] + v[2 * j + 1];
+  const double total = v[0];
+  free(v);
+  return total;
+}
+
+/* The row sums of squares of x bf16 [M, ldx] (first K columns) by R9's order. */
+int oracle_row_sumsq(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, double* out) {
+  if (M < 0 || K <= 0 || ldx < K) return -1;
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < M; ++i) out[i] = row_sumsq(x + i * ldx, K);
+  return 0;
+}
+
 /* R9: RMS normalization of x bf16 [M, ldx] (first K columns) with gain g bf16 [K]
  * into y bf16 [M, K]; r_out (optional) receives the per-row factors r_i. */
 int oracle_rmsnorm(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, const uint16_t* g, float eps,
@@ -293,11 +331,7 @@ int oracle_rmsnorm(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, const u
   if (M < 0 || K <= 0 || ldx < K || !(eps >= 0.0f)) return -1;
 #pragma omp parallel for schedule(static)
   for (int64_t i = 0; i < M; ++i) {
-    double ss = 0.0;
-    for (int64_t k = 0; k < K; ++k) {
-      const double v = (double)bf16_to_f32(x[i * ldx + k]);
-      ss += v * v;
-    }
+    const double ss = row_sumsq(x + i * ldx, K);
     const float r = (float)(1.0 / sqrt(ss / (double)K + (double)eps));
     if (r_out) r_out[i] = r;
     for (int64_t k = 0; k < K; ++k) {

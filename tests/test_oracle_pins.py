@@ -567,6 +567,43 @@ def test_rmsnorm_closed_forms():
     assert r[0] == np.float32(2.0) and np.all(bf16_bits_to_f32(y) == 0.0)
 
 
+@pytest.mark.parametrize("K", [8, 100, 1024, 4096, 14336])
+def test_row_sumsq_exact_on_small_integers(K):
+    """Integer bf16 values |x| <= 255: every partial sum is an integer below 2^53, so any
+    order gives the exact sum -- which pins that every term is present once, squared, and
+    that a short last run is included."""
+    rng = np.random.default_rng(K)
+    xi = rng.integers(-255, 256, (5, K))
+    xb = f32_to_bf16_bits(xi.astype(np.float32))
+    assert np.array_equal(bf16_bits_to_f32(xb), xi.astype(np.float32))
+    got = oracle.row_sumsq(xb)
+    want = [sum(int(v) * int(v) for v in row) for row in xi]
+    assert [int(g) for g in got] == want and all(float(w) == g for w, g in zip(want, got))
+
+
+def test_row_sumsq_order_is_the_run_tree():
+    """Hand-derived, reading R9's order.  K = 32 = four runs of 8:
+    run 0 = [2^27, 1, 1, 0 x 5]: 2^54 + 1 rounds to 2^54 (ties to even; ulp(2^54) = 4),
+    and so does the next + 1, so run 0 sums to 2^54; runs 1-3 = [1, 1, 0 x 6] sum to 2.
+    Tree: (2^54 + 2) + (2 + 2) = 2^54 + 4, since 2^54 + 2 ties to 2^54.  Summing the 32
+    squares left to right would give 2^54, and adding the run sums left to right too.
+    With five runs (K = 40, run 4 = [1, 1, 0 x 6]) the zero padding to eight gives
+    ((2^54 + 2) + (2 + 2)) + ((2 + 0) + 0) = (2^54 + 4) + 2 = 2^54 + 6, a tie between
+    2^54 + 4 (an odd multiple of the ulp 4) and 2^54 + 8, so 2^54 + 8; left to right the
+    run sums would give 2^54."""
+    def row(nruns):
+        x = np.zeros(8 * nruns, np.float32)
+        x[0] = 2.0 ** 27
+        x[1] = x[2] = 1.0
+        for j in range(1, nruns):
+            x[8 * j] = x[8 * j + 1] = 1.0
+        return f32_to_bf16_bits(x[None, :])
+    assert oracle.row_sumsq(row(4))[0] == 2.0 ** 54 + 4
+    assert oracle.row_sumsq(row(5))[0] == 2.0 ** 54 + 8
+    # one run: left to right inside it
+    assert oracle.row_sumsq(row(1))[0] == 2.0 ** 54
+
+
 # ------------------------------------------------------------ ablation variants (R13)
 
 def _abl_inputs(fmt, M=5, K=256, seed=31):
