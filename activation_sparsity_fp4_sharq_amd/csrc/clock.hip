@@ -8,6 +8,7 @@
 // instructions from registers for `iters` iterations per wave; wave 0 of work-group 0
 // reads the shader-clock counter (s_memtime) and the constant 100 MHz counter
 // (s_memrealtime) around its loop, so cycles / (ticks / 100 MHz) is the clock it ran at.
+#include "fp4_codec.h"
 #include "sharq_internal.h"
 
 namespace sharq {
@@ -103,7 +104,50 @@ __global__ __launch_bounds__(kStreamThreads) void stream_probe_kernel(const u32x
   }
 }
 
+// Rounding check of bf16x2_rne_hw against bf16_rne_bits over every fp32 pattern: lane
+// i of the grid-stride loop converts the pair (2i, 2i+1); patterns with an all-ones
+// exponent (infinities, NaN) are skipped.  out[0] += mismatches, out[1] = min pattern.
+constexpr int kRoundThreads = 256;
+constexpr int kRoundBlocks = 4096;
+
+__global__ void rounding_init_kernel(unsigned long long* out) {
+  out[0] = 0ull;
+  out[1] = ~0ull;
+}
+
+__global__ __launch_bounds__(kRoundThreads) void rounding_probe_kernel(unsigned long long* out) {
+  constexpr uint64_t kPairs = 1ull << 31;
+  unsigned long long bad = 0, first = ~0ull;
+  for (uint64_t i = (uint64_t)blockIdx.x * kRoundThreads + threadIdx.x; i < kPairs;
+       i += (uint64_t)kRoundBlocks * kRoundThreads) {
+    const uint32_t a = (uint32_t)(2 * i), b = a + 1u;
+    const uint32_t hw = codec::bf16x2_rne_hw(__uint_as_float(a), __uint_as_float(b));
+    const bool fa = (a & 0x7F800000u) != 0x7F800000u, fb = (b & 0x7F800000u) != 0x7F800000u;
+    if (fa && (hw & 0xFFFFu) != codec::bf16_rne_bits(__uint_as_float(a))) {
+      ++bad;
+      first = first < a ? first : a;
+    }
+    if (fb && (hw >> 16) != codec::bf16_rne_bits(__uint_as_float(b))) {
+      ++bad;
+      first = first < b ? first : b;
+    }
+  }
+  if (bad) {
+    atomicAdd(&out[0], bad);
+    atomicMin(&out[1], first);
+  }
+}
+
 }  // namespace
+
+hipError_t launch_rounding_probe(uint64_t* out, hipStream_t stream) {
+  unsigned long long* o = reinterpret_cast<unsigned long long*>(out);
+  rounding_init_kernel<<<dim3(1), dim3(1), 0, stream>>>(o);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  rounding_probe_kernel<<<dim3(kRoundBlocks), dim3(kRoundThreads), 0, stream>>>(o);
+  return hipGetLastError();
+}
 
 hipError_t launch_matrix_rate_probe(int form, int64_t iters, uint64_t* out, hipStream_t stream) {
   int dev = 0, cus = 0;

@@ -88,6 +88,27 @@ __device__ __forceinline__ uint32_t bf16_rne_bits(float f) {
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;  // finite values (the contract)
 }
 
+// Two fp32 values to two bf16 (a in the low half) with the gfx950 packed conversion,
+// which rounds to nearest even and keeps subnormals under the kernels' fp32 mode.  On
+// every finite fp32 pattern it agrees with bf16_rne_bits (sharq_bf16_rounding_probe
+// checks all 2^32 patterns on the device).
+typedef __bf16 bf16x2_cvt_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_cvt_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t bf16x2_rne_hw(float a, float b) {
+  const f32x2_cvt_t p = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(p, bf16x2_cvt_t));
+}
+
+// rms_scale_pair for one dword of two bf16 x and one of two bf16 gains, returning the two
+// bf16 results as fp32 values (rounded by bf16x2_rne_hw).
+__device__ __forceinline__ void rms_scale_f2(uint32_t w, uint32_t gw, float r, float& y0, float& y1) {
+  const uint32_t b = bf16x2_rne_hw(__fmul_rn(__fmul_rn(__uint_as_float(w << 16), r), __uint_as_float(gw << 16)),
+                                   __fmul_rn(__fmul_rn(__uint_as_float(w & 0xFFFF0000u), r),
+                                             __uint_as_float(gw & 0xFFFF0000u)));
+  y0 = __uint_as_float(b << 16);
+  y1 = __uint_as_float(b & 0xFFFF0000u);
+}
+
 __device__ __forceinline__ uint32_t rms_scale_pair(uint32_t w, uint32_t gw, float r) {
   const float y0 = __fmul_rn(__fmul_rn(__uint_as_float(w << 16), r), __uint_as_float(gw << 16));
   const float y1 = __fmul_rn(__fmul_rn(__uint_as_float(w & 0xFFFF0000u), r), __uint_as_float(gw & 0xFFFF0000u));

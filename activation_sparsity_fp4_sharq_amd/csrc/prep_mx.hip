@@ -104,17 +104,10 @@ __device__ __forceinline__ void store_scales(uint8_t* dst, int64_t b, int64_t nb
 // residual (direct N:M sparsity + FP4; the residual payload is all zero).  Every
 // lane of the quad must call it together (the block maxima are quad exchanges).
 // `keep` (bit j = element j kept) is only computed when a caller uses it.
+// codec_block_f takes the 8 values as fp32 (each a bf16 value, exactly).
 template <int MODE, int SPM>
-__device__ __forceinline__ void codec_block(const uint32_t w[4], uint32_t& keep, uint32_t& bbyte,
-                                            uint32_t& bpacked, uint32_t& rbyte, uint32_t& rpacked) {
-  // x as fp32 (exact)
-  float xf[8];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    xf[2 * i] = __uint_as_float(w[i] << 16);
-    xf[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
-  }
-
+__device__ __forceinline__ void codec_block_f(const float xf[8], uint32_t& keep, uint32_t& bbyte,
+                                              uint32_t& bpacked, uint32_t& rbyte, uint32_t& rpacked) {
   float r[8];
   keep = 0xFFu; bbyte = 0; bpacked = 0;
   if constexpr (MODE != 1) {
@@ -163,6 +156,19 @@ __device__ __forceinline__ void codec_block(const uint32_t w[4], uint32_t& keep,
   const uint32_t rsb = scale_bits_of(quad_max(abs_max8(r)));
   rbyte = rsb >> 23;
   rpacked = quant8(r, __uint_as_float(rsb));
+}
+
+template <int MODE, int SPM>
+__device__ __forceinline__ void codec_block(const uint32_t w[4], uint32_t& keep, uint32_t& bbyte,
+                                            uint32_t& bpacked, uint32_t& rbyte, uint32_t& rpacked) {
+  // x as fp32 (exact)
+  float xf[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    xf[2 * i] = __uint_as_float(w[i] << 16);
+    xf[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+  }
+  codec_block_f<MODE, SPM>(xf, keep, bbyte, bpacked, rbyte, rpacked);
 }
 
 // Optional RMS normalization applied to the loaded bf16 values (XF == kXfRms): per-row
@@ -333,6 +339,226 @@ __global__ __launch_bounds__(kThreads) void prep_mx_tiled_kernel(
   }
 }
 
+// RMS normalization and preparation in one read of X (tiled output).  A work-group owns
+// R whole rows; L = 64/R lanes share a row, lane p of a row covering, in each step of
+// 32L elements, the four consecutive 32-element blocks 4(p/4)..4(p/4)+3, elements
+// 8(p%4)..8(p%4)+7 of each: a quad of lanes per block, as the codec wants, and the four
+// scale bytes of one tiled scale word in one lane.  Wave w holds steps [w*KS, w*KS+KS)
+// of the rows in registers.  The row's sum of squares is evaluated in the defined order
+// (runs of 8 in index order, then a balanced tree over the run index): run
+// c = 4L*step + 16(p/4) + 4u + p%4 of the row is lane p's block u, so the tree's two
+// lowest levels are xor exchanges over p%4, the next two the lane's blocks u, then xor
+// exchanges over p/4, then the lane's steps (KS a power of two: each wave's steps are an
+// aligned power-of-two range of runs), and the top levels combine the waves' sums,
+// zero-padded to 16.  The factor r, the gain and the codec then work from the same
+// registers.  With one step per wave the gain is loaded with X, so no load waits between
+// the phases; with two, its registers would not fit, and each step loads it in turn.
+// fp64 value of another lane through a DPP pattern (both halves).
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double v) {
+  const uint64_t u = __double_as_longlong(v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)u, CTRL, 0xF, 0xF, true);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)(u >> 32), CTRL, 0xF, 0xF, true);
+  return __longlong_as_double((int64_t)(((uint64_t)hi << 32) | lo));
+}
+
+template <int R, int SPM, int KS, bool WRITE_MASK>
+__global__ __launch_bounds__(1024) void prep_mx_rms_tiled_kernel(
+    const uint16_t* __restrict__ x, int64_t M, int64_t K, int64_t ldx, int64_t Mp, int64_t Kp,
+    const uint16_t* __restrict__ gamma, double eps, uint8_t* __restrict__ bcodes, uint8_t* __restrict__ bscales,
+    uint8_t* __restrict__ rcodes, uint8_t* __restrict__ rscales, uint8_t* __restrict__ mask) {
+  constexpr int L = 64 / R;
+  static_assert(R == 4 || R == 8 || R == 16, "rows per group");
+  __shared__ double part[16][R];  // [wave][row]: each wave's share of the row sums
+  __shared__ float rfac[R];
+  extern __shared__ uint32_t tiles[];  // per wave: staging of the code stores, 2 x 64 slots of 16 B
+  const int lane = threadIdx.x & 63;
+  const int j = lane / L, p = lane % L;
+  const int q = p & 3, g4 = p >> 2;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int W = (int)(blockDim.x >> 6);
+  const int64_t r0 = (int64_t)blockIdx.x * R;  // first row of the group (uniform)
+  const int64_t r = r0 + j;
+  const int64_t nbk = K / 32, nbp = Kp / 32;
+  const bool row_ok = r < M;
+  // the group and the wave's steps wholly inside X (uniform): nothing to zero
+  const bool interior = r0 + R <= M && ((int64_t)wave * KS + KS) * L <= nbk;
+
+  // every load in flight first: X and (one step per wave) the matching gains.  Loads are
+  // unconditional, from clamped (in-bounds) addresses, and what lies outside X is zeroed
+  // afterwards: a load under a branch would have to complete before the branch joins.
+  // Addresses are a uniform base and a 32-bit lane offset.
+  constexpr bool kGainEarly = KS == 1;
+  u32x4 v[KS][4], gv[kGainEarly ? 4 : 1];
+  // rows past M read row M-1: the base is the group's first row clamped the same way,
+  // so the lane's row offset is never negative
+  const int64_t rb = r0 < M ? r0 : M - 1;
+  const uint8_t* xg = reinterpret_cast<const uint8_t*>(x + rb * ldx);
+  const uint32_t jc = (uint32_t)((row_ok ? r : M - 1) - rb);
+  const uint32_t lane_x = jc * (uint32_t)ldx * 2u + (uint32_t)q * 16u;
+  const uint32_t last_blk = (uint32_t)nbk - 1u;
+#pragma unroll
+  for (int t = 0; t < KS; ++t) {
+    const uint32_t ks = (uint32_t)(wave * KS + t);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const uint32_t bc = min(ks * L + g4 * 4 + u, last_blk);
+      v[t][u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(xg + lane_x + bc * 64u));
+      if constexpr (kGainEarly)
+        gv[u] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint8_t*>(gamma) + bc * 64u + q * 16u);
+    }
+  }
+  // outside X both the value and (one step per wave) the gain are zeroed: with r finite
+  // (rows past M take r = 1), y = (0 r) 0 is +0 there
+  if (!interior) {
+#pragma unroll
+    for (int t = 0; t < KS; ++t)
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (!(row_ok && ((int64_t)wave * KS + t) * L + g4 * 4 + u < nbk)) {
+          v[t][u] = u32x4{0u, 0u, 0u, 0u};
+          if constexpr (kGainEarly) gv[u] = u32x4{0u, 0u, 0u, 0u};
+        }
+  }
+
+  // the row sums in the defined order; the partner lanes of the tree's lane levels are
+  // DPP patterns: xor 1 and xor 2 within a quad, then (every quad, then every 8 lanes,
+  // holding one value) the half-row and row mirrors
+  double st[KS];
+#pragma unroll
+  for (int t = 0; t < KS; ++t) {
+    double su[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      // a bf16 square is exact in fp64, so a fused multiply-add rounds exactly as the
+      // addition of the square would
+      const double a0 = (double)__uint_as_float(v[t][u][0] << 16);
+      double s = __dmul_rn(a0, a0);
+      const double b0 = (double)__uint_as_float(v[t][u][0] & 0xFFFF0000u);
+      s = __fma_rn(b0, b0, s);
+#pragma unroll
+      for (int i = 1; i < 4; ++i) {
+        const double a = (double)__uint_as_float(v[t][u][i] << 16);
+        const double b = (double)__uint_as_float(v[t][u][i] & 0xFFFF0000u);
+        s = __fma_rn(a, a, s);
+        s = __fma_rn(b, b, s);
+      }
+      s = __dadd_rn(s, dpp_f64<0xB1>(s));  // runs (q, q^1): quad_perm [1,0,3,2]
+      s = __dadd_rn(s, dpp_f64<0x4E>(s));  // then pairs of those: quad_perm [2,3,0,1]
+      su[u] = s;
+    }
+    double sg = __dadd_rn(__dadd_rn(su[0], su[1]), __dadd_rn(su[2], su[3]));
+    if constexpr (L >= 8) sg = __dadd_rn(sg, dpp_f64<0x141>(sg));  // quads (0,1), (2,3): half-row mirror
+    if constexpr (L >= 16) sg = __dadd_rn(sg, dpp_f64<0x140>(sg));  // then those pairs: row mirror
+    st[t] = sg;
+  }
+#pragma unroll
+  for (int w = KS; w > 1; w /= 2)
+#pragma unroll
+    for (int i = 0; i < w / 2; ++i) st[i] = __dadd_rn(st[2 * i], st[2 * i + 1]);
+  if (p == 0) part[wave][j] = st[0];
+  __syncthreads();
+  if (threadIdx.x < R) {
+    double s[16];
+#pragma unroll
+    for (int w = 0; w < 16; ++w) s[w] = w < W ? part[w][threadIdx.x] : 0.0;
+#pragma unroll
+    for (int n = 16; n > 1; n /= 2)
+#pragma unroll
+      for (int i = 0; i < n / 2; ++i) s[i] = __dadd_rn(s[2 * i], s[2 * i + 1]);
+    rfac[threadIdx.x] = r0 + threadIdx.x < M ? (float)(1.0 / sqrt(s[0] / (double)K + eps)) : 1.0f;
+  }
+  __syncthreads();
+  const float rr = rfac[j];
+
+  // normalize and code each step of the wave
+  uint32_t* my = tiles + wave * 512;
+  uint32_t* myb = my + 256;
+  const int js = lane % R, bs = lane / R;  // the slot this lane stores: row js, block bs of the step
+  // fragment (row/32, block/2), half block%2, row%32: 16 B per (row, block)
+  uint8_t* rc_g = rcodes + (r0 >> 5) * (Kp / 64) * 1024;
+  uint8_t* bc_g = bcodes + (r0 >> 5) * (Kp / 64) * 1024;
+  const uint32_t lane_c = (uint32_t)((bs >> 1) * 1024 + (bs & 1) * 512 + (int)((r0 & 31) + js) * 16);
+  uint32_t* rs_g = reinterpret_cast<uint32_t*>(rscales) + r0;
+  uint32_t* bs_g = reinterpret_cast<uint32_t*>(bscales) + r0;
+#pragma unroll
+  for (int t = 0; t < KS; ++t) {
+    const int64_t ks = (int64_t)wave * KS + t;
+    if (ks * L >= nbp) break;  // uniform: the step starts past the padded row
+    uint32_t bword = 0, rword = 0;
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the previous step's tile reads are done
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int64_t blk = ks * L + g4 * 4 + u;
+      u32x4 g;
+      if constexpr (kGainEarly) {
+        g = gv[u];
+      } else {  // an L2 hit: shared by every row
+        g = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint8_t*>(gamma) +
+                                            min((uint32_t)blk, last_blk) * 64u + q * 16u);
+        if (!interior && !(row_ok && blk < nbk)) g = u32x4{0u, 0u, 0u, 0u};
+      }
+      // y = bf16(fp32(fp32(x r) g)), as fp32
+      float y[8];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) rms_scale_f2(v[t][u][i], g[i], rr, y[2 * i], y[2 * i + 1]);
+      uint32_t keep, bbyte, bpacked, rbyte, rpacked;
+      codec_block_f<0, SPM>(y, keep, bbyte, bpacked, rbyte, rpacked);
+      const int slot = (g4 * 4 + u) * R + j;
+      my[slot * 4 + q] = rpacked;
+      myb[slot * 4 + q] = bpacked;
+      rword |= rbyte << (8 * u);
+      bword |= bbyte << (8 * u);
+      if constexpr (WRITE_MASK)
+        if (row_ok && blk < nbk) mask[r * (K / 8) + blk * 4 + q] = (uint8_t)keep;
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // the tile is wave-private: a wave-level wait suffices
+    __builtin_amdgcn_wave_barrier();
+    if (ks * L + bs < nbp) {
+      const uint32_t off = (uint32_t)(ks * L / 2) * 1024u + lane_c;  // ks * L is even
+      *reinterpret_cast<u32x4*>(rc_g + off) = reinterpret_cast<const u32x4*>(my)[lane];
+      *reinterpret_cast<u32x4*>(bc_g + off) = reinterpret_cast<const u32x4*>(myb)[lane];
+    }
+    const int64_t word = ks * (L / 4) + g4;  // blocks 4*word .. 4*word+3
+    if (q == 0 && word < nbp / 4) {
+      const uint32_t wo = (uint32_t)word * (uint32_t)Mp + (uint32_t)j;
+      rs_g[wo] = rword;
+      bs_g[wo] = bword;
+    }
+  }
+}
+
+template <int R, int SPM, int KS, bool WRITE_MASK>
+hipError_t launch_rms_tiled_ks(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, const uint16_t* gamma,
+                               double eps, uint8_t* bcodes, uint8_t* bscales, uint8_t* rcodes, uint8_t* rscales,
+                               uint8_t* mask, hipStream_t stream) {
+  const int64_t Mp = (M + 31) / 32 * 32, Kp = (K + 127) / 128 * 128;
+  const int64_t steps = (Kp / 32 + (64 / R) - 1) / (64 / R);
+  const int waves = (int)((steps + KS - 1) / KS);
+  prep_mx_rms_tiled_kernel<R, SPM, KS, WRITE_MASK>
+      <<<dim3((unsigned)(Mp / R)), dim3(64 * waves), (size_t)waves * 2048, stream>>>(
+          x, M, K, ldx, Mp, Kp, gamma, eps, bcodes, bscales, rcodes, rscales, mask);
+  return hipGetLastError();
+}
+
+constexpr int kRmsRows = 4;  // rows per work-group of the one-read kernel
+
+template <int SPM, bool WRITE_MASK>
+hipError_t launch_rms_tiled(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, const uint16_t* gamma, double eps,
+                            uint8_t* bcodes, uint8_t* bscales, uint8_t* rcodes, uint8_t* rscales, uint8_t* mask,
+                            hipStream_t stream) {
+  constexpr int64_t span = 32 * (64 / kRmsRows);
+  const int64_t steps = ((K + 127) / 128 * 128 + span - 1) / span;
+  // the smallest step depth per wave that covers the row with at most 16 waves; a depth
+  // of 4 would need more than the 128 registers a lane has at 16 waves per group
+  if (steps <= 16)
+    return launch_rms_tiled_ks<kRmsRows, SPM, 1, WRITE_MASK>(x, M, K, ldx, gamma, eps, bcodes, bscales, rcodes,
+                                                             rscales, mask, stream);
+  return launch_rms_tiled_ks<kRmsRows, SPM, 2, WRITE_MASK>(x, M, K, ldx, gamma, eps, bcodes, bscales, rcodes, rscales,
+                                                           mask, stream);
+}
+
 template <int MODE, int SPM, bool WRITE_MASK, int XF>
 hipError_t launch_tiled(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, uint8_t* bcodes,
                         uint8_t* bscales, uint8_t* rcodes, uint8_t* rscales, uint8_t* mask, Norm nm,
@@ -425,6 +651,27 @@ hipError_t launch_prep_mx(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, 
   const int xf = swiglu ? kXfSwiglu : rnorm ? kXfRms : kXfNone;
   if (sp_m == 4) return prep_pattern<4>(x, M, K, ldx, bcodes, bscales, rcodes, rscales, mask, nm, xf, tiled, stream);
   return prep_pattern<8>(x, M, K, ldx, bcodes, bscales, rcodes, rscales, mask, nm, xf, tiled, stream);
+}
+
+bool prep_mx_rms_one_read(int64_t M, int64_t K, int64_t ldx) {
+  constexpr int64_t span = 32 * (64 / kRmsRows);  // elements per wave step
+  // rows that fit the group's registers; 32-bit lane offsets into X and the scale words
+  return M > 0 && ((K + 127) / 128 * 128 + span - 1) / span <= 32 && kRmsRows * ldx * 2 < ((int64_t)1 << 31) &&
+         M < ((int64_t)1 << 26);
+}
+
+hipError_t launch_prep_mx_rms_tiled(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, const uint16_t* gamma,
+                                    float eps, int sp_m, uint8_t* bcodes, uint8_t* bscales, uint8_t* rcodes,
+                                    uint8_t* rscales, uint8_t* mask, hipStream_t stream) {
+  if (sp_m == 4)
+    return mask ? launch_rms_tiled<4, true>(x, M, K, ldx, gamma, (double)eps, bcodes, bscales, rcodes, rscales, mask,
+                                            stream)
+                : launch_rms_tiled<4, false>(x, M, K, ldx, gamma, (double)eps, bcodes, bscales, rcodes, rscales, mask,
+                                             stream);
+  return mask ? launch_rms_tiled<8, true>(x, M, K, ldx, gamma, (double)eps, bcodes, bscales, rcodes, rscales, mask,
+                                          stream)
+              : launch_rms_tiled<8, false>(x, M, K, ldx, gamma, (double)eps, bcodes, bscales, rcodes, rscales, mask,
+                                           stream);
 }
 
 hipError_t launch_prep_mx_ablation(int variant, const uint16_t* x, int64_t M, int64_t K, int64_t ldx, int sp_m,

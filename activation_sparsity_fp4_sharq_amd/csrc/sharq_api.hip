@@ -350,6 +350,11 @@ sharq_status sharq_prep_rmsnorm(const void* x, int64_t M, int64_t K, int64_t ldx
   if ((s = check_device()) != SHARQ_OK) return s;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   const uint16_t* xb = reinterpret_cast<const uint16_t*>(x);
+  // MXFP4 to the tiled layout: one read of X (row sums, factors and codec from registers)
+  if (fmt == SHARQ_MXFP4 && backbone->layout == SHARQ_LAYOUT_TILED && prep_mx_rms_one_read(M, K, ldx))
+    return launched(launch_prep_mx_rms_tiled(xb, M, K, ldx, reinterpret_cast<const uint16_t*>(gamma), eps, sp_m,
+                                             backbone->codes, backbone->scales, residual->codes, residual->scales,
+                                             mask_bits, st));
   float* rfac = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + rms_factor_offset(fmt));
   hipError_t e = launch_row_rms(xb, M, K, ldx, eps, rfac, st);
   if (e != hipSuccess) return SHARQ_E_LAUNCH;
@@ -399,6 +404,14 @@ sharq_status sharq_stream_probe(const void* src, int64_t read_bytes, void* dst, 
   sharq_status s = check_device();
   if (s != SHARQ_OK) return s;
   return launched(launch_stream_probe(src, read_bytes, dst, write_bytes, reinterpret_cast<hipStream_t>(stream)));
+}
+
+sharq_status sharq_bf16_rounding_probe(uint64_t* counters, void* stream) {
+  if (!counters) return SHARQ_E_NULL;
+  if (reinterpret_cast<uintptr_t>(counters) & 7u) return SHARQ_E_ALIGN;
+  sharq_status s = check_device();
+  if (s != SHARQ_OK) return s;
+  return launched(launch_rounding_probe(counters, reinterpret_cast<hipStream_t>(stream)));
 }
 
 sharq_status sharq_forward(const void* x, int64_t M, int64_t K, int64_t ldx, int sp_n, int sp_m, int fmt,

@@ -18,6 +18,12 @@ hipError_t launch_prep_mx(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, 
                           int sp_m, uint8_t* bcodes, uint8_t* bscales, uint8_t* rcodes,
                           uint8_t* rscales, uint8_t* mask, const float* rnorm, const uint16_t* gamma,
                           int swiglu, int tiled, hipStream_t stream);
+// RMS normalization and MXFP4 preparation in one read of X, tiled output, for the row
+// lengths whose rows fit one work-group's registers (prep_mx_rms_one_read tells).
+bool prep_mx_rms_one_read(int64_t M, int64_t K, int64_t ldx);
+hipError_t launch_prep_mx_rms_tiled(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, const uint16_t* gamma,
+                                    float eps, int sp_m, uint8_t* bcodes, uint8_t* bscales, uint8_t* rcodes,
+                                    uint8_t* rscales, uint8_t* mask, hipStream_t stream);
 // The ablation variants of the preparation (sharq_ablation), without normalization.
 hipError_t launch_prep_mx_ablation(int variant, const uint16_t* x, int64_t M, int64_t K, int64_t ldx, int sp_m,
                                    uint8_t* bcodes, uint8_t* bscales, uint8_t* rcodes, uint8_t* rscales,
@@ -63,6 +69,7 @@ size_t linear_nv_workspace(int64_t M, int64_t N, int64_t K);
 // loop of `iters` x 4 FP4 matrix instructions while every CU runs the same loop.
 hipError_t launch_clock_probe(int64_t iters, uint64_t* out, hipStream_t stream);
 hipError_t launch_matrix_rate_probe(int form, int64_t iters, uint64_t* out, hipStream_t stream);
+hipError_t launch_rounding_probe(uint64_t* out, hipStream_t stream);
 hipError_t launch_stream_probe(const void* src, int64_t read_bytes, void* dst, int64_t write_bytes,
                                hipStream_t stream);
 

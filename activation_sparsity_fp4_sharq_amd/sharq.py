@@ -24,7 +24,8 @@ SYMBOLS = ["sharq_abi_version", "sharq_status_str", "sharq_payload_bytes", "shar
            "sharq_prep_workspace_bytes", "sharq_linear_workspace_bytes", "sharq_quantize", "sharq_prep",
            "sharq_prep_rmsnorm_workspace_bytes", "sharq_prep_rmsnorm", "sharq_linear", "sharq_linear_dense",
            "sharq_clock_probe", "sharq_prep_ablation", "sharq_dequantize", "sharq_prep_swiglu",
-           "sharq_forward", "sharq_forward_noalloc", "sharq_matrix_rate_probe", "sharq_stream_probe"]
+           "sharq_forward", "sharq_forward_noalloc", "sharq_matrix_rate_probe", "sharq_stream_probe",
+           "sharq_bf16_rounding_probe"]
 
 
 class SharqFp4(ctypes.Structure):
@@ -38,7 +39,7 @@ class SharqError(RuntimeError):
         self.status = status
 
 
-ABI_VERSION = 9  # the SHARQ_ABI_VERSION of include/sharq.h this binding marshals for
+ABI_VERSION = 10  # the SHARQ_ABI_VERSION of include/sharq.h this binding marshals for
 
 _lib = None
 
@@ -105,6 +106,8 @@ def lib():
         L.sharq_matrix_rate_probe.argtypes = [ctypes.c_int, i64, vp, vp]
         L.sharq_stream_probe.restype = ctypes.c_int
         L.sharq_stream_probe.argtypes = [vp, i64, vp, i64, vp]
+        L.sharq_bf16_rounding_probe.restype = ctypes.c_int
+        L.sharq_bf16_rounding_probe.argtypes = [vp, vp]
         L.sharq_forward_noalloc.restype = ctypes.c_int
         L.sharq_forward_noalloc.argtypes = [vp, i64, i64, i64, ctypes.c_int, ctypes.c_int, ctypes.c_int, P, P, P,
                                             i64, vp, i64, ctypes.c_int, vp]
@@ -495,6 +498,16 @@ def stream_probe(src, read_bytes, dst, write_bytes, stream=None):
         _check_device(t, src.device, what)
     _check("sharq_stream_probe", lib().sharq_stream_probe(_ptr(src), read_bytes, _ptr(dst), write_bytes,
                                                           _stream(stream)))
+
+
+def bf16_rounding_probe(device=None, stream=None):
+    """Every fp32 pattern through the device's packed bf16 conversion: returns (number of
+    finite patterns that differ from round-to-nearest-even on the bits, smallest one)."""
+    dev = device if device is not None else torch.device("cuda", torch.cuda.current_device())
+    out = torch.zeros(2, dtype=torch.int64, device=dev)
+    _check("sharq_bf16_rounding_probe", lib().sharq_bf16_rounding_probe(_ptr(out), _stream(stream)))
+    bad, first = (int(v) & 0xFFFFFFFFFFFFFFFF for v in out.cpu())
+    return bad, first
 
 
 _raw = None

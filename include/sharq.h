@@ -61,7 +61,7 @@
 extern "C" {
 #endif
 
-#define SHARQ_ABI_VERSION 9
+#define SHARQ_ABI_VERSION 10
 
 typedef enum sharq_status {
   SHARQ_OK = 0,
@@ -223,17 +223,21 @@ size_t sharq_prep_rmsnorm_workspace_bytes(int64_t M, int64_t K, int fmt);
  * normalization).  The pages do not spell the normalization out; it is read as RMS
  * normalization with a per-channel gain and no bias, producing the bf16 tensor that
  * the preparation then decomposes:
- *   r_i  = fp32( 1 / sqrt( (sum_k x_ik^2) / K + eps ) )   (sum, sqrt, division in fp64)
+ *   r_i  = fp32( 1 / sqrt( S_i / K + eps ) )   (mean, sqrt, division in fp64)
  *   y_ik = bf16_rne( fp32( fp32(x_ik * r_i) * gamma_k ) )
- * and backbone / residual / mask_bits are exactly sharq_prep's outputs for y.
+ * where S_i, the fp64 sum of the row's squares, is evaluated in one fixed order: each
+ * run of 8 consecutive squares added in index order, the run sums added in a balanced
+ * binary tree over the run index (zero-padded to a power of two) -- so r_i is a single
+ * defined number.  backbone / residual / mask_bits are exactly sharq_prep's outputs for y.
+ * MXFP4 to the tiled layout with K <= 16384 reads X once (sums, factors and the
+ * preparation from registers); other layouts, NVFP4 and longer rows launch a row-factor
+ * kernel first and keep the factors in the workspace.
  *   x, M, K, ldx, sp_n, sp_m, fmt, backbone, residual, mask_bits: as for sharq_prep
  *   gamma      device bf16 [K] gains, 16-byte aligned (may be NULL only when M == 0)
- *   eps        >= 0 and finite, else SHARQ_E_SHAPE
+ *   eps        >= 0 and finite, else SHARQ_E_SHAPE (a zero row with eps = 0 gives
+ *              r_i = infinity and NaN values)
  *   workspace  device, >= sharq_prep_rmsnorm_workspace_bytes(M, K, fmt) bytes, 16-byte
- *              aligned; holds the row factors between the two launches of the call
- * The fp64 row sums are exact up to ~K * 2^-53 relative, so the fp32 factor r_i can
- * differ from an exact evaluation's only when the exact value lies within that margin
- * of an fp32 rounding boundary. */
+ *              aligned; holds the row factors (and NVFP4's maxima) of the two-launch form */
 sharq_status sharq_prep_rmsnorm(const void* x, int64_t M, int64_t K, int64_t ldx, const void* gamma,
                                 float eps, int sp_n, int sp_m, int fmt, const sharq_fp4* backbone,
                                 const sharq_fp4* residual, uint8_t* mask_bits, void* workspace,
@@ -302,6 +306,14 @@ sharq_status sharq_matrix_rate_probe(int form, int64_t iters, uint64_t* counters
  *   read_bytes, write_bytes  >= 0, multiples of 16, else SHARQ_E_SHAPE
  *   dst's contents afterwards are unspecified. */
 sharq_status sharq_stream_probe(const void* src, int64_t read_bytes, void* dst, int64_t write_bytes, void* stream);
+
+/* Self-check of the fp32 -> bf16 rounding the one-read normalized preparation uses (the
+ * gfx950 packed conversion; reading R9 rounds y to nearest even): converts every fp32
+ * bit pattern on the device and compares with round-to-nearest-even done on the bits.
+ *   counters  device, 8-byte aligned, >= 2 uint64: [0] receives the number of finite
+ *             patterns that differ, [1] the smallest such pattern (2^64 - 1 if none)
+ * Errors: SHARQ_E_NULL, SHARQ_E_ALIGN, SHARQ_E_DEVICE, SHARQ_E_LAUNCH. */
+sharq_status sharq_bf16_rounding_probe(uint64_t* counters, void* stream);
 
 /* One SharQ linear layer end to end (SharQ, arXiv 2606.26587: the abstract's
  * decomposition as one layer; Figure 2's dataflow of the fused preparation feeding the

@@ -19,7 +19,7 @@ A = 0x10000  # a 16-byte aligned fake device address: never dereferenced by thes
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(sharq_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(sharq_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_header_symbols_exported():
@@ -33,7 +33,7 @@ def test_header_symbols_exported():
 
 def test_version_and_status_strings():
     L = sharq.lib()
-    assert L.sharq_abi_version() == 9
+    assert L.sharq_abi_version() == 10
     for s in range(9):
         assert L.sharq_status_str(s)
     assert L.sharq_status_str(99) == b"unknown status"
@@ -320,6 +320,12 @@ def test_forward_noalloc_rejects_before_launch():
     assert call(y=None) == E_NULL
     assert call(fmt=7) == E_FORMAT
     assert call() == E_DEVICE  # valid arguments, no gfx950 in this process
+
+
+def test_rounding_probe_rejects():
+    L = sharq.lib()
+    assert L.sharq_bf16_rounding_probe(None, None) == E_NULL
+    assert L.sharq_bf16_rounding_probe(A + 4, None) == E_ALIGN
 
 
 def test_measurement_probes_reject():

@@ -492,10 +492,96 @@ def test_prep_rmsnorm_matches_oracle(fmt, layout, n, m, M, K, ldx_pad):
     assert_payload_equal(rr, orr, "residual")
 
 
-def test_prep_rmsnorm_workload_full_size():
-    """The prefill workload's activation through the normalized preparation."""
-    w = WORKLOADS["prefill"]
-    print("[prep_rmsnorm] prefill full size", flush=True)
+@pytest.mark.parametrize("n,m", [(2, 4), (4, 8)])
+@pytest.mark.parametrize("M,K,ldx_pad", [(19, 2048, 0), (33, 2176, 0), (16, 3072, 128), (50, 4096, 0),
+                                         (7, 4224, 0), (5, 8192, 0), (6, 8320, 0), (3, 14336, 0),
+                                         (9, 16384, 0), (5, 16512, 0), (2, 32768, 0)])
+def test_prep_rmsnorm_tiled_row_lengths(n, m, M, K, ldx_pad):
+    """Tiled MXFP4 normalized preparation around the one-read kernel's limits: one and
+    two steps per wave, wave counts that are not powers of two, a last step past the
+    padded row, the longest rows that fit (16384) and longer ones (the two-pass path),
+    with ragged row groups; bit for bit."""
+    print(f"[prep_rmsnorm] tiled {n}:{m} M={M} K={K} pad={ldx_pad}", flush=True)
+    xb, _ = make_shape(M, 8, K, seed=M * 11 + K, dist="normal", token_sigma=0.8)
+    g = _gain(K, K + 1)
+    if ldx_pad:
+        wide = np.zeros((M, K + ldx_pad), np.uint16)
+        wide[:, :K] = xb
+        x = to_dev(wide)[:, :K]
+    else:
+        x = to_dev(xb)
+    bb, rr, mask = sharq.prep_rmsnorm(x, to_dev(g), 1e-6, n, m, sharq.MXFP4, want_mask=True, layout=sharq.TILED)
+    torch.cuda.synchronize()
+    yb, _ = oracle.rmsnorm(xb, g, 1e-6)
+    ob, orr, omask = oracle.prep(yb, n, m, sharq.MXFP4)
+    assert np.array_equal(mask.cpu().numpy(), omask), "mask bits differ"
+    assert_payload_equal(bb, ob, "backbone")
+    assert_payload_equal(rr, orr, "residual")
+
+
+def test_bf16_rounding_of_the_normalization_is_nearest_even():
+    """The packed fp32 -> bf16 conversion the one-read normalized preparation rounds y
+    with agrees with round-to-nearest-even on the bits for every finite fp32 pattern."""
+    print("[bf16 rounding probe] all 2^32 patterns", flush=True)
+    bad, first = sharq.bf16_rounding_probe()
+    assert bad == 0, f"{bad} patterns differ, first 0x{first:08x}"
+
+
+def _order_sensitive_row(K, big):
+    """A row whose fp64 sum of squares depends on the order of the additions: `big` ones
+    in the first run of 8, squares of 2^-54 everywhere else (each one lost when added
+    alone to a running sum of at least 1, kept when summed among themselves first), and
+    a probe in an otherwise zero block 1 whose normalized value, with gain 1.75, sits on
+    the bf16 midpoint below a power of two when r is a power of two."""
+    x = np.full(K, 2.0 ** -27, np.float32)
+    x[:big] = 1.0
+    x[32:64] = 0.0
+    x[40] = 146 * 2.0 ** -40
+    g = np.ones(K, np.float32)
+    g[40] = 224 * 2.0 ** -7
+    return f32_to_bf16_bits(x), f32_to_bf16_bits(g)
+
+
+@pytest.mark.parametrize("layout", [sharq.TILED, sharq.ROWMAJOR], ids=["tiled", "rowmajor"])
+@pytest.mark.parametrize("K,big,c,n,m", [(2048, 2, 5, 2, 4), (3072, 3, 5, 4, 8), (4096, 1, 6, 2, 4),
+                                         (8192, 2, 6, 4, 8), (16384, 4, 6, 2, 4), (32768, 8, 6, 4, 8)])
+def test_prep_rmsnorm_follows_the_sum_order(layout, K, big, c, n, m):
+    """The normalized preparation reproduces the defined order of the row's sum of squares:
+    with S/K = 2^-2c and eps = 2^(-2c-24), a plain left-to-right sum (= big) gives r = 2^c
+    and the defined order (slightly more) gives r = 2^c - 2^(c-24), and the probe block's
+    scale byte tells the two apart.  Other rows are random."""
+    print(f"[prep_rmsnorm] sum order layout={layout} K={K}", flush=True)
+    row, g = _order_sensitive_row(K, big)
+    eps = 2.0 ** (-2 * c - 24)
+    # the construction discriminates: a left-to-right sum lands exactly on `big`
+    vals = row.astype(np.uint32) << 16
+    left_to_right = 0.0
+    for v in vals.view(np.float32).astype(np.float64):
+        left_to_right = left_to_right + v * v
+    assert left_to_right == big and oracle.row_sumsq(row[None, :])[0] > big
+    flat = row.copy()
+    flat[(np.arange(K) >= 64) | ((np.arange(K) >= big) & (np.arange(K) < 32))] = 0  # S = big exactly
+    y_seq, r_seq = oracle.rmsnorm(flat[None, :], g, eps)
+    y_def, r_def = oracle.rmsnorm(row[None, :], g, eps)
+    assert r_seq[0] == 2.0 ** c and r_def[0] == np.float32(2.0 ** c - 2.0 ** (c - 24))
+    assert oracle.prep(y_seq, n, m)[0].scales[0, 1] != oracle.prep(y_def, n, m)[0].scales[0, 1]
+
+    rnd, _ = make_shape(21, 8, K, seed=K + big, dist="normal")
+    xb = np.concatenate([rnd[:9], row[None, :], rnd[9:]])
+    bb, rr, mask = sharq.prep_rmsnorm(to_dev(xb), to_dev(g), eps, n, m, sharq.MXFP4, want_mask=True, layout=layout)
+    torch.cuda.synchronize()
+    yb, _ = oracle.rmsnorm(xb, g, eps)
+    ob, orr, omask = oracle.prep(yb, n, m, sharq.MXFP4)
+    assert np.array_equal(mask.cpu().numpy(), omask), "mask bits differ"
+    assert_payload_equal(bb, ob, "backbone")
+    assert_payload_equal(rr, orr, "residual")
+
+
+@pytest.mark.parametrize("name", ["prefill", "dit"])
+def test_prep_rmsnorm_workload_full_size(name):
+    """The prefill and DiT workloads' activations through the normalized preparation."""
+    w = WORKLOADS[name]
+    print(f"[prep_rmsnorm] {name} full size", flush=True)
     xb, _ = make_inputs(w, with_weight=False)
     g = _gain(w.K, 1)
     bb, rr, _ = sharq.prep_rmsnorm(to_dev(xb), to_dev(g), 1e-6, w.n, w.m, w.fmt)
