@@ -614,6 +614,20 @@ def main():
                     "traffic": traffic, "bytes_per_launch": gemm_bytes,
                     "intensity_flop_per_byte": round(alg / gemm_bytes, 1),
                     "byte_convention": "both activation payloads + weight payload + bf16 output"}
+        # the streaming ceiling at the GEMM's byte counts: a plain read of its input bytes
+        # and write of its output bytes, from buffers of their own per input set
+        rd = gemm_bytes - y_bytes
+        gsrcs = [torch.empty(rd, dtype=torch.uint8, device=dev) for _ in range(nsets)]
+        gsinks = [torch.empty(y_bytes, dtype=torch.uint8, device=dev) for _ in range(nsets)]
+        t_gstream = back_to_back_seconds(
+            lambda i: sharq.stream_probe(gsrcs[i % nsets], rd, gsinks[i % nsets], y_bytes, stream=stream),
+            args.steps, stream)
+        del gsrcs, gsinks
+        roofline["stream_ceiling"] = {"kernel": "sharq_stream_probe", "read_bytes": rd, "write_bytes": y_bytes,
+                                      "ms": round(t_gstream * 1e3, 4),
+                                      "GB_s": round(gemm_bytes / t_gstream / 1e9, 1),
+                                      "pct_hbm": round(100.0 * gemm_bytes / t_gstream / 1e9 / PEAK_HBM_GBS, 2),
+                                      "linear_vs_ceiling": round(t_gstream / t_lin, 3)}
 
     out = {
         "metric": "fused SharQ linear effective TFLOPS (2MNK/t) + % MXFP4 peak; prep GB/s %HBM",
