@@ -11,9 +11,10 @@
 //                                         largest element is kept)
 //   pass 1  mask, backbone -> written; R = X - Bhat; amax|R|
 //   pass 2  R again from X and the written backbone; residual -> written
-// The maximum passes leave one partial per work-group in the caller's workspace and a
-// one-work-group kernel reduces them (no contended atomics); work-group 0 of the pass
-// after it writes that path's tensor scale.
+// The maximum passes leave one partial per work-group in the caller's workspace; every
+// work-group of the pass after a maximum pass reduces those partials itself (a few KiB
+// of L2-resident words, no atomics and no launch in between), and its work-group 0
+// writes that path's tensor scale.
 //
 // Arithmetic per 16-element block, each step one correctly rounded fp32 operation:
 //   q = amax_blk / (6*S);  s = E4M3(q) (nearest-even, saturating at 448);
@@ -43,9 +44,9 @@ constexpr int kThreads = 256;
 constexpr int kUnroll = 2;
 constexpr int kMaxGroups = 2048;  // bounded grid of the maximum passes
 constexpr float kUnitScale = 1.0f;
-// workspace (uint32): [0] max|X|, [1] max|R| (fp32 bits of non-negative values, so
-// integer maxima order them), then one partial maximum per work-group of each
-// maximum pass from kPartialBase on
+// workspace (uint32): [0] max|X| (written by pass 1 for pass 2), [1] max|R| (fp32 bits
+// of non-negative values, so integer maxima order them), then one partial maximum per
+// work-group of each maximum pass from kPartialBase on
 constexpr int kPartialBase = 16;
 static_assert((kPartialBase + 2 * kMaxGroups) * 4 <= (int)kNvPrepWorkspace, "workspace too small");
 
@@ -59,6 +60,29 @@ __device__ __forceinline__ uint32_t wave_max(uint32_t v) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) v = umax(v, __shfl_xor(v, off, 64));
   return v;
+}
+
+// Maximum of the n (<= kMaxGroups) partials at p, by the whole work-group of kThreads
+// (every thread gets it, so every thread must call it).  Each thread issues its loads
+// before using any.
+__device__ __forceinline__ uint32_t group_max_of(const uint32_t* __restrict__ p, int n, uint32_t* red) {
+  constexpr int kPer = kMaxGroups / kThreads;
+  uint32_t v[kPer];
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int i = j * kThreads + (int)threadIdx.x;
+    v[j] = i < n ? p[i] : 0u;
+  }
+  uint32_t m = 0;
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) m = umax(m, v[j]);
+  m = wave_max(m);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  uint32_t r = 0;
+#pragma unroll
+  for (int w = 0; w < kThreads / 64; ++w) r = umax(r, red[w]);
+  return r;
 }
 
 // OCP E4M3 code of q >= 0: nearest value, ties to the even code, saturating at 448.
@@ -193,10 +217,10 @@ __device__ __forceinline__ uint32_t abs_max8_bits(const float v[8]) {
 // 2-4 are the ablations of the method's choices: 2 = residual against the
 // unquantized sparse values (R = X - X*mask), 3 = a static mask (the first n of
 // every m positions; the backbone maxima are then those of the kept values), 4 = no
-// residual (all-zero residual payload, tensor scale 1).  A
-// one-work-group launch after each maximum pass reduces its partials into work[0]
-// or work[1]; work-group 0 of the pass after it writes that path's tensor scale
-// (backbone or plain: bts, residual: rts).
+// residual (all-zero residual payload, tensor scale 1).  The pass after a maximum pass
+// reduces that pass's `nparts` partials in every work-group; work-group 0 writes the
+// path's tensor scale (backbone or plain: bts, residual: rts) and pass 1's also
+// max|X| into work[0] for pass 2.
 // static mask of the lane's 8 elements (they start at a multiple of 8, so element j
 // sits at position j % SPM of its group)
 template <int SPM>
@@ -211,7 +235,7 @@ __global__ __launch_bounds__(kThreads) void prep_nv_kernel(
     uint8_t* __restrict__ bcodes, uint8_t* __restrict__ bscales, uint8_t* __restrict__ rcodes,
     uint8_t* __restrict__ rscales, uint8_t* __restrict__ mask, uint32_t* __restrict__ work,
     float* __restrict__ bts, float* __restrict__ rts, const float* __restrict__ rnorm,
-    const uint16_t* __restrict__ gamma) {
+    const uint16_t* __restrict__ gamma, int nparts) {
   const int lane = threadIdx.x & 63;
   const int64_t wave = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
   // the maximum passes walk the chunks grid-stride with a bounded grid; the last pass
@@ -220,13 +244,24 @@ __global__ __launch_bounds__(kThreads) void prep_nv_kernel(
   const int64_t nblocks = nchunks >> 1;
 
   PathScale pb{}, pr{};
-  if constexpr (PASS >= 1) {
-    pb = path_scale(work[0]);
-    if (blockIdx.x == 0 && threadIdx.x == 0 && (PASS == 1 || MODE == 1) && bts) *bts = pb.S;
+  __shared__ uint32_t pred[kThreads / 64];
+  if constexpr (PASS == 1 || (PASS == 2 && MODE == 1)) {
+    // the pass right after pass 0: max|X| from its partials
+    const uint32_t amax = group_max_of(work + kPartialBase, nparts, pred);
+    pb = path_scale(amax);
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+      if (bts) *bts = pb.S;
+      if constexpr (PASS == 1) work[0] = amax;
+    }
   }
   if constexpr (PASS == 2 && MODE != 1) {
-    pr = path_scale(work[1]);
-    if (blockIdx.x == 0 && threadIdx.x == 0 && rts) *rts = pr.S;
+    pb = path_scale(work[0]);
+    const uint32_t rmax = group_max_of(work + kPartialBase + kMaxGroups, nparts, pred);
+    pr = path_scale(rmax);
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+      work[1] = rmax;
+      if (rts) *rts = pr.S;
+    }
   }
 
   uint32_t run_max = 0;
@@ -373,30 +408,6 @@ __global__ __launch_bounds__(kThreads) void prep_nv_kernel(
   }
 }
 
-// work[slot] = max of the `n` partials of a maximum pass (one work-group).  Every
-// thread issues its kMaxGroups / 256 loads before using any (a fixed, unrolled count:
-// a strided loop over n would wait for each load in turn).
-__global__ void nv_reduce_kernel(uint32_t* work, int slot, int n) {
-  __shared__ uint32_t red[256];
-  constexpr int kPer = kMaxGroups / 256;
-  uint32_t v[kPer];
-#pragma unroll
-  for (int j = 0; j < kPer; ++j) {
-    const int i = j * 256 + (int)threadIdx.x;
-    v[j] = i < n ? work[kPartialBase + slot * kMaxGroups + i] : 0u;
-  }
-  uint32_t m = 0;
-#pragma unroll
-  for (int j = 0; j < kPer; ++j) m = umax(m, v[j]);
-  red[threadIdx.x] = m;
-  __syncthreads();
-  for (int w = 128; w > 0; w >>= 1) {
-    if ((int)threadIdx.x < w) red[threadIdx.x] = umax(red[threadIdx.x], red[threadIdx.x + w]);
-    __syncthreads();
-  }
-  if (threadIdx.x == 0) work[slot] = red[0];
-}
-
 // Empty tensors: both maxima 0, tensor scales 1.
 __global__ void nv_empty_kernel(uint32_t* work, float* t0, float* t1) {
   if (threadIdx.x == 0) {
@@ -414,16 +425,14 @@ hipError_t run_passes(const uint16_t* x, int64_t ldx, int64_t cpr, int64_t nchun
   const int64_t per_wg = (kThreads / 64) * 64 * kUnroll;
   const int64_t grid = (nchunks + per_wg - 1) / per_wg;
   const unsigned rgrid = (unsigned)(grid < kMaxGroups ? grid : kMaxGroups);
+  const int np = (int)rgrid;  // partials per maximum pass
   prep_nv_kernel<0, MODE, SPM, DENSE, WRITE_MASK, XF><<<dim3(rgrid), kThreads, 0, st>>>(
-      x, ldx, cpr, nchunks, bcodes, bscales, rcodes, rscales, mask, work, bts, rts, rnorm, gamma);
-  nv_reduce_kernel<<<1, 256, 0, st>>>(work, 0, (int)rgrid);
-  if constexpr (MODE != 1) {
+      x, ldx, cpr, nchunks, bcodes, bscales, rcodes, rscales, mask, work, bts, rts, rnorm, gamma, np);
+  if constexpr (MODE != 1)
     prep_nv_kernel<1, MODE, SPM, DENSE, WRITE_MASK, XF><<<dim3(rgrid), kThreads, 0, st>>>(
-        x, ldx, cpr, nchunks, bcodes, bscales, rcodes, rscales, mask, work, bts, rts, rnorm, gamma);
-    nv_reduce_kernel<<<1, 256, 0, st>>>(work, 1, (int)rgrid);
-  }
+        x, ldx, cpr, nchunks, bcodes, bscales, rcodes, rscales, mask, work, bts, rts, rnorm, gamma, np);
   prep_nv_kernel<2, MODE, SPM, DENSE, WRITE_MASK, XF><<<dim3((unsigned)grid), kThreads, 0, st>>>(
-      x, ldx, cpr, nchunks, bcodes, bscales, rcodes, rscales, mask, work, bts, rts, rnorm, gamma);
+      x, ldx, cpr, nchunks, bcodes, bscales, rcodes, rscales, mask, work, bts, rts, rnorm, gamma, np);
   return hipGetLastError();
 }
 
