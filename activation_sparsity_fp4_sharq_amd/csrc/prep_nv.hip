@@ -42,7 +42,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
 constexpr int kUnroll = 2;
-constexpr int kMaxGroups = 2048;  // bounded grid of the maximum passes
+constexpr int kMaxGroups = 2048;  // bounded grid of the maximum passes: at most this many partials each
 constexpr float kUnitScale = 1.0f;
 // workspace (uint32): [0] max|X| (written by pass 1 for pass 2), [1] max|R| (fp32 bits
 // of non-negative values, so integer maxima order them), then one partial maximum per
@@ -62,15 +62,16 @@ __device__ __forceinline__ uint32_t wave_max(uint32_t v) {
   return v;
 }
 
-// Maximum of the n (<= kMaxGroups) partials at p, by the whole work-group of kThreads
-// (every thread gets it, so every thread must call it).  Each thread issues its loads
-// before using any.
+// Maximum of the n (<= kMaxGroups) partials at p, by the whole work-group of TPB
+// threads (every thread gets it, so every thread must call it).  Each thread issues
+// its loads before using any.
+template <int TPB>
 __device__ __forceinline__ uint32_t group_max_of(const uint32_t* __restrict__ p, int n, uint32_t* red) {
-  constexpr int kPer = kMaxGroups / kThreads;
+  constexpr int kPer = kMaxGroups / TPB;
   uint32_t v[kPer];
 #pragma unroll
   for (int j = 0; j < kPer; ++j) {
-    const int i = j * kThreads + (int)threadIdx.x;
+    const int i = j * TPB + (int)threadIdx.x;
     v[j] = i < n ? p[i] : 0u;
   }
   uint32_t m = 0;
@@ -81,7 +82,7 @@ __device__ __forceinline__ uint32_t group_max_of(const uint32_t* __restrict__ p,
   __syncthreads();
   uint32_t r = 0;
 #pragma unroll
-  for (int w = 0; w < kThreads / 64; ++w) r = umax(r, red[w]);
+  for (int w = 0; w < TPB / 64; ++w) r = umax(r, red[w]);
   return r;
 }
 
@@ -211,6 +212,18 @@ __device__ __forceinline__ uint32_t abs_max8_bits(const float v[8]) {
   return __float_as_uint(fmaxf(m1, m2));
 }
 
+// Work-group shape of a pass.  The plain preparation's maximum passes over dense rows
+// run 1024-thread work-groups held to 64 registers (two per CU: 8 waves per SIMD), so a
+// pass leaves at most 512 partials for the next one to reduce; every other variant
+// (its pass 1 needs more registers) keeps 256-thread work-groups.
+template <int PASS, int MODE, bool DENSE_ROWS, bool WRITE_MASK, int XF>
+struct NvShape {
+  static constexpr bool kWide = PASS <= 1 && DENSE_ROWS && MODE == 0 && !WRITE_MASK && XF == kXfNone;
+  static constexpr int kTpb = kWide ? 1024 : kThreads;
+  static constexpr int kMinWaves = kWide ? 8 : 1;
+  static constexpr int kGroups = kWide ? 512 : kMaxGroups;  // bounded grid of a maximum pass
+};
+
 // PASS 0: amax|X| partials.  PASS 1 (MODE 0): backbone written, amax|R| partials.
 // PASS 2: MODE 0 writes the residual from X and the written backbone; MODE 1 (plain
 // NVFP4 quantization, used for weights) quantizes X into (rcodes, rscales).  MODEs
@@ -230,24 +243,26 @@ __device__ __forceinline__ void static_mask(bool kept[8]) {
 }
 
 template <int PASS, int MODE, int SPM, bool DENSE_ROWS, bool WRITE_MASK, int XF>
-__global__ __launch_bounds__(kThreads) void prep_nv_kernel(
+__global__ __launch_bounds__((NvShape<PASS, MODE, DENSE_ROWS, WRITE_MASK, XF>::kTpb))
+__attribute__((amdgpu_waves_per_eu(NvShape<PASS, MODE, DENSE_ROWS, WRITE_MASK, XF>::kMinWaves, 8))) void prep_nv_kernel(
     const uint16_t* __restrict__ x, int64_t ldx, int64_t chunks_per_row, int64_t nchunks,
     uint8_t* __restrict__ bcodes, uint8_t* __restrict__ bscales, uint8_t* __restrict__ rcodes,
     uint8_t* __restrict__ rscales, uint8_t* __restrict__ mask, uint32_t* __restrict__ work,
     float* __restrict__ bts, float* __restrict__ rts, const float* __restrict__ rnorm,
     const uint16_t* __restrict__ gamma, int nparts) {
   const int lane = threadIdx.x & 63;
-  const int64_t wave = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+  constexpr int TPB = NvShape<PASS, MODE, DENSE_ROWS, WRITE_MASK, XF>::kTpb;  // threads per work-group
+  const int64_t wave = (int64_t)blockIdx.x * (TPB / 64) + (threadIdx.x >> 6);
   // the maximum passes walk the chunks grid-stride with a bounded grid; the last pass
   // covers everything with one iteration per wave
-  const int64_t stride = PASS <= 1 ? (int64_t)gridDim.x * (kThreads / 64) * 64 * kUnroll : nchunks;
+  const int64_t stride = PASS <= 1 ? (int64_t)gridDim.x * (TPB / 64) * 64 * kUnroll : nchunks;
   const int64_t nblocks = nchunks >> 1;
 
   PathScale pb{}, pr{};
-  __shared__ uint32_t pred[kThreads / 64];
+  __shared__ uint32_t pred[TPB / 64];
   if constexpr (PASS == 1 || (PASS == 2 && MODE == 1)) {
     // the pass right after pass 0: max|X| from its partials
-    const uint32_t amax = group_max_of(work + kPartialBase, nparts, pred);
+    const uint32_t amax = group_max_of<TPB>(work + kPartialBase, nparts, pred);
     pb = path_scale(amax);
     if (blockIdx.x == 0 && threadIdx.x == 0) {
       if (bts) *bts = pb.S;
@@ -256,7 +271,7 @@ __global__ __launch_bounds__(kThreads) void prep_nv_kernel(
   }
   if constexpr (PASS == 2 && MODE != 1) {
     pb = path_scale(work[0]);
-    const uint32_t rmax = group_max_of(work + kPartialBase + kMaxGroups, nparts, pred);
+    const uint32_t rmax = group_max_of<TPB>(work + kPartialBase + kMaxGroups, nparts, pred);
     pr = path_scale(rmax);
     if (blockIdx.x == 0 && threadIdx.x == 0) {
       work[1] = rmax;
@@ -396,13 +411,13 @@ __global__ __launch_bounds__(kThreads) void prep_nv_kernel(
     // work-group maximum -> one partial per work-group.  (Atomic maxima on one word
     // from every work-group serialize across the chip's separate L2s: a reduction
     // launch is far cheaper.)
-    __shared__ uint32_t red[kThreads / 64];
+    __shared__ uint32_t red[TPB / 64];
     run_max = wave_max(run_max);
     if (lane == 0) red[threadIdx.x >> 6] = run_max;
     __syncthreads();
     if (threadIdx.x == 0) {
       uint32_t m = 0;
-      for (int i = 0; i < kThreads / 64; ++i) m = umax(m, red[i]);
+      for (int i = 0; i < TPB / 64; ++i) m = umax(m, red[i]);
       work[kPartialBase + PASS * kMaxGroups + blockIdx.x] = m;
     }
   }
@@ -423,13 +438,18 @@ hipError_t run_passes(const uint16_t* x, int64_t ldx, int64_t cpr, int64_t nchun
                       uint8_t* bscales, float* bts, uint8_t* rcodes, uint8_t* rscales, float* rts, uint8_t* mask,
                       uint32_t* work, const float* rnorm, const uint16_t* gamma, hipStream_t st) {
   const int64_t per_wg = (kThreads / 64) * 64 * kUnroll;
+  using S0 = NvShape<0, MODE, DENSE, WRITE_MASK, XF>;
+  using S1 = NvShape<1, MODE, DENSE, WRITE_MASK, XF>;
+  static_assert(S0::kTpb == S1::kTpb && S0::kGroups == S1::kGroups, "both maximum passes share a shape");
+  const int64_t per_wg_max = (S0::kTpb / 64) * 64 * kUnroll;
   const int64_t grid = (nchunks + per_wg - 1) / per_wg;
-  const unsigned rgrid = (unsigned)(grid < kMaxGroups ? grid : kMaxGroups);
+  const int64_t mgrid = (nchunks + per_wg_max - 1) / per_wg_max;
+  const unsigned rgrid = (unsigned)(mgrid < S0::kGroups ? mgrid : S0::kGroups);
   const int np = (int)rgrid;  // partials per maximum pass
-  prep_nv_kernel<0, MODE, SPM, DENSE, WRITE_MASK, XF><<<dim3(rgrid), kThreads, 0, st>>>(
+  prep_nv_kernel<0, MODE, SPM, DENSE, WRITE_MASK, XF><<<dim3(rgrid), S0::kTpb, 0, st>>>(
       x, ldx, cpr, nchunks, bcodes, bscales, rcodes, rscales, mask, work, bts, rts, rnorm, gamma, np);
   if constexpr (MODE != 1)
-    prep_nv_kernel<1, MODE, SPM, DENSE, WRITE_MASK, XF><<<dim3(rgrid), kThreads, 0, st>>>(
+    prep_nv_kernel<1, MODE, SPM, DENSE, WRITE_MASK, XF><<<dim3(rgrid), S1::kTpb, 0, st>>>(
         x, ldx, cpr, nchunks, bcodes, bscales, rcodes, rscales, mask, work, bts, rts, rnorm, gamma, np);
   prep_nv_kernel<2, MODE, SPM, DENSE, WRITE_MASK, XF><<<dim3((unsigned)grid), kThreads, 0, st>>>(
       x, ldx, cpr, nchunks, bcodes, bscales, rcodes, rscales, mask, work, bts, rts, rnorm, gamma, np);
