@@ -351,8 +351,7 @@ __global__ __launch_bounds__(kThreads) void prep_mx_tiled_kernel(
 // exchanges over p/4, then the lane's steps (KS a power of two: each wave's steps are an
 // aligned power-of-two range of runs), and the top levels combine the waves' sums,
 // zero-padded to 16.  The factor r, the gain and the codec then work from the same
-// registers.  With one step per wave the gain is loaded with X, so no load waits between
-// the phases; with two, its registers would not fit, and each step loads it in turn.
+// registers.
 // fp64 value of another lane through a DPP pattern (both halves).
 template <int CTRL>
 __device__ __forceinline__ double dpp_f64(double v) {
@@ -363,7 +362,7 @@ __device__ __forceinline__ double dpp_f64(double v) {
 }
 
 template <int R, int SPM, int KS, bool WRITE_MASK>
-__global__ __launch_bounds__(1024) void prep_mx_rms_tiled_kernel(
+__global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(KS == 1 ? 8 : 1, 8))) void prep_mx_rms_tiled_kernel(
     const uint16_t* __restrict__ x, int64_t M, int64_t K, int64_t ldx, int64_t Mp, int64_t Kp,
     const uint16_t* __restrict__ gamma, double eps, uint8_t* __restrict__ bcodes, uint8_t* __restrict__ bscales,
     uint8_t* __restrict__ rcodes, uint8_t* __restrict__ rscales, uint8_t* __restrict__ mask) {
@@ -384,12 +383,12 @@ __global__ __launch_bounds__(1024) void prep_mx_rms_tiled_kernel(
   // the group and the wave's steps wholly inside X (uniform): nothing to zero
   const bool interior = r0 + R <= M && ((int64_t)wave * KS + KS) * L <= nbk;
 
-  // every load in flight first: X and (one step per wave) the matching gains.  Loads are
-  // unconditional, from clamped (in-bounds) addresses, and what lies outside X is zeroed
-  // afterwards: a load under a branch would have to complete before the branch joins.
-  // Addresses are a uniform base and a 32-bit lane offset.
-  constexpr bool kGainEarly = KS == 1;
-  u32x4 v[KS][4], gv[kGainEarly ? 4 : 1];
+  // every load of X in flight first.  Loads are unconditional, from clamped (in-bounds)
+  // addresses, and what lies outside X is zeroed afterwards: a load under a branch would
+  // have to complete before the branch joins.  Addresses are a uniform base and a 32-bit
+  // lane offset.  The gains are loaded per block in the coding loop (L2 hits shared by
+  // every row group): holding them from the start would take 16 more registers.
+  u32x4 v[KS][4];
   // rows past M read row M-1: the base is the group's first row clamped the same way,
   // so the lane's row offset is never negative
   const int64_t rb = r0 < M ? r0 : M - 1;
@@ -404,21 +403,16 @@ __global__ __launch_bounds__(1024) void prep_mx_rms_tiled_kernel(
     for (int u = 0; u < 4; ++u) {
       const uint32_t bc = min(ks * L + g4 * 4 + u, last_blk);
       v[t][u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(xg + lane_x + bc * 64u));
-      if constexpr (kGainEarly)
-        gv[u] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint8_t*>(gamma) + bc * 64u + q * 16u);
     }
   }
-  // outside X both the value and (one step per wave) the gain are zeroed: with r finite
-  // (rows past M take r = 1), y = (0 r) 0 is +0 there
+  // outside X the value (and, below, the gain) is zeroed: with r finite (rows past M
+  // take r = 1), y = (0 r) 0 is +0 there
   if (!interior) {
 #pragma unroll
     for (int t = 0; t < KS; ++t)
 #pragma unroll
       for (int u = 0; u < 4; ++u)
-        if (!(row_ok && ((int64_t)wave * KS + t) * L + g4 * 4 + u < nbk)) {
-          v[t][u] = u32x4{0u, 0u, 0u, 0u};
-          if constexpr (kGainEarly) gv[u] = u32x4{0u, 0u, 0u, 0u};
-        }
+        if (!(row_ok && ((int64_t)wave * KS + t) * L + g4 * 4 + u < nbk)) v[t][u] = u32x4{0u, 0u, 0u, 0u};
   }
 
   // the row sums in the defined order; the partner lanes of the tree's lane levels are
@@ -457,6 +451,14 @@ __global__ __launch_bounds__(1024) void prep_mx_rms_tiled_kernel(
 #pragma unroll
     for (int i = 0; i < w / 2; ++i) st[i] = __dadd_rn(st[2 * i], st[2 * i + 1]);
   if (p == 0) part[wave][j] = st[0];
+  // the normalization re-extracts the fp32 values from the bf16 pairs: keeping the sum's
+  // extraction alive across the barriers would take 32 more registers per step, and at
+  // one step per wave the kernel is held to 64 (8 waves per SIMD: every row group of a
+  // prefill-sized X resident at once)
+#pragma unroll
+  for (int t = 0; t < KS; ++t)
+#pragma unroll
+    for (int u = 0; u < 4; ++u) asm volatile("" : "+v"(v[t][u]));
   __syncthreads();
   if (threadIdx.x < R) {
     double s[16];
@@ -491,14 +493,9 @@ __global__ __launch_bounds__(1024) void prep_mx_rms_tiled_kernel(
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int64_t blk = ks * L + g4 * 4 + u;
-      u32x4 g;
-      if constexpr (kGainEarly) {
-        g = gv[u];
-      } else {  // an L2 hit: shared by every row
-        g = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint8_t*>(gamma) +
-                                            min((uint32_t)blk, last_blk) * 64u + q * 16u);
-        if (!interior && !(row_ok && blk < nbk)) g = u32x4{0u, 0u, 0u, 0u};
-      }
+      u32x4 g = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint8_t*>(gamma) +
+                                                min((uint32_t)blk, last_blk) * 64u + q * 16u);
+      if (!interior && !(row_ok && blk < nbk)) g = u32x4{0u, 0u, 0u, 0u};
       // y = bf16(fp32(fp32(x r) g)), as fp32
       float y[8];
 #pragma unroll
