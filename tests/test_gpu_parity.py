@@ -296,6 +296,58 @@ def test_linear_small_full_compare(fmt, layout, M, N, K):
         assert fro <= TOL
 
 
+def _random_forward_cases(count=24, seed=20261204):
+    """Seeded random configurations of the whole layer: format, layout, pattern, ragged
+    M, N and K (a multiple of the format's block), padded rows of X, input distribution
+    and output type."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(count):
+        fmt = int(rng.integers(0, 2))
+        layout = sharq.ROWMAJOR if fmt == sharq.NVFP4 else (sharq.TILED if rng.random() < 0.6 else sharq.ROWMAJOR)
+        n, m = [(2, 4), (4, 8)][int(rng.integers(0, 2))]
+        blk = 16 if fmt == sharq.NVFP4 else 32
+        M = int(rng.choice([int(rng.integers(1, 33)), int(rng.integers(33, 700))]))
+        N = int(rng.integers(1, 700))
+        K = blk * int(rng.integers(1, 2048 // blk + 1))
+        pad = 8 * int(rng.integers(0, 9))
+        dist = ["normal", "laplace", "student_t3"][int(rng.integers(0, 3))]
+        out = int(rng.integers(0, 2))
+        cases.append((i, fmt, layout, n, m, M, N, K, pad, dist, out))
+    return cases
+
+
+@pytest.mark.parametrize("case", _random_forward_cases(), ids=lambda c: f"case{c[0]}")
+def test_forward_random_shapes(case):
+    """sharq_forward (the launch bench.py times) on seeded random configurations:
+    payloads bit for bit, Y within the summation bound of the oracle's exact value."""
+    i, fmt, layout, n, m, M, N, K, pad, dist, out = case
+    print(f"[forward random] {case}", flush=True)
+    xb, wb = make_shape(M, N, K, seed=1000 + i, dist=dist, token_sigma=0.5)
+    if pad:
+        wide = np.zeros((M, K + pad), np.uint16)
+        wide[:, :K] = xb
+        x = to_dev(wide)[:, :K]
+    else:
+        x = to_dev(xb)
+    weight = sharq.quantize(to_dev(wb), fmt, layout=layout)
+    bufs = (sharq.Payload.empty(M, K, fmt, DEV, layout), sharq.Payload.empty(M, K, fmt, DEV, layout))
+    y, (bb, rr) = sharq.forward(x, weight, n, m, out_dtype=out, bufs=bufs)
+    torch.cuda.synchronize()
+    ob, orr, _ = oracle.prep(xb, n, m, fmt)
+    ow = oracle.quantize(wb, fmt)
+    assert_payload_equal(bb, ob, "backbone")
+    assert_payload_equal(rr, orr, "residual")
+    assert_payload_equal(weight, ow, "weight")
+    yref = oracle.linear(ob, orr, ow, fmt)
+    abssum = abs_linear(ob, orr, ow, fmt)
+    if out == sharq.OUT_FP32:
+        assert rel_maxnorm(y.cpu().numpy().astype(np.float64), yref) <= TOL
+        assert fp32_bound_check(y, yref, abssum, K) <= 1.0
+    else:
+        assert bf16_bound_check(y, yref, abssum, K) <= 1.0
+
+
 @pytest.mark.parametrize("fmt,layout", FMT_LAYOUTS, ids=FL_IDS)
 @pytest.mark.parametrize("M,N,K", [(1, 1, 32), (16, 512, 512), (37, 70, 96), (257, 513, 1056),
                                    (64, 256, 2048), (520, 300, 384), (33, 96, 640)])
