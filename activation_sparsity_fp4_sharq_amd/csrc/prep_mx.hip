@@ -339,6 +339,15 @@ __global__ __launch_bounds__(kThreads) void prep_mx_tiled_kernel(
   }
 }
 
+// fp64 value of another lane through a DPP pattern (both halves).
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double v) {
+  const uint64_t u = __double_as_longlong(v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)u, CTRL, 0xF, 0xF, true);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)(u >> 32), CTRL, 0xF, 0xF, true);
+  return __longlong_as_double((int64_t)(((uint64_t)hi << 32) | lo));
+}
+
 // RMS normalization and preparation in one read of X (tiled output).  A work-group owns
 // R whole rows; L = 64/R lanes share a row, lane p of a row covering, in each step of
 // 32L elements, the four consecutive 32-element blocks 4(p/4)..4(p/4)+3, elements
@@ -351,16 +360,7 @@ __global__ __launch_bounds__(kThreads) void prep_mx_tiled_kernel(
 // exchanges over p/4, then the lane's steps (KS a power of two: each wave's steps are an
 // aligned power-of-two range of runs), and the top levels combine the waves' sums,
 // zero-padded to 16.  The factor r, the gain and the codec then work from the same
-// registers.
-// fp64 value of another lane through a DPP pattern (both halves).
-template <int CTRL>
-__device__ __forceinline__ double dpp_f64(double v) {
-  const uint64_t u = __double_as_longlong(v);
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)u, CTRL, 0xF, 0xF, true);
-  const uint32_t hi = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)(u >> 32), CTRL, 0xF, 0xF, true);
-  return __longlong_as_double((int64_t)(((uint64_t)hi << 32) | lo));
-}
-
+// registers.  At one step per wave the kernel is held to 64 registers (8 waves per SIMD).
 template <int R, int SPM, int KS, bool WRITE_MASK>
 __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(KS == 1 ? 8 : 1, 8))) void prep_mx_rms_tiled_kernel(
     const uint16_t* __restrict__ x, int64_t M, int64_t K, int64_t ldx, int64_t Mp, int64_t Kp,
