@@ -62,9 +62,10 @@ __device__ __forceinline__ uint32_t wave_max(uint32_t v) {
   return v;
 }
 
-// Maximum of the n (<= kMaxGroups) partials at p, by the whole work-group of TPB
-// threads (every thread gets it, so every thread must call it).  Each thread issues
-// its loads before using any.
+// Maximum of the n (1 <= n <= kMaxGroups) partials at p, by the whole work-group of TPB
+// threads (every thread gets it, so every thread must call it).  Every load is issued
+// before any is used: indices past n re-read partial n-1 (a maximum is unchanged by a
+// repeated element), so no load sits under a branch that would have to wait for it.
 template <int TPB>
 __device__ __forceinline__ uint32_t group_max_of(const uint32_t* __restrict__ p, int n, uint32_t* red) {
   constexpr int kPer = kMaxGroups / TPB;
@@ -72,7 +73,7 @@ __device__ __forceinline__ uint32_t group_max_of(const uint32_t* __restrict__ p,
 #pragma unroll
   for (int j = 0; j < kPer; ++j) {
     const int i = j * TPB + (int)threadIdx.x;
-    v[j] = i < n ? p[i] : 0u;
+    v[j] = p[i < n ? i : n - 1];
   }
   uint32_t m = 0;
 #pragma unroll
