@@ -138,7 +138,46 @@ __global__ __launch_bounds__(kRoundThreads) void rounding_probe_kernel(unsigned 
   }
 }
 
+// Conversion check of e4m3_encode_hw against e4m3_encode_def over every fp32 pattern
+// with the sign bit clear (the block-scale operand is a non-negative quotient; +inf and
+// NaN included), and of e4m3_value_hw against e4m3_value_def on the codes 0..0x7E (the
+// first 127 threads of work-group 0).  out[0] += mismatches, out[1] = min of the
+// mismatching fp32 pattern, or 2^32 + code for a decode mismatch.
+__global__ __launch_bounds__(kRoundThreads) void e4m3_probe_kernel(unsigned long long* out) {
+  constexpr uint64_t kPatterns = 1ull << 31;
+  unsigned long long bad = 0, first = ~0ull;
+  for (uint64_t i = (uint64_t)blockIdx.x * kRoundThreads + threadIdx.x; i < kPatterns;
+       i += (uint64_t)kRoundBlocks * kRoundThreads) {
+    const float q = __uint_as_float((uint32_t)i);
+    if (codec::e4m3_encode_hw(q) != codec::e4m3_encode_def(q)) {
+      ++bad;
+      first = first < i ? first : i;
+    }
+  }
+  if (blockIdx.x == 0 && threadIdx.x <= 0x7Eu) {
+    const uint32_t s = threadIdx.x;
+    if (__float_as_uint(codec::e4m3_value_hw(s)) != __float_as_uint(codec::e4m3_value_def(s))) {
+      ++bad;
+      const unsigned long long tag = (1ull << 32) | s;
+      first = first < tag ? first : tag;
+    }
+  }
+  if (bad) {
+    atomicAdd(&out[0], bad);
+    atomicMin(&out[1], first);
+  }
+}
+
 }  // namespace
+
+hipError_t launch_e4m3_probe(uint64_t* out, hipStream_t stream) {
+  unsigned long long* o = reinterpret_cast<unsigned long long*>(out);
+  rounding_init_kernel<<<dim3(1), dim3(1), 0, stream>>>(o);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  e4m3_probe_kernel<<<dim3(kRoundBlocks), dim3(kRoundThreads), 0, stream>>>(o);
+  return hipGetLastError();
+}
 
 hipError_t launch_rounding_probe(uint64_t* out, hipStream_t stream) {
   unsigned long long* o = reinterpret_cast<unsigned long long*>(out);

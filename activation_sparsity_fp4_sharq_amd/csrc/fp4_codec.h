@@ -99,6 +99,42 @@ __device__ __forceinline__ uint32_t bf16x2_rne_hw(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(p, bf16x2_cvt_t));
 }
 
+// OCP E4M3 (the NVFP4 block-scale format: 4 exponent bits, bias 7, 3 mantissa bits, no
+// infinities, 0x7F the NaN) of q >= 0 from the format's definition, worked on the fp32
+// bits: nearest value, ties to the even code, saturating at 448 (0x7E); +0 and NaN give 0.
+__device__ __forceinline__ uint32_t e4m3_encode_def(float q) {
+  if (!(q > 0.0f)) return 0;
+  if (q >= 448.0f) return 0x7E;
+  if (q < 0.015625f) return (uint32_t)__builtin_rintf(q * 512.0f);  // subnormal step 2^-9 (exact scaling)
+  const uint32_t u = __float_as_uint(q);
+  const uint32_t ef = (u >> 23) - 120;  // E4M3 exponent field: (e - 127) + 7
+  uint32_t code = (ef << 3) | ((u >> 20) & 7u);
+  const uint32_t rem = u & 0xFFFFFu, half = 0x80000u;
+  if (rem > half || (rem == half && (code & 1u))) code += 1;  // a carry moves into the exponent
+  return code;
+}
+
+// The value of an E4M3 code 0..0x7E from the definition: m * 2^-9 when the exponent
+// field is 0, else (1 + m/8) * 2^(e - 7).
+__device__ __forceinline__ float e4m3_value_def(uint32_t s) {
+  const uint32_t ef = (s >> 3) & 15u, m = s & 7u;
+  const float normal = __uint_as_float(((ef + 120u) << 23) | (m << 20));
+  const float subnormal = (float)m * 0.001953125f;  // m * 2^-9
+  return ef == 0 ? subnormal : normal;
+}
+
+// The same two maps through gfx950's fp8 conversions (OCP E4M3, nearest-even).  The
+// operand is first held to [0, 448] (NaN to 0), so no overflow or NaN rule of the
+// instruction is relied on.  sharq_e4m3_conversion_probe checks both against the
+// definition forms on the device: every fp32 pattern with the sign bit clear, and every
+// code up to 0x7E.
+__device__ __forceinline__ uint32_t e4m3_encode_hw(float q) {
+  const float c = q > 0.0f ? (q < 448.0f ? q : 448.0f) : 0.0f;
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, c, 0, false) & 0xFFu;
+}
+
+__device__ __forceinline__ float e4m3_value_hw(uint32_t s) { return __builtin_amdgcn_cvt_f32_fp8((int)s, 0); }
+
 // rms_scale_pair for one dword of two bf16 x and one of two bf16 gains, returning the two
 // bf16 results as fp32 values (rounded by bf16x2_rne_hw).
 __device__ __forceinline__ void rms_scale_f2(uint32_t w, uint32_t gw, float r, float& y0, float& y1) {

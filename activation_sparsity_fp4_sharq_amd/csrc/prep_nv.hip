@@ -26,7 +26,10 @@
 // returns the correctly rounded x / d while the intermediates stay in the normal
 // range (divisors below 2^-90 use the full division).
 // E2M1 rounding uses the gfx950 scaled conversion with a unit scale (nearest-even,
-// saturating, sign kept -- checked bit-for-bit against the format definition).
+// saturating, sign kept -- checked bit-for-bit against the format definition); the
+// E4M3 block scale is coded and decoded with the fp8 conversions (e4m3_encode_hw and
+// e4m3_value_hw, checked against the definition on every operand the block scale can
+// take).
 //
 // Work mapping: lane = 8 consecutive elements (16-byte load) of the flat element
 // sequence; an NVFP4 block is a lane pair, a mask group never straddles a lane.
@@ -41,7 +44,11 @@ using namespace codec;
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
-constexpr int kUnroll = 2;
+constexpr int kUnroll = 2;  // chunks per lane and loop step
+// Bounded grid of pass 2 (grid-stride beyond it): each work-group's prologue -- both
+// tensor scales, the partial maxima of pass 1, the divisor tables -- is then paid a few
+// times per lane instead of once per two chunks.
+constexpr int kLastGroups = 2048;
 constexpr int kMaxGroups = 2048;  // bounded grid of the maximum passes: at most this many partials each
 constexpr float kUnitScale = 1.0f;
 // workspace (uint32): [0] max|X| (written by pass 1 for pass 2), [1] max|R| (fp32 bits
@@ -87,25 +94,6 @@ __device__ __forceinline__ uint32_t group_max_of(const uint32_t* __restrict__ p,
   return r;
 }
 
-// OCP E4M3 code of q >= 0: nearest value, ties to the even code, saturating at 448.
-__device__ __forceinline__ uint32_t e4m3_encode(float q) {
-  if (!(q > 0.0f)) return 0;
-  if (q >= 448.0f) return 0x7E;
-  if (q < 0.015625f) return (uint32_t)__builtin_rintf(q * 512.0f);  // subnormal step 2^-9 (exact scaling)
-  const uint32_t u = __float_as_uint(q);
-  const uint32_t ef = (u >> 23) - 120;  // E4M3 exponent field: (e - 127) + 7
-  uint32_t code = (ef << 3) | ((u >> 20) & 7u);
-  const uint32_t rem = u & 0xFFFFFu, half = 0x80000u;
-  if (rem > half || (rem == half && (code & 1u))) code += 1;  // a carry moves into the exponent
-  return code;
-}
-
-__device__ __forceinline__ float e4m3_value(uint32_t s) {
-  const uint32_t ef = s >> 3, m = s & 7u;
-  if (ef == 0) return (float)m * 0.001953125f;  // m * 2^-9
-  return __uint_as_float(((ef + 120u) << 23) | (m << 20));
-}
-
 __device__ __forceinline__ float tensor_scale_of(uint32_t amax_bits) {
   const float amax = __uint_as_float(amax_bits);
   return amax == 0.0f ? 1.0f : __fdiv_rn(amax, 2688.0f);
@@ -143,17 +131,30 @@ __device__ __forceinline__ PathScale path_scale(uint32_t amax_bits) {
   return p;
 }
 
-// Block divisor d = E4M3(amax_blk / (6S)) * S and its scale byte.
-__device__ __forceinline__ float block_divisor(float amax_blk, const PathScale& ps, uint32_t& sbyte) {
-  sbyte = e4m3_encode(div_rn(amax_blk, ps.S6, ps.yS6));
-  return __fmul_rn(e4m3_value(sbyte), ps.S);
+// A path's block divisors by scale code: {d(s), y(s)} with d(s) = fp32(value(s) * S) and
+// y(s) = RN(1/d(s)) (recip_rn), for every E4M3 code s.  Each work-group fills its own
+// copy in LDS once (one entry per thread) -- a block then looks its divisor up instead
+// of decoding its scale and dividing for the reciprocal.
+constexpr int kDivCodes = 128;
+
+__device__ __forceinline__ float2 divisor_entry(uint32_t s, const PathScale& ps) {
+  const float d = __fmul_rn(e4m3_value_hw(s), ps.S);
+  return float2{d, recip_rn(d)};
 }
 
-// 8 values -> 8 E2M1 codes of v / d (one dword; 0 when d == 0).
-__device__ __forceinline__ uint32_t nv_codes(const float v[8], float d) {
+// Block divisor d = E4M3(amax_blk / (6S)) * S, its reciprocal and its scale byte.
+__device__ __forceinline__ float block_divisor(float amax_blk, const PathScale& ps, const float2* tab,
+                                               uint32_t& sbyte, float& y) {
+  sbyte = e4m3_encode_hw(div_rn(amax_blk, ps.S6, ps.yS6));
+  const float2 e = tab[sbyte];
+  y = e.y;
+  return e.x;
+}
+
+// 8 values -> 8 E2M1 codes of v / d (one dword; 0 when d == 0); y = recip_rn(d).
+__device__ __forceinline__ uint32_t nv_codes(const float v[8], float d, float y) {
   float t[8];
   if (d >= kFastDivisorMin) {
-    const float y = __fdiv_rn(1.0f, d);
 #pragma unroll
     for (int j = 0; j < 8; ++j) t[j] = div_step(v[j], d, y);
   } else {
@@ -180,11 +181,13 @@ __device__ __forceinline__ void nv_dequant(uint32_t packed, float d, float deq[8
 }
 
 // Gather the scale bytes of the 32 blocks of a wave into 8 dwords held by lanes
-// 0, 8, ..., 56 (block 4k+i is the lane pair starting at lane 8k+2i).
+// 0, 8, ..., 56 (block 4k+i is the lane pair starting at lane 8k+2i).  Lanes 8k+2,
+// 8k+4 and 8k+6 lie in lane 8k's row of 16, so row shifts (DPP row_shl, lane i reads
+// lane i+n of its row) bring the three bytes in without an LDS permute.
 __device__ __forceinline__ uint32_t gather_scales(uint32_t byte) {
-  uint32_t b1 = __shfl_down(byte, 2, 64);
-  uint32_t b2 = __shfl_down(byte, 4, 64);
-  uint32_t b3 = __shfl_down(byte, 6, 64);
+  const uint32_t b1 = (uint32_t)__builtin_amdgcn_mov_dpp((int)byte, 0x102, 0xF, 0xF, true);
+  const uint32_t b2 = (uint32_t)__builtin_amdgcn_mov_dpp((int)byte, 0x104, 0xF, 0xF, true);
+  const uint32_t b3 = (uint32_t)__builtin_amdgcn_mov_dpp((int)byte, 0x106, 0xF, 0xF, true);
   return byte | (b1 << 8) | (b2 << 16) | (b3 << 24);
 }
 
@@ -254,9 +257,9 @@ __attribute__((amdgpu_waves_per_eu(NvShape<PASS, MODE, DENSE_ROWS, WRITE_MASK, X
   const int lane = threadIdx.x & 63;
   constexpr int TPB = NvShape<PASS, MODE, DENSE_ROWS, WRITE_MASK, XF>::kTpb;  // threads per work-group
   const int64_t wave = (int64_t)blockIdx.x * (TPB / 64) + (threadIdx.x >> 6);
-  // the maximum passes walk the chunks grid-stride with a bounded grid; the last pass
-  // covers everything with one iteration per wave
-  const int64_t stride = PASS <= 1 ? (int64_t)gridDim.x * (TPB / 64) * 64 * kUnroll : nchunks;
+  // every pass walks the chunks grid-stride over a bounded grid
+  constexpr int U = kUnroll;
+  const int64_t stride = (int64_t)gridDim.x * (TPB / 64) * 64 * U;
   const int64_t nblocks = nchunks >> 1;
 
   PathScale pb{}, pr{};
@@ -279,13 +282,23 @@ __attribute__((amdgpu_waves_per_eu(NvShape<PASS, MODE, DENSE_ROWS, WRITE_MASK, X
       if (rts) *rts = pr.S;
     }
   }
+  // the block-divisor tables of the backbone path [0] and the residual path [1]
+  __shared__ float2 dtab[2][kDivCodes];
+  if constexpr (PASS >= 1) {
+    static_assert(TPB >= 2 * kDivCodes, "one table entry per thread");
+    if (threadIdx.x < 2 * kDivCodes) {
+      const uint32_t s = threadIdx.x & (kDivCodes - 1);
+      dtab[threadIdx.x / kDivCodes][s] = divisor_entry(s, threadIdx.x < kDivCodes ? pb : pr);
+    }
+    __syncthreads();
+  }
 
   uint32_t run_max = 0;
-  for (int64_t base = wave * 64 * kUnroll; base < nchunks; base += stride) {
-    u32x4 v[kUnroll];
-    uint32_t bpk_in[kUnroll], bsb_in[kUnroll];
+  for (int64_t base = wave * 64 * U; base < nchunks; base += stride) {
+    u32x4 v[U];
+    uint32_t bpk_in[U], bsb_in[U];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
+    for (int u = 0; u < U; ++u) {
       const int64_t c = base + u * 64 + lane;
       v[u] = u32x4{0u, 0u, 0u, 0u};
       bpk_in[u] = 0;
@@ -320,7 +333,7 @@ __attribute__((amdgpu_waves_per_eu(NvShape<PASS, MODE, DENSE_ROWS, WRITE_MASK, X
     }
 
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
+    for (int u = 0; u < U; ++u) {
       const int64_t c = base + u * 64 + lane;
       const bool valid = c < nchunks;
       float xf[8];
@@ -344,8 +357,9 @@ __attribute__((amdgpu_waves_per_eu(NvShape<PASS, MODE, DENSE_ROWS, WRITE_MASK, X
       if constexpr (MODE == 1) {
         // plain quantization of X with its own tensor scale (PASS 2 only)
         uint32_t sbyte;
-        const float d = block_divisor(__uint_as_float(pair_max(xmax)), pb, sbyte);
-        const uint32_t packed = nv_codes(xf, d);
+        float y;
+        const float d = block_divisor(__uint_as_float(pair_max(xmax)), pb, dtab[0], sbyte, y);
+        const uint32_t packed = nv_codes(xf, d, y);
         const uint32_t pk = gather_scales(sbyte);
         if (valid) *reinterpret_cast<uint32_t*>(rcodes + c * 4) = packed;
         store_scale_words(rscales, g0, nblocks, lane, pk);
@@ -362,8 +376,9 @@ __attribute__((amdgpu_waves_per_eu(NvShape<PASS, MODE, DENSE_ROWS, WRITE_MASK, X
 #pragma unroll
           for (int j = 0; j < 8; ++j) kv[j] = kept[j] ? xf[j] : 0.0f;  // dropped: +0 -> code 0x0
           uint32_t bbyte;
-          const float d = block_divisor(__uint_as_float(pair_max(xmax)), pb, bbyte);
-          const uint32_t bpacked = nv_codes(kv, d);
+          float y;
+          const float d = block_divisor(__uint_as_float(pair_max(xmax)), pb, dtab[0], bbyte, y);
+          const uint32_t bpacked = nv_codes(kv, d, y);
           nv_dequant(bpacked, d, bh);
           const uint32_t pk = gather_scales(bbyte);
           if (valid) {
@@ -378,7 +393,7 @@ __attribute__((amdgpu_waves_per_eu(NvShape<PASS, MODE, DENSE_ROWS, WRITE_MASK, X
           store_scale_words(bscales, g0, nblocks, lane, pk);
         } else if constexpr (MODE == 0 || MODE == 3) {
           // the backbone as written by pass 1
-          const float d = __fmul_rn(e4m3_value(bsb_in[u]), pb.S);
+          const float d = dtab[0][bsb_in[u] & (kDivCodes - 1)].x;  // a code pass 1 wrote: <= 0x7E
           nv_dequant(bpk_in[u], d, bh);
         } else if constexpr (MODE == 2) {
           keep_mask<SPM>(xf, kept);  // the same mask as pass 1's
@@ -399,8 +414,9 @@ __attribute__((amdgpu_waves_per_eu(NvShape<PASS, MODE, DENSE_ROWS, WRITE_MASK, X
           continue;
         } else {
           uint32_t rbyte;
-          const float d = block_divisor(__uint_as_float(pair_max(rmax)), pr, rbyte);
-          const uint32_t rpacked = nv_codes(r, d);
+          float y;
+          const float d = block_divisor(__uint_as_float(pair_max(rmax)), pr, dtab[1], rbyte, y);
+          const uint32_t rpacked = nv_codes(r, d, y);
           const uint32_t pk = gather_scales(rbyte);
           if (valid) *reinterpret_cast<uint32_t*>(rcodes + c * 4) = rpacked;
           store_scale_words(rscales, g0, nblocks, lane, pk);
@@ -452,7 +468,8 @@ hipError_t run_passes(const uint16_t* x, int64_t ldx, int64_t cpr, int64_t nchun
   if constexpr (MODE != 1)
     prep_nv_kernel<1, MODE, SPM, DENSE, WRITE_MASK, XF><<<dim3(rgrid), S1::kTpb, 0, st>>>(
         x, ldx, cpr, nchunks, bcodes, bscales, rcodes, rscales, mask, work, bts, rts, rnorm, gamma, np);
-  prep_nv_kernel<2, MODE, SPM, DENSE, WRITE_MASK, XF><<<dim3((unsigned)grid), kThreads, 0, st>>>(
+  const unsigned lgrid = (unsigned)(grid < kLastGroups ? grid : kLastGroups);
+  prep_nv_kernel<2, MODE, SPM, DENSE, WRITE_MASK, XF><<<dim3(lgrid), kThreads, 0, st>>>(
       x, ldx, cpr, nchunks, bcodes, bscales, rcodes, rscales, mask, work, bts, rts, rnorm, gamma, np);
   return hipGetLastError();
 }

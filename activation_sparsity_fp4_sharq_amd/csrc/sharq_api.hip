@@ -414,6 +414,14 @@ sharq_status sharq_bf16_rounding_probe(uint64_t* counters, void* stream) {
   return launched(launch_rounding_probe(counters, reinterpret_cast<hipStream_t>(stream)));
 }
 
+sharq_status sharq_e4m3_conversion_probe(uint64_t* counters, void* stream) {
+  if (!counters) return SHARQ_E_NULL;
+  if (reinterpret_cast<uintptr_t>(counters) & 7u) return SHARQ_E_ALIGN;
+  sharq_status s = check_device();
+  if (s != SHARQ_OK) return s;
+  return launched(launch_e4m3_probe(counters, reinterpret_cast<hipStream_t>(stream)));
+}
+
 sharq_status sharq_forward(const void* x, int64_t M, int64_t K, int64_t ldx, int sp_n, int sp_m, int fmt,
                            const sharq_fp4* backbone, const sharq_fp4* residual, const sharq_fp4* weight,
                            int64_t N, void* y, int64_t ldy, int out_dtype, void* workspace,

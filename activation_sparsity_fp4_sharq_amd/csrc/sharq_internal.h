@@ -70,6 +70,7 @@ size_t linear_nv_workspace(int64_t M, int64_t N, int64_t K);
 hipError_t launch_clock_probe(int64_t iters, uint64_t* out, hipStream_t stream);
 hipError_t launch_matrix_rate_probe(int form, int64_t iters, uint64_t* out, hipStream_t stream);
 hipError_t launch_rounding_probe(uint64_t* out, hipStream_t stream);
+hipError_t launch_e4m3_probe(uint64_t* out, hipStream_t stream);
 hipError_t launch_stream_probe(const void* src, int64_t read_bytes, void* dst, int64_t write_bytes,
                                hipStream_t stream);
 

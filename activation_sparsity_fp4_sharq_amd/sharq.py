@@ -25,7 +25,7 @@ SYMBOLS = ["sharq_abi_version", "sharq_status_str", "sharq_payload_bytes", "shar
            "sharq_prep_rmsnorm_workspace_bytes", "sharq_prep_rmsnorm", "sharq_linear", "sharq_linear_dense",
            "sharq_clock_probe", "sharq_prep_ablation", "sharq_dequantize", "sharq_prep_swiglu",
            "sharq_forward", "sharq_forward_noalloc", "sharq_matrix_rate_probe", "sharq_stream_probe",
-           "sharq_bf16_rounding_probe"]
+           "sharq_bf16_rounding_probe", "sharq_e4m3_conversion_probe"]
 
 
 class SharqFp4(ctypes.Structure):
@@ -39,7 +39,7 @@ class SharqError(RuntimeError):
         self.status = status
 
 
-ABI_VERSION = 10  # the SHARQ_ABI_VERSION of include/sharq.h this binding marshals for
+ABI_VERSION = 11  # the SHARQ_ABI_VERSION of include/sharq.h this binding marshals for
 
 _lib = None
 
@@ -108,6 +108,8 @@ def lib():
         L.sharq_stream_probe.argtypes = [vp, i64, vp, i64, vp]
         L.sharq_bf16_rounding_probe.restype = ctypes.c_int
         L.sharq_bf16_rounding_probe.argtypes = [vp, vp]
+        L.sharq_e4m3_conversion_probe.restype = ctypes.c_int
+        L.sharq_e4m3_conversion_probe.argtypes = [vp, vp]
         L.sharq_forward_noalloc.restype = ctypes.c_int
         L.sharq_forward_noalloc.argtypes = [vp, i64, i64, i64, ctypes.c_int, ctypes.c_int, ctypes.c_int, P, P, P,
                                             i64, vp, i64, ctypes.c_int, vp]
@@ -506,6 +508,17 @@ def bf16_rounding_probe(device=None, stream=None):
     dev = device if device is not None else torch.device("cuda", torch.cuda.current_device())
     out = torch.zeros(2, dtype=torch.int64, device=dev)
     _check("sharq_bf16_rounding_probe", lib().sharq_bf16_rounding_probe(_ptr(out), _stream(stream)))
+    bad, first = (int(v) & 0xFFFFFFFFFFFFFFFF for v in out.cpu())
+    return bad, first
+
+
+def e4m3_conversion_probe(device=None, stream=None):
+    """The device's E4M3 conversions against the format's definition: returns (number of
+    mismatches over every non-negative fp32 operand and every code 0..0x7E, smallest
+    mismatching pattern, or 2^32 + code for a decode)."""
+    dev = device if device is not None else torch.device("cuda", torch.cuda.current_device())
+    out = torch.zeros(2, dtype=torch.int64, device=dev)
+    _check("sharq_e4m3_conversion_probe", lib().sharq_e4m3_conversion_probe(_ptr(out), _stream(stream)))
     bad, first = (int(v) & 0xFFFFFFFFFFFFFFFF for v in out.cpu())
     return bad, first
 

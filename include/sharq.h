@@ -61,7 +61,7 @@
 extern "C" {
 #endif
 
-#define SHARQ_ABI_VERSION 10
+#define SHARQ_ABI_VERSION 11
 
 typedef enum sharq_status {
   SHARQ_OK = 0,
@@ -314,6 +314,17 @@ sharq_status sharq_stream_probe(const void* src, int64_t read_bytes, void* dst, 
  *             patterns that differ, [1] the smallest such pattern (2^64 - 1 if none)
  * Errors: SHARQ_E_NULL, SHARQ_E_ALIGN, SHARQ_E_DEVICE, SHARQ_E_LAUNCH. */
 sharq_status sharq_bf16_rounding_probe(uint64_t* counters, void* stream);
+
+/* Self-check of the E4M3 conversions the NVFP4 preparation uses for its block scales
+ * (the gfx950 fp8 conversions; reading R5 codes each block scale to the nearest E4M3
+ * value, ties to the even code, saturating at 448): codes every fp32 pattern with the
+ * sign bit clear and decodes every code 0..0x7E on the device, and compares both with
+ * the format's definition worked on the bits.
+ *   counters  device, 8-byte aligned, >= 2 uint64: [0] receives the number of
+ *             mismatches, [1] the smallest mismatching fp32 pattern, or 2^32 + code for a
+ *             decode mismatch (2^64 - 1 if none)
+ * Errors: SHARQ_E_NULL, SHARQ_E_ALIGN, SHARQ_E_DEVICE, SHARQ_E_LAUNCH. */
+sharq_status sharq_e4m3_conversion_probe(uint64_t* counters, void* stream);
 
 /* One SharQ linear layer end to end (SharQ, arXiv 2606.26587: the abstract's
  * decomposition as one layer; Figure 2's dataflow of the fused preparation feeding the

@@ -33,7 +33,7 @@ def test_header_symbols_exported():
 
 def test_version_and_status_strings():
     L = sharq.lib()
-    assert L.sharq_abi_version() == 10
+    assert L.sharq_abi_version() == 11
     for s in range(9):
         assert L.sharq_status_str(s)
     assert L.sharq_status_str(99) == b"unknown status"
@@ -326,6 +326,8 @@ def test_rounding_probe_rejects():
     L = sharq.lib()
     assert L.sharq_bf16_rounding_probe(None, None) == E_NULL
     assert L.sharq_bf16_rounding_probe(A + 4, None) == E_ALIGN
+    assert L.sharq_e4m3_conversion_probe(None, None) == E_NULL
+    assert L.sharq_e4m3_conversion_probe(A + 4, None) == E_ALIGN
 
 
 def test_measurement_probes_reject():

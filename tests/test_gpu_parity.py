@@ -579,6 +579,15 @@ def test_bf16_rounding_of_the_normalization_is_nearest_even():
     assert bad == 0, f"{bad} patterns differ, first 0x{first:08x}"
 
 
+def test_e4m3_block_scale_conversion_follows_the_format():
+    """The fp8 conversions the NVFP4 preparation codes and decodes its block scales with
+    agree with E4M3's definition (nearest value, ties to the even code, saturating at 448)
+    on every fp32 operand with the sign bit clear, and on every code up to 0x7E."""
+    print("[e4m3 conversion probe] all 2^31 non-negative patterns, codes 0..0x7E", flush=True)
+    bad, first = sharq.e4m3_conversion_probe()
+    assert bad == 0, f"{bad} mismatches, first 0x{first:x}"
+
+
 def _order_sensitive_row(K, big):
     """A row whose fp64 sum of squares depends on the order of the additions: `big` ones
     in the first run of 8, squares of 2^-54 everywhere else (each one lost when added
