@@ -23,8 +23,8 @@
 // The quotients share their divisor (6*S per tensor, d per block), so each divisor's
 // correctly rounded reciprocal y is formed once and every quotient takes one
 // remainder step (Markstein): q0 = x*y, r = x - q0*d (fma), q = q0 + r*y (fma), which
-// returns the correctly rounded x / d while the intermediates stay in the normal
-// range (divisors below 2^-90 use the full division).
+// returns the correctly rounded x / d, the sign of a zero included (div_step), while the
+// intermediates stay in the normal range (divisors below 2^-90 use the full division).
 // E2M1 rounding uses the gfx950 scaled conversion with a unit scale (nearest-even,
 // saturating, sign kept -- checked bit-for-bit against the format definition); the
 // E4M3 block scale is coded and decoded with the fp8 conversions (e4m3_encode_hw and
@@ -107,11 +107,15 @@ constexpr float kFastDivisorMin = 0x1p-90f;
 // Correctly rounded 1/d for the remainder step (0 when the step is not used).
 __device__ __forceinline__ float recip_rn(float d) { return d >= kFastDivisorMin ? __fdiv_rn(1.0f, d) : 0.0f; }
 
-// x / d correctly rounded, from y = RN(1/d): one remainder step.
+// x / d correctly rounded, from y = RN(1/d): one remainder step.  The remainder is
+// formed negated, t = q0*d - x = -r (exact), and the correction is q0 + (-t)*y: where
+// the remainder is zero, -t is -0 and leaves q0's sign alone, so x = -0 gives -0 as the
+// division does (x - q0*d itself would be +0 there, and +0 + -0 = +0 would drop the
+// sign that E2M1 keeps as code 0x8).
 __device__ __forceinline__ float div_step(float x, float d, float y) {
   const float q0 = __fmul_rn(x, y);
-  const float r = __builtin_fmaf(-q0, d, x);
-  return __builtin_fmaf(r, y, q0);
+  const float t = __builtin_fmaf(q0, d, -x);
+  return __builtin_fmaf(-t, y, q0);
 }
 
 __device__ __forceinline__ float div_rn(float x, float d, float y) {

@@ -79,3 +79,22 @@ def test_remainder_step_is_correctly_rounded_division():
         assert step_quotient(X, D) == rn32(X / D), (x, d)
         checked += 1
     assert checked > 10000
+
+
+def test_remainder_step_keeps_the_sign_of_zero():
+    """On a zero dividend every step of the remainder form works on zeros and exact
+    products, so IEEE's zero-sign rules decide the result; binary64 follows the same rules,
+    which lets Python floats model it.  The kernels' form, t = q0*d - x and q = q0 + (-t)*y,
+    returns -0 for x = -0 (the quotient's sign, kept by E2M1 as code 0x8); the textbook
+    order r = x - q0*d, q = q0 + r*y would return +0 there."""
+    import math
+    for d in (2.0 ** -90, 0.75, 1.5e35):
+        y = 1.0 / d
+        for x in (0.0, -0.0):
+            q0 = x * y
+            t = q0 * d + (-x)          # fma(q0, d, -x): an exact zero
+            q = (-t) * y + q0          # fma(-t, y, q0)
+            assert q == 0.0 and math.copysign(1.0, q) == math.copysign(1.0, x)
+            r = (-q0) * d + x          # fma(-q0, d, x)
+            q_textbook = r * y + q0
+            assert math.copysign(1.0, q_textbook) == 1.0  # the sign a -0 dividend would lose

@@ -152,6 +152,22 @@ def test_prep_adversarial(fmt, layout, n, m):
 
 
 @pytest.mark.parametrize("fmt,layout", FMT_LAYOUTS, ids=FL_IDS)
+@pytest.mark.parametrize("n,m", [(2, 4), (4, 8)])
+def test_prep_signed_zeros_beside_ordinary_values(fmt, layout, n, m):
+    """+0 and -0 among ordinary values, so that zeros sit in blocks with a nonzero scale:
+    a -0 that is kept, or dropped and so carried into the residual, codes as 0x8 (E2M1
+    keeps the sign of a zero quotient), a +0 as 0x0."""
+    print(f"[prep] signed zeros {n}:{m} fmt={fmt} layout={layout}", flush=True)
+    rng = np.random.default_rng(21)
+    x = rng.standard_normal((64, 256)).astype(np.float32)
+    z = rng.random((64, 256))
+    x[z < 0.3] = -0.0
+    x[(z >= 0.3) & (z < 0.45)] = 0.0
+    xb = f32_to_bf16_bits(x)
+    check_prep(xb, n, m, fmt, layout=layout)
+
+
+@pytest.mark.parametrize("fmt,layout", FMT_LAYOUTS, ids=FL_IDS)
 def test_prep_strided_rows(fmt, layout):
     print(f"[prep] strided ldx fmt={fmt} layout={layout}", flush=True)
     xb, _ = make_shape(37, 8, 256, seed=5)
@@ -761,6 +777,30 @@ def test_prep_swiglu_matches_oracle(fmt, layout, n, m, M, I, pad):
     h = oracle.swiglu(gu, I)
     ob, orr, omask = oracle.prep(h, n, m, fmt)
     assert np.array_equal(mask.cpu().numpy(), omask), "mask bits differ"
+    assert_payload_equal(bb, ob, "backbone")
+    assert_payload_equal(rr, orr, "residual")
+
+
+@pytest.mark.parametrize("fmt,layout", FMT_LAYOUTS, ids=FL_IDS)
+def test_prep_swiglu_every_bf16_gate(fmt, layout):
+    """Every finite bf16 pattern as a gate (512 rows x 128: the tiled MXFP4 path looks silu
+    up in a table over part of them and applies a rule to the rest), each row's gates in
+    shuffled order beside up values in (-1, 1) -- so that h stays finite, as the contract
+    asks (|silu(g)| <= |g|)."""
+    print(f"[prep_swiglu] every bf16 gate fmt={fmt} layout={layout}", flush=True)
+    M, I = 512, 128
+    rng = np.random.default_rng(11)
+    gates = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    gates[(gates & 0x7F80) == 0x7F80] = 0  # infinities and NaN are not part of the contract
+    rng.shuffle(gates)
+    gu = np.zeros((M, 2 * I), np.uint16)
+    gu[:, :I] = gates.reshape(M, I)
+    gu[:, I:] = f32_to_bf16_bits(rng.uniform(-0.99, 0.99, (M, I)).astype(np.float32))
+    h = oracle.swiglu(gu, I)
+    assert not np.any((h & 0x7F80) == 0x7F80), "the input must keep h finite"
+    bb, rr, _ = sharq.prep_swiglu(to_dev(gu), I, 2, 4, fmt, layout=layout)
+    torch.cuda.synchronize()
+    ob, orr, _ = oracle.prep(h, 2, 4, fmt)
     assert_payload_equal(bb, ob, "backbone")
     assert_payload_equal(rr, orr, "residual")
 
