@@ -186,5 +186,45 @@ __device__ __forceinline__ uint32_t swiglu_pair(uint32_t gw, uint32_t uw) {
   return bf16_rne_bits(h0) | (bf16_rne_bits(h1) << 16);
 }
 
+// silu_f32 of a bf16 gate by lookup.  The gate is one of 2^16 patterns, so silu_f32 can
+// be tabulated; only the patterns with exponent field 103..133 (|g| in [2^-24, 2^7))
+// need the table (2 signs x 31 exponents x 128 mantissas).  Below that range e rounds
+// to 1, the divisor is 2 and silu_f32(g) = g/2 exactly; above it silu_f32(g) is g for
+// g > 0 (e is 0 or subnormal, the divisor rounds to 1) and -0 for g < 0 (e overflows
+// to +inf).  Each rule equals silu_f32 on every finite bf16 it covers.  (Non-finite
+// inputs are outside the preparation's contract; the rules send +inf to +inf and -inf
+// to -0, NaN to itself or -0, and never index outside the table.)  A work-group fills
+// its LDS copy of the table once (silu_table_fill) and reads it for every gate after.
+constexpr uint32_t kSiluElo = 103, kSiluSpan = 31;        // exponent fields 103..133
+constexpr uint32_t kSiluHalf = kSiluSpan * 128;           // entries per sign
+constexpr int kSiluEntries = 2 * (int)kSiluHalf;          // 7936 floats = 31 KiB
+
+__device__ __forceinline__ void silu_table_fill(float* tab, int tid, int nthreads) {
+  for (int i = tid; i < kSiluEntries; i += nthreads) {
+    const uint32_t sign = (uint32_t)i >= kSiluHalf ? 1u : 0u;
+    const uint32_t b = (sign << 15) | ((kSiluElo << 7) + ((uint32_t)i - sign * kSiluHalf));
+    tab[i] = silu_f32(__uint_as_float(b << 16));
+  }
+}
+
+// b: a bf16 pattern in the low 16 bits.
+__device__ __forceinline__ float silu_lookup(const float* tab, uint32_t b) {
+  const uint32_t mag = b & 0x7FFFu, sign = b >> 15;
+  const uint32_t off = mag - (kSiluElo << 7);  // wraps above the window's top for small gates
+  const bool in = off < kSiluHalf;
+  const float t = tab[in ? sign * kSiluHalf + off : 0u];
+  const uint32_t gb = b << 16;
+  const float small = __fmul_rn(__uint_as_float(gb), 0.5f);
+  const float large = __uint_as_float(sign ? 0x80000000u : gb);
+  return in ? t : (mag < (kSiluElo << 7) ? small : large);
+}
+
+// swiglu_pair with silu_f32 looked up.
+__device__ __forceinline__ uint32_t swiglu_pair_tab(const float* tab, uint32_t gw, uint32_t uw) {
+  const float h0 = __fmul_rn(silu_lookup(tab, gw & 0xFFFFu), __uint_as_float(uw << 16));
+  const float h1 = __fmul_rn(silu_lookup(tab, gw >> 16), __uint_as_float(uw & 0xFFFF0000u));
+  return bf16_rne_bits(h0) | (bf16_rne_bits(h1) << 16);
+}
+
 }  // namespace codec
 }  // namespace sharq

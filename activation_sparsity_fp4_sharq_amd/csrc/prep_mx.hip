@@ -182,6 +182,12 @@ __device__ __forceinline__ u32x4 swiglu8(const u32x4& g, const u32x4& u) {
   return u32x4{swiglu_pair(g[0], u[0]), swiglu_pair(g[1], u[1]), swiglu_pair(g[2], u[2]), swiglu_pair(g[3], u[3])};
 }
 
+// swiglu8 with the SiLU table (silu_lookup).
+__device__ __forceinline__ u32x4 swiglu8_tab(const float* tab, const u32x4& g, const u32x4& u) {
+  return u32x4{swiglu_pair_tab(tab, g[0], u[0]), swiglu_pair_tab(tab, g[1], u[1]), swiglu_pair_tab(tab, g[2], u[2]),
+               swiglu_pair_tab(tab, g[3], u[3])};
+}
+
 __device__ __forceinline__ u32x4 rms_scale8(const u32x4& v, const Norm& nm, int64_t row, int64_t col) {
   const float r = nm.r[row];
   const u32x4 g = *reinterpret_cast<const u32x4*>(nm.g + col);
@@ -254,18 +260,93 @@ __global__ __launch_bounds__(kThreads) void prep_mx_kernel(
 }
 
 // Tiled-layout output (the layout the fused GEMM loads; see sharq.h).  A wave owns
-// 16 consecutive rows x one 128-element K-step: quad k is row 16*rg + k and walks the
-// step's 4 blocks (u = 0..3).  Each store instruction then writes the 16-byte slots of
-// 16 consecutive rows of one fragment (256 contiguous bytes), and each quad leader
-// ends with its row's 4 scale bytes = one scale word, so a wave's scale words are 64
-// contiguous bytes.  Rows >= M and blocks >= K/32 are processed as zeros, which
-// writes the layout's zero padding.  The grid is (K-step groups of 4, row groups):
-// a work-group's 4 waves take 4 consecutive K-steps of the same 16 rows.
+// 16 consecutive rows x one 128-element K-step (an item): quad k is row 16*rg + k and
+// walks the step's 4 blocks (u = 0..3).  Each store instruction then writes the 16-byte
+// slots of 16 consecutive rows of one fragment (256 contiguous bytes), and each quad
+// leader ends with its row's 4 scale bytes = one scale word, so a wave's scale words are
+// 64 contiguous bytes.  Rows >= M and blocks >= K/32 are processed as zeros, which
+// writes the layout's zero padding.
+
+// The item's 4 x 8 elements of this lane from the rows at x (row stride ldx): zeros
+// outside X.  A wave wholly inside X loads unguarded.
+__device__ __forceinline__ void tiled_load(const uint16_t* __restrict__ x, int64_t M, int64_t K, int64_t ldx,
+                                           int64_t ks, int64_t rg, u32x4 (&v)[4]) {
+  const int lane = threadIdx.x & 63;
+  const int q = lane & 3, k = lane >> 2;
+  const int64_t r0 = rg * 16;
+  const uint16_t* xrow = x + r0 * ldx + ks * 128;  // uniform base
+  const int64_t lane_off = (int64_t)k * ldx + q * 8;
+  if (r0 + 16 <= M && ks * 4 + 4 <= K / 32) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(xrow + lane_off + u * 32));
+  } else {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      v[u] = u32x4{0u, 0u, 0u, 0u};
+      if (r0 + k < M && ks * 4 + u < K / 32)
+        v[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(xrow + lane_off + u * 32));
+    }
+  }
+}
+
+// Codes of the item's (transformed) elements v: mask, backbone, residual, through the
+// wave's private LDS staging `my`, `myb` (2 x 1 KiB) so that every global store writes
+// 16 B per lane: lane L then holds slot (row L%16, block u = L/16), and the four 256-byte
+// row runs of the wave are fragment (r/32, 2ks + u/2), slots (r%32) + 32(u%2).
+template <int MODE, int SPM, bool WRITE_MASK>
+__device__ __forceinline__ void tiled_code(const u32x4 (&v)[4], int64_t M, int64_t K, int64_t Mp, int64_t Kp,
+                                           int64_t ks, int64_t rg, uint8_t* __restrict__ bcodes,
+                                           uint8_t* __restrict__ bscales, uint8_t* __restrict__ rcodes,
+                                           uint8_t* __restrict__ rscales, uint8_t* __restrict__ mask, uint32_t* my,
+                                           uint32_t* myb) {
+  const int lane = threadIdx.x & 63;
+  const int q = lane & 3, k = lane >> 2;
+  const int64_t r0 = rg * 16;
+  const int64_t r = r0 + k;
+  const int64_t nbk = K / 32;
+  uint32_t bword = 0, rword = 0;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const uint32_t w[4] = {v[u][0], v[u][1], v[u][2], v[u][3]};
+    uint32_t keep, bbyte, bpacked, rbyte, rpacked;
+    codec_block<MODE, SPM>(w, keep, bbyte, bpacked, rbyte, rpacked);
+    my[u * 64 + lane] = rpacked;  // = slot (u, k), dword q
+    rword |= rbyte << (8 * u);
+    if constexpr (MODE != 1) {
+      myb[u * 64 + lane] = bpacked;
+      bword |= bbyte << (8 * u);
+      if constexpr (WRITE_MASK)
+        if (r < M && ks * 4 + u < nbk) mask[r * (K / 8) + (ks * 4 + u) * 4 + q] = (uint8_t)keep;
+    }
+  }
+  // the staging is wave-private: a wave-level wait on the LDS writes is enough
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+  __builtin_amdgcn_wave_barrier();
+  const int64_t frag0 = ((r0 >> 5) * (Kp / 64) + 2 * ks) * 1024;
+  const int su = lane >> 4;
+  const int off = (su >> 1) * 1024 + (su & 1) * 512 + (int)(((r0 & 31) + (lane & 15)) * 16);
+  // ordinary (cached) stores: the GEMM reads these payloads next (measured: non-temporal
+  // stores here cost the 32760x3072 preparation about 4 %)
+  *reinterpret_cast<u32x4*>(rcodes + frag0 + off) = reinterpret_cast<const u32x4*>(my)[lane];
+  if constexpr (MODE != 1)
+    *reinterpret_cast<u32x4*>(bcodes + frag0 + off) = reinterpret_cast<const u32x4*>(myb)[lane];
+  if (q == 0) {
+    reinterpret_cast<uint32_t*>(rscales)[ks * Mp + r] = rword;
+    if constexpr (MODE != 1) reinterpret_cast<uint32_t*>(bscales)[ks * Mp + r] = bword;
+  }
+}
+
+// One item per wave, loads, codec and stores in one body (the same steps as tiled_load
+// and tiled_code; written out here because the split form measured slower for this
+// kernel: 11.9 against 11.2 us at 4096 x 4096).  The grid is (K-step groups of 4, row
+// groups): a work-group's 4 waves take 4 consecutive K-steps of the same 16 rows.  XF:
+// none or RMS normalization.
 template <int MODE, int SPM, bool WRITE_MASK, int XF>
 __global__ __launch_bounds__(kThreads) void prep_mx_tiled_kernel(
     const uint16_t* __restrict__ x, int64_t M, int64_t K, int64_t ldx, int64_t Mp, int64_t Kp,
     int64_t rg0, uint8_t* __restrict__ bcodes, uint8_t* __restrict__ bscales,
     uint8_t* __restrict__ rcodes, uint8_t* __restrict__ rscales, uint8_t* __restrict__ mask, Norm nm) {
+  static_assert(XF != kXfSwiglu, "the SwiGLU transform runs prep_mx_tiled_swiglu_kernel");
   const int lane = threadIdx.x & 63;
   const int q = lane & 3, k = lane >> 2;
   const int64_t nks = Kp / 128;
@@ -284,8 +365,6 @@ __global__ __launch_bounds__(kThreads) void prep_mx_tiled_kernel(
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       v[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(xrow + lane_off + u * 32));
-      if constexpr (XF == kXfSwiglu)
-        v[u] = swiglu8(v[u], __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(xrow + lane_off + u * 32 + K)));
       if constexpr (XF == kXfRms) v[u] = rms_scale8(v[u], nm, r, ks * 128 + u * 32 + q * 8);
     }
   } else {
@@ -294,8 +373,6 @@ __global__ __launch_bounds__(kThreads) void prep_mx_tiled_kernel(
       v[u] = u32x4{0u, 0u, 0u, 0u};
       if (r < M && ks * 4 + u < nbk) {
         v[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(xrow + lane_off + u * 32));
-        if constexpr (XF == kXfSwiglu)
-          v[u] = swiglu8(v[u], __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(xrow + lane_off + u * 32 + K)));
         if constexpr (XF == kXfRms) v[u] = rms_scale8(v[u], nm, r, ks * 128 + u * 32 + q * 8);
       }
     }
@@ -336,6 +413,59 @@ __global__ __launch_bounds__(kThreads) void prep_mx_tiled_kernel(
   if (q == 0) {
     reinterpret_cast<uint32_t*>(rscales)[ks * Mp + r] = rword;
     if constexpr (MODE != 1) reinterpret_cast<uint32_t*>(bscales)[ks * Mp + r] = bword;
+  }
+}
+
+// The same tiled preparation of h = SwiGLU(gate, up) (gate in columns [0, K) of each row
+// of x, up in [K, 2K)), with silu_f32 looked up: each work-group fills its 31 KiB SiLU
+// table once, then its waves walk the (row group, K-step) items grid-stride -- K-steps
+// fastest, so consecutive waves take consecutive K-steps of the same 16 rows.  A wave
+// issues the loads of its next item before it codes the current one, and its first
+// loads before the table fill, so the memory traffic runs under the arithmetic.  The
+// bounded grid (kSwigluGroups work-groups of 1024 threads) pays for each table over
+// several items per wave.  Outside X, gate and up load as zeros, so h is +0 there as
+// the padding needs.
+constexpr int kSwigluThreads = 1024;
+constexpr int kSwigluGroups = 256;
+
+template <int SPM, bool WRITE_MASK>
+__global__ __launch_bounds__(kSwigluThreads) void prep_mx_tiled_swiglu_kernel(
+    const uint16_t* __restrict__ x, int64_t M, int64_t K, int64_t ldx, int64_t Mp, int64_t Kp,
+    uint8_t* __restrict__ bcodes, uint8_t* __restrict__ bscales, uint8_t* __restrict__ rcodes,
+    uint8_t* __restrict__ rscales, uint8_t* __restrict__ mask) {
+  __shared__ float stab[kSiluEntries];
+  __shared__ uint32_t tile[kSwigluThreads / 64][2][4 * 16 * 4];
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t nks = Kp / 128, items = nks * (Mp / 16);
+  const int64_t nwaves = (int64_t)gridDim.x * (kSwigluThreads / 64);
+  int64_t it = (int64_t)blockIdx.x * (kSwigluThreads / 64) + wv;
+  u32x4 g[4], up[4];
+  if (it < items) {
+    const int64_t rg = it / nks;
+    tiled_load(x, M, K, ldx, it - rg * nks, rg, g);
+    tiled_load(x + K, M, K, ldx, it - rg * nks, rg, up);
+  }
+  silu_table_fill(stab, (int)threadIdx.x, kSwigluThreads);
+  __syncthreads();
+  for (; it < items; it += nwaves) {
+    const int64_t rg = it / nks, ks = it - rg * nks;
+    const int64_t nx = it + nwaves;
+    u32x4 gn[4], upn[4];
+    if (nx < items) {  // uniform
+      const int64_t nrg = nx / nks;
+      tiled_load(x, M, K, ldx, nx - nrg * nks, nrg, gn);
+      tiled_load(x + K, M, K, ldx, nx - nrg * nks, nrg, upn);
+    }
+    u32x4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v[u] = swiglu8_tab(stab, g[u], up[u]);
+    tiled_code<0, SPM, WRITE_MASK>(v, M, K, Mp, Kp, ks, rg, bcodes, bscales, rcodes, rscales, mask, tile[wv][0],
+                                   tile[wv][1]);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      g[u] = gn[u];
+      up[u] = upn[u];
+    }
   }
 }
 
@@ -563,16 +693,26 @@ hipError_t launch_tiled(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, ui
   const int64_t Mp = (M + 31) / 32 * 32, Kp = (K + 127) / 128 * 128;
   const int64_t nks = Kp / 128, nrg = Mp / 16;
   if (nks == 0 || nrg == 0) return hipSuccess;
-  const int64_t gx = (nks + kThreads / 64 - 1) / (kThreads / 64);
-  constexpr int64_t kMaxGridY = 65535;
-  for (int64_t rg0 = 0; rg0 < nrg; rg0 += kMaxGridY) {
-    const int64_t gy = nrg - rg0 < kMaxGridY ? nrg - rg0 : kMaxGridY;
-    prep_mx_tiled_kernel<MODE, SPM, WRITE_MASK, XF><<<dim3((unsigned)gx, (unsigned)gy), dim3(kThreads), 0, stream>>>(
-        x, M, K, ldx, Mp, Kp, rg0, bcodes, bscales, rcodes, rscales, mask, nm);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+  if constexpr (XF == kXfSwiglu) {
+    static_assert(MODE == 0, "SwiGLU is folded into the SharQ preparation only");
+    const int64_t waves = nks * nrg;
+    const int64_t groups = (waves + kSwigluThreads / 64 - 1) / (kSwigluThreads / 64);
+    const unsigned grid = (unsigned)(groups < kSwigluGroups ? groups : kSwigluGroups);
+    prep_mx_tiled_swiglu_kernel<SPM, WRITE_MASK><<<dim3(grid), dim3(kSwigluThreads), 0, stream>>>(
+        x, M, K, ldx, Mp, Kp, bcodes, bscales, rcodes, rscales, mask);
+    return hipGetLastError();
+  } else {
+    const int64_t gx = (nks + kThreads / 64 - 1) / (kThreads / 64);
+    constexpr int64_t kMaxGridY = 65535;
+    for (int64_t rg0 = 0; rg0 < nrg; rg0 += kMaxGridY) {
+      const int64_t gy = nrg - rg0 < kMaxGridY ? nrg - rg0 : kMaxGridY;
+      prep_mx_tiled_kernel<MODE, SPM, WRITE_MASK, XF><<<dim3((unsigned)gx, (unsigned)gy), dim3(kThreads), 0, stream>>>(
+          x, M, K, ldx, Mp, Kp, rg0, bcodes, bscales, rcodes, rscales, mask, nm);
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
   }
-  return hipSuccess;
 }
 
 template <int MODE, int SPM, bool WRITE_MASK, int XF>

@@ -166,7 +166,9 @@ sharq_status sharq_prep(const void* x, int64_t M, int64_t K, int64_t ldx, int sp
  *   by Cody and Waite's range reduction (t = -g clamped to [-150, 150],
  *   n = rint(t log2 e), r = (t - n ln2_hi) - n ln2_lo with a 15-bit ln2_hi) and the
  *   degree-7 Taylor polynomial of e^r times 2^n -- every operation one fp32
- *   rounding in a fixed order, so h is reproducible bit for bit.
+ *   rounding in a fixed order, so h is reproducible bit for bit.  An h that rounds to
+ *   an infinity (|silu(g) * u| beyond bf16's range) is outside the contract, as a
+ *   non-finite input is.
  *   gate_up  device bf16 [M, ld]: gate in columns [0, I), up in [I, 2I) of each row
  *            (the output of one linear over the concatenated gate and up weights);
  *            16-byte aligned, ld % 8 == 0, ld >= 2I
