@@ -168,6 +168,20 @@ def test_prep_signed_zeros_beside_ordinary_values(fmt, layout, n, m):
 
 
 @pytest.mark.parametrize("fmt,layout", FMT_LAYOUTS, ids=FL_IDS)
+@pytest.mark.parametrize("n,m", [(2, 4), (4, 8)])
+def test_prep_every_bf16_value(fmt, layout, n, m):
+    """Every finite bf16 pattern once, shuffled over 512 rows x 128 columns: each block
+    mixes magnitudes from subnormals to the bf16 maximum (which also sets NVFP4's tensor
+    scales), signed zeros included."""
+    print(f"[prep] every bf16 value {n}:{m} fmt={fmt} layout={layout}", flush=True)
+    rng = np.random.default_rng(13)
+    xb = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    xb[(xb & 0x7F80) == 0x7F80] = 0  # infinities and NaN are not part of the contract
+    rng.shuffle(xb)
+    check_prep(xb.reshape(512, 128), n, m, fmt, layout=layout)
+
+
+@pytest.mark.parametrize("fmt,layout", FMT_LAYOUTS, ids=FL_IDS)
 def test_prep_strided_rows(fmt, layout):
     print(f"[prep] strided ldx fmt={fmt} layout={layout}", flush=True)
     xb, _ = make_shape(37, 8, 256, seed=5)
