@@ -574,6 +574,27 @@ def test_prep_rmsnorm_matches_oracle(fmt, layout, n, m, M, K, ldx_pad):
     assert_payload_equal(rr, orr, "residual")
 
 
+@pytest.mark.parametrize("fmt,layout", FMT_LAYOUTS, ids=FL_IDS)
+def test_prep_rmsnorm_every_bf16_value(fmt, layout):
+    """Every finite bf16 pattern once, shuffled over 32 rows of K = 2048 (the tiled MXFP4
+    form reads each row once): every row's factor is set by near-maximum values, so most
+    normalized values land among the subnormals and zeros of either sign."""
+    print(f"[prep_rmsnorm] every bf16 value fmt={fmt} layout={layout}", flush=True)
+    rng = np.random.default_rng(17)
+    xb = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    xb[(xb & 0x7F80) == 0x7F80] = 0  # infinities and NaN are not part of the contract
+    rng.shuffle(xb)
+    xb = xb.reshape(32, 2048)
+    g = _gain(2048, 3)
+    bb, rr, mask = sharq.prep_rmsnorm(to_dev(xb), to_dev(g), 1e-5, 2, 4, fmt, want_mask=True, layout=layout)
+    torch.cuda.synchronize()
+    yb, _ = oracle.rmsnorm(xb, g, 1e-5)
+    ob, orr, omask = oracle.prep(yb, 2, 4, fmt)
+    assert np.array_equal(mask.cpu().numpy(), omask), "mask bits differ"
+    assert_payload_equal(bb, ob, "backbone")
+    assert_payload_equal(rr, orr, "residual")
+
+
 @pytest.mark.parametrize("n,m", [(2, 4), (4, 8)])
 @pytest.mark.parametrize("M,K,ldx_pad", [(19, 2048, 0), (33, 2176, 0), (16, 3072, 128), (50, 4096, 0),
                                          (7, 4224, 0), (5, 8192, 0), (6, 8320, 0), (3, 14336, 0),
