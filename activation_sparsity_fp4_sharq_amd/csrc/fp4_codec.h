@@ -1,7 +1,9 @@
-// fp4_codec.h -- device helpers shared by the two activation preparations: the
-// top-n-of-m selection on a lane's 8 consecutive elements (SharQ's input-adaptive N:M
-// mask: keep the n largest magnitudes of every group of m consecutive elements along
-// K, lower index first on equal magnitude).
+// fp4_codec.h -- device helpers shared by the activation preparations (and the
+// conversion self-checks): the top-n-of-m selection on a lane's 8 consecutive elements
+// (SharQ's input-adaptive N:M mask: keep the n largest magnitudes of every group of m
+// consecutive elements along K, lower index first on equal magnitude); bf16 rounding;
+// E4M3 coding of NVFP4 block scales; the input transforms folded into the preparation
+// (RMS normalization, SwiGLU) and the SiLU table of the SwiGLU form.
 #pragma once
 #include <stdint.h>
 
