@@ -20,6 +20,7 @@ timed on a bounded row sample of the same workload.
 import argparse
 import hashlib
 import json
+import re
 import os
 import sys
 import time
@@ -78,11 +79,24 @@ def calibrate_copy(mib):
     print(json.dumps({"calibration": "device copy", "bytes_read": n, "bytes_written": n, "dispatches": 5}))
 
 
+def kernel_source_code(text):
+    """A HIP source with its comments and blank lines removed and runs of spaces folded:
+    what the compiler sees, so that editing a comment does not retire a measurement."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    lines = []
+    for line in text.splitlines():
+        line = re.sub(r"//.*", "", line)
+        line = " ".join(line.split())
+        if line:
+            lines.append(line)
+    return "\n".join(lines)
+
+
 def kernel_source_digest(paths):
     h = hashlib.sha256()
     for p in paths:
-        with open(os.path.join(ROOT, p), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, p), encoding="utf-8") as f:
+            h.update(kernel_source_code(f.read()).encode())
     return h.hexdigest()[:16]
 
 
