@@ -61,6 +61,8 @@ struct Args {
   int tiles_m, tiles_n;
   int64_t Mp, Np, Kp;  // padded extents of the tiled layout
   bool y_aligned;      // y 16-byte aligned and ldy a multiple of 8 elements
+  int splits;          // K split across this many work-groups per tile (1: none)
+  float* part;         // fp32 partial sums [splits][M][N] when splits > 1
 };
 
 // An FP4 operand is the low 4 dwords of the instruction's 8-dword operand; the upper
@@ -75,12 +77,14 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   return (uint16_t)(u >> 16);
 }
 
-// Map the hardware work-group id to a tile so that the ids one XCD receives
-// (id % 8 == x) form a contiguous run of tiles, walked in groups of 4 tile-rows.
-__device__ __forceinline__ void tile_of(int id, int tiles_m, int tiles_n, int& tm, int& tn) {
-  const int total = tiles_m * tiles_n;
-  int logical = id;
-  if (total % kXcds == 0) logical = (id % kXcds) * (total / kXcds) + id / kXcds;
+// The hardware hands work-group id to XCD id % 8; renumber the ids so that each XCD's
+// share of the `total` ids is one contiguous run.
+__device__ __forceinline__ int xcd_contiguous(int id, int total) {
+  return total % kXcds == 0 ? (id % kXcds) * (total / kXcds) + id / kXcds : id;
+}
+
+// Tile of a contiguous id: runs of ids walk the tiles in groups of 4 tile-rows.
+__device__ __forceinline__ void tile_of_run(int logical, int tiles_m, int tiles_n, int& tm, int& tn) {
   constexpr int G = 4;
   const int group = logical / (G * tiles_n);
   const int first_m = group * G;
@@ -88,6 +92,12 @@ __device__ __forceinline__ void tile_of(int id, int tiles_m, int tiles_n, int& t
   const int in_group = logical - group * G * tiles_n;
   tm = first_m + in_group % gm;
   tn = in_group / gm;
+}
+
+// Map the hardware work-group id to a tile so that the ids one XCD receives
+// (id % 8 == x) form a contiguous run of tiles, walked in groups of 4 tile-rows.
+__device__ __forceinline__ void tile_of(int id, int tiles_m, int tiles_n, int& tm, int& tn) {
+  tile_of_run(xcd_contiguous(id, tiles_m * tiles_n), tiles_m, tiles_n, tm, tn);
 }
 
 // Epilogue shared by both kernels: lane holds column r32 of each 32x32 tile and rows
@@ -343,10 +353,58 @@ __device__ __forceinline__ void store_swapped(const Args& a, const v16f (&acc)[M
       }
 }
 
+// The fp32 partial tile of a wave (64 rows x 128 columns, accumulator layout as above)
+// into part (row pitch N): staged through the wave's LDS region 32 rows at a time, so
+// that each store instruction writes two whole 512-byte row runs.  A tile reaching past
+// M or N, or rows that are not 16-byte aligned (N % 4 != 0), store element runs directly.
+__device__ __forceinline__ void store_partial(float* part, int64_t M, int64_t N, const v16f (&acc)[2][4],
+                                              int64_t row0, int64_t col0, int lane, uint8_t* lds) {
+  const int r32 = lane & 31, h = lane >> 5;
+  if (row0 + 64 > M || col0 + 128 > N || (N & 3) != 0) {
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int64_t row = row0 + mt * 32 + r32;
+          const int64_t col = col0 + nt * 32 + 8 * g + 4 * h;
+          if (row >= M) continue;
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (col + i < N) part[row * N + col + i] = acc[mt][nt][4 * g + i];
+        }
+    return;
+  }
+  constexpr int pitch = 128 * 4 + 16;
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt) {
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        *reinterpret_cast<f32x4*>(lds + r32 * pitch + (nt * 32 + 8 * g + 4 * h) * 4) =
+            f32x4{acc[mt][nt][4 * g], acc[mt][nt][4 * g + 1], acc[mt][nt][4 * g + 2], acc[mt][nt][4 * g + 3]};
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the wave-private region is written
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int it = 0; it < 16; ++it) {
+      const int row = 2 * it + (lane >> 5), c = lane & 31;
+      *reinterpret_cast<f32x4*>(part + (row0 + mt * 32 + row) * N + col0 + 4 * c) =
+          *reinterpret_cast<const f32x4*>(lds + row * pitch + c * 16);
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // every read of the region done before it is rewritten
+    __builtin_amdgcn_wave_barrier();
+  }
+}
+
 // s_waitcnt with only the vector-memory counter constrained (expcnt/lgkmcnt left free).
 #define SHARQ_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (7 << 4) | (15 << 8) | (((n) >> 4) << 14))
 
-template <bool OUT_F32, bool DUAL>
+// SPLIT: work-group s of a tile sums the K-steps
+// [s*steps/splits, (s+1)*steps/splits) and stores its fp32 tile into part[s]; the
+// partials are summed in order by reduce_splits_kernel.
+template <bool OUT_F32, bool DUAL, bool SPLIT>
 __global__ __launch_bounds__(kThreads, 1) void linear_mx_dma_kernel(Args a) {
   extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
   const int tid = threadIdx.x;
@@ -356,9 +414,25 @@ __global__ __launch_bounds__(kThreads, 1) void linear_mx_dma_kernel(Args a) {
   const int r32 = lane & 31, h = lane >> 5;
 
   int tm, tn;
-  tile_of(blockIdx.x, a.tiles_m, a.tiles_n, tm, tn);
+  int split = 0;
+  if constexpr (SPLIT) {
+    // each XCD gets a contiguous run of (split, tile) ids, split-major, so that the tiles
+    // it holds at once share activation and weight panels as in the unsplit order
+    const int tiles = a.tiles_m * a.tiles_n;
+    const int id = xcd_contiguous((int)blockIdx.x, tiles * a.splits);
+    split = id / tiles;
+    tile_of_run(id - split * tiles, a.tiles_m, a.tiles_n, tm, tn);
+  } else {
+    tile_of(blockIdx.x, a.tiles_m, a.tiles_n, tm, tn);
+  }
   const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
-  const int nk = (int)(a.Kp / 128);
+  int nk = (int)(a.Kp / 128);
+  int k0 = 0;  // first K-step
+  if constexpr (SPLIT) {
+    const int steps = nk;
+    k0 = split * steps / a.splits;
+    nk = (split + 1) * steps / a.splits - k0;
+  }
 
   // Each wave fills 6 of the 48 fragments of a stage (A_b, A_r, W x 16; 4 of 32
   // without A_b): one contiguous 1 KiB fragment of the tiled payload per load.  Row
@@ -376,6 +450,7 @@ __global__ __launch_bounds__(kThreads, 1) void linear_mx_dma_kernel(Args a) {
     int64_t t = (op == 2 ? n0 : m0) / 32 + rt;
     t = t < ntiles ? t : ntiles - 1;
     fsrc[j] = base + (t * (a.Kp / 64) + sub) * kFragBytes;  // wave-uniform; lane adds 16 * lane
+    if constexpr (SPLIT) fsrc[j] += 2 * (int64_t)k0 * kFragBytes;
     fdst[j] = op * kOpTileBytes + fi * kFragBytes;
   }
   // Scale words: one operand's 256 words per K-step are 1 KiB contiguous; the first
@@ -395,6 +470,7 @@ __global__ __launch_bounds__(kThreads, 1) void linear_mx_dma_kernel(Args a) {
     const int64_t row0 = op == 2 ? n0 : m0;
     ssrc = base + row0 * 4;  // wave-uniform; lane adds 16 * lane (4 rows)
     sstep = rp * 4;
+    if constexpr (SPLIT) ssrc += k0 * sstep;
     sbytes = (uint32_t)((rp - row0) * 4 < 1024 ? (rp - row0) * 4 : 1024);
     sdst = 3 * kOpTileBytes + op * 1024;
   }
@@ -521,24 +597,102 @@ __global__ __launch_bounds__(kThreads, 1) void linear_mx_dma_kernel(Args a) {
   SHARQ_WAIT_VMCNT(0);  // trailing loads land before the stage ring is reused
 
   __syncthreads();  // every wave is done with the stage ring; reuse it for the epilogue
-  store_swapped<OUT_F32, 2, 4>(a, acc, m0 + wm * 64, n0 + wn * 128, lane,
-                               smem + wave * (64 * (256 + kEpiPad)), a.y_aligned);
+  if constexpr (SPLIT) {
+    store_partial(a.part + (int64_t)split * a.M * a.N, a.M, a.N, acc, m0 + wm * 64, n0 + wn * 128, lane,
+                  smem + wave * (32 * (128 * 4 + 16)));
+  } else {
+    store_swapped<OUT_F32, 2, 4>(a, acc, m0 + wm * 64, n0 + wn * 128, lane,
+                                 smem + wave * (64 * (256 + kEpiPad)), a.y_aligned);
+  }
 }
 
-template <bool OUT_F32, bool DUAL>
-hipError_t launch_dma(const Args& a, hipStream_t stream) {
+// y = sum over s of part[s], in order s = 0, 1, ... (one fp32 rounding per addition,
+// the same order every call), rounded to bf16 or stored as fp32.  Four consecutive
+// outputs per thread: 16-byte partial loads when N is a multiple of 4 (part is 16-byte
+// aligned), one 8- or 16-byte store when y allows it (vec_y), element by element
+// otherwise and in a row's last partial quad.
+template <bool OUT_F32>
+__global__ __launch_bounds__(256) void reduce_splits_kernel(const float* __restrict__ part, int splits, int64_t M,
+                                                            int64_t N, void* __restrict__ y, int64_t ldy,
+                                                            bool vec_y) {
+  const int64_t nq = (N + 3) / 4;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= M * nq) return;
+  const int64_t row = i / nq, c0 = (i - row * nq) * 4;
+  const int64_t plane = M * N;
+  const float* p = part + row * N + c0;
+  if ((N & 3) == 0) {
+    f32x4 acc = *reinterpret_cast<const f32x4*>(p);
+    for (int s = 1; s < splits; ++s) {
+      const f32x4 t = *reinterpret_cast<const f32x4*>(p + s * plane);
+      acc = f32x4{__fadd_rn(acc[0], t[0]), __fadd_rn(acc[1], t[1]), __fadd_rn(acc[2], t[2]), __fadd_rn(acc[3], t[3])};
+    }
+    if (vec_y) {
+      if constexpr (OUT_F32) {
+        *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(y) + row * ldy + c0) = acc;
+      } else {
+        const uint32_t lo = f32_to_bf16_rne(acc[0]) | ((uint32_t)f32_to_bf16_rne(acc[1]) << 16);
+        const uint32_t hi = f32_to_bf16_rne(acc[2]) | ((uint32_t)f32_to_bf16_rne(acc[3]) << 16);
+        *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(y) + row * ldy + c0) = make_uint2(lo, hi);
+      }
+      return;
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if constexpr (OUT_F32)
+        reinterpret_cast<float*>(y)[row * ldy + c0 + j] = acc[j];
+      else
+        reinterpret_cast<uint16_t*>(y)[row * ldy + c0 + j] = f32_to_bf16_rne(acc[j]);
+    }
+    return;
+  }
+  const int cn = N - c0 < 4 ? (int)(N - c0) : 4;
+  for (int j = 0; j < cn; ++j) {
+    float acc = p[j];
+    for (int s = 1; s < splits; ++s) acc = __fadd_rn(acc, p[j + s * plane]);
+    if constexpr (OUT_F32)
+      reinterpret_cast<float*>(y)[row * ldy + c0 + j] = acc;
+    else
+      reinterpret_cast<uint16_t*>(y)[row * ldy + c0 + j] = f32_to_bf16_rne(acc);
+  }
+}
+
+// The dynamic-LDS limit is a per-device function attribute, set once per kernel and device
+// (setting it twice is harmless).
+template <bool OUT_F32, bool DUAL, bool SPLIT>
+hipError_t configure_dma() {
   static std::atomic<bool> configured[kMaxDevices];
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
   if (dev < 0 || dev >= kMaxDevices || !configured[dev].load(std::memory_order_acquire)) {
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&linear_mx_dma_kernel<OUT_F32, DUAL>),
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&linear_mx_dma_kernel<OUT_F32, DUAL, SPLIT>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, kDmaStages * kDmaStageBytes);
     if (e != hipSuccess) return e;
     if (dev >= 0 && dev < kMaxDevices) configured[dev].store(true, std::memory_order_release);
   }
-  const int grid = a.tiles_m * a.tiles_n;
-  linear_mx_dma_kernel<OUT_F32, DUAL><<<dim3(grid), dim3(kThreads), kDmaStages * kDmaStageBytes, stream>>>(a);
+  return hipSuccess;
+}
+
+template <bool OUT_F32, bool DUAL>
+hipError_t launch_dma(const Args& a, hipStream_t stream) {
+  const int tiles = a.tiles_m * a.tiles_n;
+  if (a.splits > 1) {
+    hipError_t e = configure_dma<true, DUAL, true>();
+    if (e != hipSuccess) return e;
+    linear_mx_dma_kernel<true, DUAL, true>
+        <<<dim3(tiles * a.splits), dim3(kThreads), kDmaStages * kDmaStageBytes, stream>>>(a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    const int64_t quads = a.M * ((a.N + 3) / 4);
+    const uintptr_t ya = reinterpret_cast<uintptr_t>(a.y);
+    const bool vec_y = a.N % 4 == 0 && a.ldy % 4 == 0 && (ya & (OUT_F32 ? 15u : 7u)) == 0;
+    reduce_splits_kernel<OUT_F32><<<dim3((unsigned)((quads + 255) / 256)), dim3(256), 0, stream>>>(
+        a.part, a.splits, a.M, a.N, a.y, a.ldy, vec_y);
+    return hipGetLastError();
+  }
+  hipError_t e = configure_dma<OUT_F32, DUAL, false>();
+  if (e != hipSuccess) return e;
+  linear_mx_dma_kernel<OUT_F32, DUAL, false><<<dim3(tiles), dim3(kThreads), kDmaStages * kDmaStageBytes, stream>>>(a);
   return hipGetLastError();
 }
 
@@ -702,18 +856,45 @@ hipError_t dispatch(const Args& a, bool tiled, bool out_fp32, hipStream_t stream
   return out_fp32 ? launch<true, false, DUAL>(a, stream) : launch<false, false, DUAL>(a, stream);
 }
 
+// K split of the tiled GEMM: a shape with fewer 256x256 output tiles than the part has
+// compute units splits each tile's K-steps over up to kMaxSplits work-groups, as many as
+// fill the compute units, each keeping at least kMinSplitSteps K-steps (128 elements each).
+constexpr int64_t kComputeUnits = 256;
+constexpr int64_t kMinSplitSteps = 16;
+constexpr int64_t kMaxSplits = 4;
+
+int mx_splits(int64_t M, int64_t N, int64_t K) {
+  if (M <= 32) return 1;  // the small-M kernel
+  const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+  int64_t s = kComputeUnits / tiles;
+  s = s < round_up(K, 128) / 128 / kMinSplitSteps ? s : round_up(K, 128) / 128 / kMinSplitSteps;
+  s = s < kMaxSplits ? s : kMaxSplits;
+  return s >= 2 ? (int)s : 1;
+}
+
 }  // namespace
 
 size_t linear_mx_workspace(int64_t, int64_t, int64_t) { return 0; }
 
+size_t linear_mx_split_workspace(int64_t M, int64_t N, int64_t K) {
+  const int s = mx_splits(M, N, K);
+  return s > 1 ? (size_t)s * (size_t)M * (size_t)N * sizeof(float) : 0;
+}
+
 hipError_t launch_linear_mx(const sharq_fp4* b, const sharq_fp4& r, int64_t M, const sharq_fp4& w,
-                            int64_t N, int64_t K, void* y, int64_t ldy, int out_fp32, void*, size_t,
-                            hipStream_t stream) {
+                            int64_t N, int64_t K, void* y, int64_t ldy, int out_fp32, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream) {
   if (M == 0 || N == 0) return hipSuccess;
+  const bool tiled = r.layout == SHARQ_LAYOUT_TILED;
+  // the K split runs only when the workspace holds its partial sums
+  int splits = tiled ? mx_splits(M, N, K) : 1;
+  if (splits > 1 && (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 15u) ||
+                     workspace_bytes < linear_mx_split_workspace(M, N, K)))
+    splits = 1;
   Args a{b ? b->codes : nullptr, b ? b->scales : nullptr, r.codes, r.scales, w.codes, w.scales, y, M, N, K, ldy,
          (int)((M + BM - 1) / BM), (int)((N + BN - 1) / BN), round_up(M, 32), round_up(N, 32), round_up(K, 128),
-         (reinterpret_cast<uintptr_t>(y) & 15u) == 0 && ldy % 8 == 0};
-  const bool tiled = r.layout == SHARQ_LAYOUT_TILED;
+         (reinterpret_cast<uintptr_t>(y) & 15u) == 0 && ldy % 8 == 0, splits,
+         splits > 1 ? reinterpret_cast<float*>(workspace) : nullptr};
   return b ? dispatch<true>(a, tiled, out_fp32, stream) : dispatch<false>(a, tiled, out_fp32, stream);
 }
 

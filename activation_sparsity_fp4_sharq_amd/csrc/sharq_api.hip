@@ -224,6 +224,11 @@ size_t sharq_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, int fmt) {
   return fmt == SHARQ_NVFP4 ? linear_nv_workspace(M, N, K) : linear_mx_workspace(M, N, K);
 }
 
+size_t sharq_linear_split_workspace_bytes(int64_t M, int64_t N, int64_t K, int fmt) {
+  if (M <= 0 || N <= 0 || K <= 0 || fmt != SHARQ_MXFP4) return 0;
+  return linear_mx_split_workspace(M, N, K);
+}
+
 sharq_status sharq_quantize(const void* x, int64_t rows, int64_t K, int64_t ldx, int fmt,
                             const sharq_fp4* out, void* workspace, size_t workspace_bytes,
                             void* stream) {

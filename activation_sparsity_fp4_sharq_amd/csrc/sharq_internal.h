@@ -59,6 +59,8 @@ hipError_t launch_linear_mx(const sharq_fp4* b, const sharq_fp4& r, int64_t M, c
                             int64_t N, int64_t K, void* y, int64_t ldy, int out_fp32,
                             void* work, size_t work_bytes, hipStream_t stream);
 size_t linear_mx_workspace(int64_t M, int64_t N, int64_t K);
+// Workspace bytes that let the tiled MXFP4 GEMM split K (0 when the shape does not split).
+size_t linear_mx_split_workspace(int64_t M, int64_t N, int64_t K);
 
 hipError_t launch_linear_nv(const sharq_fp4* b, const sharq_fp4& r, int64_t M, const sharq_fp4& w,
                             int64_t N, int64_t K, void* y, int64_t ldy, int out_fp32,

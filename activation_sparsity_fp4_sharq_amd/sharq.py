@@ -25,7 +25,7 @@ SYMBOLS = ["sharq_abi_version", "sharq_status_str", "sharq_payload_bytes", "shar
            "sharq_prep_rmsnorm_workspace_bytes", "sharq_prep_rmsnorm", "sharq_linear", "sharq_linear_dense",
            "sharq_clock_probe", "sharq_prep_ablation", "sharq_dequantize", "sharq_prep_swiglu",
            "sharq_forward", "sharq_forward_noalloc", "sharq_matrix_rate_probe", "sharq_stream_probe",
-           "sharq_bf16_rounding_probe", "sharq_e4m3_conversion_probe"]
+           "sharq_bf16_rounding_probe", "sharq_e4m3_conversion_probe", "sharq_linear_split_workspace_bytes"]
 
 
 class SharqFp4(ctypes.Structure):
@@ -39,7 +39,7 @@ class SharqError(RuntimeError):
         self.status = status
 
 
-ABI_VERSION = 11  # the SHARQ_ABI_VERSION of include/sharq.h this binding marshals for
+ABI_VERSION = 12  # the SHARQ_ABI_VERSION of include/sharq.h this binding marshals for
 
 _lib = None
 
@@ -74,6 +74,8 @@ def lib():
         L.sharq_prep_workspace_bytes.argtypes = [i64, i64, ctypes.c_int]
         L.sharq_linear_workspace_bytes.restype = sz
         L.sharq_linear_workspace_bytes.argtypes = [i64, i64, i64, ctypes.c_int]
+        L.sharq_linear_split_workspace_bytes.restype = sz
+        L.sharq_linear_split_workspace_bytes.argtypes = [i64, i64, i64, ctypes.c_int]
         L.sharq_quantize.restype = ctypes.c_int
         L.sharq_quantize.argtypes = [vp, i64, i64, i64, ctypes.c_int, P, vp, sz, vp]
         L.sharq_prep.restype = ctypes.c_int
@@ -360,8 +362,8 @@ def linear(backbone, residual, weight, out_dtype=OUT_BF16, y=None, ws=None, stre
         y = torch.empty((M, N), dtype=torch.float32 if out_dtype == OUT_FP32 else torch.bfloat16, device=dev)
     _check_output(y, M, N, out_dtype, dev)
     need = lib().sharq_linear_workspace_bytes(M, N, K, fmt)
-    if ws is None:
-        ws = workspace(need, dev)
+    if ws is None:  # with room for the K split where the shape has one
+        ws = workspace(max(need, lib().sharq_linear_split_workspace_bytes(M, N, K, fmt)), dev)
     _check_workspace(ws, need, dev)
     sb, sr, sw = backbone.struct(), residual.struct(), weight.struct()
     _check("sharq_linear", lib().sharq_linear(ctypes.byref(sb), ctypes.byref(sr), M, ctypes.byref(sw), N, K,
@@ -383,8 +385,8 @@ def linear_dense(a, weight, out_dtype=OUT_BF16, y=None, ws=None, stream=None):
         y = torch.empty((M, N), dtype=torch.float32 if out_dtype == OUT_FP32 else torch.bfloat16, device=dev)
     _check_output(y, M, N, out_dtype, dev)
     need = lib().sharq_linear_workspace_bytes(M, N, K, fmt)
-    if ws is None:
-        ws = workspace(need, dev)
+    if ws is None:  # with room for the K split where the shape has one
+        ws = workspace(max(need, lib().sharq_linear_split_workspace_bytes(M, N, K, fmt)), dev)
     _check_workspace(ws, need, dev)
     sa, sw = a.struct(), weight.struct()
     _check("sharq_linear_dense", lib().sharq_linear_dense(ctypes.byref(sa), M, ctypes.byref(sw), N, K, fmt, _ptr(y),
@@ -476,8 +478,8 @@ def _forward_args(x, weight, out_dtype, bufs, y, ws, with_workspace=True):
     _check_output(y, M, N, out_dtype, dev)
     if with_workspace:
         need = max(lib().sharq_prep_workspace_bytes(M, K, fmt), lib().sharq_linear_workspace_bytes(M, N, K, fmt))
-        if ws is None:
-            ws = workspace(need, dev)
+        if ws is None:  # with room for the K split where the shape has one
+            ws = workspace(max(need, lib().sharq_linear_split_workspace_bytes(M, N, K, fmt)), dev)
         _check_workspace(ws, need, dev)
     return x, bb, rr, y, ws, M, K, N, fmt
 

@@ -381,8 +381,11 @@ def run_mlp_block(args):
                          gu=torch.empty((M, 2 * I), dtype=torch.bfloat16, device=dev),
                          b2=sharq.Payload.empty(M, I, b.fmt, dev), r2=sharq.Payload.empty(M, I, b.fmt, dev),
                          y=torch.empty((M, H), dtype=torch.bfloat16, device=dev)))
-    ws = sharq.workspace(max(sharq.lib().sharq_prep_workspace_bytes(M, max(H, I), b.fmt),
-                             sharq.lib().sharq_linear_workspace_bytes(M, 2 * I, max(H, I), b.fmt)), dev)
+    L = sharq.lib()
+    ws = sharq.workspace(max(L.sharq_prep_workspace_bytes(M, max(H, I), b.fmt),
+                             L.sharq_linear_workspace_bytes(M, 2 * I, max(H, I), b.fmt),
+                             L.sharq_linear_split_workspace_bytes(M, 2 * I, H, b.fmt),  # gate/up
+                             L.sharq_linear_split_workspace_bytes(M, H, I, b.fmt)), dev)  # down
     stream = torch.cuda.current_stream()
 
     def prep1(i):
@@ -509,7 +512,8 @@ def main():
         sets.append((x, weight, bb, rr, y))
     ws = sharq.workspace(max(sharq.lib().sharq_prep_workspace_bytes(M, K, w.fmt),
                              sharq.lib().sharq_prep_rmsnorm_workspace_bytes(M, K, w.fmt),
-                             sharq.lib().sharq_linear_workspace_bytes(M, N, K, w.fmt)), dev)
+                             sharq.lib().sharq_linear_workspace_bytes(M, N, K, w.fmt),
+                             sharq.lib().sharq_linear_split_workspace_bytes(M, N, K, w.fmt)), dev)
     stream = torch.cuda.current_stream()
     # the normalization gain: seeded, around 1 (random-init layer, no checkpoint)
     gamma = torch.from_numpy(np.random.default_rng(1).normal(1.0, 0.1, K).astype(np.float32)).to(dev)

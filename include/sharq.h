@@ -61,7 +61,7 @@
 extern "C" {
 #endif
 
-#define SHARQ_ABI_VERSION 11
+#define SHARQ_ABI_VERSION 12
 
 typedef enum sharq_status {
   SHARQ_OK = 0,
@@ -116,6 +116,17 @@ size_t sharq_prep_workspace_bytes(int64_t rows, int64_t K, int fmt);
 /* Bytes of device workspace sharq_linear needs for these sizes (the split-K
  * partial sums of small-M shapes; 0 when the shape runs without split-K). */
 size_t sharq_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, int fmt);
+
+/* Bytes of workspace that let sharq_linear (and sharq_forward, sharq_linear_dense) split
+ * K for these sizes: a tiled MXFP4 product with fewer 256 x 256 output tiles than the GPU
+ * has compute units (256) and long rows gives each tile's K-steps to up to 4 work-groups,
+ * which store fp32 partial sums [splits][M][N] in the workspace; a second kernel adds
+ * them in split order and rounds Y.  0 when the shape does not split (NVFP4, row-major
+ * payloads, M <= 32, enough tiles, or fewer than 2 x 2048 columns of K per split).  Any
+ * smaller workspace (also none) is accepted: the call then runs unsplit.  A split call
+ * sums in a different order than an unsplit one, so the two agree to the fp32 summation
+ * bound, not bit for bit; each is deterministic. */
+size_t sharq_linear_split_workspace_bytes(int64_t M, int64_t N, int64_t K, int fmt);
 
 /* Plain FP4 quantization (no mask, no residual) of a bf16 matrix -- how a weight
  * payload W is produced (the pages quantize the weights once, and both GEMMs of the
@@ -254,7 +265,9 @@ sharq_status sharq_prep_rmsnorm(const void* x, int64_t M, int64_t K, int64_t ldx
  *                       are tiled; any row-major payload takes a slower generic kernel.
  *   y                   device [M, ldy] bf16 (round to nearest even) or fp32; ldy >= N;
  *                       aligned to its element size
- *   workspace           device, >= sharq_linear_workspace_bytes(M, N, K, fmt) bytes
+ *   workspace           device, >= sharq_linear_workspace_bytes(M, N, K, fmt) bytes; with
+ *                       sharq_linear_split_workspace_bytes(...) bytes (16-byte aligned) a
+ *                       shape with few output tiles splits K (see there)
  * MXFP4 runs on the gfx950 block-scaled FP4 matrix cores, so every product of two
  * FP4 values and their scales is exact and only the fp32 summation order differs
  * from an exact result.  NVFP4 (E4M3 block scales, which the FP4 matrix cores

@@ -33,7 +33,7 @@ def test_header_symbols_exported():
 
 def test_version_and_status_strings():
     L = sharq.lib()
-    assert L.sharq_abi_version() == 11
+    assert L.sharq_abi_version() == 12
     for s in range(9):
         assert L.sharq_status_str(s)
     assert L.sharq_status_str(99) == b"unknown status"
@@ -44,6 +44,22 @@ def test_workspace_sizes():
     assert L.sharq_prep_workspace_bytes(4096, 4096, sharq.MXFP4) == 0
     assert L.sharq_prep_workspace_bytes(4096, 4096, sharq.NVFP4) >= 8
     assert L.sharq_linear_workspace_bytes(0, 10, 32, sharq.MXFP4) == 0
+    assert L.sharq_linear_workspace_bytes(2048, 4096, 14336, sharq.MXFP4) == 0  # the split is optional
+
+
+def test_split_workspace_sizes():
+    """K splits for tiled MXFP4 shapes with fewer 256x256 tiles than 256 compute units:
+    as many splits as fill them, at most 4, each with at least 16 K-steps of 128."""
+    L = sharq.lib()
+    f = L.sharq_linear_split_workspace_bytes
+    assert f(2048, 4096, 14336, sharq.MXFP4) == 2 * 2048 * 4096 * 4  # 128 tiles, 112 steps
+    assert f(600, 512, 8192, sharq.MXFP4) == 4 * 600 * 512 * 4      # 6 tiles: capped at 4
+    assert f(300, 1000, 6144, sharq.MXFP4) == 3 * 300 * 1000 * 4    # 48 steps: 3 of 16
+    assert f(4096, 4096, 4096, sharq.MXFP4) == 0                     # 256 tiles fill the part
+    assert f(2048, 4096, 2048, sharq.MXFP4) == 0                     # 16 steps: one split
+    assert f(32, 4096, 14336, sharq.MXFP4) == 0                      # the small-M kernel
+    assert f(2048, 4096, 14336, sharq.NVFP4) == 0
+    assert f(0, 4096, 14336, sharq.MXFP4) == 0 and f(64, 0, 4096, sharq.MXFP4) == 0
 
 
 def fp4(codes=A, scales=A, ts=A, layout=0, reserved=0):

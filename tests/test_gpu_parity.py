@@ -326,6 +326,61 @@ def test_linear_small_full_compare(fmt, layout, M, N, K):
         assert fro <= TOL
 
 
+@pytest.mark.parametrize("M,N,K", [(600, 512, 8192), (1024, 2048, 4096), (300, 1000, 6144), (40, 300, 4096)])
+def test_linear_split_k_matches_oracle(M, N, K):
+    """Tiled MXFP4 shapes with few output tiles split K over 2-4 work-groups when the
+    workspace holds the partial sums: every output within the fp32 summation bound (any
+    summation order), bf16 within one ulp plus it, deterministic across calls; the same
+    call with a workspace too small for the partials runs unsplit and meets the same bound.
+    A padded, odd ldy takes the reduction's element-wise store."""
+    fmt, layout = sharq.MXFP4, sharq.TILED
+    need = sharq.lib().sharq_linear_split_workspace_bytes(M, N, K, fmt)
+    print(f"[linear split-K] M={M} N={N} K={K} partials={need} B", flush=True)
+    assert need > 0, "the shape is meant to split"
+    xb, wb = make_shape(M, N, K, seed=M + N + K, dist="laplace", token_sigma=0.3)
+    weight = sharq.quantize(to_dev(wb), fmt, layout=layout)
+    bb, rr, _ = sharq.prep(to_dev(xb), 2, 4, fmt, layout=layout)
+    ws = sharq.workspace(need, DEV)
+    small = torch.zeros(16, dtype=torch.uint8, device=DEV)
+    y32 = sharq.linear(bb, rr, weight, sharq.OUT_FP32, ws=ws)
+    y32b = sharq.linear(bb, rr, weight, sharq.OUT_FP32, ws=ws)
+    y32u = sharq.linear(bb, rr, weight, sharq.OUT_FP32, ws=small)
+    y16 = sharq.linear(bb, rr, weight, sharq.OUT_BF16, ws=ws)
+    ybuf = torch.zeros((M, N + 3), dtype=torch.bfloat16, device=DEV)
+    y16p = sharq.linear(bb, rr, weight, sharq.OUT_BF16, y=ybuf[:, :N], ws=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(y32.view(torch.int32), y32b.view(torch.int32)), "split-K is not deterministic"
+    assert torch.equal(y16.view(torch.int16), y16p.view(torch.int16)), "padded ldy differs"
+    assert torch.all(ybuf[:, N:].view(torch.int16) == 0), "write into the padding"
+    ob, orr, _ = oracle.prep(xb, 2, 4, fmt)
+    ow = oracle.quantize(wb, fmt)
+    yref = oracle.linear(ob, orr, ow, fmt)
+    abssum = abs_linear(ob, orr, ow, fmt)
+    assert fp32_bound_check(y32, yref, abssum, K) <= 1.0
+    assert fp32_bound_check(y32u, yref, abssum, K) <= 1.0
+    assert bf16_bound_check(y16, yref, abssum, K) <= 1.0
+    assert rel_maxnorm(y32.cpu().numpy().astype(np.float64), yref) <= TOL
+
+
+def test_linear_split_k_mlp_down_full_size():
+    """The MLP block's down projection (M=2048, N=4096, K=14336, MXFP4 2:4, tiled) splits K
+    in two: 64 sampled rows against the oracle within the fp32 summation bound."""
+    M, N, K = 2048, 4096, 14336
+    assert sharq.lib().sharq_linear_split_workspace_bytes(M, N, K, sharq.MXFP4) == 2 * M * N * 4
+    print(f"[linear split-K] full size M={M} N={N} K={K}", flush=True)
+    xb, wb = make_shape(M, N, K, seed=14, dist="laplace", token_sigma=0.3)
+    weight = sharq.quantize(to_dev(wb), sharq.MXFP4, layout=sharq.TILED)
+    bb, rr, _ = sharq.prep(to_dev(xb), 2, 4, sharq.MXFP4, layout=sharq.TILED)
+    y32 = sharq.linear(bb, rr, weight, sharq.OUT_FP32)  # the binding sizes the workspace for the split
+    torch.cuda.synchronize()
+    rows = np.sort(np.random.default_rng(3).choice(M, 64, replace=False))
+    ob, orr, _ = oracle.prep(xb[rows], 2, 4, sharq.MXFP4)
+    ow = oracle.quantize(wb, sharq.MXFP4)
+    yref = oracle.linear(ob, orr, ow, sharq.MXFP4)
+    abssum = abs_linear(ob, orr, ow, sharq.MXFP4)
+    assert fp32_bound_check(y32.cpu().numpy()[rows].astype(np.float64), yref, abssum, K) <= 1.0
+
+
 def _random_forward_cases(count=24, seed=20261204):
     """Seeded random configurations of the whole layer: format, layout, pattern, ragged
     M, N and K (a multiple of the format's block), padded rows of X, input distribution
