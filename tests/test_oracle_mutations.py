@@ -1,6 +1,9 @@
-"""The NVFP4 worked examples pin reading R5's fp32 steps: each test below plants
-one plausible deviation from R5 in a temporary copy of the oracle's C source
-(on the CPU), builds it, and checks that a stored worked example then fails.
+"""The worked examples pin the oracle's readings: each test below plants one
+plausible deviation in a temporary copy of the oracle's C source (on the CPU),
+builds it, and checks that a stored worked example then fails.  The NVFP4
+examples pin reading R5's fp32 steps; the MXFP4 examples pin the mask (R1), the
+E8M0 block exponent (R2), E2M1 rounding (R3), the residual taken against the
+dequantized backbone (R4) and the nibble packing (R6).
 
 R5 (NVFP4 with per-path tensor scales; SharQ, arXiv 2606.26587, abstract: the
 method runs on NVFP4 and names path-specific scale views): S = fp32(amax/2688),
@@ -41,6 +44,37 @@ MUTATIONS = [
      " (float)oracle_e4m3_value(sb) * Sb, xv);"),
 ]
 
+# (name, text of the step in the oracle, the same step with the deviation): readings
+# R1-R4 and R6 of the MXFP4 path (SharQ, arXiv 2606.26587, abstract and Core claim:
+# an input-adaptive N:M mask keeps the outlier-dominated values, the residual is taken
+# against the quantized backbone; the block format is the OCP MX rule the page cites)
+MX_MUTATIONS = [
+    ("mask ties to the higher index", "      if (kl > kj || (kl == kj && l < j)) ++rank;",
+     "      if (kl > kj || (kl == kj && l > j)) ++rank;"),
+    ("mask on signed values instead of magnitudes",
+     "    uint16_t kj = xg[j] & 0x7FFF;\n    int rank = 0;\n    for (int l = 0; l < m; ++l) {\n"
+     "      uint16_t kl = xg[l] & 0x7FFF;",
+     "    uint16_t kj = (xg[j] & 0x8000) ? (uint16_t)(0x7FFF - (xg[j] & 0x7FFF)) : (uint16_t)(xg[j] | 0x8000);\n"
+     "    int rank = 0;\n    for (int l = 0; l < m; ++l) {\n"
+     "      uint16_t kl = (xg[l] & 0x8000) ? (uint16_t)(0x7FFF - (xg[l] & 0x7FFF)) : (uint16_t)(xg[l] | 0x8000);"),
+    ("mask keeps the smallest magnitudes", "    keep[j] = rank < n;", "    keep[j] = rank >= m - n;"),
+    ("block exponent floor(log2 amax) - 1", "  int e = (e2 - 1) - 2;", "  int e = (e2 - 1) - 1;"),
+    ("block exponent ceil(log2 amax) - 2", "  int e = (e2 - 1) - 2;",
+     "  int e = (frexp(amax, &e2) == 0.5 ? e2 - 1 : e2) - 2;"),
+    ("E2M1 ties away from zero", "    if (a > mid || (a == mid && (upper & 1) == 0)) mag = (uint8_t)upper;",
+     "    if (a >= mid) mag = (uint8_t)upper;"),
+    ("E2M1 ties toward zero", "    if (a > mid || (a == mid && (upper & 1) == 0)) mag = (uint8_t)upper;",
+     "    if (a > mid) mag = (uint8_t)upper;"),
+    ("E2M1 drops the sign of a value rounding to zero", "  return (uint8_t)((signbit(t) ? 8 : 0) | mag);",
+     "  return (uint8_t)((signbit(t) && mag ? 8 : 0) | mag);"),
+    ("residual against the unquantized sparse values", "        float r = xv - bh;                                            /* R4 */",
+     "        float r = xv - (keep[i * K + k0 + j] ? xv : 0.0f); (void)bh;"),
+    ("dequantization off by one binade", "  return (float)ldexp(oracle_e2m1_value(code), (int)scale_byte - 127);",
+     "  return (float)ldexp(oracle_e2m1_value(code), (int)scale_byte - 128);"),
+    ("nibbles packed high first", "  if (k & 1) *b = (uint8_t)((*b & 0x0F) | (code << 4));\n  else *b = (uint8_t)((*b & 0xF0) | (code & 0x0F));",
+     "  if (!(k & 1)) *b = (uint8_t)((*b & 0x0F) | (code << 4));\n  else *b = (uint8_t)((*b & 0xF0) | (code & 0x0F));"),
+]
+
 # an E4M3 encoder of an unrounded quotient, for the "q unrounded" deviation
 EXACT_ENCODER = r"""
 static uint8_t oracle_e4m3_encode_exact(double q) {
@@ -61,9 +95,13 @@ static uint8_t oracle_e4m3_encode_exact(double q) {
 """
 
 
-def _nv_examples():
+def _examples(fmt):
     with open(GOLDEN) as f:
-        return [e for e in json.load(f)["examples"] if e["fmt"] == "nvfp4"]
+        return [e for e in json.load(f)["examples"] if e["fmt"] == fmt]
+
+
+def _nv_examples():
+    return _examples("nvfp4")
 
 
 def _num(v):
@@ -98,16 +136,19 @@ def _outputs(L, ex):
     xb = f32_to_bf16_bits(x)
     assert np.array_equal(bf16_bits_to_f32(xb), x)
     K = x.shape[1]
+    nv = ex["fmt"] == "nvfp4"
     bc = np.zeros((1, K // 2), np.uint8)
-    bs = np.zeros((1, K // 16), np.uint8)
+    bs = np.zeros((1, K // (16 if nv else 32)), np.uint8)
     rc = np.zeros_like(bc)
     rs = np.zeros_like(bs)
     bt = np.ones(1, np.float32)
     rt = np.ones(1, np.float32)
     resid = np.zeros((1, K), np.float32)
+    mask = np.zeros((1, K // 8), np.uint8)
     ptr = lambda a: a.ctypes.data_as(ctypes.c_void_p)
-    rcode = L.oracle_prep_variant(xb, 1, K, K, ex["n"], ex["m"], 1, 0, bc, bs, ptr(bt), rc, rs, ptr(rt), None,
-                                  None, ptr(resid))
+    rcode = L.oracle_prep_variant(xb, 1, K, K, ex["n"], ex["m"], 1 if nv else 0, 0, bc, bs,
+                                  ptr(bt) if nv else None, rc, rs, ptr(rt) if nv else None, ptr(mask), None,
+                                  ptr(resid))
     assert rcode == 0
 
     def unpack(p):
@@ -117,14 +158,18 @@ def _outputs(L, ex):
         return out.tolist()
 
     want_r = np.array([_num(v) for v in ex["residual"]], np.float32)
-    return {
+    out = {
+        "mask_bytes": mask[0].tolist() == ex["mask_bytes"],
         "backbone_codes": unpack(bc) == ex["backbone_codes"],
         "backbone_scales": bs[0].tolist() == ex["backbone_scales"],
         "residual_codes": unpack(rc) == ex["residual_codes"],
-        "residual_scales": rs[0].tolist() == ex["residual_scales"],
-        "tensor_scales": bt[0] == ex["backbone_tensor_scale"] and rt[0] == ex["residual_tensor_scale"],
         "residual": np.array_equal(resid[0].view(np.uint32), want_r.view(np.uint32)),
     }
+    if "residual_scales" in ex:
+        out["residual_scales"] = rs[0].tolist() == ex["residual_scales"]
+    if nv:
+        out["tensor_scales"] = bt[0] == ex["backbone_tensor_scale"] and rt[0] == ex["residual_tensor_scale"]
+    return out
 
 
 @pytest.mark.skipif(shutil.which("gcc") is None, reason="needs gcc to build the oracle variants")
@@ -139,4 +184,19 @@ def test_unmodified_copy_reproduces_every_nv_example(tmp_path):
 def test_nv_examples_catch_a_deviation_from_r5(tmp_path, name, old, new):
     L = _build_variant(tmp_path, old, new)
     failed = {ex["name"]: [k for k, ok in _outputs(L, ex).items() if not ok] for ex in _nv_examples()}
+    assert any(failed.values()), f"no worked example detects: {name}"
+
+
+@pytest.mark.skipif(shutil.which("gcc") is None, reason="needs gcc to build the oracle variants")
+def test_unmodified_copy_reproduces_every_mx_example(tmp_path):
+    L = _build_variant(tmp_path, "  int e = (e2 - 1) - 2;", "  int e = (e2 - 1) - 2;")
+    for ex in _examples("mxfp4"):
+        assert all(_outputs(L, ex).values()), ex["name"]
+
+
+@pytest.mark.skipif(shutil.which("gcc") is None, reason="needs gcc to build the oracle variants")
+@pytest.mark.parametrize("name,old,new", MX_MUTATIONS, ids=[m[0] for m in MX_MUTATIONS])
+def test_mx_examples_catch_a_deviation(tmp_path, name, old, new):
+    L = _build_variant(tmp_path, old, new)
+    failed = {ex["name"]: [k for k, ok in _outputs(L, ex).items() if not ok] for ex in _examples("mxfp4")}
     assert any(failed.values()), f"no worked example detects: {name}"
