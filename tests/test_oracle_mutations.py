@@ -17,6 +17,7 @@ import json
 import os
 import shutil
 import subprocess
+from fractions import Fraction
 
 import numpy as np
 import pytest
@@ -200,3 +201,84 @@ def test_mx_examples_catch_a_deviation(tmp_path, name, old, new):
     L = _build_variant(tmp_path, old, new)
     failed = {ex["name"]: [k for k, ok in _outputs(L, ex).items() if not ok] for ex in _examples("mxfp4")}
     assert any(failed.values()), f"no worked example detects: {name}"
+
+
+# Deviations from reading R7 (Y = Bhat W^T + Rhat W^T, exact products summed in fp64;
+# SharQ, abstract: a sparse FP4 GEMM over the backbone and a dense FP4 GEMM over the
+# residual share one weight payload and their products are summed), each caught by
+# the exact-rational GEMM pin: Y computed from the payloads' values with Fractions.
+GEMM_MUTATIONS = [
+    ("residual product dropped", "      y[r * N + o] = yb + yr;", "      y[r * N + o] = yb; (void)yr;"),
+    ("backbone product dropped", "      y[r * N + o] = yb + yr;", "      y[r * N + o] = yr; (void)yb;"),
+    ("weight read transposed", "      const double* w = wd + o * K;", "      const double* w = wd + o;"),
+    ("fp32 accumulation", "      double yb = 0.0, yr = 0.0;", "      float yb = 0.0f, yr = 0.0f;"),
+    ("scale bias 128", "      out[i * K + k] = fmt == ORACLE_MXFP4 ? ldexp(v, (int)s - 127)",
+     "      out[i * K + k] = fmt == ORACLE_MXFP4 ? ldexp(v, (int)s - 128)"),
+]
+
+_E2M1 = [Fraction(0), Fraction(1, 2), Fraction(1), Fraction(3, 2), Fraction(2), Fraction(3), Fraction(4),
+         Fraction(6)]
+
+
+def _exact_mx_rows(codes, scales, K):
+    rows = []
+    for i in range(codes.shape[0]):
+        row = []
+        for k in range(K):
+            c = (codes[i, k // 2] >> (4 * (k & 1))) & 15
+            v = -_E2M1[c & 7] if c & 8 else _E2M1[c & 7]
+            row.append(v * Fraction(2) ** (int(scales[i, k // 32]) - 127))
+        rows.append(row)
+    return rows
+
+
+def _linear_variant(L, bb, rr, w, M, N, K):
+    u8p = np.ctypeslib.ndpointer(np.uint8, flags="C_CONTIGUOUS")
+    f64p = np.ctypeslib.ndpointer(np.float64, flags="C_CONTIGUOUS")
+    i64, f32 = ctypes.c_int64, ctypes.c_float
+    L.oracle_linear.restype = ctypes.c_int
+    L.oracle_linear.argtypes = [u8p, u8p, f32, u8p, u8p, f32, i64, u8p, u8p, f32, i64, i64, ctypes.c_int,
+                                ctypes.c_void_p, i64, f64p]
+    y = np.zeros((M, N), np.float64)
+    assert L.oracle_linear(bb.codes, bb.scales, 1.0, rr.codes, rr.scales, 1.0, M, w.codes, w.scales, 1.0, N, K,
+                           0, None, M, y) == 0
+    return y
+
+
+def _matches_exact(y, bb, rr, w, K):
+    B, R, W = (_exact_mx_rows(p.codes, p.scales, K) for p in (bb, rr, w))
+    for i in range(len(B)):
+        for o in range(len(W)):
+            exact = sum(B[i][k] * W[o][k] for k in range(K)) + sum(R[i][k] * W[o][k] for k in range(K))
+            mag = sum(abs(B[i][k] * W[o][k]) + abs(R[i][k] * W[o][k]) for k in range(K))
+            if abs(Fraction(y[i, o]) - exact) > Fraction(2 * K + 2) * Fraction(2) ** -53 * mag:
+                return False
+    return True
+
+
+def _gemm_case():
+    import oracle
+    from activation_sparsity_fp4_sharq_amd.workloads import make_activation
+    M, N, K = 3, 5, 96
+    rng = np.random.default_rng(7)
+    x = bf16_bits_to_f32(make_activation(rng, M, K, "normal", n_out=2, out_scale=20.0))
+    # blocks 2^14 apart, so partial sums need more than fp32's 24 bits
+    x = x * np.repeat(2.0 ** (14 * np.arange(K // 32)), 32)[None, :].astype(np.float32)
+    wb = f32_to_bf16_bits(rng.normal(0, 0.02, (N, K)).astype(np.float32))
+    bb, rr, _ = oracle.prep(f32_to_bf16_bits(x), 2, 4)
+    return bb, rr, oracle.quantize(wb), M, N, K
+
+
+@pytest.mark.skipif(shutil.which("gcc") is None, reason="needs gcc to build the oracle variants")
+def test_unmodified_copy_meets_the_exact_gemm(tmp_path):
+    bb, rr, w, M, N, K = _gemm_case()
+    L = _build_variant(tmp_path, "      y[r * N + o] = yb + yr;", "      y[r * N + o] = yb + yr;")
+    assert _matches_exact(_linear_variant(L, bb, rr, w, M, N, K), bb, rr, w, K)
+
+
+@pytest.mark.skipif(shutil.which("gcc") is None, reason="needs gcc to build the oracle variants")
+@pytest.mark.parametrize("name,old,new", GEMM_MUTATIONS, ids=[m[0] for m in GEMM_MUTATIONS])
+def test_exact_gemm_catches_a_deviation(tmp_path, name, old, new):
+    bb, rr, w, M, N, K = _gemm_case()
+    L = _build_variant(tmp_path, old, new)
+    assert not _matches_exact(_linear_variant(L, bb, rr, w, M, N, K), bb, rr, w, K), f"not detected: {name}"
