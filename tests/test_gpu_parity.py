@@ -18,7 +18,7 @@ import torch
 import layout_ref
 import oracle
 from activation_sparsity_fp4_sharq_amd import sharq
-from activation_sparsity_fp4_sharq_amd.workloads import (WORKLOADS, adversarial_activation,
+from activation_sparsity_fp4_sharq_amd.workloads import (WORKLOADS, adversarial_activation, bf16_bits_to_f32,
                                                           f32_to_bf16_bits, make_inputs, make_shape)
 
 pytestmark = pytest.mark.gpu
@@ -934,3 +934,76 @@ def test_mlp_block_chain_matches_oracle():
     yref = oracle.linear(ob2, or2, oracle.quantize(wdb, b.fmt), b.fmt)
     err = rel_maxnorm(y32.cpu().numpy().astype(np.float64), yref)
     assert err <= TOL, err
+
+
+# ------------------------------------------------------------------ beyond 32-bit offsets
+
+def _tiled_rows(p, rows):
+    """Row-major codes and scales of the given rows of a tiled MXFP4 payload, gathered on
+    the device by the layout's definition (codes: fragment (r//32, b//2) at byte
+    ((r//32) * Kp/64 + b//2) * 1024, slot (r%32) + 32 (b%2) of 16 bytes; scales: byte b%4
+    of word (b//4) * Rp + r), so only the sampled rows travel to the host."""
+    Rp, Kp = layout_ref.padded(p.rows, p.K)
+    nb = p.K // 32
+    r = torch.as_tensor(rows, dtype=torch.int64, device=p.codes.device)[:, None]
+    b = torch.arange(nb, dtype=torch.int64, device=p.codes.device)[None, :]
+    slot = ((r // 32) * (Kp // 64) + b // 2) * 1024 + ((r % 32) + 32 * (b % 2)) * 16
+    idx = (slot[:, :, None] + torch.arange(16, device=p.codes.device)).reshape(-1)
+    codes = p.codes[idx].reshape(len(rows), p.K // 2).cpu().numpy()
+    sidx = ((b // 4) * Rp + r) * 4 + b % 4
+    scales = p.scales[sidx.reshape(-1)].reshape(len(rows), nb).cpu().numpy()
+    return codes, scales
+
+
+def test_prep_and_linear_beyond_32bit_offsets():
+    """X of 2.2 M x 2048 bf16 (4.5 G elements, 9 GB): more row groups than one launch's
+    grid holds, code payloads past 2^31 bytes and X past 2^31 elements, so every 64-bit
+    offset of the preparation (tiled and row-major) and of the tiled GEMM is exercised.
+    X repeats a seeded 4096-row block, each repetition scaled by a power of two (exact in
+    bf16), so the oracle computes the sampled rows from the block alone (MXFP4 rows are
+    independent); the rows sampled sit at the launch and 2^31 boundaries and at the ends."""
+    M, K, N, base_rows = 2_200_000, 2048, 256, 4096
+    print(f"[big] prep + linear M={M} K={K} N={N} (sampled rows)", flush=True)
+    xb_base, wb = make_shape(base_rows, N, K, seed=2024, out_frac=0.01, out_scale=30.0)
+    shift = lambda i: (i // base_rows) % 7 - 3  # the power of two applied to row i
+    x = torch.empty((M, K), dtype=torch.bfloat16, device=DEV)
+    base = to_dev(xb_base)
+    for j in range((M + base_rows - 1) // base_rows):  # exact: power-of-two factors
+        n = min(base_rows, M - j * base_rows)
+        x[j * base_rows:j * base_rows + n] = base[:n] * (2.0 ** shift(j * base_rows))
+    del base
+    weight = sharq.quantize(to_dev(wb), sharq.MXFP4)
+
+    launch_rows = 65535 * 16
+    rows = sorted({0, 1, 31, 32, launch_rows - 1, launch_rows, launch_rows + 1, 2 * launch_rows,
+                   (1 << 31) // K - 1, (1 << 31) // K, (1 << 31) // (K // 2) - 1, (1 << 31) // (K // 2),
+                   (1 << 31) // (K // 2) + 33, M - 33, M - 32, M - 2, M - 1}
+                  | set(int(v) for v in np.random.default_rng(7).integers(0, M, 15)))
+    xs = np.stack([f32_to_bf16_bits(bf16_bits_to_f32(xb_base[i % base_rows]) * np.float32(2.0 ** shift(i)))
+                   for i in rows])
+    ob, orr, _ = oracle.prep(xs, 2, 4, sharq.MXFP4)
+    ow = oracle.quantize(wb, sharq.MXFP4)
+
+    bb, rr, _ = sharq.prep(x, 2, 4, sharq.MXFP4, layout=sharq.TILED)
+    torch.cuda.synchronize()
+    for p, want, what in ((bb, ob, "backbone"), (rr, orr, "residual")):
+        c, s = _tiled_rows(p, rows)
+        bad = np.nonzero((c != want.codes).any(axis=1) | (s != want.scales).any(axis=1))[0]
+        assert bad.size == 0, f"tiled {what}: rows {[rows[i] for i in bad[:8]]} differ"
+
+    y = sharq.linear(bb, rr, weight, out_dtype=sharq.OUT_FP32)
+    torch.cuda.synchronize()
+    ys = y[torch.as_tensor(rows, device=DEV)].cpu().numpy().astype(np.float64)
+    del y, bb, rr
+    yref = oracle.linear(ob, orr, ow)
+    assert rel_maxnorm(ys, yref) <= TOL
+    worst = fp32_bound_check(ys, yref, abs_linear(ob, orr, ow, sharq.MXFP4), K)
+    assert worst <= 1.0, f"sampled GEMM rows beyond the summation bound ({worst:.3g} of it)"
+
+    bb, rr, _ = sharq.prep(x, 2, 4, sharq.MXFP4, layout=sharq.ROWMAJOR)
+    torch.cuda.synchronize()
+    ridx = torch.as_tensor(rows, device=DEV)
+    for p, want, what in ((bb, ob, "backbone"), (rr, orr, "residual")):
+        c = p.codes.view(M, K // 2)[ridx].cpu().numpy()
+        s = p.scales.view(M, K // 32)[ridx].cpu().numpy()
+        assert np.array_equal(c, want.codes) and np.array_equal(s, want.scales), f"row-major {what} differs"
