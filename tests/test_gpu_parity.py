@@ -1002,8 +1002,57 @@ def test_prep_and_linear_beyond_32bit_offsets():
 
     bb, rr, _ = sharq.prep(x, 2, 4, sharq.MXFP4, layout=sharq.ROWMAJOR)
     torch.cuda.synchronize()
+    del x
     ridx = torch.as_tensor(rows, device=DEV)
     for p, want, what in ((bb, ob, "backbone"), (rr, orr, "residual")):
         c = p.codes.view(M, K // 2)[ridx].cpu().numpy()
         s = p.scales.view(M, K // 32)[ridx].cpu().numpy()
         assert np.array_equal(c, want.codes) and np.array_equal(s, want.scales), f"row-major {what} differs"
+    # the row-major GEMM over the same (row-major) payloads
+    y = sharq.linear(bb, rr, weight.convert(sharq.ROWMAJOR), out_dtype=sharq.OUT_FP32)
+    torch.cuda.synchronize()
+    ys = y[ridx].cpu().numpy().astype(np.float64)
+    del y
+    worst = fp32_bound_check(ys, yref, abs_linear(ob, orr, ow, sharq.MXFP4), K)
+    assert worst <= 1.0, f"row-major GEMM rows beyond the summation bound ({worst:.3g} of it)"
+
+
+@pytest.mark.parametrize("K", [1024, 1040])
+def test_linear_nvfp4_payloads_past_2gib(K):
+    """NVFP4 GEMM with activation payloads past 2 GiB (rows x K/2 >= 2^31 bytes): the
+    kernels taken there (streaming for K % 64 == 0, register-staged otherwise) against the
+    oracle on sampled rows.  The payloads are seeded synthetic FP4 data (random codes, E4M3
+    block scales around 1, tensor scales that are not powers of two) repeating a 4096-row
+    block, so the oracle sees only the block's rows; none comes from the library."""
+    M, N, base_rows = ((1 << 31) // (K // 2)) + 4100, 128, 4096
+    print(f"[big] nvfp4 linear M={M} N={N} K={K} (sampled rows)", flush=True)
+    rng = np.random.default_rng(99 + K)
+
+    def synth(rows, tscale):
+        codes = rng.integers(0, 256, (rows, K // 2), dtype=np.uint8)
+        scales = rng.integers(0x28, 0x49, (rows, K // 16), dtype=np.uint8)
+        return oracle.Payload(codes, scales, np.float32(tscale))
+
+    ob, orr, ow = synth(base_rows, 0.7), synth(base_rows, 0.03125 * 1.3), synth(N, 0.011)
+
+    def dev_payload(p, rows):
+        reps = (rows + base_rows - 1) // base_rows
+        codes = torch.from_numpy(p.codes).to(DEV).repeat(reps, 1)[:rows].contiguous().view(-1)
+        scales = torch.from_numpy(p.scales).to(DEV).repeat(reps, 1)[:rows].contiguous().view(-1)
+        ts = torch.full((4,), float(p.tscale), dtype=torch.float32, device=DEV)
+        return sharq.Payload(codes, scales, ts, sharq.NVFP4, sharq.ROWMAJOR, rows, K)
+
+    bb, rr, w = dev_payload(ob, M), dev_payload(orr, M), dev_payload(ow, N)
+    y = sharq.linear(bb, rr, w, out_dtype=sharq.OUT_FP32)
+    torch.cuda.synchronize()
+    rows = sorted({0, 1, 127, 128, (1 << 31) // (K // 2) - 1, (1 << 31) // (K // 2), M - 129, M - 1}
+                  | set(int(v) for v in np.random.default_rng(5).integers(0, M, 8)))
+    ys = y[torch.as_tensor(rows, device=DEV)].cpu().numpy().astype(np.float64)
+    del y, bb, rr
+    pick = [i % base_rows for i in rows]
+    sb = oracle.Payload(ob.codes[pick], ob.scales[pick], ob.tscale)
+    sr = oracle.Payload(orr.codes[pick], orr.scales[pick], orr.tscale)
+    yref = oracle.linear(sb, sr, ow, sharq.NVFP4)
+    assert rel_maxnorm(ys, yref) <= TOL
+    worst = fp32_bound_check(ys, yref, abs_linear(sb, sr, ow, sharq.NVFP4), K)
+    assert worst <= 1.0, f"sampled rows beyond the summation bound ({worst:.3g} of it)"
