@@ -1056,3 +1056,30 @@ def test_linear_nvfp4_payloads_past_2gib(K):
     assert rel_maxnorm(ys, yref) <= TOL
     worst = fp32_bound_check(ys, yref, abs_linear(sb, sr, ow, sharq.NVFP4), K)
     assert worst <= 1.0, f"sampled rows beyond the summation bound ({worst:.3g} of it)"
+
+
+def test_prep_nvfp4_beyond_32bit_elements():
+    """NVFP4 preparation of X with more than 2^31 elements (1.1 M x 2048 bf16).  X repeats
+    one seeded 4096-row block unchanged, so both tensor maxima -- of X and of the residual
+    -- are the block's, and the oracle's preparation of the block alone fixes every row's
+    payload and both tensor scales; rows sampled at the 2^31-element boundary, the ends
+    and at random are compared bit for bit."""
+    M, K, base_rows = 1_100_000, 2048, 4096
+    print(f"[big] nvfp4 prep M={M} K={K} (sampled rows)", flush=True)
+    xb_base, _ = make_shape(base_rows, 16, K, seed=404, dist="laplace", out_frac=0.01, out_scale=20.0)
+    reps = (M + base_rows - 1) // base_rows
+    x = to_dev(xb_base).repeat(reps, 1)[:M].contiguous()
+    bb, rr, _ = sharq.prep(x, 2, 4, sharq.NVFP4)
+    torch.cuda.synchronize()
+    del x
+    ob, orr, _ = oracle.prep(xb_base, 2, 4, sharq.NVFP4)
+    rows = sorted({0, 1, (1 << 31) // K - 1, (1 << 31) // K, (1 << 31) // K + 1, M - 2, M - 1}
+                  | set(int(v) for v in np.random.default_rng(3).integers(0, M, 12)))
+    ridx = torch.as_tensor(rows, device=DEV)
+    pick = [i % base_rows for i in rows]
+    for p, want, what in ((bb, ob, "backbone"), (rr, orr, "residual")):
+        c = p.codes.view(M, K // 2)[ridx].cpu().numpy()
+        s = p.scales.view(M, K // 16)[ridx].cpu().numpy()
+        assert np.array_equal(c, want.codes[pick]), f"{what} codes differ"
+        assert np.array_equal(s, want.scales[pick]), f"{what} scales differ"
+        assert np.float32(p.tensor_scale[0].item()) == np.float32(want.tscale), f"{what} tensor scale differs"
