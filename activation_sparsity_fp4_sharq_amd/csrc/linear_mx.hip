@@ -63,6 +63,7 @@ struct Args {
   bool y_aligned;      // y 16-byte aligned and ldy a multiple of 8 elements
   int splits;          // K split across this many work-groups per tile (1: none)
   float* part;         // fp32 partial sums [splits][M][N] when splits > 1
+  int64_t wsp;         // row pitch of the weight's tiled scale words (its whole payload's padded rows)
 };
 
 // An FP4 operand is the low 4 dwords of the instruction's 8-dword operand; the upper
@@ -403,9 +404,13 @@ __device__ __forceinline__ void store_partial(float* part, int64_t M, int64_t N,
 
 // SPLIT: work-group s of a tile sums the K-steps
 // [s*steps/splits, (s+1)*steps/splits) and stores its fp32 tile into part[s]; the
-// partials are summed in order by reduce_splits_kernel.
-template <bool OUT_F32, bool DUAL, bool SPLIT>
+// partials are summed in order by reduce_splits_kernel.  TN: tile columns, 256 or 128
+// (each wave then owns 64 x TN/2 outputs: TN/64 instructions across per path and row tile).
+template <bool OUT_F32, bool DUAL, bool SPLIT, int TN = BN>
 __global__ __launch_bounds__(kThreads, 1) void linear_mx_dma_kernel(Args a) {
+  static_assert(TN == 256 || TN == 128, "tile columns");
+  static_assert(!SPLIT || TN == 256, "the K split runs 256-column tiles");
+  constexpr int NT = TN / 64;  // 32-column instruction tiles per wave
   extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -425,7 +430,7 @@ __global__ __launch_bounds__(kThreads, 1) void linear_mx_dma_kernel(Args a) {
   } else {
     tile_of(blockIdx.x, a.tiles_m, a.tiles_n, tm, tn);
   }
-  const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
+  const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * TN;
   int nk = (int)(a.Kp / 128);
   int k0 = 0;  // first K-step
   if constexpr (SPLIT) {
@@ -434,10 +439,11 @@ __global__ __launch_bounds__(kThreads, 1) void linear_mx_dma_kernel(Args a) {
     nk = (split + 1) * steps / a.splits - k0;
   }
 
-  // Each wave fills 6 of the 48 fragments of a stage (A_b, A_r, W x 16; 4 of 32
-  // without A_b): one contiguous 1 KiB fragment of the tiled payload per load.  Row
-  // tiles past the padded extent are clamped to the last one (computed, never stored).
-  constexpr int kFragLoads = DUAL ? 6 : 4;
+  // Each wave fills 6 of the 48 fragments of a stage (A_b, A_r x 16, W x TN/16; 4 of 32
+  // without A_b; 5 of 40 and 3 of 24 with 128 columns): one contiguous 1 KiB fragment of
+  // the tiled payload per load.  Row tiles past the padded extent are clamped to the last
+  // one (computed, never stored).
+  constexpr int kFragLoads = ((DUAL ? 32 : 16) + TN / 16) / 8;
   constexpr int kOp0 = DUAL ? 0 : 1;  // first activation operand present
   const uint8_t* fsrc[6];  // (fixed extent: a template-dependent one drops the host launch stub)
   int fdst[6];
@@ -469,7 +475,7 @@ __global__ __launch_bounds__(kThreads, 1) void linear_mx_dma_kernel(Args a) {
     const int64_t rp = op == 2 ? a.Np : a.Mp;
     const int64_t row0 = op == 2 ? n0 : m0;
     ssrc = base + row0 * 4;  // wave-uniform; lane adds 16 * lane (4 rows)
-    sstep = rp * 4;
+    sstep = (op == 2 ? a.wsp : rp) * 4;
     if constexpr (SPLIT) ssrc += k0 * sstep;
     sbytes = (uint32_t)((rp - row0) * 4 < 1024 ? (rp - row0) * 4 : 1024);
     sdst = 3 * kOpTileBytes + op * 1024;
@@ -486,11 +492,11 @@ __global__ __launch_bounds__(kThreads, 1) void linear_mx_dma_kernel(Args a) {
       buffer_lds16(ssrc + kc * sstep, sbytes, st + sdst, 16 * lane);
   };
 
-  v16f acc[2][4];
+  v16f acc[2][NT];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = v16f{};
+    for (int j = 0; j < NT; ++j) acc[i][j] = v16f{};
 
   // Software pipeline across the K-steps, one barrier per step placed between its two
   // sub-steps, so the LDS latency of every fragment read hides under matrix work:
@@ -500,7 +506,7 @@ __global__ __launch_bounds__(kThreads, 1) void linear_mx_dma_kernel(Args a) {
   //   [C] read scales + sub-step 0 fragments of ks+1  |  16 MFMA on sub-step 1 of ks,
   //       with the DMA of stage ks+3 into slot ks%3 spread between them
   // (stages past the last are clamped re-loads into slots nobody reads)
-  auto read_frags = [&](v4i (&af)[2][2], v4i (&wf)[4], const uint8_t* st, int sub) {
+  auto read_frags = [&](v4i (&af)[2][2], v4i (&wf)[NT], const uint8_t* st, int sub) {
 #pragma unroll
     for (int p = kOp0; p < 2; ++p)
 #pragma unroll
@@ -508,40 +514,40 @@ __global__ __launch_bounds__(kThreads, 1) void linear_mx_dma_kernel(Args a) {
         af[p][mt] = *reinterpret_cast<const v4i*>(st + p * kOpTileBytes + ((wm * 2 + mt) * 2 + sub) * kFragBytes +
                                                   lane * 16);
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt)
-      wf[nt] = *reinterpret_cast<const v4i*>(st + 2 * kOpTileBytes + ((wn * 4 + nt) * 2 + sub) * kFragBytes +
+    for (int nt = 0; nt < NT; ++nt)
+      wf[nt] = *reinterpret_cast<const v4i*>(st + 2 * kOpTileBytes + ((wn * NT + nt) * 2 + sub) * kFragBytes +
                                              lane * 16);
   };
-  auto read_scales = [&](uint32_t (&as)[2][2], uint32_t (&ws)[4], const uint8_t* st) {
+  auto read_scales = [&](uint32_t (&as)[2][2], uint32_t (&ws)[NT], const uint8_t* st) {
     const uint32_t* sc = reinterpret_cast<const uint32_t*>(st + 3 * kOpTileBytes);
 #pragma unroll
     for (int p = kOp0; p < 2; ++p)
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt) as[p][mt] = sc[p * 256 + wm * 64 + mt * 32 + r32];
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) ws[nt] = sc[512 + wn * 128 + nt * 32 + r32];
+    for (int nt = 0; nt < NT; ++nt) ws[nt] = sc[512 + wn * (TN / 2) + nt * 32 + r32];
   };
-  // 16 matrix instructions of one sub-step; with ISSUE, the loads of stage ld spread
-  // between them (one per kEvery instructions)
-  auto mma = [&](const v4i (&af)[2][2], const v4i (&wf)[4], const uint32_t (&as)[2][2], const uint32_t (&ws)[4],
+  // The matrix instructions of one sub-step (16 with both paths and 256 columns); with
+  // ISSUE, the loads of stage ld spread between them (one per kEvery instructions)
+  auto mma = [&](const v4i (&af)[2][2], const v4i (&wf)[NT], const uint32_t (&as)[2][2], const uint32_t (&ws)[NT],
                  auto sub_c, auto issue_c, int ld) {
     constexpr int SUB = decltype(sub_c)::value;
     constexpr bool ISSUE = decltype(issue_c)::value;
-    constexpr int kPerSub = 8 * (2 - kOp0), kEvery = kPerSub / kLoads;
+    constexpr int kPerSub = 2 * NT * (2 - kOp0), kEvery = kPerSub / kLoads;
     static_assert(kEvery >= 1 && kPerSub / kEvery >= kLoads, "every load of a stage must be issued");
 #pragma unroll
     for (int p = kOp0; p < 2; ++p)
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt) {
+        for (int nt = 0; nt < NT; ++nt) {
           // weights as the instruction's A operand: each lane's accumulators are then
           // 4 consecutive output columns of one output row (see store_swapped)
           acc[mt][nt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
               widen(wf[nt]), widen(af[p][mt]), acc[mt][nt], 4, 4, 2 * SUB, (int)(ws[nt] >> (8 * h)), 2 * SUB,
               (int)(as[p][mt] >> (8 * h)));
           if constexpr (ISSUE) {
-            const int i = ((p - kOp0) * 2 + mt) * 4 + nt;
+            const int i = ((p - kOp0) * 2 + mt) * NT + nt;
             if (i % kEvery == kEvery - 1 && i / kEvery < kLoads) {
               issue_one(i / kEvery, ld);
               __builtin_amdgcn_sched_barrier(0);  // keep the loads spread between the instructions
@@ -560,8 +566,8 @@ __global__ __launch_bounds__(kThreads, 1) void linear_mx_dma_kernel(Args a) {
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
 
-  v4i af0[2][2], wf0[4], af1[2][2], wf1[4];
-  uint32_t as[2][2], ws[4], asn[2][2], wsn[4];
+  v4i af0[2][2], wf0[NT], af1[2][2], wf1[NT];
+  uint32_t as[2][2], ws[NT], asn[2][2], wsn[NT];
   read_scales(as, ws, smem);
   read_frags(af0, wf0, smem, 0);
   using C0 = std::integral_constant<int, 0>;
@@ -592,7 +598,7 @@ __global__ __launch_bounds__(kThreads, 1) void linear_mx_dma_kernel(Args a) {
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt) as[p][mt] = asn[p][mt];
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) ws[nt] = wsn[nt];
+    for (int nt = 0; nt < NT; ++nt) ws[nt] = wsn[nt];
   }
   SHARQ_WAIT_VMCNT(0);  // trailing loads land before the stage ring is reused
 
@@ -601,8 +607,8 @@ __global__ __launch_bounds__(kThreads, 1) void linear_mx_dma_kernel(Args a) {
     store_partial(a.part + (int64_t)split * a.M * a.N, a.M, a.N, acc, m0 + wm * 64, n0 + wn * 128, lane,
                   smem + wave * (32 * (128 * 4 + 16)));
   } else {
-    store_swapped<OUT_F32, 2, 4>(a, acc, m0 + wm * 64, n0 + wn * 128, lane,
-                                 smem + wave * (64 * (256 + kEpiPad)), a.y_aligned);
+    store_swapped<OUT_F32, 2, NT>(a, acc, m0 + wm * 64, n0 + wn * (TN / 2), lane,
+                                  smem + wave * (64 * (NT * 64 + kEpiPad)), a.y_aligned);
   }
 }
 
@@ -659,19 +665,31 @@ __global__ __launch_bounds__(256) void reduce_splits_kernel(const float* __restr
 
 // The dynamic-LDS limit is a per-device function attribute, set once per kernel and device
 // (setting it twice is harmless).
-template <bool OUT_F32, bool DUAL, bool SPLIT>
+template <bool OUT_F32, bool DUAL, bool SPLIT, int TN = BN>
 hipError_t configure_dma() {
   static std::atomic<bool> configured[kMaxDevices];
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
   if (dev < 0 || dev >= kMaxDevices || !configured[dev].load(std::memory_order_acquire)) {
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&linear_mx_dma_kernel<OUT_F32, DUAL, SPLIT>),
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&linear_mx_dma_kernel<OUT_F32, DUAL, SPLIT, TN>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, kDmaStages * kDmaStageBytes);
     if (e != hipSuccess) return e;
     if (dev >= 0 && dev < kMaxDevices) configured[dev].store(true, std::memory_order_release);
   }
   return hipSuccess;
+}
+
+// Columns of 256-wide tiles to run as a tail of 128-wide tiles (0: none): when the tiles
+// overflow whole waves of work-groups (one per compute unit) by at most half a wave and
+// that overflow is whole tile columns, so the tail's 256 x 128 tiles fill at most one wave.
+constexpr int kWave = 256;  // work-groups of this kernel resident at once (one per compute unit)
+
+int tail_columns(int tiles_m, int tiles_n) {
+  const int64_t tiles = (int64_t)tiles_m * tiles_n;
+  const int64_t rem = tiles % kWave;
+  if (tiles <= kWave || rem == 0 || rem % tiles_m != 0 || 2 * rem > kWave) return 0;
+  return (int)(rem / tiles_m);
 }
 
 template <bool OUT_F32, bool DUAL>
@@ -690,9 +708,35 @@ hipError_t launch_dma(const Args& a, hipStream_t stream) {
         a.part, a.splits, a.M, a.N, a.y, a.ldy, vec_y);
     return hipGetLastError();
   }
+  // A last wave of work-groups that would run at most half full (tiles % 256 <= 128,
+  // whole tile columns) is run instead as one wave of 256 x 128 tiles over those columns,
+  // after the whole waves: the head and tail are two products over disjoint column
+  // ranges of W and Y (the weight's scale words keep the whole payload's pitch).
+  const int tail_cols = tail_columns(a.tiles_m, a.tiles_n);
   hipError_t e = configure_dma<OUT_F32, DUAL, false>();
   if (e != hipSuccess) return e;
-  linear_mx_dma_kernel<OUT_F32, DUAL, false><<<dim3(tiles), dim3(kThreads), kDmaStages * kDmaStageBytes, stream>>>(a);
+  if (tail_cols == 0) {
+    linear_mx_dma_kernel<OUT_F32, DUAL, false><<<dim3(tiles), dim3(kThreads), kDmaStages * kDmaStageBytes, stream>>>(a);
+    return hipGetLastError();
+  }
+  Args head = a, tail = a;
+  const int64_t n1 = (int64_t)(a.tiles_n - tail_cols) * BN;  // first column of the tail
+  head.N = n1;
+  head.Np = n1;
+  head.tiles_n = a.tiles_n - tail_cols;
+  linear_mx_dma_kernel<OUT_F32, DUAL, false>
+      <<<dim3(head.tiles_m * head.tiles_n), dim3(kThreads), kDmaStages * kDmaStageBytes, stream>>>(head);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  tail.N = a.N - n1;
+  tail.Np = a.Np - n1;
+  tail.tiles_n = (int)((tail.N + 127) / 128);
+  tail.wc = a.wc + (n1 / 32) * (a.Kp / 64) * kFragBytes;  // row tiles n1/32 onwards
+  tail.ws = a.ws + n1 * 4;                                // scale word (ks, n1 + r) at ks * wsp + n1 + r
+  tail.y = static_cast<uint8_t*>(a.y) + n1 * (OUT_F32 ? 4 : 2);
+  tail.y_aligned = a.y_aligned;  // n1 is a multiple of 256 columns
+  if ((e = configure_dma<OUT_F32, DUAL, false, 128>()) != hipSuccess) return e;
+  linear_mx_dma_kernel<OUT_F32, DUAL, false, 128>
+      <<<dim3(tail.tiles_m * tail.tiles_n), dim3(kThreads), kDmaStages * kDmaStageBytes, stream>>>(tail);
   return hipGetLastError();
 }
 
@@ -894,7 +938,7 @@ hipError_t launch_linear_mx(const sharq_fp4* b, const sharq_fp4& r, int64_t M, c
   Args a{b ? b->codes : nullptr, b ? b->scales : nullptr, r.codes, r.scales, w.codes, w.scales, y, M, N, K, ldy,
          (int)((M + BM - 1) / BM), (int)((N + BN - 1) / BN), round_up(M, 32), round_up(N, 32), round_up(K, 128),
          (reinterpret_cast<uintptr_t>(y) & 15u) == 0 && ldy % 8 == 0, splits,
-         splits > 1 ? reinterpret_cast<float*>(workspace) : nullptr};
+         splits > 1 ? reinterpret_cast<float*>(workspace) : nullptr, round_up(N, 32)};
   return b ? dispatch<true>(a, tiled, out_fp32, stream) : dispatch<false>(a, tiled, out_fp32, stream);
 }
 

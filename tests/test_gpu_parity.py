@@ -560,6 +560,46 @@ def test_linear_large_tiles_strided_output(fmt, M, N, K):
         assert np.array_equal(rows[:, :N], ref), f"ld={ld}: values differ from the contiguous output"
 
 
+@pytest.mark.parametrize("M,N,K", [(400, 32974, 256), (2048, 8448, 128), (512, 40960, 64)])
+def test_linear_tail_of_half_width_tiles(M, N, K):
+    """Shapes whose 256 x 256 tiles overflow whole waves of work-groups by at most half a
+    wave of whole tile columns (258 tiles: one column of 2; 264: one of 8; 320: 32 of 2)
+    run those columns as a second launch of 256 x 128 tiles.  Every output of both paths
+    and of the one-operand form is compared with the oracle (fp32 per-element bound, bf16
+    one ulp plus the bound), and a padded, odd row pitch gets the same values with nothing
+    written into its padding."""
+    print(f"[linear] tail columns M={M} N={N} K={K}", flush=True)
+    xb, wb = make_shape(M, N, K, seed=17)
+    weight = sharq.quantize(to_dev(wb), sharq.MXFP4)
+    bb, rr, _ = sharq.prep(to_dev(xb), 2, 4, sharq.MXFP4)
+    y32 = sharq.linear(bb, rr, weight, sharq.OUT_FP32)
+    y16 = sharq.linear(bb, rr, weight, sharq.OUT_BF16)
+    yd = sharq.linear_dense(rr, weight, sharq.OUT_FP32)
+    torch.cuda.synchronize()
+    ob, orr, _ = oracle.prep(xb, 2, 4, sharq.MXFP4)
+    ow = oracle.quantize(wb, sharq.MXFP4)
+    yref = oracle.linear(ob, orr, ow)
+    abssum = abs_linear(ob, orr, ow, sharq.MXFP4)
+    y = y32.cpu().numpy().astype(np.float64)
+    assert rel_maxnorm(y, yref) <= TOL
+    assert fp32_bound_check(y, yref, abssum, K) <= 1.0, "fp32 output beyond the summation bound"
+    assert bf16_bound_check(y16, yref, abssum, K) <= 1.0, "bf16 output beyond one ulp + the bound"
+    dref = oracle.linear_dense(orr, ow)
+    dabs = np.abs(oracle.dequant(orr, sharq.MXFP4)) @ np.abs(oracle.dequant(ow, sharq.MXFP4)).T
+    assert fp32_bound_check(yd.cpu().numpy().astype(np.float64), dref, dabs, K) <= 1.0, "one-operand form"
+    ref = y16.view(torch.int16).cpu().numpy()
+    ld = N + 3
+    big = torch.full(((M + 1) * ld,), -1, dtype=torch.int16, device=DEV)  # 0xFFFF: a bf16 NaN
+    yp = big.view(torch.bfloat16)[:M * ld].view(M, ld)[:, :N]
+    sharq.linear(bb, rr, weight, sharq.OUT_BF16, y=yp)
+    torch.cuda.synchronize()
+    out = big.cpu().numpy()
+    assert np.all(out[M * ld:] == -1), "write past the output"
+    rows = out[:M * ld].reshape(M, ld)
+    assert np.all(rows[:, N:] == -1), "write into the row padding"
+    assert np.array_equal(rows[:, :N], ref), "values differ from the contiguous output"
+
+
 # ------------------------------------------------------------------ layouts
 
 @pytest.mark.parametrize("rows,K", [(1, 32), (37, 96), (300, 1056), (64, 4096)])
