@@ -78,6 +78,8 @@ CASES = [
     (300, 384, 640, sharq.MXFP4, 8, sharq.TILED),      # tiled LDS-DMA kernel, ragged M and N
     (200, 160, 384, sharq.MXFP4, 4, sharq.ROWMAJOR),  # row-major kernel
     (130, 256, 512, sharq.NVFP4, 4, None),             # NVFP4: three preparation passes + reductions
+    (600, 512, 8192, sharq.MXFP4, 4, sharq.TILED),     # 6 tiles: K split in four + the ordered reduction
+    (400, 32974, 128, sharq.MXFP4, 8, sharq.TILED),    # 258 tiles: 256 + a tail of 128-column tiles
 ]
 
 
@@ -90,7 +92,8 @@ def make_step(M, N, K, fmt, m, layout):
     rr = sharq.Payload.empty(M, K, fmt, DEV, **kw)
     y = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
     ws = sharq.workspace(max(sharq.lib().sharq_prep_workspace_bytes(M, K, fmt),
-                             sharq.lib().sharq_linear_workspace_bytes(M, N, K, fmt)), DEV)
+                             sharq.lib().sharq_linear_workspace_bytes(M, N, K, fmt),
+                             sharq.lib().sharq_linear_split_workspace_bytes(M, N, K, fmt)), DEV)
 
     def step():
         sharq.prep(x, m // 2, m, fmt, out=(bb, rr), ws=ws)
