@@ -481,8 +481,8 @@ __global__ __launch_bounds__(kThreads, 1) void linear_mx_dma_kernel(Args a) {
     sdst = 3 * kOpTileBytes + op * 1024;
   }
   constexpr int kLoads = kFragLoads + 1;  // per wave and stage
-  // load j of stage ks (indices past the last K-step re-load the last one into a slot
-  // nobody reads again, keeping the count per iteration constant)
+  // load j of stage ks (a stage past the last K-step -- only the prologue's, when K has
+  // fewer than three steps -- re-loads the last one into a slot nobody reads)
   auto issue_one = [&](int j, int ks) {
     uint8_t* st = smem + (ks % kDmaStages) * kDmaStageBytes;
     const int64_t kc = ks < nk ? ks : nk - 1;
@@ -505,7 +505,7 @@ __global__ __launch_bounds__(kThreads, 1) void linear_mx_dma_kernel(Args a) {
   //       barrier: stage ks+1 visible, slot ks%3 free
   //   [C] read scales + sub-step 0 fragments of ks+1  |  16 MFMA on sub-step 1 of ks,
   //       with the DMA of stage ks+3 into slot ks%3 spread between them
-  // (stages past the last are clamped re-loads into slots nobody reads)
+  // (the last three K-steps issue no loads: the stages they read are already in flight)
   auto read_frags = [&](v4i (&af)[2][2], v4i (&wf)[NT], const uint8_t* st, int sub) {
 #pragma unroll
     for (int p = kOp0; p < 2; ++p)
@@ -574,7 +574,10 @@ __global__ __launch_bounds__(kThreads, 1) void linear_mx_dma_kernel(Args a) {
   using C1 = std::integral_constant<int, 1>;
   using NoIssue = std::integral_constant<bool, false>;
   using Issue = std::integral_constant<bool, true>;
-  for (int ks = 0; ks < nk; ++ks) {
+  // One K-step.  ISSUE: the loads of stage ks+3 go out during it; WAIT: the loads this
+  // wave may leave in flight at the barrier (the stage after ks has landed then).
+  auto kstep = [&](int ks, auto issue_c, auto wait_c) {
+    constexpr int WAIT = decltype(wait_c)::value;
     const uint8_t* st = smem + (ks % kDmaStages) * kDmaStageBytes;
     const uint8_t* nx = smem + ((ks + 1) % kDmaStages) * kDmaStageBytes;
     // [A]
@@ -583,7 +586,7 @@ __global__ __launch_bounds__(kThreads, 1) void linear_mx_dma_kernel(Args a) {
     mma(af0, wf0, as, ws, C0{}, NoIssue{}, 0);
     // [B]
     __builtin_amdgcn_sched_barrier(0);
-    SHARQ_WAIT_VMCNT(kLoads);            // this wave's loads of stage ks+1 landed
+    SHARQ_WAIT_VMCNT(WAIT);              // this wave's loads of stage ks+1 landed
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's reads of stage ks are done
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
@@ -592,14 +595,23 @@ __global__ __launch_bounds__(kThreads, 1) void linear_mx_dma_kernel(Args a) {
     read_scales(asn, wsn, nx);
     read_frags(af0, wf0, nx, 0);
     __builtin_amdgcn_sched_barrier(0);
-    mma(af1, wf1, as, ws, C1{}, Issue{}, ks + 3);
+    mma(af1, wf1, as, ws, C1{}, issue_c, ks + 3);
 #pragma unroll
     for (int p = 0; p < 2; ++p)
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt) as[p][mt] = asn[p][mt];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) ws[nt] = wsn[nt];
-  }
+  };
+  using Keep = std::integral_constant<int, kLoads>;
+  using None = std::integral_constant<int, 0>;
+  // every K-step but the last three loads a stage three ahead; those three load nothing
+  // (all the stages they read are in flight), so no stage past the last is fetched
+  const int nmain = nk > 3 ? nk - 3 : 0;
+  for (int ks = 0; ks < nmain; ++ks) kstep(ks, Issue{}, Keep{});
+  if (nk >= 3) kstep(nk - 3, NoIssue{}, Keep{});
+  if (nk >= 2) kstep(nk - 2, NoIssue{}, None{});
+  kstep(nk - 1, NoIssue{}, None{});
   SHARQ_WAIT_VMCNT(0);  // trailing loads land before the stage ring is reused
 
   __syncthreads();  // every wave is done with the stage ring; reuse it for the epilogue
