@@ -66,6 +66,14 @@
  *      row_sumsq) -- an order any split of the row into aligned power-of-two pieces
  *      reproduces exactly.
  *
+ * Pins (tests/test_oracle_pins.py, tests/test_oracle_mutations.py): every reading above is
+ * checked against brute force, exact rational arithmetic, closed forms, invariants or a
+ * hand-worked example, and a planted deviation from it fails one of them.  One part is
+ * pinned only through an error bound: the fp32 steps of R14's exponential agree with the
+ * mathematical SiLU to within 4 fp32 ulps (every bf16 gate in [-100, 100]) and on its
+ * closed forms, but another correct evaluation (a library expf, a degree-6 polynomial)
+ * stays within that bound, so those steps' exact bits are parity unpinned.
+ *
  * Compile: gcc -O2 -ffp-contract=off -fno-fast-math -fopenmp -shared -fPIC.
  * The row loops carry an OpenMP pragma; every output element has a fixed
  * evaluation order, so results do not depend on the thread count.

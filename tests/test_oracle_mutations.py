@@ -282,3 +282,90 @@ def test_exact_gemm_catches_a_deviation(tmp_path, name, old, new):
     bb, rr, w, M, N, K = _gemm_case()
     L = _build_variant(tmp_path, old, new)
     assert not _matches_exact(_linear_variant(L, bb, rr, w, M, N, K), bb, rr, w, K), f"not detected: {name}"
+
+
+# Deviations from reading R9 (RMS normalization folded into the preparation) and R14 (the
+# MLP block's SwiGLU), each planted in a copy of the oracle, which then serves the pins of
+# tests/test_oracle_pins.py (through the oracle module, its library swapped for the copy's):
+# at least one pin must fail.  Not caught, and so pinned only through their error bound
+# against the mathematical value: R14's exponential evaluated by another correct method
+# (a library expf, or a degree-6 instead of a degree-7 polynomial) -- both stay within the
+# 4-ulp bound of the fp64 SiLU that the pins check.
+R9_MUTATIONS = [
+    ("mean over K + 1", "    const float r = (float)(1.0 / sqrt(ss / (double)K + (double)eps));",
+     "    const float r = (float)(1.0 / sqrt(ss / (double)(K + 1) + (double)eps));"),
+    ("eps outside the root", "    const float r = (float)(1.0 / sqrt(ss / (double)K + (double)eps));",
+     "    const float r = (float)(1.0 / (sqrt(ss / (double)K) + (double)eps));"),
+    ("r in fp32", "    const float r = (float)(1.0 / sqrt(ss / (double)K + (double)eps));",
+     "    const float r = 1.0f / sqrtf((float)(ss / (double)K) + eps);"),
+    ("gain applied first", "      const float t = bf16_to_f32(x[i * ldx + k]) * r;\n      const float u = t * bf16_to_f32(g[k]);",
+     "      const float t = bf16_to_f32(x[i * ldx + k]) * bf16_to_f32(g[k]);\n      const float u = t * r;"),
+    ("r and gain in one product", "      const float t = bf16_to_f32(x[i * ldx + k]) * r;\n      const float u = t * bf16_to_f32(g[k]);",
+     "      const float u = bf16_to_f32(x[i * ldx + k]) * (r * bf16_to_f32(g[k]));"),
+    ("sum of squares left to right", "  for (int64_t w = p; w > 1; w /= 2)\n    for (int64_t j = 0; j < w / 2; ++j) v[j] = v[2 * j] + v[2 * j + 1];",
+     "  for (int64_t j = 1; j < p; ++j) v[0] = v[0] + v[j];"),
+    ("bf16 by truncation", "      y[i * K + k] = f32_to_bf16(u);",
+     "      { union { float f; uint32_t b; } c; c.f = u; y[i * K + k] = (uint16_t)(c.b >> 16); }"),
+]
+R14_MUTATIONS = [
+    ("gate and up swapped", "      h[i * I + k] = f32_to_bf16(oracle_silu(g) * u);",
+     "      h[i * I + k] = f32_to_bf16(oracle_silu(u) * g);"),
+    ("logistic without the 1", "  const float d = 1.0f + swiglu_exp_neg(g);", "  const float d = swiglu_exp_neg(g);"),
+    ("ln 2 without its low part", "  const float r = (t - n * ln2_hi) - n * ln2_lo;",
+     "  const float r = t - n * ln2_hi; (void)ln2_lo;"),
+    ("exponent clamped at 80", "  if (t > 150.0f) t = 150.0f;", "  if (t > 80.0f) t = 80.0f;"),
+]
+
+
+def _pins_fail(tmp_path, old, new, calls):
+    import oracle
+    _build_variant(tmp_path, old, new)  # writes liboracle_variant.so
+    saved = (oracle._lib, oracle._LIB_PATH)
+    oracle._lib, oracle._LIB_PATH = None, str(tmp_path / "liboracle_variant.so")
+    try:
+        oracle.lib()
+        failed = []
+        for name, call in calls:
+            try:
+                call()
+            except AssertionError:
+                failed.append(name)
+        return failed
+    finally:
+        oracle._lib, oracle._LIB_PATH = saved
+
+
+def _r9_pins():
+    import test_oracle_pins as p
+    return [("closed forms", p.test_rmsnorm_closed_forms),
+            ("unit mean square", p.test_rmsnorm_unit_mean_square_with_unit_gain),
+            ("power-of-two input scaling", lambda: p.test_rmsnorm_invariant_under_power_of_two_input_scaling(3)),
+            ("power-of-two gain", lambda: p.test_rmsnorm_gain_power_of_two_is_exact(2)),
+            ("small-integer sums", lambda: p.test_row_sumsq_exact_on_small_integers(1024)),
+            ("run-tree order", p.test_row_sumsq_order_is_the_run_tree),
+            ("hand-worked rounding sequence", p.test_rmsnorm_hand_worked_rounding_sequence)]
+
+
+def _r14_pins():
+    import test_oracle_pins as p
+    return [("closed forms", p.test_silu_closed_forms),
+            ("error bound over every bf16", p.test_silu_matches_the_mathematics_over_every_bf16_in_range),
+            ("layout and special inputs", p.test_swiglu_layout_and_special_inputs)]
+
+
+@pytest.mark.skipif(shutil.which("gcc") is None, reason="needs gcc to build the oracle variants")
+def test_unmodified_copy_meets_the_r9_and_r14_pins(tmp_path):
+    old = "  if (t > 150.0f) t = 150.0f;"
+    assert _pins_fail(tmp_path, old, old, _r9_pins() + _r14_pins()) == []
+
+
+@pytest.mark.skipif(shutil.which("gcc") is None, reason="needs gcc to build the oracle variants")
+@pytest.mark.parametrize("name,old,new", R9_MUTATIONS, ids=[m[0] for m in R9_MUTATIONS])
+def test_r9_pins_catch_a_deviation(tmp_path, name, old, new):
+    assert _pins_fail(tmp_path, old, new, _r9_pins()), f"no R9 pin detects: {name}"
+
+
+@pytest.mark.skipif(shutil.which("gcc") is None, reason="needs gcc to build the oracle variants")
+@pytest.mark.parametrize("name,old,new", R14_MUTATIONS, ids=[m[0] for m in R14_MUTATIONS])
+def test_r14_pins_catch_a_deviation(tmp_path, name, old, new):
+    assert _pins_fail(tmp_path, old, new, _r14_pins()), f"no R14 pin detects: {name}"

@@ -716,3 +716,21 @@ def test_swiglu_layout_and_special_inputs():
     h0 = bf16_bits_to_f32(oracle.swiglu(gu, I))
     assert np.all(h0 == 0.0)
 
+
+
+def test_rmsnorm_hand_worked_rounding_sequence():
+    """Reading R9's rounding sequence against a hand-worked example
+    (tests/golden/rmsnorm_examples.json): r in fp64 then fp32, then fp32(x r), then
+    fp32(. g), then bf16 round-to-nearest-even.  Row 0 puts an element exactly on a bf16
+    tie (the order of the two multiplies decides it), row 1 one fp32 ulp above one (r in
+    fp32 instead of fp64 decides it)."""
+    with open(os.path.join(os.path.dirname(__file__), "golden", "rmsnorm_examples.json")) as f:
+        ex = json.load(f)
+    K = ex["K"]
+    x = f32_to_bf16_bits(np.array([row["x"] for row in ex["rows"]], np.float32))
+    g = f32_to_bf16_bits(np.array(ex["gain"], np.float32))
+    assert np.array_equal(bf16_bits_to_f32(g), np.array(ex["gain"], np.float32))  # the gains are bf16 values
+    y, r = oracle.rmsnorm(x, g, ex["eps"])
+    for i, row in enumerate(ex["rows"]):
+        assert int(np.float32(r[i]).view(np.uint32)) == int(row["r_bits"], 16), f"row {i}: r"
+        assert [int(v) for v in y[i, :K]] == [int(b, 16) for b in row["y_bits"]], f"row {i}: y"
