@@ -11,9 +11,7 @@ NVFP4 rule is a reading of the pages (they name the format, not its arithmetic);
 two hand-worked NVFP4 examples fix its fp32 rounding sequence step by step, and a
 test plants each plausible deviation from it in a copy of the oracle and sees an
 example fail (likewise for the mask, the MX scale and rounding, the residual, the
-packing, the GEMM and the RMS normalization).  The SwiGLU's fp32 exponential is
-pinned only to within 4 ulps of the mathematical value: its exact bits are parity
-unpinned.
+packing, the GEMM, the RMS normalization and the SwiGLU).
 """
 import ctypes
 import os

@@ -68,11 +68,12 @@
  *
  * Pins (tests/test_oracle_pins.py, tests/test_oracle_mutations.py): every reading above is
  * checked against brute force, exact rational arithmetic, closed forms, invariants or a
- * hand-worked example, and a planted deviation from it fails one of them.  One part is
- * pinned only through an error bound: the fp32 steps of R14's exponential agree with the
- * mathematical SiLU to within 4 fp32 ulps (every bf16 gate in [-100, 100]) and on its
- * closed forms, but another correct evaluation (a library expf, a degree-6 polynomial)
- * stays within that bound, so those steps' exact bits are parity unpinned.
+ * hand-worked example, and a planted deviation from it fails one of them.  R14's fp32
+ * exponential is pinned by a hand-worked SwiGLU example where one fp32 ulp of it reaches
+ * h, and to within 4 fp32 ulps of the mathematical SiLU; other correct evaluations that
+ * differ from it in some fp32 SiLU values (glibc's expf, a degree-6 polynomial) give the
+ * same bf16 h for every bf16 up value in [2^-7, 2^8), so the path's output cannot tell
+ * them apart.
  *
  * Compile: gcc -O2 -ffp-contract=off -fno-fast-math -fopenmp -shared -fPIC.
  * The row loops carry an OpenMP pragma; every output element has a fixed

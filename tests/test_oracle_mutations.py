@@ -287,10 +287,12 @@ def test_exact_gemm_catches_a_deviation(tmp_path, name, old, new):
 # Deviations from reading R9 (RMS normalization folded into the preparation) and R14 (the
 # MLP block's SwiGLU), each planted in a copy of the oracle, which then serves the pins of
 # tests/test_oracle_pins.py (through the oracle module, its library swapped for the copy's):
-# at least one pin must fail.  Not caught, and so pinned only through their error bound
-# against the mathematical value: R14's exponential evaluated by another correct method
-# (a library expf, or a degree-6 instead of a degree-7 polynomial) -- both stay within the
-# 4-ulp bound of the fp64 SiLU that the pins check.
+# at least one pin must fail.  Not caught, because they never reach the path's output h:
+# R14's exponential evaluated by another correct method -- glibc's expf changes the fp32 SiLU
+# of 124 bf16 gates in [-60, 60], a degree-6 instead of a degree-7 polynomial of 174 -- gives
+# the same h for every bf16 up value in [2^-7, 2^8) (searched exhaustively), and both stay
+# within the 4-ulp bound of the fp64 SiLU that the pins check.  An exponential one fp32 ulp
+# off the reading's where that does reach h is caught by the hand-worked SwiGLU example.
 R9_MUTATIONS = [
     ("mean over K + 1", "    const float r = (float)(1.0 / sqrt(ss / (double)K + (double)eps));",
      "    const float r = (float)(1.0 / sqrt(ss / (double)(K + 1) + (double)eps));"),
@@ -314,6 +316,7 @@ R14_MUTATIONS = [
     ("ln 2 without its low part", "  const float r = (t - n * ln2_hi) - n * ln2_lo;",
      "  const float r = t - n * ln2_hi; (void)ln2_lo;"),
     ("exponent clamped at 80", "  if (t > 150.0f) t = 150.0f;", "  if (t > 80.0f) t = 80.0f;"),
+    ("exponential one ulp high", "  return ldexpf(p, (int)n);", "  return nextafterf(ldexpf(p, (int)n), INFINITY);"),
 ]
 
 
@@ -350,7 +353,8 @@ def _r14_pins():
     import test_oracle_pins as p
     return [("closed forms", p.test_silu_closed_forms),
             ("error bound over every bf16", p.test_silu_matches_the_mathematics_over_every_bf16_in_range),
-            ("layout and special inputs", p.test_swiglu_layout_and_special_inputs)]
+            ("layout and special inputs", p.test_swiglu_layout_and_special_inputs),
+            ("hand-worked example", p.test_swiglu_hand_worked_example)]
 
 
 @pytest.mark.skipif(shutil.which("gcc") is None, reason="needs gcc to build the oracle variants")

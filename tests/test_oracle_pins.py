@@ -734,3 +734,17 @@ def test_rmsnorm_hand_worked_rounding_sequence():
     for i, row in enumerate(ex["rows"]):
         assert int(np.float32(r[i]).view(np.uint32)) == int(row["r_bits"], 16), f"row {i}: r"
         assert [int(v) for v in y[i, :K]] == [int(b, 16) for b in row["y_bits"]], f"row {i}: y"
+
+
+def test_swiglu_hand_worked_example():
+    """Reading R14's fp32 steps against a hand-worked example
+    (tests/golden/swiglu_examples.json): the gate and up values put fp32(silu(g) u) one
+    ulp beyond a bf16 tie, so an exponential one fp32 ulp off the reading's changes h."""
+    with open(os.path.join(os.path.dirname(__file__), "golden", "swiglu_examples.json")) as f:
+        exs = json.load(f)["examples"]
+    for ex in exs:
+        g, u = np.float32(ex["gate"]), np.float32(ex["up"])
+        gu = f32_to_bf16_bits(np.array([[g, u]], np.float32))
+        assert np.array_equal(bf16_bits_to_f32(gu), np.array([[g, u]], np.float32))  # both are bf16 values
+        assert int(np.float32(oracle.silu(float(g))).view(np.uint32)) == int(ex["silu_bits"], 16)
+        assert int(oracle.swiglu(gu, 1)[0, 0]) == int(ex["h_bits"], 16)
