@@ -483,8 +483,8 @@ __global__ __launch_bounds__(kThreads, 1) void linear_mx_dma_kernel(Args a) {
   constexpr int kLoads = kFragLoads + 1;  // per wave and stage
   // load j of stage ks (a stage past the last K-step -- only the prologue's, when K has
   // fewer than three steps -- re-loads the last one into a slot nobody reads)
-  auto issue_one = [&](int j, int ks) {
-    uint8_t* st = smem + (ks % kDmaStages) * kDmaStageBytes;
+  auto issue_one = [&](int j, int ks, int slot) {
+    uint8_t* st = smem + slot * kDmaStageBytes;
     const int64_t kc = ks < nk ? ks : nk - 1;
     if (j < kFragLoads)
       buffer_lds16(fsrc[j] + kc * 2 * kFragBytes, kFragBytes, st + fdst[j], 16 * lane);
@@ -530,7 +530,7 @@ __global__ __launch_bounds__(kThreads, 1) void linear_mx_dma_kernel(Args a) {
   // The matrix instructions of one sub-step (16 with both paths and 256 columns); with
   // ISSUE, the loads of stage ld spread between them (one per kEvery instructions)
   auto mma = [&](const v4i (&af)[2][2], const v4i (&wf)[NT], const uint32_t (&as)[2][2], const uint32_t (&ws)[NT],
-                 auto sub_c, auto issue_c, int ld) {
+                 auto sub_c, auto issue_c, int ld, int slot) {
     constexpr int SUB = decltype(sub_c)::value;
     constexpr bool ISSUE = decltype(issue_c)::value;
     constexpr int kPerSub = 2 * NT * (2 - kOp0), kEvery = kPerSub / kLoads;
@@ -549,7 +549,7 @@ __global__ __launch_bounds__(kThreads, 1) void linear_mx_dma_kernel(Args a) {
           if constexpr (ISSUE) {
             const int i = ((p - kOp0) * 2 + mt) * NT + nt;
             if (i % kEvery == kEvery - 1 && i / kEvery < kLoads) {
-              issue_one(i / kEvery, ld);
+              issue_one(i / kEvery, ld, slot);
               __builtin_amdgcn_sched_barrier(0);  // keep the loads spread between the instructions
             }
           }
@@ -557,11 +557,11 @@ __global__ __launch_bounds__(kThreads, 1) void linear_mx_dma_kernel(Args a) {
   };
 
 #pragma unroll
-  for (int j = 0; j < kLoads; ++j) issue_one(j, 0);
+  for (int j = 0; j < kLoads; ++j) issue_one(j, 0, 0);
 #pragma unroll
-  for (int j = 0; j < kLoads; ++j) issue_one(j, 1);
+  for (int j = 0; j < kLoads; ++j) issue_one(j, 1, 1);
 #pragma unroll
-  for (int j = 0; j < kLoads; ++j) issue_one(j, 2);
+  for (int j = 0; j < kLoads; ++j) issue_one(j, 2, 2);
   SHARQ_WAIT_VMCNT(2 * kLoads);  // this wave's loads of stage 0 landed
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
@@ -575,15 +575,18 @@ __global__ __launch_bounds__(kThreads, 1) void linear_mx_dma_kernel(Args a) {
   using NoIssue = std::integral_constant<bool, false>;
   using Issue = std::integral_constant<bool, true>;
   // One K-step.  ISSUE: the loads of stage ks+3 go out during it; WAIT: the loads this
-  // wave may leave in flight at the barrier (the stage after ks has landed then).
-  auto kstep = [&](int ks, auto issue_c, auto wait_c) {
+  // wave may leave in flight at the barrier (the stage after ks has landed then); slot:
+  // ks % 3, the ring slot it reads and refills.  The loop runs whole rounds of the ring, so
+  // the slots -- and every LDS address -- are compile-time constants there.
+  auto kstep = [&](int ks, auto issue_c, auto wait_c, auto slot_c) {
     constexpr int WAIT = decltype(wait_c)::value;
-    const uint8_t* st = smem + (ks % kDmaStages) * kDmaStageBytes;
-    const uint8_t* nx = smem + ((ks + 1) % kDmaStages) * kDmaStageBytes;
+    const int S = slot_c;  // ks % 3: a constant in the unrolled loop
+    const uint8_t* st = smem + S * kDmaStageBytes;
+    const uint8_t* nx = smem + (S == kDmaStages - 1 ? 0 : S + 1) * kDmaStageBytes;
     // [A]
     read_frags(af1, wf1, st, 1);
     __builtin_amdgcn_sched_barrier(0);
-    mma(af0, wf0, as, ws, C0{}, NoIssue{}, 0);
+    mma(af0, wf0, as, ws, C0{}, NoIssue{}, 0, 0);
     // [B]
     __builtin_amdgcn_sched_barrier(0);
     SHARQ_WAIT_VMCNT(WAIT);              // this wave's loads of stage ks+1 landed
@@ -595,7 +598,7 @@ __global__ __launch_bounds__(kThreads, 1) void linear_mx_dma_kernel(Args a) {
     read_scales(asn, wsn, nx);
     read_frags(af0, wf0, nx, 0);
     __builtin_amdgcn_sched_barrier(0);
-    mma(af1, wf1, as, ws, C1{}, issue_c, ks + 3);
+    mma(af1, wf1, as, ws, C1{}, issue_c, ks + 3, S);
 #pragma unroll
     for (int p = 0; p < 2; ++p)
 #pragma unroll
@@ -608,10 +611,20 @@ __global__ __launch_bounds__(kThreads, 1) void linear_mx_dma_kernel(Args a) {
   // every K-step but the last three loads a stage three ahead; those three load nothing
   // (all the stages they read are in flight), so no stage past the last is fetched
   const int nmain = nk > 3 ? nk - 3 : 0;
-  for (int ks = 0; ks < nmain; ++ks) kstep(ks, Issue{}, Keep{});
-  if (nk >= 3) kstep(nk - 3, NoIssue{}, Keep{});
-  if (nk >= 2) kstep(nk - 2, NoIssue{}, None{});
-  kstep(nk - 1, NoIssue{}, None{});
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  using S2 = std::integral_constant<int, 2>;
+  int ks = 0;
+  for (; ks + 3 <= nmain; ks += 3) {  // one round of the stage ring: slots known at compile time
+    kstep(ks, Issue{}, Keep{}, S0{});
+    kstep(ks + 1, Issue{}, Keep{}, S1{});
+    kstep(ks + 2, Issue{}, Keep{}, S2{});
+  }
+  if (ks < nmain) kstep(ks++, Issue{}, Keep{}, S0{});
+  if (ks < nmain) kstep(ks++, Issue{}, Keep{}, S1{});
+  if (nk >= 3) kstep(nk - 3, NoIssue{}, Keep{}, (nk - 3) % kDmaStages);
+  if (nk >= 2) kstep(nk - 2, NoIssue{}, None{}, (nk - 2) % kDmaStages);
+  kstep(nk - 1, NoIssue{}, None{}, (nk - 1) % kDmaStages);
   SHARQ_WAIT_VMCNT(0);  // trailing loads land before the stage ring is reused
 
   __syncthreads();  // every wave is done with the stage ring; reuse it for the epilogue
