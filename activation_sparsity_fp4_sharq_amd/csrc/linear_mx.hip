@@ -483,11 +483,19 @@ __global__ __launch_bounds__(kThreads, 1) void linear_mx_dma_kernel(Args a) {
   constexpr int kLoads = kFragLoads + 1;  // per wave and stage
   // load j of stage ks (a stage past the last K-step -- only the prologue's, when K has
   // fewer than three steps -- re-loads the last one into a slot nobody reads)
+  // the fragment loads go through loop-invariant resources over the tile's whole K range
+  // (the K-step is the scalar offset), the scale block through one per K-step
+  __amdgpu_buffer_rsrc_t frsrc[6];
+#pragma unroll
+  for (int j = 0; j < kFragLoads; ++j)
+    frsrc[j] = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(fsrc[j]), 0,
+                                                 (uint32_t)nk * 2u * (uint32_t)kFragBytes, kRsrcWord3);
   auto issue_one = [&](int j, int ks, int slot) {
     uint8_t* st = smem + slot * kDmaStageBytes;
     const int64_t kc = ks < nk ? ks : nk - 1;
     if (j < kFragLoads)
-      buffer_lds16(fsrc[j] + kc * 2 * kFragBytes, kFragBytes, st + fdst[j], 16 * lane);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(frsrc[j], (lds_void_t*)(st + fdst[j]), 16, 16 * lane,
+                                               (int)(kc * 2 * kFragBytes), 0, 0);
     else
       buffer_lds16(ssrc + kc * sstep, sbytes, st + sdst, 16 * lane);
   };

@@ -40,6 +40,9 @@ void* scratch_address(int dev) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// The tiled GEMM addresses a row tile's whole K range with 32-bit buffer offsets.
+constexpr int64_t kMaxTiledGemmK = (int64_t)1 << 27;
+
 int block_of(int fmt) { return fmt == SHARQ_MXFP4 ? 32 : 16; }
 
 sharq_status check_format(int fmt) {
@@ -124,6 +127,7 @@ static sharq_status check_forward(const void* x, int64_t M, int64_t K, int64_t l
   if ((s = check_payload(residual, fmt, M)) != SHARQ_OK) return s;
   if ((s = check_payload(weight, fmt, N)) != SHARQ_OK) return s;
   if (backbone->layout != residual->layout || backbone->layout != weight->layout) return SHARQ_E_FORMAT;
+  if (backbone->layout == SHARQ_LAYOUT_TILED && K > kMaxTiledGemmK) return SHARQ_E_SHAPE;
   if (M > 0 && !y) return SHARQ_E_NULL;
   if (reinterpret_cast<uintptr_t>(y) & (out_dtype == SHARQ_OUT_FP32 ? 3u : 1u)) return SHARQ_E_ALIGN;
   const size_t np = sharq_prep_workspace_bytes(M, K, fmt);
@@ -147,6 +151,7 @@ static sharq_status linear_common(const sharq_fp4* backbone, const sharq_fp4* re
   if ((s = check_payload(residual, fmt, M)) != SHARQ_OK) return s;
   if (residual->layout != weight->layout || (backbone && backbone->layout != residual->layout))
     return SHARQ_E_FORMAT;
+  if (residual->layout == SHARQ_LAYOUT_TILED && K > kMaxTiledGemmK) return SHARQ_E_SHAPE;
   if (M > 0) {
     if (!y) return SHARQ_E_NULL;
     if (reinterpret_cast<uintptr_t>(y) & (out_dtype == SHARQ_OUT_FP32 ? 3u : 1u)) return SHARQ_E_ALIGN;

@@ -262,7 +262,9 @@ sharq_status sharq_prep_rmsnorm(const void* x, int64_t M, int64_t K, int64_t ldx
  *   backbone, residual  payloads [M, K] from sharq_prep (same format)
  *   weight              payload [N, K] (e.g. from sharq_quantize)
  *                       MXFP4 runs its fast pipelined kernel when all three payloads
- *                       are tiled; any row-major payload takes a slower generic kernel.
+ *                       are tiled (then K <= 2^27, else SHARQ_E_SHAPE: the kernel addresses
+ *                       a row tile's K range with 32-bit offsets); any row-major payload
+ *                       takes a slower generic kernel.
  *   y                   device [M, ldy] bf16 (round to nearest even) or fp32; ldy >= N;
  *                       aligned to its element size
  *   workspace           device, >= sharq_linear_workspace_bytes(M, N, K, fmt) bytes; with

@@ -156,6 +156,23 @@ def test_linear_dense_rejects(kwargs, status):
     assert linear_dense(**kwargs) == status
 
 
+def test_tiled_gemm_k_limit():
+    """Tiled payloads: the pipelined GEMM addresses a row tile's K range with 32-bit
+    offsets, so K above 2^27 is rejected before anything runs (row-major payloads keep the
+    general 2^30 limit); K = 2^27 passes every shape check."""
+    import torch
+    t = dict(bb=fp4(layout=1), rr=fp4(layout=1), w=fp4(layout=1))
+    assert linear(K=(1 << 27) + 32, **t) == E_SHAPE
+    assert linear_dense(K=(1 << 27) + 32, a=fp4(layout=1), w=fp4(layout=1)) == E_SHAPE
+    L = sharq.lib()
+    bb, rr, w = fp4(layout=1), fp4(layout=1), fp4(layout=1)
+    assert L.sharq_forward(A, 4, (1 << 27) + 32, (1 << 27) + 32, 2, 4, 0, ctypes.byref(bb), ctypes.byref(rr),
+                           ctypes.byref(w), 8, A, 8, 0, None, 0, None) == E_SHAPE
+    if not torch.cuda.is_available():
+        assert linear(K=1 << 27, **t) == E_DEVICE
+        assert linear(K=(1 << 27) + 32) == E_DEVICE  # row-major: past every shape check
+
+
 def test_linear_null_backbone_is_rejected():
     rr, w = fp4(), fp4()
     assert sharq.lib().sharq_linear(None, ctypes.byref(rr), 4, ctypes.byref(w), 8, 64, 0, A, 8, 0, None, 0,
