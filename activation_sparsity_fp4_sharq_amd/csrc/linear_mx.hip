@@ -526,6 +526,18 @@ __global__ __launch_bounds__(kThreads, 1) void linear_mx_dma_kernel(Args a) {
       wf[nt] = *reinterpret_cast<const v4i*>(st + 2 * kOpTileBytes + ((wn * NT + nt) * 2 + sub) * kFragBytes +
                                              lane * 16);
   };
+  // Fragment j of sub-step 0 in read_frags' order (the activation fragments, then the weight's)
+  constexpr int kReads = 2 * (2 - kOp0) + NT;
+  auto read_one = [&](v4i (&af)[2][2], v4i (&wf)[NT], const uint8_t* st, int j) {
+    constexpr int na = 2 * (2 - kOp0);
+    if (j < na) {
+      const int p = kOp0 + j / 2, mt = j % 2;
+      af[p][mt] = *reinterpret_cast<const v4i*>(st + p * kOpTileBytes + ((wm * 2 + mt) * 2) * kFragBytes + lane * 16);
+    } else {
+      const int nt = j - na;
+      wf[nt] = *reinterpret_cast<const v4i*>(st + 2 * kOpTileBytes + ((wn * NT + nt) * 2) * kFragBytes + lane * 16);
+    }
+  };
   auto read_scales = [&](uint32_t (&as)[2][2], uint32_t (&ws)[NT], const uint8_t* st) {
     const uint32_t* sc = reinterpret_cast<const uint32_t*>(st + 3 * kOpTileBytes);
 #pragma unroll
@@ -535,12 +547,18 @@ __global__ __launch_bounds__(kThreads, 1) void linear_mx_dma_kernel(Args a) {
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) ws[nt] = sc[512 + wn * (TN / 2) + nt * 32 + r32];
   };
-  // The matrix instructions of one sub-step (16 with both paths and 256 columns); with
-  // ISSUE, the loads of stage ld spread between them (one per kEvery instructions)
+  // The matrix instructions of one sub-step (16 with both paths and 256 columns).  With
+  // ISSUE, the loads of stage ld spread between them (one per kEvery instructions), and
+  // the LDS stage rst's sub-step-0 fragments (into raf / rwf, one after each of the first
+  // kReads instructions) and scale words (ras / rws, after the next one) are read between
+  // them instead of all ahead of them, so that the LDS issue queue never holds the wave
+  // back before its first matrix instruction.
   auto mma = [&](const v4i (&af)[2][2], const v4i (&wf)[NT], const uint32_t (&as)[2][2], const uint32_t (&ws)[NT],
-                 auto sub_c, auto issue_c, int ld, int slot) {
+                 auto sub_c, auto issue_c, int ld, int slot, v4i (&raf)[2][2], v4i (&rwf)[NT], const uint8_t* rst,
+                 uint32_t (&ras)[2][2], uint32_t (&rws)[NT]) {
     constexpr int SUB = decltype(sub_c)::value;
     constexpr bool ISSUE = decltype(issue_c)::value;
+    static_assert(2 * NT * (2 - kOp0) >= kReads, "one fragment read per matrix instruction");
     constexpr int kPerSub = 2 * NT * (2 - kOp0), kEvery = kPerSub / kLoads;
     static_assert(kEvery >= 1 && kPerSub / kEvery >= kLoads, "every load of a stage must be issued");
 #pragma unroll
@@ -556,6 +574,8 @@ __global__ __launch_bounds__(kThreads, 1) void linear_mx_dma_kernel(Args a) {
               (int)(as[p][mt] >> (8 * h)));
           if constexpr (ISSUE) {
             const int i = ((p - kOp0) * 2 + mt) * NT + nt;
+            if (i < kReads) read_one(raf, rwf, rst, i);
+            if (i == kReads) read_scales(ras, rws, rst);
             if (i % kEvery == kEvery - 1 && i / kEvery < kLoads) {
               issue_one(i / kEvery, ld, slot);
               __builtin_amdgcn_sched_barrier(0);  // keep the loads spread between the instructions
@@ -592,9 +612,16 @@ __global__ __launch_bounds__(kThreads, 1) void linear_mx_dma_kernel(Args a) {
     const uint8_t* st = smem + S * kDmaStageBytes;
     const uint8_t* nx = smem + (S == kDmaStages - 1 ? 0 : S + 1) * kDmaStageBytes;
     // [A]
+    // sub-step 1's fragments, one read after each of the first sub-step-0 instructions (the
+    // scheduling groups: 1 matrix instruction, 1 LDS read, ..., then the remaining ones)
     read_frags(af1, wf1, st, 1);
-    __builtin_amdgcn_sched_barrier(0);
-    mma(af0, wf0, as, ws, C0{}, NoIssue{}, 0, 0);
+    mma(af0, wf0, as, ws, C0{}, NoIssue{}, 0, 0, af0, wf0, st, asn, wsn);  // (no ISSUE: reads nothing)
+#pragma unroll
+    for (int i = 0; i < kReads; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 2 * NT * (2 - kOp0) - kReads, 0);
     // [B]
     __builtin_amdgcn_sched_barrier(0);
     SHARQ_WAIT_VMCNT(WAIT);              // this wave's loads of stage ks+1 landed
@@ -603,10 +630,14 @@ __global__ __launch_bounds__(kThreads, 1) void linear_mx_dma_kernel(Args a) {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
     __builtin_amdgcn_sched_barrier(0);
     // [C]
-    read_scales(asn, wsn, nx);
-    read_frags(af0, wf0, nx, 0);
+    // the next stage's sub-step-0 fragments and scale words: inside the mma when it issues
+    // loads, ahead of it otherwise
+    if constexpr (!decltype(issue_c)::value) {
+      read_scales(asn, wsn, nx);
+      read_frags(af0, wf0, nx, 0);
+    }
     __builtin_amdgcn_sched_barrier(0);
-    mma(af1, wf1, as, ws, C1{}, issue_c, ks + 3, S);
+    mma(af1, wf1, as, ws, C1{}, issue_c, ks + 3, S, af0, wf0, nx, asn, wsn);
 #pragma unroll
     for (int p = 0; p < 2; ++p)
 #pragma unroll
