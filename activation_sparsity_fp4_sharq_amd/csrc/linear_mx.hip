@@ -78,6 +78,17 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   return (uint16_t)(u >> 16);
 }
 
+// Two fp32 values to two bf16 (a in the low half) in one gfx950 packed conversion
+// (v_cvt_pk_bf16_f32): round to nearest even, so on every finite fp32 value the same
+// bits as f32_to_bf16_rne (sharq_bf16_rounding_probe runs all 2^32 patterns through the
+// same conversion on the device).  One instruction per pair against about six.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t f32x2_to_bf16x2_rne(float a, float b) {
+  const f32x2_t p = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(p, bf16x2_t));
+}
+
 // The hardware hands work-group id to XCD id % 8; renumber the ids so that each XCD's
 // share of the `total` ids is one contiguous run.
 __device__ __forceinline__ int xcd_contiguous(int id, int total) {
@@ -318,8 +329,8 @@ __device__ __forceinline__ void store_swapped(const Args& a, const v16f (&acc)[M
         for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
-            const uint32_t lo = f32_to_bf16_rne(acc[mt][nt][4 * g]) | ((uint32_t)f32_to_bf16_rne(acc[mt][nt][4 * g + 1]) << 16);
-            const uint32_t hi = f32_to_bf16_rne(acc[mt][nt][4 * g + 2]) | ((uint32_t)f32_to_bf16_rne(acc[mt][nt][4 * g + 3]) << 16);
+            const uint32_t lo = f32x2_to_bf16x2_rne(acc[mt][nt][4 * g], acc[mt][nt][4 * g + 1]);
+            const uint32_t hi = f32x2_to_bf16x2_rne(acc[mt][nt][4 * g + 2], acc[mt][nt][4 * g + 3]);
             *reinterpret_cast<uint2*>(lds + (mt * 32 + r32) * pitch + (nt * 32 + 8 * g + 4 * h) * 2) = make_uint2(lo, hi);
           }
       constexpr int lanes_per_row = 32 * NT * 2 / 16;
